@@ -1,0 +1,233 @@
+"""CPU oracle for the fused mixed-precision clip + multi-tensor AdamW step.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path never imports this
+package, and this package imports nothing from the product.
+
+The arithmetic lives in ``mta_oracle.c`` (plain loops, one IEEE float32
+operation at a time, compiled without FMA contraction); this module marshals
+numpy arrays into it and drives a whole tensor list in list order.
+
+Sources, by page title and section:
+  * "Mica 7.7: a training step on the card, in every float type",
+    "The whole model in one call": ClipGradNorms (joint L2 norm, one cap),
+    AdamWSteps (each group updated as AdamWStep alone), ScaleTensors.
+  * "BendTorch main.bend", "Optimizers": the Adam-family element arithmetic
+    in PyTorch's order, the packed-bfloat16 moments, the bias-correction
+    scalars; "Training": q1 = 1 - b1^t, q2 = 1 - b2^t with t = 1 first.
+
+Layouts accepted here:
+  * float32 arrays: ``numpy.float32``;
+  * bfloat16 gradients: ``numpy.uint16`` bit patterns, one per element;
+  * packed bfloat16 moments: ``numpy.uint32`` words, ceil(n / 2) of them,
+    element 2k in the low half of word k.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py``
+against values fixed by the pages or by mathematics (closed forms, exact
+sums, hand-computed steps, library routines for the special cases they
+share).  Nothing here is "parity unpinned" except bitwise agreement with
+PyTorch's own kernels, which the pages do not fix.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+MOM_F32, MOM_BF16X2 = 0, 1
+
+_lib = None
+
+
+def lib():
+    """Load the oracle library, compiling it first if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        vp, i64, f32, f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_double)
+        L.mto_bf16_of_bits.argtypes = [ctypes.c_uint32]
+        L.mto_bf16_of_bits.restype = ctypes.c_uint32
+        L.mto_f32_of_bf16.argtypes = [ctypes.c_uint32]
+        L.mto_f32_of_bf16.restype = f32
+        L.mto_bf16_of_bits_array.argtypes = [i64, vp, vp]
+        L.mto_bf16_of_bits_array.restype = None
+        L.mto_scalars.argtypes = [f64, f64, f64, f64, f64, i64, vp]
+        L.mto_scalars.restype = None
+        L.mto_scale_tensor.argtypes = [i64, vp, ctypes.c_int, f32]
+        L.mto_scale_tensor.restype = None
+        L.mto_sumsq_accumulate.argtypes = [i64, vp, ctypes.c_int, f32, vp]
+        L.mto_sumsq_accumulate.restype = None
+        L.mto_clip_coef.argtypes = [f32, f32]
+        L.mto_clip_coef.restype = f32
+        L.mto_adamw_tensor.argtypes = [i64, vp, vp, ctypes.c_int, vp,
+                                       ctypes.c_int, vp, ctypes.c_int, f32,
+                                       f32, vp]
+        L.mto_adamw_tensor.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a, dtype):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype:
+        raise TypeError(f"expected a numpy {np.dtype(dtype).name} array")
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("array must be C-contiguous")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _grad_dtype(gtype):
+    return np.uint16 if gtype == BF16 else np.float32
+
+
+def _mom_dtype(kind):
+    return np.uint32 if kind == MOM_BF16X2 else np.float32
+
+
+def packed_words(n):
+    """Number of u32 words that hold n packed bfloat16 values: ceil(n/2)."""
+    return (n + 1) // 2
+
+
+# ---------------------------------------------------------------- bfloat16
+
+def bf16_of_bits(u):
+    """float32 bit pattern -> bfloat16 bit pattern (RNE, NaN -> 0xFFFF)."""
+    return int(lib().mto_bf16_of_bits(int(u) & 0xFFFFFFFF))
+
+
+def bf16_of_f32(x):
+    """Round a float32 array to bfloat16 bit patterns (numpy uint16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().mto_bf16_of_bits_array(x.size, _ptr(x.view(np.uint32), np.uint32),
+                                 _ptr(out, np.uint16))
+    return out
+
+
+def f32_of_bf16(h):
+    """bfloat16 bit patterns -> float32 (exact: the bits move up 16)."""
+    h = np.asarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def unpack_words(words, n):
+    """Packed u32 words -> n bfloat16 bit patterns, element order."""
+    words = np.asarray(words, dtype=np.uint32)
+    out = np.empty(2 * words.size, dtype=np.uint16)
+    out[0::2] = (words & np.uint32(0xFFFF)).astype(np.uint16)
+    out[1::2] = (words >> np.uint32(16)).astype(np.uint16)
+    return out[:n]
+
+
+def pack_halves(h):
+    """n bfloat16 bit patterns -> ceil(n/2) u32 words (pad half zero)."""
+    h = np.asarray(h, dtype=np.uint16)
+    n = h.size
+    padded = np.zeros(2 * packed_words(n), dtype=np.uint32)
+    padded[:n] = h
+    return (padded[0::2] | (padded[1::2] << np.uint32(16))).astype(np.uint32)
+
+
+# ---------------------------------------------------------------- scalars
+
+def scalars(lr, beta1, beta2, eps, weight_decay, t):
+    """{step, bc2, c1, c2, b2, eps, dec} as float32, formed in float64."""
+    if t < 1:
+        raise ValueError("t counts from 1")
+    out = np.zeros(7, dtype=np.float32)
+    lib().mto_scalars(lr, beta1, beta2, eps, weight_decay, int(t),
+                      _ptr(out, np.float32))
+    return out
+
+
+SCALAR_NAMES = ("step", "bc2", "c1", "c2", "b2", "eps", "dec")
+
+
+# ---------------------------------------------------------------- scale
+
+def scale_(g, gtype, s):
+    """ScaleTensors in place on one gradient array (bf16 rounds back)."""
+    lib().mto_scale_tensor(g.size, _ptr(g, _grad_dtype(gtype)), gtype,
+                           float(s))
+
+
+# ---------------------------------------------------------------- norm
+
+def sumsq(grads, gtype, s=1.0):
+    """Joint sum of squares of f32(g*s) over a list of gradient arrays."""
+    state = np.zeros(2, dtype=np.float64)
+    L = lib()
+    for g in grads:
+        L.mto_sumsq_accumulate(g.size, _ptr(g, _grad_dtype(gtype)), gtype,
+                               float(s), _ptr(state, np.float64))
+    return float(state[0] + state[1])
+
+
+def norm(grads, gtype, s=1.0):
+    """Joint L2 norm (float64, effectively exact)."""
+    return math.sqrt(sumsq(grads, gtype, s))
+
+
+def clip_coef(max_norm, norm_f32):
+    """min(1, max/(norm + 1e-6)) in float32; NaN passes through."""
+    return np.float32(lib().mto_clip_coef(float(np.float32(max_norm)),
+                                          float(np.float32(norm_f32))))
+
+
+# ---------------------------------------------------------------- AdamW
+
+def adamw_(w, g, m, v, gtype, mkind, vkind, sc, s=1.0, coef=1.0):
+    """One AdamW step over one tensor, in place on w, m, v."""
+    n = w.size
+    if g.size != n:
+        raise ValueError("gradient size differs from the weight's")
+    for buf, kind in ((m, mkind), (v, vkind)):
+        want = packed_words(n) if kind == MOM_BF16X2 else n
+        if buf.size != want:
+            raise ValueError("moment buffer has the wrong size")
+    sc = np.ascontiguousarray(sc, dtype=np.float32)
+    lib().mto_adamw_tensor(n, _ptr(w, np.float32), _ptr(g, _grad_dtype(gtype)),
+                           gtype, _ptr(m, _mom_dtype(mkind)), mkind,
+                           _ptr(v, _mom_dtype(vkind)), vkind,
+                           float(np.float32(s)), float(np.float32(coef)),
+                           _ptr(sc, np.float32))
+
+
+class Tensor:
+    """One parameter group: weight, gradient and the two moments."""
+
+    def __init__(self, w, g, m, v):
+        self.w, self.g, self.m, self.v = w, g, m, v
+
+    @property
+    def n(self):
+        return self.w.size
+
+
+def step_(tensors, gtype, mkind, vkind, lr, beta1, beta2, eps, weight_decay,
+          t, s=1.0, max_norm=None, coef=None):
+    """The whole step over a tensor list, in list order.
+
+    Unscale by ``s`` (in registers), clip by the joint norm when
+    ``max_norm`` is given, then AdamW every group.  ``coef`` overrides the
+    coefficient the oracle would compute (used to compare against a device
+    run in lockstep).  Returns ``(norm_f64, coef_f32)``; the norm is None
+    when no clip is asked for.
+    """
+    nrm = None
+    c = np.float32(1.0)
+    if max_norm is not None:
+        nrm = norm([x.g for x in tensors], gtype, s)
+        c = clip_coef(max_norm, np.float32(nrm))
+    if coef is not None:
+        c = np.float32(coef)
+    sc = scalars(lr, beta1, beta2, eps, weight_decay, t)
+    for x in tensors:
+        adamw_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c)
+    return nrm, c

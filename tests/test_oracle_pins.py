@@ -1,0 +1,563 @@
+"""Pins for the CPU oracle: values fixed by the pages or by mathematics.
+
+None of these compares the oracle with a retyped copy of itself.  They use
+hand-derived exact steps (tests/golden), closed forms of the AdamW
+recurrence, exact sums (math.fsum), an independent distance-based
+nearest-even rounding, and library routines (torch) for the special cases
+they share with the method.  Each test names the page passage it pins.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def f32bits(x):
+    return int(np.asarray(x, dtype=np.float32).view(np.uint32))
+
+
+def ulp_dist(a, b):
+    """ulp distance between float32 arrays (monotone integer map)."""
+    a = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
+    a = np.where(a < 0, -(a & 0x7FFFFFFF), a)
+    b = np.where(b < 0, -(b & 0x7FFFFFFF), b)
+    return np.abs(a - b)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding ("BendTorch main.bend", Optimizers, ph_of_bits / ph_to)
+# ---------------------------------------------------------------------------
+
+def test_bf16_golden_cases():
+    for row in _golden_rows("bf16_cases.txt"):
+        u, h = int(row[0], 16), int(row[1], 16)
+        assert O.bf16_of_bits(u) == h, row
+
+
+def _rne_by_distance(bits):
+    """Nearest-even bfloat16 by comparing exact distances (no bit tricks
+    beyond truncation): an independent reference for non-NaN inputs."""
+    bits = bits.astype(np.uint32)
+    x = bits.view(np.float32).astype(np.float64)
+    lo = (bits >> np.uint32(16)).astype(np.uint32)        # toward zero
+    hi = lo + np.uint32(1)                                  # away from zero
+    vlo = (lo << np.uint32(16)).view(np.float32).astype(np.float64)
+    hi_exp_all_ones = (hi & np.uint32(0x7F80)) == np.uint32(0x7F80)
+    with np.errstate(invalid="ignore"):
+        vhi = np.where(hi_exp_all_ones,
+                       np.copysign(2.0 ** 128, x),
+                       (hi << np.uint32(16)).view(np.float32)
+                       .astype(np.float64))
+    with np.errstate(invalid="ignore"):
+        dlo = np.abs(x - vlo)
+        dhi = np.abs(vhi - x)
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((lo & np.uint32(1)) == 1))
+    out = np.where(pick_hi, hi, lo)
+    inf = np.isinf(x)
+    out = np.where(inf, lo, out)
+    return out.astype(np.uint32)
+
+
+def test_bf16_rne_against_distance_rounding():
+    # every bfloat16 high half, with low halves that cover exact values,
+    # ties, both sides of a tie and the extremes, plus random ones
+    rng = np.random.default_rng(20261202)
+    lows = np.concatenate([
+        np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000,
+                  0xC000], dtype=np.uint32),
+        rng.integers(0, 0x10000, size=24, dtype=np.uint32)])
+    highs = np.arange(0x10000, dtype=np.uint32)
+    bits = (highs[:, None] << np.uint32(16) | lows[None, :]).ravel()
+    x = bits.view(np.float32)
+    got = O.bf16_of_f32(x).astype(np.uint32)
+    nan = np.isnan(x)
+    assert np.all(got[nan] == 0xFFFF)
+    want = _rne_by_distance(bits[~nan])
+    bad = np.nonzero(got[~nan] != want)[0]
+    assert bad.size == 0, [hex(int(b)) for b in bits[~nan][bad[:5]]]
+
+
+def test_bf16_rne_matches_torch_on_finite():
+    # torch's float32 -> bfloat16 conversion is round-to-nearest-even too;
+    # it differs only in the NaN pattern it writes
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(
+        np.uint32)
+    x = bits.view(np.float32)
+    keep = ~np.isnan(x)
+    x = x[keep]
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_of_f32(x), ref)
+
+
+def test_bf16_round_trip_identity():
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    x = O.f32_of_bf16(h)
+    back = O.bf16_of_f32(x)
+    nan = np.isnan(x)
+    assert np.array_equal(back[~nan], h[~nan])
+    assert np.all(back[nan] == 0xFFFF)
+    # bf16 -> f32 is the value torch gives for the same bits
+    t = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float()
+    tn = t.numpy()
+    assert np.array_equal(tn[~nan].view(np.uint32), x[~nan].view(np.uint32))
+
+
+def test_packed_layout_is_little_endian_bf16_array():
+    # PTree comment: element 2k in the low half of word k.  That is exactly
+    # the memory of a bfloat16 array of n elements on a little-endian host.
+    h = np.array([0x1111, 0x2222, 0x3333, 0x4444, 0x5555], dtype=np.uint16)
+    words = O.pack_halves(h)
+    assert [hex(int(w)) for w in words] == ["0x22221111", "0x44443333",
+                                            "0x5555"]
+    assert np.array_equal(words[:2].view(np.uint16), h[:4])
+    assert np.array_equal(O.unpack_words(words, 5), h)
+
+
+# ---------------------------------------------------------------------------
+# scalars ("BendTorch main.bend": Opt type comment, Opt.at, comment on
+# adam_m; Training: q1 = 1 - b1^t, q2 = 1 - b2^t, t = 1 first)
+# ---------------------------------------------------------------------------
+
+def _f32_nearest(fr):
+    """The float32 nearest to an exact Fraction (via float64 is enough for
+    these magnitudes only when no double rounding occurs; checked below by
+    comparing neighbours exactly)."""
+    cand = np.float32(float(fr))
+    best, bd = cand, abs(Fraction(float(cand)) - fr)
+    for nb in (np.nextafter(cand, np.float32(np.inf)),
+               np.nextafter(cand, np.float32(-np.inf))):
+        d = abs(Fraction(float(nb)) - fr)
+        if d < bd:
+            best, bd = nb, d
+    return best
+
+
+def test_scalars_first_step_closed_form():
+    sc = dict(zip(O.SCALAR_NAMES, O.scalars(3e-4, 0.9, 0.999, 1e-8, 0.1, 1)))
+    # t = 1: step = lr / (1 - b1) = 0.003, bc2 = sqrt(0.001)
+    assert sc["step"] == np.float32(0.003)
+    assert sc["bc2"] == np.float32(0.0316227766016838)   # sqrt(1/1000)
+    assert sc["c1"] == np.float32(0.1)
+    assert sc["c2"] == np.float32(0.001)
+    assert sc["b2"] == np.float32(0.999)
+    assert sc["eps"] == np.float32(1e-8)
+    assert sc["dec"] == np.float32(0.99997)               # 1 - 3e-4 * 0.1
+
+
+def test_scalars_late_steps_tend_to_lr_and_one():
+    sc = dict(zip(O.SCALAR_NAMES,
+                  O.scalars(3e-4, 0.9, 0.999, 1e-8, 0.1, 10 ** 6)))
+    assert sc["step"] == np.float32(3e-4)
+    assert sc["bc2"] == np.float32(1.0)
+
+
+def test_c2_formed_in_float64_not_float32():
+    # comment on adam_m: 1 - b2 taken in F32 from b2 = 0.999 is 1.3e-5 too
+    # small; the constant must be the float32 nearest 0.001 instead
+    c2 = O.scalars(3e-4, 0.9, 0.999, 1e-8, 0.1, 1)[3]
+    assert c2 == np.float32(0.001)
+    f32_way = np.float32(1.0) - np.float32(0.999)
+    rel = (float(f32_way) - 0.001) / 0.001
+    assert -1.35e-5 < rel < -1.25e-5        # the page's 1.3e-5, too small
+    assert f32_way != c2
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 10, 100, 1000, 12345])
+def test_scalars_against_exact_rationals(t):
+    lr, b1, b2, wd = 3e-4, 0.9, 0.999, 0.1
+    sc = dict(zip(O.SCALAR_NAMES, O.scalars(lr, b1, b2, 1e-8, wd, t)))
+    L, B1, B2, WD = (Fraction(x) for x in (lr, b1, b2, wd))
+    step = L / (1 - B1 ** t)
+    # float64 pow and division then one float32 rounding: within 1 ulp of
+    # the float32 nearest the exact value
+    assert ulp_dist(sc["step"], _f32_nearest(step)) <= 1
+    bc2_sq = 1 - B2 ** t
+    near = _f32_nearest(Fraction(math.sqrt(float(bc2_sq))))
+    assert ulp_dist(sc["bc2"], near) <= 1
+    # and bc2^2 brackets 1 - b2^t
+    lo = Fraction(float(np.nextafter(sc["bc2"], np.float32(0))))
+    hi = Fraction(float(np.nextafter(sc["bc2"], np.float32(2))))
+    assert lo * lo < bc2_sq < hi * hi
+    assert sc["dec"] == _f32_nearest(1 - L * WD)
+    assert sc["c1"] == _f32_nearest(1 - B1)
+    assert sc["c2"] == _f32_nearest(1 - B2)
+
+
+def test_scalars_reject_step_zero():
+    with pytest.raises(ValueError):
+        O.scalars(3e-4, 0.9, 0.999, 1e-8, 0.1, 0)
+
+
+# ---------------------------------------------------------------------------
+# AdamW element steps (hand-derived, exact)
+# ---------------------------------------------------------------------------
+
+def _kind(s):
+    return O.MOM_BF16X2 if s == "bf16x2" else O.MOM_F32
+
+
+def _mom_buf(kind, val):
+    if kind == O.MOM_BF16X2:
+        return O.pack_halves(O.bf16_of_f32(np.array([val], np.float32)))
+    return np.array([val], dtype=np.float32)
+
+
+def _mom_val(kind, buf):
+    if kind == O.MOM_BF16X2:
+        return float(O.f32_of_bf16(O.unpack_words(buf, 1))[0])
+    return float(buf[0])
+
+
+@pytest.mark.parametrize("row", _golden_rows("hand_steps.txt"),
+                         ids=lambda r: f"{r[0]}-t{r[1]}")
+def test_hand_derived_steps(row):
+    case, t, mk, vk, eps, w0, g0, m0, v0, w1, m1, v1 = row
+    mkind, vkind = _kind(mk), _kind(vk)
+    w = np.array([float(w0)], np.float32)
+    g = np.array([float(g0)], np.float32)
+    assert float(g[0]) == float(Fraction(g0))          # exact input
+    m, v = _mom_buf(mkind, float(m0)), _mom_buf(vkind, float(v0))
+    sc = O.scalars(0.125, 0.5, 0.75, float(eps), 0.5, int(t))
+    O.adamw_(w, g, m, v, O.F32, mkind, vkind, sc)
+    assert float(w[0]) == float(Fraction(w1))
+    assert _mom_val(mkind, m) == float(Fraction(m1))
+    assert _mom_val(vkind, v) == float(Fraction(v1))
+
+
+def test_packed_element_layout_and_pad_half_untouched():
+    # g_k = 2^-k with c1 = 0.5 gives m_k = 2^-(k+1), exact in bfloat16:
+    # bits 0x3F00 - 0x80*k.  Element 2k sits in the low half of word k and
+    # the pad half of the last word keeps whatever it held.
+    n = 5
+    g = np.array([2.0 ** -k for k in range(n)], np.float32)
+    w = np.ones(n, np.float32)
+    m = np.zeros(3, np.uint32)
+    v = np.zeros(3, np.uint32)
+    m[2] = 0xBEEF0000
+    v[2] = 0xCAFE0000
+    sc = O.scalars(0.125, 0.5, 0.75, 0.5, 0.5, 1)
+    O.adamw_(w, g, m, v, O.F32, O.MOM_BF16X2, O.MOM_BF16X2, sc)
+    want = [0x3F00 - 0x80 * k for k in range(n)]
+    assert int(m[0]) == (want[1] << 16) | want[0]
+    assert int(m[1]) == (want[3] << 16) | want[2]
+    assert int(m[2]) == 0xBEEF0000 | want[4]
+    assert int(v[2]) >> 16 == 0xCAFE
+
+
+# ---------------------------------------------------------------------------
+# AdamW against the textbook recurrence (closed forms; float64)
+# ---------------------------------------------------------------------------
+
+def test_first_step_closed_form():
+    # From zero moments at t = 1, exact arithmetic gives
+    #   w1 = w * (1 - lr*wd) - lr * g / (|g| + eps)
+    rng = np.random.default_rng(1)
+    n = 4096
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    g = rng.normal(0, 1e-3, n).astype(np.float32)
+    g[:16] = 0.0
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.999, 1e-8, 0.1
+    want = (w.astype(np.float64) * (1 - lr * wd)
+            - lr * g.astype(np.float64) / (np.abs(g.astype(np.float64)) + eps))
+    ww = w.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    O.adamw_(ww, g, m, v, O.F32, O.MOM_F32, O.MOM_F32,
+             O.scalars(lr, b1, b2, eps, wd, 1))
+    err = np.abs(ww.astype(np.float64) - want)
+    # a few float32 roundings of w1, plus a few relative roundings of the
+    # update term (about lr in size) itself
+    tol = (4 * np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+           + 16 * 2.0 ** -24 * lr)
+    assert np.all(err <= tol)
+    # a zero gradient leaves exactly the decayed weight
+    dec = np.float32(1 - lr * wd)
+    assert np.array_equal(ww[:16], w[:16] * dec)
+
+
+def _textbook_adamw(w, gs, lr, b1, b2, eps, wd):
+    """Loshchilov & Hutter's AdamW in float64, bias-corrected moments."""
+    w = w.astype(np.float64).copy()
+    m = np.zeros_like(w)
+    v = np.zeros_like(w)
+    for t, g in enumerate(gs, start=1):
+        g = g.astype(np.float64)
+        w = w * (1 - lr * wd)
+        m = b1 * m + (1 - b1) * g
+        v = b2 * v + (1 - b2) * g * g
+        mh = m / (1 - b1 ** t)
+        vh = v / (1 - b2 ** t)
+        w = w - lr * mh / (np.sqrt(vh) + eps)
+    return w, m, v
+
+
+@pytest.mark.parametrize("mk,vk", [("f32", "f32"), ("bf16x2", "bf16x2"),
+                                   ("bf16x2", "f32")])
+def test_multi_step_against_textbook_float64(mk, vk):
+    rng = np.random.default_rng(2)
+    n, steps = 2048, 12
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.999, 1e-8, 0.1
+    w0 = rng.normal(0, 0.02, n).astype(np.float32)
+    gs = [rng.normal(0, 1e-3, n).astype(np.float32) for _ in range(steps)]
+    mkind, vkind = _kind(mk), _kind(vk)
+    w = w0.copy()
+    m = np.zeros(O.packed_words(n) if mkind else n,
+                 np.uint32 if mkind else np.float32)
+    v = np.zeros(O.packed_words(n) if vkind else n,
+                 np.uint32 if vkind else np.float32)
+    for t, g in enumerate(gs, start=1):
+        O.adamw_(w, g, m, v, O.F32, mkind, vkind,
+                 O.scalars(lr, b1, b2, eps, wd, t))
+    wt, mt, vt = _textbook_adamw(w0, gs, lr, b1, b2, eps, wd)
+    # per-step displacement is ~lr; float32 rounding of the update
+    # (f32 moments) or bfloat16 moments (relative 2^-9) bound the drift
+    rel = 2.0 ** -20 if mkind == O.MOM_F32 and vkind == O.MOM_F32 else 2.0 ** -7
+    bound = steps * lr * rel * 4 + 4 * np.spacing(np.abs(wt).astype(np.float32))
+    assert np.all(np.abs(w - wt) <= bound)
+    mm = (O.f32_of_bf16(O.unpack_words(m, n)) if mkind else m)
+    vv = (O.f32_of_bf16(O.unpack_words(v, n)) if vkind else v)
+    mrel = 2.0 ** -7 if mkind else 2.0 ** -18
+    vrel = 2.0 ** -7 if vkind else 2.0 ** -18
+    # m is a signed sum: its rounding error scales with the terms (about
+    # c1 * |g| = 1e-4), not with |m| itself
+    assert np.all(np.abs(mm - mt) <= mrel * (np.abs(mt) + 1e-4) * steps)
+    assert np.all(np.abs(vv - vt) <= vrel * np.abs(vt) * steps + 1e-30)
+
+
+def test_adamw_against_torch_cpu():
+    # torch.optim.AdamW (single-tensor path) performs the same operations in
+    # the same order; its lerp may use a fused multiply-add on this CPU, so
+    # agreement is to a few ulp rather than bitwise.
+    rng = np.random.default_rng(3)
+    n, steps = 4096, 10
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.999, 1e-8, 0.1
+    w0 = rng.normal(0, 0.02, n).astype(np.float32)
+    gs = [rng.normal(0, 1e-2, n).astype(np.float32) for _ in range(steps)]
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.AdamW([p], lr=lr, betas=(b1, b2), eps=eps,
+                            weight_decay=wd, foreach=False, fused=False)
+    w = w0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    for t, g in enumerate(gs, start=1):
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        O.adamw_(w, g, m, v, O.F32, O.MOM_F32, O.MOM_F32,
+                 O.scalars(lr, b1, b2, eps, wd, t))
+    st = opt.state[p]
+    wt = p.detach().numpy()
+    mt = st["exp_avg"].numpy()
+    # the fused lerp differs by an ulp of the terms (c1*|g| ~ 1e-3), which
+    # is many ulps of an m that cancels to near zero; so compare on the
+    # scale of the terms, and w on its own scale plus that of the update
+    u = 2.0 ** -24
+    # each step rounds w at the size it had then (at most |w0| + t*lr)
+    wscale = np.abs(w0) + steps * lr
+    assert np.all(np.abs(w - wt) <= steps * (np.spacing(wscale) + 4 * u * lr))
+    assert np.all(np.abs(m - mt) <= steps * 2 * u * (np.abs(mt) + 1e-2))
+    assert ulp_dist(v, st["exp_avg_sq"].numpy()).max() <= 4
+
+
+# ---------------------------------------------------------------------------
+# joint norm and clip (Mica: ClipGradNorms, "one cap over the joint length")
+# ---------------------------------------------------------------------------
+
+def test_norm_is_exact_sum_of_squares():
+    rng = np.random.default_rng(4)
+    gs = [rng.normal(0, 1e-3, n).astype(np.float32) for n in (0, 1, 7, 1000,
+                                                              65537)]
+    s = O.sumsq(gs, O.F32)
+    exact = math.fsum(float(x) * float(x) for g in gs for x in g)
+    assert abs(s - exact) <= 1e-15 * exact
+
+
+def test_norm_closed_forms():
+    a = np.float32(0.75)
+    for n in (1, 3, 1024, 1000003):
+        g = np.full(n, a, np.float32)
+        assert O.sumsq([g], O.F32) == n * 0.5625
+        assert abs(O.norm([g], O.F32) - 0.75 * math.sqrt(n)) <= \
+            1e-15 * math.sqrt(n)
+    assert O.norm([], O.F32) == 0.0
+    assert O.norm([np.zeros(10, np.float32)], O.F32) == 0.0
+
+
+def test_norm_power_of_two_scaling_and_bf16_unscale():
+    rng = np.random.default_rng(5)
+    g = rng.normal(0, 1e-3, 50000).astype(np.float32)
+    gb = O.bf16_of_f32(g * np.float32(65536.0))
+    # unscaling by 2^-16 in registers is exact: the norm scales exactly
+    n_raw = O.norm([gb], O.BF16, 1.0)
+    n_uns = O.norm([gb], O.BF16, 2.0 ** -16)
+    assert n_uns == n_raw * 2.0 ** -16
+    # bf16 values are the same numbers torch reads from the same bits
+    tv = torch.from_numpy(gb.view(np.int16).copy()).view(torch.bfloat16)
+    exact = math.fsum(float(x) ** 2 for x in tv.float().numpy())
+    assert abs(O.sumsq([gb], O.BF16) - exact) <= 1e-15 * exact
+
+
+def test_clip_coef_special_cases():
+    assert O.clip_coef(1.0, 0.0) == 1.0            # all-zero list
+    assert O.clip_coef(1.0, 0.5) == 1.0
+    assert O.clip_coef(1.0, np.float32(1.0) - np.float32(1e-6)) == 1.0
+    assert O.clip_coef(1.0, np.inf) == 0.0
+    assert np.isnan(O.clip_coef(1.0, np.nan))
+    assert O.clip_coef(2.0, 4.0) < 0.5
+
+
+def test_clip_matches_torch_clip_grad_norm():
+    # torch.nn.utils.clip_grad_norm_: coef = max/(norm + 1e-6), clamp at 1,
+    # gradients multiplied in float32.  With max = 1 its reciprocal-multiply
+    # is the same correctly rounded quotient.
+    rng = np.random.default_rng(6)
+    gs = [rng.normal(0, 0.05, n).astype(np.float32) for n in (100, 333, 4096)]
+    ps = [torch.nn.Parameter(torch.zeros(len(g))) for g in gs]
+    for p, g in zip(ps, gs):
+        p.grad = torch.from_numpy(g.copy())
+    tn = torch.nn.utils.clip_grad_norm_(ps, 1.0, foreach=False)
+    nrm = O.norm(gs, O.F32)
+    assert abs(float(tn) - nrm) <= 1e-6 * nrm
+    c = O.clip_coef(1.0, np.float32(float(tn)))
+    for p, g in zip(ps, gs):
+        assert np.array_equal(p.grad.numpy(), (g * c).astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_clip_invariant_post_clip_norm(seed):
+    rng = np.random.default_rng(100 + seed)
+    scale = [1e-4, 1e-2, 1.0, 10.0, 1e3][seed]
+    gs = [rng.normal(0, scale, n).astype(np.float32) for n in (17, 500, 3000)]
+    max_norm = 1.0
+    nrm = O.norm(gs, O.F32)
+    c = O.clip_coef(max_norm, np.float32(nrm))
+    post = math.sqrt(math.fsum(float(x) ** 2 for g in gs
+                               for x in (g * c).astype(np.float32)))
+    assert post <= max_norm * (1 + 1e-6)
+    if nrm <= max_norm - 1e-6:
+        assert c == 1.0
+
+
+def test_step_with_no_clip_leaves_gradient_bitwise():
+    # coef = 1 must leave ge == x bitwise, so a step with a huge max_norm
+    # equals a step with no clip at all
+    rng = np.random.default_rng(8)
+    n = 999
+    mk = lambda: O.Tensor(rng.normal(0, .02, n).astype(np.float32),
+                          rng.normal(0, 1e-3, n).astype(np.float32),
+                          np.zeros(n, np.float32), np.zeros(n, np.float32))
+    a = mk()
+    b = O.Tensor(a.w.copy(), a.g.copy(), a.m.copy(), a.v.copy())
+    hp = (3e-4, 0.9, 0.999, 1e-8, 0.1)
+    O.step_([a], O.F32, O.MOM_F32, O.MOM_F32, *hp, t=1, max_norm=1e6)
+    O.step_([b], O.F32, O.MOM_F32, O.MOM_F32, *hp, t=1)
+    assert np.array_equal(a.w, b.w) and np.array_equal(a.m, b.m)
+
+
+# ---------------------------------------------------------------------------
+# multi-tensor == per-tensor (Mica: each group updated as AdamWStep alone)
+# ---------------------------------------------------------------------------
+
+def _rand_list(rng, sizes, gtype, mkind, vkind):
+    out = []
+    for n in sizes:
+        w = rng.normal(0, 0.02, n).astype(np.float32)
+        g = rng.normal(0, 1e-2, n).astype(np.float32)
+        if gtype == O.BF16:
+            g = O.bf16_of_f32(g)
+        m = (O.pack_halves(O.bf16_of_f32(rng.normal(0, 1e-3, n)
+                                         .astype(np.float32)))
+             if mkind else rng.normal(0, 1e-3, n).astype(np.float32))
+        v = (O.pack_halves(O.bf16_of_f32(np.abs(rng.normal(0, 1e-5, n))
+                                         .astype(np.float32)))
+             if vkind else np.abs(rng.normal(0, 1e-5, n)).astype(np.float32))
+        out.append(O.Tensor(w, g, m, v))
+    return out
+
+
+def _copy(ts):
+    return [O.Tensor(x.w.copy(), x.g.copy(), x.m.copy(), x.v.copy())
+            for x in ts]
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind",
+                         [(0, 0, 0), (1, 0, 0), (0, 1, 1), (1, 1, 0)])
+def test_multi_tensor_equals_per_tensor(gtype, mkind, vkind):
+    rng = np.random.default_rng(9)
+    for trial in range(20):
+        k = rng.integers(1, 7)
+        sizes = rng.integers(0, 18, size=k)
+        ts = _rand_list(rng, sizes, gtype, mkind, vkind)
+        hp = (3e-4, 0.9, 0.999, 1e-8, 0.1)
+        joint = _copy(ts)
+        nrm, c = O.step_(joint, gtype, mkind, vkind, *hp, t=3, s=0.5,
+                         max_norm=0.01)
+        perm = rng.permutation(k)
+        for i in perm:                          # any order, one at a time
+            one = _copy([ts[i]])
+            O.step_(one, gtype, mkind, vkind, *hp, t=3, s=0.5, coef=c)
+            for a, b in ((one[0].w, joint[i].w), (one[0].m, joint[i].m),
+                         (one[0].v, joint[i].v)):
+                assert np.array_equal(a.view(np.uint32) if a.dtype ==
+                                      np.float32 else a,
+                                      b.view(np.uint32) if b.dtype ==
+                                      np.float32 else b)
+
+
+def test_deferred_unscale_equals_in_place_scale_f32():
+    # ScaleTensors then AdamW: for float32 gradients, scaling in registers
+    # and scaling the stored gradient first give the same bits
+    rng = np.random.default_rng(10)
+    ts = _rand_list(rng, [1000, 31], O.F32, 0, 0)
+    a, b = _copy(ts), _copy(ts)
+    hp = (3e-4, 0.9, 0.999, 1e-8, 0.1)
+    s = np.float32(1.0 / 3.0)
+    O.step_(a, O.F32, 0, 0, *hp, t=2, s=s, max_norm=0.05)
+    for x in b:
+        O.scale_(x.g, O.F32, s)
+    O.step_(b, O.F32, 0, 0, *hp, t=2, s=1.0, max_norm=0.05)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.w, y.w) and np.array_equal(x.v, y.v)
+
+
+def test_in_place_scale_bf16_matches_torch_rounding():
+    rng = np.random.default_rng(11)
+    g = O.bf16_of_f32(rng.normal(0, 60.0, 10000).astype(np.float32))
+    for s in (2.0 ** -16, 0.3):
+        x = g.copy()
+        O.scale_(x, O.BF16, s)
+        t = torch.from_numpy(g.view(np.int16).copy()).view(torch.bfloat16)
+        ref = (t.float() * np.float32(s)).to(torch.bfloat16)
+        assert np.array_equal(x, ref.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_nonfinite_gradient_propagates():
+    g = np.array([1.0, np.nan, 2.0], np.float32)
+    nrm = O.norm([g], O.F32)
+    assert math.isnan(nrm)
+    c = O.clip_coef(1.0, np.float32(nrm))
+    assert np.isnan(c)
+    g = np.array([1.0, np.inf], np.float32)
+    assert O.norm([g], O.F32) == math.inf
+    assert O.clip_coef(1.0, np.float32(O.norm([g], O.F32))) == 0.0
+    g = np.array([np.inf, 1.0, -np.inf], np.float32)
+    assert O.norm([g], O.F32) == math.inf
