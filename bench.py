@@ -1,0 +1,204 @@
+"""Benchmark of the fused clip + multi-tensor AdamW step on one MI355X.
+
+One step = mta_clip_norm (joint norm + clip coefficient, one launch) and
+mta_adamw_step (AdamW over every tensor, one launch), plus the deferred
+unscale where the workload has one (no launch), over inputs resident in HBM.
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "mixed_precision_optimizer_mta_amd", "csrc",
+                          "mta_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs, or
+    None when there are none for this workload or the kernel source changed
+    since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(arena, wl, steps):
+    """The oracle as it stands (single thread) on host copies of the same
+    list: `steps` whole steps (norm + AdamW)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    def host(t, bf16):
+        t = t.detach().cpu()
+        if bf16:
+            return t.view(torch.int16).numpy().view(np.uint16).copy()
+        return t.numpy().copy()
+
+    ts = []
+    for i in range(wl.count):
+        m = host(arena.view("m", i), wl.mkind == 1)
+        v = host(arena.view("v", i), wl.vkind == 1)
+        ts.append(O.Tensor(host(arena.view("w", i), False),
+                           host(arena.view("g", i), wl.gtype == 1),
+                           O.pack_halves(m) if wl.mkind == 1 else m,
+                           O.pack_halves(v) if wl.vkind == 1 else v))
+    O.lib()
+    t0 = time.perf_counter()
+    for t in range(1, steps + 1):
+        O.step_(ts, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1, wl.beta2,
+                wl.eps, wl.weight_decay, t, s=wl.scale, max_norm=wl.max_norm)
+    dt = time.perf_counter() - t0
+    return {"value": wl.n * steps / dt, "unit": "params/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} whole steps (joint norm + clip + AdamW) of "
+                      f"the full {wl.n:,}-param list, one host thread, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--cpu-steps", type=int, default=3,
+                    help="oracle steps of the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU "
+              "path (the sharded design is described, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixed_precision_optimizer_mta_amd as M
+    from mixed_precision_optimizer_mta_amd import workloads as WL
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    M.lib()
+    wl = WL.get(args.workload)
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_weights()
+    arena.fill_grads(1)
+    L = M.MtaList([], entries=arena.entries(), gtype=wl.gtype, mkind=wl.mkind,
+                  vkind=wl.vkind)
+    info = L.info()
+    norm_d = torch.zeros(1, device="cuda")
+    coef_d = torch.zeros(1, device="cuda")
+    stream = torch.cuda.current_stream()
+    hp = wl.hparams
+    defer = wl.scale != 1.0
+
+    def step(t, ev=None):
+        if defer:
+            L.scale(wl.scale, defer=True)
+        if ev is not None:
+            ev[0].record(stream)
+        L.clip_norm(wl.max_norm, norm_d, coef_d)
+        if ev is not None:
+            ev[1].record(stream)
+        L.adamw_step(hp, t, coef_d)
+        if ev is not None:
+            ev[2].record(stream)
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        step(t)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        t += 1
+        step(t, evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    dev_ms = start.elapsed_time(end)
+    ms_per_step = dev_ms / args.steps
+    norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    adamw_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    assert torch.isfinite(norm_d).all() and torch.isfinite(coef_d).all()
+
+    bpp = wl.bytes_per_param()
+    step_bytes = wl.n * (bpp["norm"] + bpp["update"])
+    adamw_bytes = wl.n * bpp["update"]
+    norm_bytes = wl.n * bpp["norm"]
+    value = wl.n * args.steps / (host_s)
+    achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name, "k_adamw")
+    out = {
+        "metric": "params updated/sec and achieved HBM GB/s (% of peak) per "
+                  "fused clip+AdamW step",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": host_s * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "params": wl.n, "tensors": wl.count,
+            "grad": ["f32", "bf16"][wl.gtype],
+            "m": ["f32", "bf16x2"][wl.mkind], "v": ["f32", "bf16x2"][wl.vkind],
+            "bytes_per_param": bpp["norm"] + bpp["update"],
+            "tiles": info["tiles"], "grid_update": info["grid_update"],
+            "grid_norm": info["grid_norm"], "parallelism": "single GPU",
+        },
+        "step_gbs": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9,
+        "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9
+        / HBM_PEAK_GBS,
+        "device_ms_per_step": ms_per_step,
+        "kernels_ms": {"k_sumsq": norm_ms, "k_adamw": adamw_ms},
+        "norm_gbs": norm_bytes / (norm_ms * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "k_adamw", "bound": "hbm", "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "bytes_per_launch": adamw_bytes,
+        },
+    }
+    L.close()
+    if args.cpu_steps > 0:
+        out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * mta.h -- fused mixed-precision gradient clip + multi-tensor AdamW step for
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The operations and their sources (by page title and section):
+ *
+ *   mta_scale       ScaleTensors -- "Mica 7.7: a training step on the card, in
+ *                   every float type", section "The whole model in one call":
+ *                   every cell of several tensors times one factor, the
+ *                   unscaling a float16 step needs before its clip.
+ *   mta_clip_norm   ClipGradNorms -- same page and section: one cap over the
+ *                   joint L2 norm of every gradient; section "Values that stay
+ *                   on the card": the norm is measured and the factor decided
+ *                   on the device, and both stay there until the host asks.
+ *   mta_adamw_step  AdamWSteps -- same page and section: one launch however
+ *                   many tensors, each group updated exactly as a lone
+ *                   AdamWStep would update it.  The element arithmetic is that
+ *                   of "BendTorch main.bend", section "Optimizers" (adam_decay,
+ *                   adam_m, adam_v, adam_w in PyTorch's order; packed
+ *                   bfloat16 moments as in adamh_l / adamhv_l; bias
+ *                   correction step = lr/(1-b1^t), bc2 = sqrt(1-b2^t) as in
+ *                   Opt.at and the Training section, t = 1 on the first step).
+ *
+ * Memory and ownership.  Every w, g, m, v pointer is device memory owned by
+ * the caller (for example a PyTorch tensor's data pointer).  The library never
+ * allocates, frees or resizes caller memory.  A list handle owns a small
+ * device table (tensor descriptors and a tile table) and the scratch of the
+ * norm reduction; it is created once and reused every step, so the caller's
+ * buffers must stay at the same addresses for the handle's life.
+ *
+ * Layouts.
+ *   w            float32, n elements.
+ *   g            float32 or bfloat16 (MTA_F32 / MTA_BF16, whole list), n elements.
+ *   m, v         MTA_MOM_F32: float32, n elements.
+ *                MTA_MOM_BF16X2: packed bfloat16, two per 32-bit word, element
+ *                2k in the low half of word k ("BendTorch main.bend", PTree
+ *                comment).  On this little-endian device that is byte for
+ *                byte a bfloat16 array of n elements, so a torch.bfloat16
+ *                tensor's data pointer can be passed.  For odd n the last
+ *                word's high half is never read or written; the buffer only
+ *                needs 2n bytes.
+ *   Alignment    float32 buffers 4 bytes, bfloat16 buffers 2 bytes.  A tensor
+ *                whose buffers are all 16-byte aligned takes the 16-byte
+ *                vector path; any other tensor is processed element by element.
+ *   Buffers of one list must not overlap (checked at create).
+ *
+ * Streams.  Every device call enqueues its work on the caller's hipStream_t
+ * (passed as void*, NULL = the null stream) and returns without waiting.  A
+ * list is used on one stream at a time: the norm scratch is shared by all
+ * calls on the list, so calls on one list that overlap in time race.
+ *
+ * Errors.  Functions return MTA_OK (0) or a negative mta_status.  On failure
+ * nothing has been enqueued and mta_last_error() (per host thread) says why.
+ * Arguments are checked before any device work.  A fault inside a kernel is
+ * asynchronous: it is reported by the caller's next synchronizing act (or, with
+ * the environment variable MTA_DEBUG_SYNC=1, by the call that launched it,
+ * which then waits for its own work and returns MTA_EHIP).
+ */
+#ifndef MTA_H
+#define MTA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTA_ABI_VERSION 1
+
+typedef struct mta_list mta_list; /* opaque */
+
+typedef enum { MTA_F32 = 0, MTA_BF16 = 1 } mta_gtype;
+typedef enum { MTA_MOM_F32 = 0, MTA_MOM_BF16X2 = 1 } mta_mkind;
+
+typedef enum {
+  MTA_OK = 0,
+  MTA_EINVAL = -1, /* bad argument value (null, negative size, bad hparam) */
+  MTA_EALIGN = -2, /* pointer not aligned to its element size */
+  MTA_EDTYPE = -3, /* unknown gradient type or moment kind */
+  MTA_ENOMEM = -4, /* device or host allocation failed (create only) */
+  MTA_EHIP = -5,   /* the HIP runtime reported an error */
+  MTA_ESTATE = -6  /* call not allowed in the handle's current state */
+} mta_status;
+
+/* One parameter group: the caller's device buffers and the element count. */
+typedef struct {
+  float *w;  /* master weights, float32 [n]               (read, written) */
+  void *g;   /* gradient, list's gradient type [n]        (read; written only by MTA_SCALE_INPLACE) */
+  void *m;   /* first moment, list's m kind               (read, written) */
+  void *v;   /* second moment, list's v kind              (read, written) */
+  int64_t n; /* elements; 0 is allowed and skipped */
+} mta_tensor;
+
+/* AdamW hyperparameters as the caller states them (float64).  The kernel's
+ * float32 constants are formed from these in float64 and rounded once:
+ * step = lr/(1-beta1^t), bc2 = sqrt(1-beta2^t), c1 = 1-beta1, c2 = 1-beta2,
+ * b2 = beta2, eps, dec = 1 - lr*weight_decay (decoupled decay). */
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+} mta_adamw_hparams;
+
+/* Shape of a list handle, for callers and tests that want to see it. */
+typedef struct {
+  int64_t count;       /* tensors in the list */
+  int64_t elements;    /* sum of n */
+  int64_t tiles;       /* work tiles (each covers up to tile_elems of one tensor) */
+  int32_t tile_elems;  /* elements per tile */
+  int32_t grid_update; /* workgroups of the AdamW / scale launch */
+  int32_t grid_norm;   /* workgroups of the norm launch (= norm partials) */
+  int32_t device;      /* HIP device the list lives on */
+  int32_t vector_tensors; /* tensors that take the 16-byte vector path */
+  int32_t gtype, mkind, vkind;
+} mta_list_info_t;
+
+/* Flags of mta_scale. */
+#define MTA_SCALE_INPLACE 1 /* launch now: g = g * factor, rounded to g's type */
+#define MTA_SCALE_DEFER 2   /* no launch: the next mta_clip_norm and
+                               mta_adamw_step read f32(g * factor) in registers */
+
+/* Create a list handle over `count` (>= 0) tensors described by the host array
+ * `tensors`.  Validates every entry, builds the tensor and tile tables and
+ * copies them to the current device on `stream`, then waits for that copy.
+ * Allocates device memory (the only call that does).  On success *out owns the
+ * handle; release it with mta_list_destroy. */
+int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
+                    int mkind, int vkind, void *stream, mta_list **out);
+
+/* Free a handle.  The caller must have synchronized every stream that used it.
+ * NULL is accepted and ignored. */
+int mta_list_destroy(mta_list *list);
+
+/* ScaleTensors over the list's gradients.  MTA_SCALE_INPLACE launches one
+ * kernel that writes g = g*factor (bfloat16 gradients are rounded back to
+ * nearest-even).  MTA_SCALE_DEFER records the factor in the handle without a
+ * launch; it applies to the next mta_clip_norm calls and to the next
+ * mta_adamw_step, which clears it.  A second MTA_SCALE_DEFER before that step
+ * returns MTA_ESTATE.  factor must be finite. */
+int mta_scale(mta_list *list, float factor, int flags, void *stream);
+
+/* ClipGradNorms: one launch.  Computes the joint L2 norm of f32(g*s) over
+ * every gradient of the list (s = the deferred scale factor, else 1), and
+ * coef = min(1, max_norm / (norm + 1e-6)) in float32 (a NaN norm gives a NaN
+ * coef, an infinite norm gives 0).  Writes the float32 norm to *d_norm (device
+ * pointer, may be NULL) and coef to *d_coef (device pointer, required).
+ * The gradients are not modified: the coefficient is applied by
+ * mta_adamw_step.  max_norm must be > 0 (infinity allowed, NaN not). */
+int mta_clip_norm(mta_list *list, float max_norm, float *d_norm, float *d_coef,
+                  void *stream);
+
+/* AdamWSteps: one launch over every tensor of the list, step number t >= 1.
+ * Per element, in float32 with every operation rounded on its own:
+ *   ge = f32(f32(g*s) * coef)        (coef = *d_coef, or 1 when d_coef is NULL)
+ *   w' = w*dec;  m = m + c1*(ge - m);  v = (v*b2) + ((c2*ge)*ge)
+ *   packed kinds: m, v rounded to bfloat16 (nearest-even, NaN -> 0xFFFF),
+ *   stored, and the rounded values used below
+ *   w  = w' + ((-step*m) / ((sqrt(v)/bc2) + eps))
+ * Hyperparameters follow PyTorch's AdamW checks: 0 <= beta1, beta2 < 1,
+ * lr >= 0, eps >= 0, weight_decay >= 0, all finite.  Clears a deferred scale
+ * factor. */
+int mta_adamw_step(mta_list *list, const mta_adamw_hparams *hp, int64_t t,
+                   const float *d_coef, void *stream);
+
+/* Host only, no device work: the seven float32 constants the AdamW kernel
+ * receives for step t, in the order {step, bc2, c1, c2, b2, eps, dec}. */
+int mta_adamw_scalars(const mta_adamw_hparams *hp, int64_t t, float out[7]);
+
+/* Host only: describe a handle. */
+int mta_list_info(const mta_list *list, mta_list_info_t *out);
+
+/* Message for the last failure on the calling host thread ("" if none). */
+const char *mta_last_error(void);
+
+/* MTA_ABI_VERSION of the built library. */
+int mta_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTA_H */

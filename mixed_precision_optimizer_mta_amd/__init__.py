@@ -1,0 +1,14 @@
+"""Fused mixed-precision gradient clip + multi-tensor AdamW for MI355X.
+
+The work runs in libmta.so (HIP, gfx950) behind the C ABI of include/mta.h.
+``_binding`` mirrors that ABI name for name; ``MtaList`` marshals PyTorch
+tensors and the current HIP stream into it.  Nothing here computes any part
+of the step, and nothing falls back to another implementation: if
+libmta.so is missing the first call raises.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, MTA_BF16, MTA_F32, MTA_MOM_BF16X2, MTA_MOM_F32,
+    MTA_SCALE_DEFER, MTA_SCALE_INPLACE, MtaError, lib, mta_abi_version,
+    mta_adamw_scalars, mta_adamw_step, mta_clip_norm, mta_last_error,
+    mta_list_create, mta_list_destroy, mta_list_info, mta_scale)
+from .torch_list import MtaList  # noqa: F401

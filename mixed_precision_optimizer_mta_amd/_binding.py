@@ -1,0 +1,158 @@
+"""ctypes binding of libmta.so: the C ABI of include/mta.h, same names.
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+library.  If the library is not built, loading fails loudly; there is no
+fallback of any kind.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmta.so")
+
+MTA_F32, MTA_BF16 = 0, 1
+MTA_MOM_F32, MTA_MOM_BF16X2 = 0, 1
+MTA_SCALE_INPLACE, MTA_SCALE_DEFER = 1, 2
+
+MTA_OK = 0
+STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
+                -3: "MTA_EDTYPE", -4: "MTA_ENOMEM", -5: "MTA_EHIP",
+                -6: "MTA_ESTATE"}
+
+# every symbol include/mta.h declares
+EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
+           "mta_clip_norm", "mta_adamw_step", "mta_adamw_scalars",
+           "mta_list_info", "mta_last_error", "mta_abi_version")
+
+
+class mta_tensor(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n", ctypes.c_int64)]
+
+
+class mta_adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double)]
+
+
+class mta_list_info_t(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int64), ("elements", ctypes.c_int64),
+                ("tiles", ctypes.c_int64), ("tile_elems", ctypes.c_int32),
+                ("grid_update", ctypes.c_int32), ("grid_norm", ctypes.c_int32),
+                ("device", ctypes.c_int32), ("vector_tensors", ctypes.c_int32),
+                ("gtype", ctypes.c_int32), ("mkind", ctypes.c_int32),
+                ("vkind", ctypes.c_int32)]
+
+
+class MtaError(RuntimeError):
+    """A libmta call returned a negative mta_status."""
+
+    def __init__(self, code, func, msg):
+        self.code = code
+        super().__init__(f"{func}: {STATUS_NAMES.get(code, code)}: {msg}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmta.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m "
+                "mixed_precision_optimizer_mta_amd.build` (or "
+                "__graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, c_int, f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_float)
+        L.mta_list_create.argtypes = [ctypes.POINTER(mta_tensor), i64, c_int,
+                                      c_int, c_int, vp,
+                                      ctypes.POINTER(vp)]
+        L.mta_list_destroy.argtypes = [vp]
+        L.mta_scale.argtypes = [vp, f32, c_int, vp]
+        L.mta_clip_norm.argtypes = [vp, f32, vp, vp, vp]
+        L.mta_adamw_step.argtypes = [vp, ctypes.POINTER(mta_adamw_hparams),
+                                     i64, vp, vp]
+        L.mta_adamw_scalars.argtypes = [ctypes.POINTER(mta_adamw_hparams),
+                                        i64, ctypes.POINTER(ctypes.c_float)]
+        L.mta_list_info.argtypes = [vp, ctypes.POINTER(mta_list_info_t)]
+        L.mta_last_error.argtypes = []
+        L.mta_last_error.restype = ctypes.c_char_p
+        L.mta_abi_version.argtypes = []
+        for name in EXPORTS:
+            if name != "mta_last_error":
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc, func):
+    if rc != MTA_OK:
+        raise MtaError(rc, func, mta_last_error())
+
+
+def mta_last_error():
+    return lib().mta_last_error().decode()
+
+
+def mta_abi_version():
+    return lib().mta_abi_version()
+
+
+def _hparams(hp):
+    if isinstance(hp, mta_adamw_hparams):
+        return hp
+    if isinstance(hp, dict):
+        return mta_adamw_hparams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                 hp["weight_decay"])
+    return mta_adamw_hparams(*hp)
+
+
+def mta_list_create(tensors, gtype, mkind, vkind, stream=0):
+    """tensors: sequence of (w_ptr, g_ptr, m_ptr, v_ptr, n).  Returns the
+    opaque handle (an int)."""
+    arr = (mta_tensor * max(1, len(tensors)))()
+    for i, (w, g, m, v, n) in enumerate(tensors):
+        arr[i] = mta_tensor(w, g, m, v, n)
+    out = ctypes.c_void_p()
+    rc = lib().mta_list_create(arr, len(tensors), gtype, mkind, vkind,
+                               stream, ctypes.byref(out))
+    _check(rc, "mta_list_create")
+    return out.value
+
+
+def mta_list_destroy(handle):
+    _check(lib().mta_list_destroy(handle), "mta_list_destroy")
+
+
+def mta_scale(handle, factor, flags, stream=0):
+    _check(lib().mta_scale(handle, factor, flags, stream), "mta_scale")
+
+
+def mta_clip_norm(handle, max_norm, d_norm, d_coef, stream=0):
+    _check(lib().mta_clip_norm(handle, max_norm, d_norm, d_coef, stream),
+           "mta_clip_norm")
+
+
+def mta_adamw_step(handle, hp, t, d_coef, stream=0):
+    h = _hparams(hp)
+    _check(lib().mta_adamw_step(handle, ctypes.byref(h), t, d_coef, stream),
+           "mta_adamw_step")
+
+
+def mta_adamw_scalars(hp, t):
+    h = _hparams(hp)
+    out = (ctypes.c_float * 7)()
+    _check(lib().mta_adamw_scalars(ctypes.byref(h), t, out),
+           "mta_adamw_scalars")
+    return [out[i] for i in range(7)]
+
+
+def mta_list_info(handle):
+    info = mta_list_info_t()
+    _check(lib().mta_list_info(handle, ctypes.byref(info)), "mta_list_info")
+    return {name: getattr(info, name) for name, _ in mta_list_info_t._fields_}

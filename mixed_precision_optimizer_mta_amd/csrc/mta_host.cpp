@@ -1,0 +1,443 @@
+// mta_host.cpp -- host runtime and C ABI of libmta (see include/mta.h).
+//
+// Validation, the per-list device table (tensor descriptors + tile table),
+// the float64 -> float32 scalar preparation of each AdamW step, the launch
+// policy, and error reporting.  No C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/mta.h"
+#include "mta_internal.h"
+
+struct mta_list {
+  int device = 0;
+  int gtype = 0, mkind = 0, vkind = 0;
+  int64_t count = 0;
+  int64_t elements = 0;
+  uint32_t ntiles = 0;
+  int grid_update = 1;
+  int grid_norm = 1;
+  int vector_tensors = 0;
+  void *dev_block = nullptr;  // one allocation: descriptors, tiles, scratch
+  mta::TensorDesc *d_td = nullptr;
+  mta::Tile *d_tiles = nullptr;
+  double *d_partials = nullptr;
+  unsigned int *d_ticket = nullptr;
+  bool deferred = false;  // a MTA_SCALE_DEFER factor is pending
+  float deferred_s = 1.0f;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MTA_OK;
+}
+
+int env_int(const char *name, int dflt, int lo, int hi) {
+  const char *s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  char *end = nullptr;
+  long v = std::strtol(s, &end, 10);
+  if (*end != '\0' || v < lo || v > hi) return dflt;
+  return static_cast<int>(v);
+}
+
+bool debug_sync() {
+  static const bool on = env_int("MTA_DEBUG_SYNC", 0, 0, 1) == 1;
+  return on;
+}
+
+// Workgroups per compute unit of the persistent launches.  A workgroup is
+// four wave64s; the grid walks the tile table with a grid stride.  Measured
+// on gfx950 (MI355X): the update streams within noise from 2 to 16
+// workgroups per CU and 8 is the most even across the lists; the norm pays
+// one release fence and one ticket atomic per workgroup, so it runs fastest
+// with few workgroups that each keep two tiles of loads in flight.
+constexpr int kUpdateBlocksPerCu = 8;
+constexpr int kNormBlocksPerCu = 2;
+
+int after_launch(hipError_t e, hipStream_t stream, const char *what) {
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  if (debug_sync()) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+      return fail(MTA_EHIP, "%s: kernel failed: %s", what,
+                  hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int check_device(const mta_list *L) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev != L->device)
+    return fail(MTA_EINVAL,
+                "list lives on device %d but device %d is current", L->device,
+                dev);
+  return MTA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// PyTorch's AdamW argument checks, plus t >= 1 (the first step is t = 1).
+int check_hparams(const mta_adamw_hparams *hp, int64_t t) {
+  if (!hp) return fail(MTA_EINVAL, "hparams is NULL");
+  if (!(std::isfinite(hp->lr) && hp->lr >= 0.0))
+    return fail(MTA_EINVAL, "lr must be finite and >= 0 (got %g)", hp->lr);
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0))
+    return fail(MTA_EINVAL, "beta1 must be in [0, 1) (got %g)", hp->beta1);
+  if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return fail(MTA_EINVAL, "beta2 must be in [0, 1) (got %g)", hp->beta2);
+  if (!(std::isfinite(hp->eps) && hp->eps >= 0.0))
+    return fail(MTA_EINVAL, "eps must be finite and >= 0 (got %g)", hp->eps);
+  if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+    return fail(MTA_EINVAL, "weight_decay must be finite and >= 0 (got %g)",
+                hp->weight_decay);
+  if (t < 1) return fail(MTA_EINVAL, "step t must be >= 1 (got %lld)",
+                         static_cast<long long>(t));
+  return MTA_OK;
+}
+
+// The step's float32 constants, each formed in float64 and rounded once:
+// bias corrections 1 - beta^t from pow (as Python's beta ** t), the step size
+// lr / (1 - beta1^t) and sqrt(1 - beta2^t) ("BendTorch main.bend": Opt type
+// comment and Opt.at; Training section for q1, q2), 1 - beta formed in
+// float64 (comment on adam_m), and the decoupled decay factor 1 - lr*wd.
+void make_scalars(const mta_adamw_hparams &hp, int64_t t, float out[7]) {
+  const double td = static_cast<double>(t);
+  const double bias1 = 1.0 - std::pow(hp.beta1, td);
+  const double bias2 = 1.0 - std::pow(hp.beta2, td);
+  out[0] = static_cast<float>(hp.lr / bias1);
+  out[1] = static_cast<float>(std::sqrt(bias2));
+  out[2] = static_cast<float>(1.0 - hp.beta1);
+  out[3] = static_cast<float>(1.0 - hp.beta2);
+  out[4] = static_cast<float>(hp.beta2);
+  out[5] = static_cast<float>(hp.eps);
+  out[6] = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
+}
+
+struct Span {
+  uintptr_t lo, hi;
+  int64_t tensor;
+  int which;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+mta::Work work_of(const mta_list *L, int grid, void *stream) {
+  mta::Work w;
+  w.td = L->d_td;
+  w.tiles = L->d_tiles;
+  w.ntiles = L->ntiles;
+  w.grid = grid;
+  w.stream = static_cast<hipStream_t>(stream);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mta_abi_version(void) { return MTA_ABI_VERSION; }
+
+const char *mta_last_error(void) { return g_err; }
+
+int mta_adamw_scalars(const mta_adamw_hparams *hp, int64_t t, float out[7]) {
+  int rc = check_hparams(hp, t);
+  if (rc) return rc;
+  if (!out) return fail(MTA_EINVAL, "out is NULL");
+  make_scalars(*hp, t, out);
+  return ok();
+}
+
+int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
+                    int mkind, int vkind, void *stream, mta_list **out) {
+  if (!out) return fail(MTA_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (count < 0) return fail(MTA_EINVAL, "count must be >= 0");
+  if (count > 0 && !tensors) return fail(MTA_EINVAL, "tensors is NULL");
+  if (count > static_cast<int64_t>(UINT32_MAX))
+    return fail(MTA_EINVAL, "too many tensors");
+  if (gtype != MTA_F32 && gtype != MTA_BF16)
+    return fail(MTA_EDTYPE, "unknown gradient type %d", gtype);
+  if (mkind != MTA_MOM_F32 && mkind != MTA_MOM_BF16X2)
+    return fail(MTA_EDTYPE, "unknown m kind %d", mkind);
+  if (vkind != MTA_MOM_F32 && vkind != MTA_MOM_BF16X2)
+    return fail(MTA_EDTYPE, "unknown v kind %d", vkind);
+
+  const uintptr_t gsz = gtype == MTA_BF16 ? 2 : 4;
+  const uintptr_t msz = mkind == MTA_MOM_BF16X2 ? 2 : 4;
+  const uintptr_t vsz = vkind == MTA_MOM_BF16X2 ? 2 : 4;
+
+  std::vector<mta::TensorDesc> td;
+  std::vector<mta::Tile> tiles;
+  std::vector<Span> spans;
+  int64_t elements = 0;
+  int vec_tensors = 0;
+  try {
+    td.resize(static_cast<size_t>(count));
+    spans.reserve(static_cast<size_t>(count) * 4);
+    uint64_t ntiles = 0;
+    for (int64_t i = 0; i < count; ++i) {
+      const mta_tensor &x = tensors[i];
+      if (x.n < 0)
+        return fail(MTA_EINVAL, "tensor %lld: n < 0", static_cast<long long>(i));
+      if (x.n > (INT64_MAX / 8))
+        return fail(MTA_EINVAL, "tensor %lld: n too large",
+                    static_cast<long long>(i));
+      mta::TensorDesc &d = td[static_cast<size_t>(i)];
+      d.w = x.w;
+      d.g = x.g;
+      d.m = x.m;
+      d.v = x.v;
+      d.n = x.n;
+      d.vec = 0;
+      d.pad = 0;
+      if (x.n == 0) continue;
+      if (!x.w || !x.g || !x.m || !x.v)
+        return fail(MTA_EINVAL, "tensor %lld: a buffer pointer is NULL",
+                    static_cast<long long>(i));
+      if (!aligned(x.w, 4) || !aligned(x.g, gsz) || !aligned(x.m, msz) ||
+          !aligned(x.v, vsz))
+        return fail(MTA_EALIGN,
+                    "tensor %lld: a buffer is not aligned to its element size",
+                    static_cast<long long>(i));
+      d.vec = (aligned(x.w, 16) && aligned(x.g, 16) && aligned(x.m, 16) &&
+               aligned(x.v, 16))
+                  ? 1u
+                  : 0u;
+      vec_tensors += static_cast<int>(d.vec);
+      const uintptr_t n = static_cast<uintptr_t>(x.n);
+      const void *bufs[4] = {x.w, x.g, x.m, x.v};
+      const uintptr_t sizes[4] = {4, gsz, msz, vsz};
+      for (int b = 0; b < 4; ++b) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(bufs[b]);
+        spans.push_back(Span{lo, lo + n * sizes[b], i, b});
+      }
+      elements += x.n;
+      const uint64_t nt = (static_cast<uint64_t>(x.n) + mta::kTileElems - 1) /
+                          mta::kTileElems;
+      ntiles += nt;
+      if (ntiles > UINT32_MAX) return fail(MTA_EINVAL, "list too large");
+    }
+    std::sort(spans.begin(), spans.end(),
+              [](const Span &a, const Span &b) { return a.lo < b.lo; });
+    static const char *names[4] = {"w", "g", "m", "v"};
+    for (size_t k = 1; k < spans.size(); ++k) {
+      if (spans[k].lo < spans[k - 1].hi)
+        return fail(MTA_EINVAL, "buffers overlap: tensor %lld %s and tensor %lld %s",
+                    static_cast<long long>(spans[k - 1].tensor),
+                    names[spans[k - 1].which],
+                    static_cast<long long>(spans[k].tensor),
+                    names[spans[k].which]);
+    }
+    tiles.reserve(static_cast<size_t>(ntiles));
+    for (int64_t i = 0; i < count; ++i) {
+      const int64_t n = td[static_cast<size_t>(i)].n;
+      const int64_t nt = (n + mta::kTileElems - 1) / mta::kTileElems;
+      for (int64_t k = 0; k < nt; ++k)
+        tiles.push_back(mta::Tile{static_cast<uint32_t>(i),
+                                  static_cast<uint32_t>(k)});
+    }
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0)
+    return fail(MTA_EHIP, "cannot read the compute-unit count: %s",
+                hipGetErrorString(e));
+
+  mta_list *L = new (std::nothrow) mta_list;
+  if (!L) return fail(MTA_ENOMEM, "host allocation failed");
+  L->device = dev;
+  L->gtype = gtype;
+  L->mkind = mkind;
+  L->vkind = vkind;
+  L->count = count;
+  L->elements = elements;
+  L->ntiles = static_cast<uint32_t>(tiles.size());
+  L->vector_tensors = vec_tensors;
+  const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
+  const int bpc_n = env_int("MTA_NORM_BLOCKS_PER_CU", kNormBlocksPerCu, 1, 64);
+  const int64_t tiles_or_one = std::max<int64_t>(1, L->ntiles);
+  L->grid_update = static_cast<int>(
+      std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_u));
+  L->grid_norm = static_cast<int>(
+      std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_n));
+
+  const size_t off_td = 0;
+  const size_t off_tiles =
+      round_up(off_td + td.size() * sizeof(mta::TensorDesc), 256);
+  const size_t off_part =
+      round_up(off_tiles + tiles.size() * sizeof(mta::Tile), 256);
+  const size_t off_ticket =
+      round_up(off_part + static_cast<size_t>(L->grid_norm) * sizeof(double),
+               256);
+  const size_t total = off_ticket + 256;
+
+  e = hipMalloc(&L->dev_block, total);
+  if (e != hipSuccess) {
+    delete L;
+    return fail(MTA_ENOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
+  }
+  char *base = static_cast<char *>(L->dev_block);
+  L->d_td = reinterpret_cast<mta::TensorDesc *>(base + off_td);
+  L->d_tiles = reinterpret_cast<mta::Tile *>(base + off_tiles);
+  L->d_partials = reinterpret_cast<double *>(base + off_part);
+  L->d_ticket = reinterpret_cast<unsigned int *>(base + off_ticket);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e = hipSuccess;
+  if (!td.empty())
+    e = hipMemcpyAsync(L->d_td, td.data(), td.size() * sizeof(mta::TensorDesc),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !tiles.empty())
+    e = hipMemcpyAsync(L->d_tiles, tiles.data(),
+                       tiles.size() * sizeof(mta::Tile), hipMemcpyHostToDevice,
+                       s);
+  if (e == hipSuccess) e = hipMemsetAsync(L->d_ticket, 0, 256, s);
+  // the host vectors die with this call: wait for the copies
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(L->dev_block);
+    delete L;
+    return fail(MTA_EHIP, "uploading the list table: %s", hipGetErrorString(e));
+  }
+  *out = L;
+  return ok();
+}
+
+int mta_list_destroy(mta_list *L) {
+  if (!L) return ok();
+  hipError_t e = hipFree(L->dev_block);
+  delete L;
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "hipFree: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mta_list_info(const mta_list *L, mta_list_info_t *out) {
+  if (!L || !out) return fail(MTA_EINVAL, "NULL argument");
+  out->count = L->count;
+  out->elements = L->elements;
+  out->tiles = L->ntiles;
+  out->tile_elems = mta::kTileElems;
+  out->grid_update = L->grid_update;
+  out->grid_norm = L->grid_norm;
+  out->device = L->device;
+  out->vector_tensors = L->vector_tensors;
+  out->gtype = L->gtype;
+  out->mkind = L->mkind;
+  out->vkind = L->vkind;
+  return ok();
+}
+
+int mta_scale(mta_list *L, float factor, int flags, void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  if (!std::isfinite(factor))
+    return fail(MTA_EINVAL, "scale factor must be finite");
+  if (flags == MTA_SCALE_DEFER) {
+    if (L->deferred)
+      return fail(MTA_ESTATE,
+                  "a deferred scale factor is already pending; run "
+                  "mta_adamw_step first");
+    L->deferred = true;
+    L->deferred_s = factor;
+    return ok();
+  }
+  if (flags != MTA_SCALE_INPLACE)
+    return fail(MTA_EINVAL, "flags must be MTA_SCALE_INPLACE or MTA_SCALE_DEFER");
+  int rc = check_device(L);
+  if (rc) return rc;
+  if (L->ntiles == 0) return ok();
+  const mta::Work wk = work_of(L, L->grid_update, stream);
+  return after_launch(mta::launch_scale(L->gtype, wk, factor), wk.stream,
+                      "mta_scale");
+}
+
+int mta_clip_norm(mta_list *L, float max_norm, float *d_norm, float *d_coef,
+                  void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  if (!(max_norm > 0.0f))
+    return fail(MTA_EINVAL, "max_norm must be > 0 (got %g)",
+                static_cast<double>(max_norm));
+  if (!d_coef) return fail(MTA_EINVAL, "d_coef is NULL");
+  if (!aligned(d_coef, 4) || (d_norm && !aligned(d_norm, 4)))
+    return fail(MTA_EALIGN, "d_norm / d_coef must be 4-byte aligned");
+  int rc = check_device(L);
+  if (rc) return rc;
+  const mta::Work wk = work_of(L, L->grid_norm, stream);
+  const float s = L->deferred ? L->deferred_s : 1.0f;
+  return after_launch(
+      mta::launch_sumsq(L->gtype, wk, s, max_norm,
+                        mta::NormScratch{L->d_partials, L->d_ticket}, d_norm,
+                        d_coef),
+      wk.stream, "mta_clip_norm");
+}
+
+int mta_adamw_step(mta_list *L, const mta_adamw_hparams *hp, int64_t t,
+                   const float *d_coef, void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  int rc = check_hparams(hp, t);
+  if (rc) return rc;
+  if (d_coef && !aligned(d_coef, 4))
+    return fail(MTA_EALIGN, "d_coef must be 4-byte aligned");
+  rc = check_device(L);
+  if (rc) return rc;
+  float c[7];
+  make_scalars(*hp, t, c);
+  mta::StepScalars sc;
+  sc.nstep = -c[0];
+  sc.bc2 = c[1];
+  sc.c1 = c[2];
+  sc.c2 = c[3];
+  sc.b2 = c[4];
+  sc.eps = c[5];
+  sc.dec = c[6];
+  sc.s = L->deferred ? L->deferred_s : 1.0f;
+  if (L->ntiles > 0) {
+    const mta::Work wk = work_of(L, L->grid_update, stream);
+    const hipError_t e =
+        mta::launch_adamw(L->gtype, L->mkind, L->vkind, wk, sc, d_coef);
+    if (e != hipSuccess)  // nothing enqueued: the deferred factor stays
+      return after_launch(e, wk.stream, "mta_adamw_step");
+    L->deferred = false;
+    L->deferred_s = 1.0f;
+    return after_launch(hipSuccess, wk.stream, "mta_adamw_step");
+  }
+  L->deferred = false;
+  L->deferred_s = 1.0f;
+  return ok();
+}
+
+}  // extern "C"

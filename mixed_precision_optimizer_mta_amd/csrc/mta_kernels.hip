@@ -1,0 +1,542 @@
+// mta_kernels.hip -- gfx950 kernels of the fused clip + multi-tensor AdamW step.
+//
+// Three kernels, each one launch over the whole tensor list:
+//   k_sumsq  joint sum of squares -> norm and clip coefficient (ClipGradNorms,
+//            "Mica 7.7: a training step on the card, in every float type",
+//            section "The whole model in one call"; the norm and coefficient
+//            stay in device memory, section "Values that stay on the card").
+//   k_adamw  AdamW over every (w, g, m, v) group (AdamWSteps, same section),
+//            with the element arithmetic of "BendTorch main.bend", section
+//            "Optimizers": adam_decay, adam_m, adam_v, adam_w, and the packed
+//            bfloat16 moments of adamh_l / adamhv_l (ph_of_bits, ph_to).
+//   k_scale  ScaleTensors in place (same Mica section).
+//
+// Work is cut into tiles of kTileElems elements of one tensor (the tile table
+// is built once per list on the host).  A persistent grid walks the tiles with
+// a grid stride.  Inside a full tile of a 16-byte-aligned tensor every wave
+// instruction reads or writes one contiguous run of memory: lane l of group j
+// owns elements j*G + V*l .. j*G + V*l + V-1, where V is 4 for k_adamw (a
+// 16-byte access of a float32 buffer, 8 bytes of a bfloat16 one, so all four
+// buffers share one element mapping) and 16 bytes' worth for the single-buffer
+// kernels.  The tail tile of a tensor and the tiles of an unaligned tensor use
+// the same mapping with masked one-element accesses, all loads issued first.
+// A lane owns whole elements, so a packed bfloat16 moment is written with
+// 8-byte or 16-bit stores and no 32-bit word is ever shared between lanes (no
+// read-modify-write of a neighbour's half).
+//
+// Numerics: this file is compiled with -ffp-contract=off.  Every float32
+// operation of the AdamW update is rounded on its own, '/' and sqrtf are the
+// correctly rounded ones, and denormals are kept.  The only fused multiply-adds
+// are the explicit float64 fma of the norm's accumulation, which needs to be
+// accurate, not to follow a fixed rounding sequence.
+#include <type_traits>
+
+#include "mta_internal.h"
+
+namespace mta {
+namespace {
+
+// ---------------------------------------------------------------------------
+// bfloat16 <-> float32 ("BendTorch main.bend", Optimizers: ph_to, ph_of_bits)
+// ---------------------------------------------------------------------------
+
+// bfloat16 bits (low 16 bits of h) -> float32, exact.
+__device__ __forceinline__ float from_bf16(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; any NaN -> 0xFFFF.
+__device__ __forceinline__ uint32_t to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0xFFFFu : r;
+}
+
+// float32 -> the float32 value of its bfloat16 rounding (low half zero).
+__device__ __forceinline__ float round_bf16(float x) {
+  return from_bf16(to_bf16(x));
+}
+
+// Two bfloat16-exact float32 values (low halves zero) -> one packed word,
+// the even element in the low half.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// ---------------------------------------------------------------------------
+// Loads and stores through global-address-space pointers.  The buffers come
+// from the descriptor table, so without the cast the compiler cannot tell
+// them from LDS and would emit flat instructions.  Every tile has a uniform
+// base pointer (SGPRs) and each lane a 32-bit element offset, which maps to
+// global_load/store with an SGPR base and a VGPR offset.  The vector accesses
+// carry the nontemporal hint: every byte is touched once per launch, and on
+// gfx950 the streaming hint measured faster for these contiguous-per-wave
+// patterns (reads and read-modify-write streams alike).
+// ---------------------------------------------------------------------------
+
+#define MTA_GLOBAL __attribute__((address_space(1)))
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Element type of a buffer: float32, or bfloat16 bits.
+template <bool Bf16>
+using elem_t = typename std::conditional<Bf16, uint16_t, float>::type;
+
+template <typename T>
+__device__ __forceinline__ MTA_GLOBAL T *gp(const void *p, int64_t elem) {
+  return (MTA_GLOBAL T *)(p) + elem;
+}
+
+// 4 consecutive elements at element offset e (a multiple of 4) of a
+// 16-byte-aligned tile base: a 16-byte access for float32, 8 bytes for
+// bfloat16 (element 2k in the low half of word k).
+template <bool Bf16>
+__device__ __forceinline__ void load4(MTA_GLOBAL const elem_t<Bf16> *p,
+                                      uint32_t e, float (&x)[4]) {
+  if constexpr (Bf16) {
+    const u32x2 a = __builtin_nontemporal_load((const MTA_GLOBAL u32x2 *)(p + e));
+    x[0] = __uint_as_float(a.x << 16);
+    x[1] = __uint_as_float(a.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(a.y << 16);
+    x[3] = __uint_as_float(a.y & 0xFFFF0000u);
+  } else {
+    const f32x4 a = __builtin_nontemporal_load((const MTA_GLOBAL f32x4 *)(p + e));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
+}
+
+// The bfloat16 form stores values that are already bfloat16-exact.
+template <bool Bf16>
+__device__ __forceinline__ void store4(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
+                                       const float (&x)[4]) {
+  if constexpr (Bf16)
+    __builtin_nontemporal_store(u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])},
+                                (MTA_GLOBAL u32x2 *)(p + e));
+  else
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]},
+                                (MTA_GLOBAL f32x4 *)(p + e));
+}
+
+// 16 bytes per lane: 4 float32 or 8 bfloat16 elements at offset e.
+template <bool Bf16>
+constexpr int kWide = Bf16 ? 8 : 4;
+
+template <bool Bf16>
+__device__ __forceinline__ void load16b(MTA_GLOBAL const elem_t<Bf16> *p,
+                                        uint32_t e, float (&x)[kWide<Bf16>]) {
+  if constexpr (Bf16) {
+    const u32x4 a = __builtin_nontemporal_load((const MTA_GLOBAL u32x4 *)(p + e));
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = __builtin_nontemporal_load((const MTA_GLOBAL f32x4 *)(p + e));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
+}
+
+template <bool Bf16>
+__device__ __forceinline__ void store16b(MTA_GLOBAL elem_t<Bf16> *p,
+                                         uint32_t e,
+                                         const float (&x)[kWide<Bf16>]) {
+  if constexpr (Bf16)
+    __builtin_nontemporal_store(
+        u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]),
+              pack2(x[6], x[7])},
+        (MTA_GLOBAL u32x4 *)(p + e));
+  else
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]},
+                                (MTA_GLOBAL f32x4 *)(p + e));
+}
+
+template <bool Bf16>
+__device__ __forceinline__ float load1(MTA_GLOBAL const elem_t<Bf16> *p,
+                                       uint32_t e) {
+  if constexpr (Bf16)
+    return from_bf16(p[e]);
+  else
+    return p[e];
+}
+
+// Writes one element; for bfloat16 a 16-bit store of the (exact) value.
+template <bool Bf16>
+__device__ __forceinline__ void store1(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
+                                       float x) {
+  if constexpr (Bf16)
+    p[e] = static_cast<uint16_t>(__float_as_uint(x) >> 16);
+  else
+    p[e] = x;
+}
+
+// Elements of the tile that starts at element `base` of a tensor of n.
+__device__ __forceinline__ uint32_t tile_len(int64_t n, int64_t base) {
+  const int64_t left = n - base;
+  return left < kTileElems ? static_cast<uint32_t>(left) : kTileElems;
+}
+
+// ---------------------------------------------------------------------------
+// The AdamW element step ("BendTorch main.bend", Optimizers), with the
+// unscale (ScaleTensors) and the clip coefficient (ClipGradNorms) applied in
+// registers first.  Packed kinds round the new moment to bfloat16 and the
+// weight update reads the rounded value (adamh_l, adamhv_l).
+// ---------------------------------------------------------------------------
+
+template <bool MPacked, bool VPacked>
+__device__ __forceinline__ void adamw_elem(float &w, float g, float &m,
+                                           float &v, const StepScalars &sc,
+                                           float coef) {
+  const float x = g * sc.s;                          // unscale
+  const float ge = x * coef;                         // clip
+  const float wd = w * sc.dec;                       // adam_decay (AdamW)
+  float m1 = m + sc.c1 * (ge - m);                   // adam_m (lerp form)
+  float v1 = (v * sc.b2) + ((sc.c2 * ge) * ge);      // adam_v
+  if constexpr (MPacked) m1 = round_bf16(m1);
+  if constexpr (VPacked) v1 = round_bf16(v1);
+  const float denom = (sqrtf(v1) / sc.bc2) + sc.eps; // adam_w
+  w = wd + ((sc.nstep * m1) / denom);
+  m = m1;
+  v = v1;
+}
+
+constexpr int kAdamVec = 4;                                   // per access
+constexpr int kAdamGroups = kTileElems / (kBlock * kAdamVec); // 4
+constexpr uint32_t kAdamStride = kBlock * kAdamVec;           // 1024
+
+template <bool GBf16, bool MPacked, bool VPacked>
+__global__ void __launch_bounds__(kBlock)
+k_adamw(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
+        uint32_t ntiles, StepScalars sc, const float *__restrict__ d_coef) {
+  const float coef = d_coef ? *d_coef : 1.0f;
+  for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const Tile tl = tiles[t];
+    const TensorDesc d = td[tl.tensor];
+    const int64_t base = static_cast<int64_t>(tl.index) * kTileElems;
+    // tile base pointers (uniform); lanes address them with 32-bit offsets
+    MTA_GLOBAL float *__restrict__ pw = gp<float>(d.w, base);
+    MTA_GLOBAL const elem_t<GBf16> *__restrict__ pg =
+        gp<elem_t<GBf16>>(d.g, base);
+    MTA_GLOBAL elem_t<MPacked> *__restrict__ pm = gp<elem_t<MPacked>>(d.m, base);
+    MTA_GLOBAL elem_t<VPacked> *__restrict__ pv = gp<elem_t<VPacked>>(d.v, base);
+    const uint32_t lim = tile_len(d.n, base);
+    const uint32_t e0 = threadIdx.x * kAdamVec;
+
+    if (d.vec && lim == kTileElems) {
+      float w[kAdamGroups][kAdamVec], g[kAdamGroups][kAdamVec],
+          m[kAdamGroups][kAdamVec], v[kAdamGroups][kAdamVec];
+      // full tile of an aligned tensor: 4 accesses per buffer per lane
+      // group j addresses a uniform base (tile base + j*kAdamStride, SGPRs)
+      // plus the lane's offset e0: one offset VGPR serves every access
+#pragma unroll
+      for (int j = 0; j < kAdamGroups; ++j) {
+        const uint32_t gj = j * kAdamStride;
+        load4<false>(pw + gj, e0, w[j]);
+        load4<GBf16>(pg + gj, e0, g[j]);
+        load4<MPacked>(pm + gj, e0, m[j]);
+        load4<VPacked>(pv + gj, e0, v[j]);
+      }
+      // every load of the tile is in flight before the first use
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kAdamGroups; ++j)
+#pragma unroll
+        for (int k = 0; k < kAdamVec; ++k)
+          adamw_elem<MPacked, VPacked>(w[j][k], g[j][k], m[j][k], v[j][k], sc,
+                                       coef);
+#pragma unroll
+      for (int j = 0; j < kAdamGroups; ++j) {
+        const uint32_t gj = j * kAdamStride;
+        store4<false>(pw + gj, e0, w[j]);
+        store4<MPacked>(pm + gj, e0, m[j]);
+        store4<VPacked>(pv + gj, e0, v[j]);
+      }
+    } else {
+      // the tail tile of a tensor, or any tile of an unaligned tensor: the
+      // same element mapping, each element loaded and stored on its own and
+      // only inside the tile; a group's loads are issued before any use
+#pragma unroll 1
+      for (int j = 0; j < kAdamGroups; ++j) {
+        float wj[kAdamVec], gj[kAdamVec], mj[kAdamVec], vj[kAdamVec];
+#pragma unroll
+        for (int k = 0; k < kAdamVec; ++k) {
+          const uint32_t e = e0 + j * kAdamStride + k;
+          wj[k] = gj[k] = mj[k] = vj[k] = 0.0f;
+          if (e < lim) {
+            wj[k] = pw[e];
+            gj[k] = load1<GBf16>(pg, e);
+            mj[k] = load1<MPacked>(pm, e);
+            vj[k] = load1<VPacked>(pv, e);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kAdamVec; ++k) {
+          const uint32_t e = e0 + j * kAdamStride + k;
+          if (e < lim) {
+            adamw_elem<MPacked, VPacked>(wj[k], gj[k], mj[k], vj[k], sc, coef);
+            pw[e] = wj[k];
+            store1<MPacked>(pm, e, mj[k]);
+            store1<VPacked>(pv, e, vj[k]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Joint sum of squares, one launch in two stages.
+//   Stage 1 (every workgroup): each thread forms x = f32(g*s), squares it in
+//   float64 (exact, and free of the float32 overflow above 1.8e19) and
+//   accumulates with a float64 fma; the wave then reduces with DPP lane moves,
+//   the four waves combine through LDS, and the workgroup writes one float64
+//   partial.
+//   Stage 2 (the last workgroup to finish, chosen by an atomic ticket): one
+//   wave sums the partials in a fixed lane-strided order, takes the square
+//   root, forms the clip coefficient and writes both, then re-arms the ticket.
+// The grid and the tile order are fixed per list, so the result is the same
+// bits on every call.
+// ---------------------------------------------------------------------------
+
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_ror:4, row_ror:8.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int Ctrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), Ctrl, 0xF,
+                                             0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), Ctrl, 0xF,
+                                             0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes of a fully active wave; every lane gets the result.
+__device__ __forceinline__ double wave_sum(double x) {
+  x += dpp_f64<kDppQuadXor1>(x);  // pairs
+  x += dpp_f64<kDppQuadXor2>(x);  // quads
+  x += dpp_f64<kDppRowRor4>(x);   // every lane of a row: 2 quads
+  x += dpp_f64<kDppRowRor8>(x);   // every lane of a row: the row's 16 lanes
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) +
+         (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+
+template <bool GBf16>
+__global__ void __launch_bounds__(kBlock)
+k_sumsq(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
+        uint32_t ntiles, float s, float max_norm, double *__restrict__ partials,
+        unsigned int *__restrict__ ticket, float *__restrict__ d_norm,
+        float *__restrict__ d_coef) {
+  constexpr int V = kWide<GBf16>;
+  constexpr int G = kTileElems / (kBlock * V);
+  // Two tiles per iteration (t and t + gridDim.x): with bfloat16 gradients a
+  // tile is only 32 bytes per lane, so a lane keeps both tiles' loads in
+  // flight before its first fma.
+  constexpr int U = 2;
+  double acc[G] = {};
+  for (uint32_t t0 = blockIdx.x; t0 < ntiles; t0 += U * gridDim.x) {
+    float x[U][G][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t t = t0 + u * gridDim.x;
+      if (t >= ntiles) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int k = 0; k < V; ++k) x[u][j][k] = 0.0f;
+        continue;
+      }
+      const Tile tl = tiles[t];
+      const TensorDesc d = td[tl.tensor];
+      const int64_t base = static_cast<int64_t>(tl.index) * kTileElems;
+      MTA_GLOBAL const elem_t<GBf16> *__restrict__ pg =
+          gp<elem_t<GBf16>>(d.g, base);
+      const uint32_t lim = tile_len(d.n, base);
+      const uint32_t e0 = threadIdx.x * V;
+      if (d.vec && lim == kTileElems) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          load16b<GBf16>(pg + j * (kBlock * V), e0, x[u][j]);
+      } else {
+        // tail tile or unaligned tensor: same mapping, masked element loads
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const uint32_t e = e0 + j * (kBlock * V) + k;
+            x[u][j][k] = e < lim ? load1<GBf16>(pg, e) : 0.0f;
+          }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads in flight first
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          const double xs = static_cast<double>(x[u][j][k] * s);
+          acc[j] = fma(xs, xs, acc[j]);
+        }
+  }
+  double mine = acc[0];
+#pragma unroll
+  for (int j = 1; j < G; ++j) mine += acc[j];
+
+  __shared__ double wave_part[kBlock / 64];
+  __shared__ bool is_last;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const double wsum = wave_sum(mine);
+  if (lane == 0) wave_part[wave] = wsum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    partials[blockIdx.x] = (wave_part[0] + wave_part[1]) +
+                           (wave_part[2] + wave_part[3]);
+    // release (agent scope): the partial is visible before the ticket moves;
+    // no acquire here, so the other workgroups keep their caches
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned int prev = __hip_atomic_fetch_add(
+        ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+
+  // Stage 2: the finishing wave.
+  if (wave != 0) return;
+  // acquire (agent scope): every other workgroup's partial is visible
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  double a = 0.0;
+  for (uint32_t i = lane; i < gridDim.x; i += 64)
+    a += __hip_atomic_load(&partials[i], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  const double total = wave_sum(a);
+  if (lane == 0) {
+    const float nrm = static_cast<float>(sqrt(total));
+    // PyTorch's clip_grad_norm_: max / (norm + 1e-6), clamped at 1; the
+    // comparison lets a NaN through and an infinite norm gives 0.
+    const float c = max_norm / (nrm + 1e-6f);
+    if (d_norm) *d_norm = nrm;
+    *d_coef = (c > 1.0f) ? 1.0f : c;
+    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// ScaleTensors in place: g = g * s, a bfloat16 gradient rounded back to
+// nearest-even.
+// ---------------------------------------------------------------------------
+
+template <bool GBf16>
+__global__ void __launch_bounds__(kBlock)
+k_scale(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
+        uint32_t ntiles, float s) {
+  constexpr int V = kWide<GBf16>;
+  constexpr int G = kTileElems / (kBlock * V);
+  for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const Tile tl = tiles[t];
+    const TensorDesc d = td[tl.tensor];
+    const int64_t base = static_cast<int64_t>(tl.index) * kTileElems;
+    MTA_GLOBAL elem_t<GBf16> *__restrict__ pg = gp<elem_t<GBf16>>(d.g, base);
+    const uint32_t lim = tile_len(d.n, base);
+    const uint32_t e0 = threadIdx.x * V;
+    float x[G][V];
+    if (d.vec && lim == kTileElems) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) load16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
+      __builtin_amdgcn_sched_barrier(0);  // all loads in flight first
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          x[j][k] = x[j][k] * s;
+          if constexpr (GBf16) x[j][k] = round_bf16(x[j][k]);
+        }
+        store16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
+      }
+    } else {
+      // tail tile or unaligned tensor: same mapping, masked element accesses
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          const uint32_t e = e0 + j * (kBlock * V) + k;
+          x[j][k] = e < lim ? load1<GBf16>(pg, e) : 0.0f;
+        }
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          const uint32_t e = e0 + j * (kBlock * V) + k;
+          if (e < lim) {
+            float y = x[j][k] * s;
+            if constexpr (GBf16) y = round_bf16(y);
+            store1<GBf16>(pg, e, y);
+          }
+        }
+    }
+  }
+}
+
+template <bool G, bool M, bool V>
+hipError_t launch_adamw_t(const Work &wk, const StepScalars &sc,
+                          const float *d_coef) {
+  hipLaunchKernelGGL((k_adamw<G, M, V>), dim3(wk.grid), dim3(kBlock), 0,
+                     wk.stream, wk.td, wk.tiles, wk.ntiles, sc, d_coef);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_adamw(int gtype, int mkind, int vkind, const Work &wk,
+                        const StepScalars &sc, const float *d_coef) {
+  const int key = (gtype << 2) | (mkind << 1) | vkind;
+  switch (key) {
+    case 0: return launch_adamw_t<false, false, false>(wk, sc, d_coef);
+    case 1: return launch_adamw_t<false, false, true>(wk, sc, d_coef);
+    case 2: return launch_adamw_t<false, true, false>(wk, sc, d_coef);
+    case 3: return launch_adamw_t<false, true, true>(wk, sc, d_coef);
+    case 4: return launch_adamw_t<true, false, false>(wk, sc, d_coef);
+    case 5: return launch_adamw_t<true, false, true>(wk, sc, d_coef);
+    case 6: return launch_adamw_t<true, true, false>(wk, sc, d_coef);
+    case 7: return launch_adamw_t<true, true, true>(wk, sc, d_coef);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_sumsq(int gtype, const Work &wk, float s, float max_norm,
+                        NormScratch scr, float *d_norm, float *d_coef) {
+  if (gtype)
+    hipLaunchKernelGGL((k_sumsq<true>), dim3(wk.grid), dim3(kBlock), 0,
+                       wk.stream, wk.td, wk.tiles, wk.ntiles, s, max_norm,
+                       scr.partials, scr.ticket, d_norm, d_coef);
+  else
+    hipLaunchKernelGGL((k_sumsq<false>), dim3(wk.grid), dim3(kBlock), 0,
+                       wk.stream, wk.td, wk.tiles, wk.ntiles, s, max_norm,
+                       scr.partials, scr.ticket, d_norm, d_coef);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(int gtype, const Work &wk, float s) {
+  if (gtype)
+    hipLaunchKernelGGL((k_scale<true>), dim3(wk.grid), dim3(kBlock), 0,
+                       wk.stream, wk.td, wk.tiles, wk.ntiles, s);
+  else
+    hipLaunchKernelGGL((k_scale<false>), dim3(wk.grid), dim3(kBlock), 0,
+                       wk.stream, wk.td, wk.tiles, wk.ntiles, s);
+  return hipGetLastError();
+}
+
+}  // namespace mta

@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mta.h declares, validates arguments before touching the device, and
+prepares the step's float32 constants exactly as the oracle does."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import mixed_precision_optimizer_mta_amd as M
+from mixed_precision_optimizer_mta_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mta.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mta_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTS) == names
+
+
+def test_abi_version():
+    assert M.mta_abi_version() == 1
+
+
+def _err(fn, *a):
+    with pytest.raises(M.MtaError) as e:
+        fn(*a)
+    return e.value.code
+
+
+def test_create_rejects_bad_arguments_before_device_work():
+    ok = (0x10000, 0x20000, 0x30000, 0x40000, 64)
+    assert _err(M.mta_list_create, [ok], 2, 0, 0) == -3            # gtype
+    assert _err(M.mta_list_create, [ok], 0, 5, 0) == -3            # mkind
+    assert _err(M.mta_list_create, [ok], 0, 0, -1) == -3           # vkind
+    assert _err(M.mta_list_create, [(0x10000, 0, 0x30000, 0x40000, 64)],
+                0, 0, 0) == -1                                      # NULL g
+    assert _err(M.mta_list_create, [(0x10000, 0x20000, 0x30000, 0x40000,
+                                      -1)], 0, 0, 0) == -1          # n < 0
+    assert _err(M.mta_list_create, [(0x10002, 0x20000, 0x30000, 0x40000,
+                                      64)], 0, 0, 0) == -2          # w align
+    assert _err(M.mta_list_create, [(0x10000, 0x20001, 0x30000, 0x40000,
+                                      64)], 1, 0, 0) == -2          # bf16 g
+    # packed moments need only 2-byte alignment; f32 ones 4
+    assert _err(M.mta_list_create, [(0x10000, 0x20000, 0x30002, 0x40000,
+                                      64)], 0, 0, 0) == -2
+    # overlap inside a tensor and across tensors
+    assert _err(M.mta_list_create, [(0x10000, 0x10010, 0x30000, 0x40000,
+                                      64)], 0, 0, 0) == -1
+    assert _err(M.mta_list_create, [ok, (0x10080, 0x50000, 0x60000,
+                                         0x70000, 8)], 0, 0, 0) == -1
+    assert "overlap" in M.mta_last_error()
+
+
+def test_adjacent_buffers_are_not_overlap_and_empty_tensors_skip_checks():
+    # w of 64 float32 ends exactly where g starts: allowed.  Without a GPU
+    # the call then fails at the device step, not at validation.
+    ents = [(0x10000, 0x10100, 0x10200, 0x10300, 64), (0, 0, 0, 0, 0)]
+    try:
+        h = M.mta_list_create(ents, 0, 0, 0)
+    except M.MtaError as e:
+        assert e.code == -5, e            # no device here
+    else:                                   # a GPU is present
+        M.mta_list_destroy(h)
+
+
+def test_calls_on_a_null_handle_fail_cleanly():
+    assert _err(M.mta_clip_norm, None, 1.0, None, 0x1000) == -1
+    assert _err(M.mta_adamw_step, None, (1e-3, .9, .999, 1e-8, 0.), 1,
+                None) == -1
+    assert _err(M.mta_scale, None, 0.5, M.MTA_SCALE_DEFER) == -1
+    M.mta_list_destroy(None)
+
+
+@pytest.mark.parametrize("hp,t", [
+    ((1e-3, 1.0, 0.999, 1e-8, 0.0), 1),      # beta1 = 1
+    ((1e-3, 0.9, -0.1, 1e-8, 0.0), 1),       # beta2 < 0
+    ((-1e-3, 0.9, 0.999, 1e-8, 0.0), 1),     # lr < 0
+    ((float("nan"), 0.9, 0.999, 1e-8, 0.0), 1),
+    ((1e-3, 0.9, 0.999, -1e-8, 0.0), 1),     # eps < 0
+    ((1e-3, 0.9, 0.999, 1e-8, -0.1), 1),     # wd < 0
+    ((1e-3, 0.9, 0.999, 1e-8, 0.1), 0),      # t = 0
+])
+def test_hparams_validation(hp, t):
+    assert _err(M.mta_adamw_scalars, hp, t) == -1
+
+
+@pytest.mark.parametrize("hp", [(3e-4, 0.9, 0.999, 1e-8, 0.1),
+                                (3e-4, 0.9, 0.999, 1e-8, 0.01),
+                                (1e-2, 0.5, 0.75, 0.5, 0.5),
+                                (6e-4, 0.95, 0.98, 1e-6, 0.0),
+                                (1.0, 0.0, 0.0, 0.0, 0.0)])
+def test_scalars_match_the_oracle_bitwise(hp):
+    for t in list(range(1, 60)) + [100, 1000, 4567, 10 ** 6]:
+        got = np.array(M.mta_adamw_scalars(hp, t), dtype=np.float32)
+        want = O.scalars(*hp, t)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (
+            hp, t, got, want)

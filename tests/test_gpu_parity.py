@@ -1,0 +1,353 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every test here runs the hot path on the device -- mta_scale (deferred or
+in place), mta_clip_norm, mta_adamw_step -- and compares with the oracle
+element by element (lockstep protocol, see parity_util).  Small lists are
+compared in full; full-size lists at sampled positions plus the full norm.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_optimizer_mta_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+from parity_util import (check_norm, compare, oracle_grads,  # noqa: E402
+                         oracle_state, sample_positions)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import mixed_precision_optimizer_mta_amd as M
+    M.lib()          # libmta.so must load; there is no other path
+    yield
+    torch.cuda.synchronize()
+
+
+def make_list(arena):
+    from mixed_precision_optimizer_mta_amd import MtaList
+    wl = arena.wl
+    return MtaList([], entries=arena.entries(), gtype=wl.gtype,
+                   mkind=wl.mkind, vkind=wl.vkind)
+
+
+def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
+             check_guards=False, clip=True):
+    """Run `steps` device steps in lockstep with the oracle; returns the
+    worst ulp distances seen."""
+    arena = WL.Arena(wl, "cuda", offsets)
+    arena.fill_weights()
+    L = make_list(arena)
+    idx = None
+    if nsample is not None:
+        idx = sample_positions(wl, arena.offsets, nsample)
+    ostate = oracle_state(arena, idx)
+    before = None
+    if check_guards:
+        before = {b: getattr(arena, b).clone() for b in "wmv"}
+    norm_d = torch.full((1,), -1.0, device="cuda")
+    coef_d = torch.full((1,), -1.0, device="cuda")
+    worst = {"w": 0, "m": 0, "v": 0}
+    for t in range(1, steps + 1):
+        arena.fill_grads(t)
+        for o, g in zip(ostate, oracle_grads(arena, idx)):
+            o.g = g
+        if wl.scale != 1.0:
+            L.scale(wl.scale, defer=True)
+        if clip:
+            L.clip_norm(wl.max_norm, norm_d, coef_d)
+            L.adamw_step(wl.hparams, t, coef_d)
+        else:
+            L.adamw_step(wl.hparams, t, None)
+        torch.cuda.synchronize()
+        coef = np.float32(1.0)
+        if clip:
+            ng = np.float32(norm_d.item())
+            coef = np.float32(coef_d.item())
+            if norm_steps is None or t in norm_steps:
+                gs = oracle_grads(arena) if idx is not None else \
+                    [o.g for o in ostate]
+                no = O.norm(gs, wl.gtype, wl.scale)
+                check_norm(ng, coef, no, wl.max_norm, f"{wl.name} t={t}")
+            else:
+                want = O.clip_coef(wl.max_norm, ng)
+                assert coef.view(np.uint32) == want.view(np.uint32)
+        O.step_(ostate, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
+                wl.beta2, wl.eps, wl.weight_decay, t, s=wl.scale, coef=coef)
+        got = compare(arena, ostate, idx, f"{wl.name} t={t}")
+        worst = {k: max(worst[k], got[k]) for k in worst}
+    if check_guards:
+        torch.cuda.synchronize()
+        inside = torch.zeros(arena.total, dtype=torch.bool, device="cuda")
+        for o, n in zip(arena.offsets, wl.sizes):
+            inside[o:o + n] = True
+        for b in "wmv":
+            now = getattr(arena, b)
+            diff = (now.view(torch.int16 if now.dtype == torch.bfloat16
+                             else torch.int32) !=
+                    before[b].view(torch.int16 if now.dtype == torch.bfloat16
+                                   else torch.int32)) & ~inside
+            assert not bool(diff.any()), f"{b} written outside its tensors"
+    L.close()
+    print(f"{wl.name}: steps={steps} worst ulp {worst}", flush=True)
+    return worst
+
+
+# ---------------------------------------------------------------- small lists
+
+SMALL = {
+    "gpt2_124m": WL.gpt2_sizes(1000, 64, 128, 2, 256),
+    "gpt2_124m_bf16g": WL.gpt2_sizes(1000, 64, 128, 2, 256),
+    "gpt2_xl": WL.gpt2_sizes(1000, 96, 64, 3, 384),
+}
+
+
+def small(name):
+    wl = WL.get(name)
+    if name == "tiny":
+        return wl
+    if name == "ragged":
+        rng = np.random.default_rng(77)
+        u = rng.random(300)
+        sizes = [int(max(1, np.floor(2.0 ** (14 * x)))) for x in u]
+        sizes += [1000 * 64] * 2
+        zero = [int(i) for i in rng.permutation(300)[:3]]
+        return WL.scaled_down(wl, sizes, zero_grad=zero)
+    return WL.scaled_down(wl, SMALL[name])
+
+
+@pytest.mark.parametrize("name", WL.NAMES)
+def test_small_lists_lockstep(name):
+    wl = small(name)
+    steps = wl.steps if name != "gpt2_124m" else 5
+    worst = lockstep(wl, steps, check_guards=True)
+    # the arithmetic is the same sequence of correctly rounded operations on
+    # both sides: expect identical bits, not just the tolerance
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+ALL_KINDS = [(g, m, v) for g in (0, 1) for m in (0, 1) for v in (0, 1)]
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind", ALL_KINDS)
+def test_edge_sizes_every_kind(gtype, mkind, vkind):
+    sizes = [0, 1, 2, 3, 7, 8, 9, 15, 17, 4095, 4096, 4097, 8191, 8193,
+             3 * 4096 + 5]
+    wl = WL.Workload("edges", sizes, gtype, mkind, vkind, steps=3,
+                     g_sigma=0.3, ident=11)
+    worst = lockstep(wl, 3, check_guards=True)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind", [(0, 0, 0), (1, 1, 0),
+                                               (1, 1, 1)])
+def test_unaligned_tensors_take_the_element_path(gtype, mkind, vkind):
+    # element offsets of 1 (mod 8) break 16-byte alignment of every buffer
+    sizes = [5000, 4096, 33, 9000]
+    offsets, pos = [], 0
+    for n in sizes:
+        offsets.append(pos + 1)             # 1 (mod 8): 4 or 2 bytes off
+        pos += -(-(n + 1) // 8) * 8 + 8
+    wl = WL.Workload("unaligned", sizes, gtype, mkind, vkind, steps=2,
+                     ident=12)
+    arena = WL.Arena(wl, "cuda", offsets)
+    L = make_list(arena)
+    assert L.info()["vector_tensors"] == 0
+    L.close()
+    worst = lockstep(wl, 2, offsets=offsets, check_guards=True)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+def test_no_clip_and_clip_at_one_agree():
+    wl = small("gpt2_124m")
+    wl = WL.scaled_down(wl, wl.sizes)
+    wl.max_norm = 1e30
+    a = lockstep(wl, 2)
+    b = lockstep(wl, 2, clip=False)
+    assert a == b == {"w": 0, "m": 0, "v": 0}
+
+
+def test_nonfinite_gradients_propagate():
+    for bad in (np.nan, np.inf):
+        wl = WL.Workload("nonfinite", [4096 * 2 + 7, 100], 0, 0, 0, steps=1,
+                         ident=13)
+        arena = WL.Arena(wl, "cuda")
+        arena.fill_weights()
+        arena.fill_grads(1)
+        arena.g[arena.offsets[0] + 5] = float(bad)
+        ostate = oracle_state(arena)
+        L = make_list(arena)
+        nd = torch.zeros(1, device="cuda")
+        cd = torch.zeros(1, device="cuda")
+        L.clip_norm(1.0, nd, cd)
+        L.adamw_step(wl.hparams, 1, cd)
+        torch.cuda.synchronize()
+        no = O.norm([o.g for o in ostate], 0)
+        check_norm(np.float32(nd.item()), np.float32(cd.item()), no, 1.0)
+        O.step_(ostate, 0, 0, 0, wl.lr, wl.beta1, wl.beta2, wl.eps,
+                wl.weight_decay, 1, coef=np.float32(cd.item()))
+        compare(arena, ostate)
+        L.close()
+
+
+def test_empty_list_and_empty_tensors():
+    from mixed_precision_optimizer_mta_amd import MtaList
+    L = MtaList([], entries=[], gtype=0, mkind=0, vkind=0)
+    nd = torch.full((1,), 7.0, device="cuda")
+    cd = torch.full((1,), 7.0, device="cuda")
+    L.clip_norm(1.0, nd, cd)
+    L.adamw_step(dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                      weight_decay=0.0), 1, cd)
+    torch.cuda.synchronize()
+    assert nd.item() == 0.0 and cd.item() == 1.0
+    assert L.info()["tiles"] == 0
+    L.close()
+    wl = WL.Workload("zeros", [0, 0, 5, 0], 0, 1, 1, steps=2, ident=14)
+    assert lockstep(wl, 2) == {"w": 0, "m": 0, "v": 0}
+
+
+def test_deferred_scale_equals_in_place_for_f32():
+    wl = WL.scaled_down(small("gpt2_124m"), SMALL["gpt2_124m"])
+    res = []
+    for defer in (True, False):
+        arena = WL.Arena(wl, "cuda")
+        arena.fill_weights()
+        arena.fill_grads(1)
+        L = make_list(arena)
+        cd = torch.zeros(1, device="cuda")
+        L.scale(0.3, defer=defer)
+        L.clip_norm(0.05, None, cd)
+        L.adamw_step(wl.hparams, 1, cd)
+        torch.cuda.synchronize()
+        res.append((arena.w.clone(), arena.m.clone(), arena.v.clone(),
+                    cd.item()))
+        L.close()
+    (w1, m1, v1, c1), (w2, m2, v2, c2) = res
+    assert c1 == c2
+    assert torch.equal(w1, w2) and torch.equal(m1, m2) and torch.equal(v1, v2)
+
+
+@pytest.mark.parametrize("gtype", [0, 1])
+def test_in_place_scale_matches_oracle(gtype):
+    sizes = [1, 4096 * 3, 4097, 77]
+    wl = WL.Workload("scale", sizes, gtype, 0, 0, steps=1, g_sigma=50.0,
+                     ident=15)
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_grads(1)
+    gs = oracle_grads(arena)
+    L = make_list(arena)
+    for s in (2.0 ** -16, 0.3):
+        L.scale(s, defer=False)
+        torch.cuda.synchronize()
+        for g in gs:
+            O.scale_(g, gtype, s)
+        got = oracle_grads(arena)
+        for a, b in zip(got, gs):
+            assert np.array_equal(a.view(np.uint16 if gtype else np.uint32),
+                                  b.view(np.uint16 if gtype else np.uint32))
+    L.close()
+
+
+def test_deferred_scale_state_machine():
+    from mixed_precision_optimizer_mta_amd import MtaError
+    wl = WL.Workload("defer", [100], 1, 0, 0, steps=1, ident=16)
+    arena = WL.Arena(wl, "cuda")
+    L = make_list(arena)
+    L.scale(0.5, defer=True)
+    with pytest.raises(MtaError) as e:
+        L.scale(0.5, defer=True)
+    assert e.value.code == -6
+    with pytest.raises(MtaError):
+        L.adamw_step(dict(lr=1e-3, beta1=1.0, beta2=0.999, eps=1e-8,
+                          weight_decay=0.0), 1)
+    L.adamw_step(wl.hparams, 1)         # consumes the factor
+    L.scale(0.5, defer=True)            # allowed again
+    L.adamw_step(wl.hparams, 2)
+    torch.cuda.synchronize()
+    L.close()
+
+
+def test_deterministic_and_rearmed_ticket():
+    wl = WL.scaled_down(small("gpt2_124m"), SMALL["gpt2_124m"])
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_weights()
+    arena.fill_grads(1)
+    L = make_list(arena)
+    norms = []
+    nd = torch.zeros(1, device="cuda")
+    cd = torch.zeros(1, device="cuda")
+    for _ in range(20):
+        L.clip_norm(1.0, nd, cd)
+        norms.append(nd.clone())
+    torch.cuda.synchronize()
+    bits = {int(n.view(torch.int32).item()) for n in norms}
+    assert len(bits) == 1
+    # two identical states stepped separately end in identical bits
+    w0, m0, v0 = arena.w.clone(), arena.m.clone(), arena.v.clone()
+    L.adamw_step(wl.hparams, 1, cd)
+    w1, m1, v1 = arena.w.clone(), arena.m.clone(), arena.v.clone()
+    arena.w.copy_(w0), arena.m.copy_(m0), arena.v.copy_(v0)
+    L.adamw_step(wl.hparams, 1, cd)
+    torch.cuda.synchronize()
+    assert torch.equal(w1, arena.w) and torch.equal(m1, arena.m) and \
+        torch.equal(v1, arena.v)
+    L.close()
+
+
+def test_tensor_order_does_not_change_results():
+    wl = small("ragged")
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_weights()
+    arena.fill_grads(1)
+    ents = arena.entries()
+    coef = torch.full((1,), 0.37, device="cuda")
+    outs = []
+    for perm in (np.arange(len(ents)), np.random.default_rng(3).permutation(
+            len(ents))):
+        arena.fill_weights()
+        from mixed_precision_optimizer_mta_amd import MtaList
+        L = MtaList([], entries=[ents[i] for i in perm], gtype=wl.gtype,
+                    mkind=wl.mkind, vkind=wl.vkind)
+        L.scale(wl.scale, defer=True)
+        L.adamw_step(wl.hparams, 1, coef)
+        torch.cuda.synchronize()
+        outs.append((arena.w.clone(), arena.m.clone(), arena.v.clone()))
+        L.close()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- full size
+
+def test_full_tiny():
+    assert lockstep(WL.get("tiny"), 10) == {"w": 0, "m": 0, "v": 0}
+
+
+def test_full_gpt2_124m_every_element():
+    wl = WL.get("gpt2_124m")
+    worst = lockstep(wl, wl.steps)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+def test_full_gpt2_124m_bf16_grads_100_steps_sampled():
+    wl = WL.get("gpt2_124m_bf16g")
+    worst = lockstep(wl, wl.steps, nsample=1 << 18,
+                     norm_steps={1, 2, 3, 10, 50, 99, 100})
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+def test_full_gpt2_xl_packed_sampled():
+    wl = WL.get("gpt2_xl")
+    worst = lockstep(wl, wl.steps, nsample=1 << 20)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+def test_full_ragged_sampled():
+    wl = WL.get("ragged")
+    worst = lockstep(wl, wl.steps, nsample=1 << 20)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst

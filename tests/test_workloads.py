@@ -1,0 +1,43 @@
+"""The synthetic workloads have the shapes and parameter counts stated for
+them, and their seeded inputs are reproducible."""
+import numpy as np
+import torch
+
+from mixed_precision_optimizer_mta_amd import workloads as WL
+
+
+def test_parameter_counts():
+    assert WL.get("tiny").n == 738_816 and WL.get("tiny").count == 3
+    c2 = WL.get("gpt2_124m")
+    assert c2.n == 124_419_840 and c2.count == 110
+    assert WL.get("gpt2_124m_bf16g").n == c2.n
+    c4 = WL.get("gpt2_xl")
+    assert c4.n == 1_557_454_400 and c4.count == 434
+    assert all(n % 2 == 0 for n in c4.sizes)
+    c5 = WL.get("ragged")
+    assert c5.count == 10_002 and len(c5.zero_grad) == 100
+    assert 8.0e8 < c5.n < 9.2e8
+    small = np.array(c5.sizes[:10_000])
+    assert small.min() >= 1 and small.max() <= 2 ** 20
+    assert 0.10 < np.mean(small < 8) < 0.20
+    assert 0.45 < np.mean(small % 2 == 1) < 0.60
+
+
+def test_bytes_per_param():
+    assert WL.get("gpt2_124m").bytes_per_param() == {"norm": 4, "update": 28}
+    assert WL.get("gpt2_124m_bf16g").bytes_per_param() == {"norm": 2,
+                                                          "update": 26}
+    assert WL.get("gpt2_xl").bytes_per_param() == {"norm": 4, "update": 20}
+    assert WL.get("ragged").bytes_per_param() == {"norm": 2, "update": 22}
+
+
+def test_seeded_inputs_reproduce_on_cpu():
+    wl = WL.scaled_down(WL.get("ragged"), [5, 300, 4097], zero_grad=[1])
+    a, b = WL.Arena(wl, "cpu"), WL.Arena(wl, "cpu")
+    for x in (a, b):
+        x.fill_weights()
+        x.fill_grads(3)
+    assert torch.equal(a.w, b.w) and torch.equal(a.g, b.g)
+    assert not bool(a.view("g", 1).any())
+    assert bool(a.view("g", 2).any())
+    assert all(o % WL.ALIGN_ELEMS == 0 for o in a.offsets)
