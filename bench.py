@@ -87,6 +87,10 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--cpu-steps", type=int, default=3,
                     help="oracle steps of the CPU baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run torch's device copy of 1 GiB, 5 times: "
+                         "the known-size kernel that scales the HBM byte "
+                         "counters of a profile")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU "
@@ -101,6 +105,18 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 28                      # 1 GiB of float32 each way
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n,
+                          "calibrate_copy_bytes_written": 4 * n,
+                          "launches": 5}), flush=True)
+        return
     M.lib()
     wl = WL.get(args.workload)
     arena = WL.Arena(wl, "cuda")

@@ -68,11 +68,11 @@ bool debug_sync() {
 
 // Workgroups per compute unit of the persistent launches.  A workgroup is
 // four wave64s; the grid walks the tile table with a grid stride.  Measured
-// on gfx950 (MI355X): the update streams within noise from 2 to 16
-// workgroups per CU and 8 is the most even across the lists; the norm pays
-// one release fence and one ticket atomic per workgroup, so it runs fastest
-// with few workgroups that each keep two tiles of loads in flight.
-constexpr int kUpdateBlocksPerCu = 8;
+// on gfx950 (MI355X): the update streams best with one long-lived workgroup
+// per CU that keeps two tiles of loads in flight (fewer concurrent streams,
+// better HBM page locality); the norm pays one release fence and one ticket
+// atomic per workgroup and runs fastest with two per CU.
+constexpr int kUpdateBlocksPerCu = 1;
 constexpr int kNormBlocksPerCu = 2;
 
 int after_launch(hipError_t e, hipStream_t stream, const char *what) {
