@@ -1,6 +1,6 @@
 // mta_host.cpp -- host runtime and C ABI of libmta (see include/mta.h).
 //
-// Validation, the per-list device table (tensor descriptors + tile table),
+// Validation, the per-list device tables (one record per tile),
 // the float64 -> float32 scalar preparation of each AdamW step, the launch
 // policy, and error reporting.  No C++ exception crosses the ABI.
 #include <hip/hip_runtime.h>
@@ -26,9 +26,9 @@ struct mta_list {
   int grid_update = 1;
   int grid_norm = 1;
   int vector_tensors = 0;
-  void *dev_block = nullptr;  // one allocation: descriptors, tiles, scratch
-  mta::TensorDesc *d_td = nullptr;
-  mta::Tile *d_tiles = nullptr;
+  void *dev_block = nullptr;  // one allocation: tile tables, norm scratch
+  mta::GradTile *d_gtiles = nullptr;
+  mta::StepTile *d_stiles = nullptr;
   double *d_partials = nullptr;
   unsigned int *d_ticket = nullptr;
   bool deferred = false;  // a MTA_SCALE_DEFER factor is pending
@@ -70,10 +70,14 @@ bool debug_sync() {
 // four wave64s; the grid walks the tile table with a grid stride.  Measured
 // on gfx950 (MI355X): the update streams best with one long-lived workgroup
 // per CU that keeps two tiles of loads in flight (fewer concurrent streams,
-// better HBM page locality); the norm pays one release fence and one ticket
-// atomic per workgroup and runs fastest with two per CU.
+// better HBM page locality).  The norm pays one release fence and one ticket
+// atomic per workgroup, so it wants few workgroups, each with two tiles of
+// loads in flight: one per CU for float32 gradients, two for bfloat16 ones
+// (half the bytes per tile, so twice the workgroups for the same bytes in
+// flight).
 constexpr int kUpdateBlocksPerCu = 1;
-constexpr int kNormBlocksPerCu = 2;
+constexpr int kNormBlocksPerCuF32 = 1;
+constexpr int kNormBlocksPerCuBf16 = 2;
 
 int after_launch(hipError_t e, hipStream_t stream, const char *what) {
   if (e != hipSuccess)
@@ -150,8 +154,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 mta::Work work_of(const mta_list *L, int grid, void *stream) {
   mta::Work w;
-  w.td = L->d_td;
-  w.tiles = L->d_tiles;
+  w.gtiles = L->d_gtiles;
+  w.stiles = L->d_stiles;
   w.ntiles = L->ntiles;
   w.grid = grid;
   w.stream = static_cast<hipStream_t>(stream);
@@ -193,13 +197,12 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   const uintptr_t msz = mkind == MTA_MOM_BF16X2 ? 2 : 4;
   const uintptr_t vsz = vkind == MTA_MOM_BF16X2 ? 2 : 4;
 
-  std::vector<mta::TensorDesc> td;
-  std::vector<mta::Tile> tiles;
+  std::vector<mta::GradTile> gtiles;
+  std::vector<mta::StepTile> stiles;
   std::vector<Span> spans;
   int64_t elements = 0;
   int vec_tensors = 0;
   try {
-    td.resize(static_cast<size_t>(count));
     spans.reserve(static_cast<size_t>(count) * 4);
     uint64_t ntiles = 0;
     for (int64_t i = 0; i < count; ++i) {
@@ -209,14 +212,6 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
       if (x.n > (INT64_MAX / 8))
         return fail(MTA_EINVAL, "tensor %lld: n too large",
                     static_cast<long long>(i));
-      mta::TensorDesc &d = td[static_cast<size_t>(i)];
-      d.w = x.w;
-      d.g = x.g;
-      d.m = x.m;
-      d.v = x.v;
-      d.n = x.n;
-      d.vec = 0;
-      d.pad = 0;
       if (x.n == 0) continue;
       if (!x.w || !x.g || !x.m || !x.v)
         return fail(MTA_EINVAL, "tensor %lld: a buffer pointer is NULL",
@@ -226,11 +221,9 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
         return fail(MTA_EALIGN,
                     "tensor %lld: a buffer is not aligned to its element size",
                     static_cast<long long>(i));
-      d.vec = (aligned(x.w, 16) && aligned(x.g, 16) && aligned(x.m, 16) &&
-               aligned(x.v, 16))
-                  ? 1u
-                  : 0u;
-      vec_tensors += static_cast<int>(d.vec);
+      const bool vec = aligned(x.w, 16) && aligned(x.g, 16) &&
+                       aligned(x.m, 16) && aligned(x.v, 16);
+      vec_tensors += vec ? 1 : 0;
       const uintptr_t n = static_cast<uintptr_t>(x.n);
       const void *bufs[4] = {x.w, x.g, x.m, x.v};
       const uintptr_t sizes[4] = {4, gsz, msz, vsz};
@@ -242,7 +235,8 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
       const uint64_t nt = (static_cast<uint64_t>(x.n) + mta::kTileElems - 1) /
                           mta::kTileElems;
       ntiles += nt;
-      if (ntiles > UINT32_MAX) return fail(MTA_EINVAL, "list too large");
+      // tile numbers and grid strides stay below 2^32 (no wrap-around)
+      if (ntiles > (uint64_t{1} << 31)) return fail(MTA_EINVAL, "list too large");
     }
     std::sort(spans.begin(), spans.end(),
               [](const Span &a, const Span &b) { return a.lo < b.lo; });
@@ -255,13 +249,33 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
                     static_cast<long long>(spans[k].tensor),
                     names[spans[k].which]);
     }
-    tiles.reserve(static_cast<size_t>(ntiles));
+    // one record per tile: buffer addresses offset to the tile's first
+    // element, its length, and whether the vector path may be taken
+    gtiles.reserve(static_cast<size_t>(ntiles));
+    stiles.reserve(static_cast<size_t>(ntiles));
     for (int64_t i = 0; i < count; ++i) {
-      const int64_t n = td[static_cast<size_t>(i)].n;
-      const int64_t nt = (n + mta::kTileElems - 1) / mta::kTileElems;
-      for (int64_t k = 0; k < nt; ++k)
-        tiles.push_back(mta::Tile{static_cast<uint32_t>(i),
-                                  static_cast<uint32_t>(k)});
+      const mta_tensor &x = tensors[i];
+      const bool vec = aligned(x.w, 16) && aligned(x.g, 16) &&
+                       aligned(x.m, 16) && aligned(x.v, 16);
+      for (int64_t base = 0; base < x.n; base += mta::kTileElems) {
+        const int64_t left = x.n - base;
+        const uint32_t lim = static_cast<uint32_t>(
+            left < mta::kTileElems ? left : mta::kTileElems);
+        const uintptr_t b = static_cast<uintptr_t>(base);
+        const auto at = [b](const void *p, uintptr_t size) {
+          return reinterpret_cast<char *>(const_cast<void *>(p)) + b * size;
+        };
+        gtiles.push_back(mta::GradTile{at(x.g, gsz), lim, vec ? 1u : 0u});
+        mta::StepTile st;
+        st.w = reinterpret_cast<float *>(at(x.w, 4));
+        st.g = at(x.g, gsz);
+        st.m = at(x.m, msz);
+        st.v = at(x.v, vsz);
+        st.lim = lim;
+        st.vec = vec ? 1u : 0u;
+        st.pad = 0;
+        stiles.push_back(st);
+      }
     }
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
@@ -285,21 +299,23 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->vkind = vkind;
   L->count = count;
   L->elements = elements;
-  L->ntiles = static_cast<uint32_t>(tiles.size());
+  L->ntiles = static_cast<uint32_t>(stiles.size());
   L->vector_tensors = vec_tensors;
   const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
-  const int bpc_n = env_int("MTA_NORM_BLOCKS_PER_CU", kNormBlocksPerCu, 1, 64);
+  const int bpc_n = env_int(
+      "MTA_NORM_BLOCKS_PER_CU",
+      gtype == MTA_BF16 ? kNormBlocksPerCuBf16 : kNormBlocksPerCuF32, 1, 64);
   const int64_t tiles_or_one = std::max<int64_t>(1, L->ntiles);
   L->grid_update = static_cast<int>(
       std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_u));
   L->grid_norm = static_cast<int>(
       std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_n));
 
-  const size_t off_td = 0;
-  const size_t off_tiles =
-      round_up(off_td + td.size() * sizeof(mta::TensorDesc), 256);
+  const size_t off_gt = 0;
+  const size_t off_st =
+      round_up(off_gt + gtiles.size() * sizeof(mta::GradTile), 256);
   const size_t off_part =
-      round_up(off_tiles + tiles.size() * sizeof(mta::Tile), 256);
+      round_up(off_st + stiles.size() * sizeof(mta::StepTile), 256);
   const size_t off_ticket =
       round_up(off_part + static_cast<size_t>(L->grid_norm) * sizeof(double),
                256);
@@ -311,20 +327,21 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
     return fail(MTA_ENOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
   }
   char *base = static_cast<char *>(L->dev_block);
-  L->d_td = reinterpret_cast<mta::TensorDesc *>(base + off_td);
-  L->d_tiles = reinterpret_cast<mta::Tile *>(base + off_tiles);
+  L->d_gtiles = reinterpret_cast<mta::GradTile *>(base + off_gt);
+  L->d_stiles = reinterpret_cast<mta::StepTile *>(base + off_st);
   L->d_partials = reinterpret_cast<double *>(base + off_part);
   L->d_ticket = reinterpret_cast<unsigned int *>(base + off_ticket);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   e = hipSuccess;
-  if (!td.empty())
-    e = hipMemcpyAsync(L->d_td, td.data(), td.size() * sizeof(mta::TensorDesc),
+  if (!gtiles.empty())
+    e = hipMemcpyAsync(L->d_gtiles, gtiles.data(),
+                       gtiles.size() * sizeof(mta::GradTile),
                        hipMemcpyHostToDevice, s);
-  if (e == hipSuccess && !tiles.empty())
-    e = hipMemcpyAsync(L->d_tiles, tiles.data(),
-                       tiles.size() * sizeof(mta::Tile), hipMemcpyHostToDevice,
-                       s);
+  if (e == hipSuccess && !stiles.empty())
+    e = hipMemcpyAsync(L->d_stiles, stiles.data(),
+                       stiles.size() * sizeof(mta::StepTile),
+                       hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(L->d_ticket, 0, 256, s);
   // the host vectors die with this call: wait for the copies
   if (e == hipSuccess) e = hipStreamSynchronize(s);

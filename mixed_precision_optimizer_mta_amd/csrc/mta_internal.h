@@ -14,23 +14,31 @@ namespace mta {
 constexpr int kBlock = 256;       // threads per workgroup (4 wave64s)
 constexpr int kTileElems = 4096;  // 16 elements per thread
 
-// One tensor of the list as the kernels see it (device-resident table).
-struct TensorDesc {
+// The kernels read one self-contained record per tile, built once per list:
+// its buffers' addresses already offset to the tile's first element, the
+// number of elements in it, and whether all of them are 16-byte aligned.  One
+// scalar load of the record is all a workgroup needs before it can issue the
+// tile's vector loads (no second, dependent lookup of a tensor descriptor).
+
+// k_sumsq and k_scale read only the gradient.
+struct GradTile {
+  const void *g;
+  uint32_t lim;  // elements in this tile, 1..kTileElems
+  uint32_t vec;  // 1: the gradient buffer is 16-byte aligned
+};
+static_assert(sizeof(GradTile) == 16, "gradient tile layout");
+
+// k_adamw reads and writes all four buffers.
+struct StepTile {
   float *w;
   const void *g;
   void *m;
   void *v;
-  int64_t n;
-  uint32_t vec;  // 1: all four buffers 16-byte aligned -> vector path
-  uint32_t pad;
+  uint32_t lim;  // elements in this tile, 1..kTileElems
+  uint32_t vec;  // 1: all four buffers 16-byte aligned
+  uint64_t pad;
 };
-static_assert(sizeof(TensorDesc) == 48, "descriptor layout");
-
-struct Tile {
-  uint32_t tensor;  // index into the descriptor table
-  uint32_t index;   // tile number inside the tensor: first element = index * kTileElems
-};
-static_assert(sizeof(Tile) == 8, "tile layout");
+static_assert(sizeof(StepTile) == 48, "step tile layout");
 
 // Per-call float32 constants of the AdamW step (formed on the host in float64,
 // rounded once).  nstep = -step: negation is exact, so (-step)*m is unchanged.
@@ -40,8 +48,8 @@ struct StepScalars {
 };
 
 struct Work {
-  const TensorDesc *td;
-  const Tile *tiles;
+  const GradTile *gtiles;
+  const StepTile *stiles;
   uint32_t ntiles;
   int grid;
   hipStream_t stream;

@@ -11,9 +11,10 @@
 //            bfloat16 moments of adamh_l / adamhv_l (ph_of_bits, ph_to).
 //   k_scale  ScaleTensors in place (same Mica section).
 //
-// Work is cut into tiles of kTileElems elements of one tensor (the tile table
-// is built once per list on the host).  A persistent grid walks the tiles with
-// a grid stride.  Inside a full tile of a 16-byte-aligned tensor every wave
+// Work is cut into tiles of kTileElems elements of one tensor.  The tile
+// tables are built once per list on the host: each record holds the tile's
+// own buffer addresses, length and alignment, so one scalar load describes a
+// tile.  A persistent grid walks the tiles with a grid stride.  Inside a full tile of a 16-byte-aligned tensor every wave
 // instruction reads or writes one contiguous run of memory: lane l of group j
 // owns elements j*G + V*l .. j*G + V*l + V-1, where V is 4 for k_adamw (a
 // 16-byte access of a float32 buffer, 8 bytes of a bfloat16 one, so all four
@@ -183,12 +184,6 @@ __device__ __forceinline__ void store1(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
     p[e] = x;
 }
 
-// Elements of the tile that starts at element `base` of a tensor of n.
-__device__ __forceinline__ uint32_t tile_len(int64_t n, int64_t base) {
-  const int64_t left = n - base;
-  return left < kTileElems ? static_cast<uint32_t>(left) : kTileElems;
-}
-
 // Element e of a tile of `lim` (>= 1) elements, or 0 past its end.  The
 // address is clamped to the tile's last element, so the load is always in
 // bounds and needs no branch: every such load of a loop issues back to back.
@@ -277,18 +272,14 @@ struct TileRef {
 
 template <bool GBf16, bool MPacked, bool VPacked>
 __device__ __forceinline__ TileRef<GBf16, MPacked, VPacked> tile_ref(
-    const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
-    uint32_t t) {
-  const Tile tl = tiles[t];
-  const TensorDesc d = td[tl.tensor];
-  const int64_t base = static_cast<int64_t>(tl.index) * kTileElems;
+    const StepTile &st) {
   TileRef<GBf16, MPacked, VPacked> r;
-  r.pw = gp<float>(d.w, base);
-  r.pg = gp<elem_t<GBf16>>(d.g, base);
-  r.pm = gp<elem_t<MPacked>>(d.m, base);
-  r.pv = gp<elem_t<VPacked>>(d.v, base);
-  r.lim = tile_len(d.n, base);
-  r.full = d.vec && r.lim == kTileElems;
+  r.pw = gp<float>(st.w, 0);
+  r.pg = gp<elem_t<GBf16>>(st.g, 0);
+  r.pm = gp<elem_t<MPacked>>(st.m, 0);
+  r.pv = gp<elem_t<VPacked>>(st.v, 0);
+  r.lim = st.lim;
+  r.full = st.vec && st.lim == kTileElems;
   return r;
 }
 
@@ -361,35 +352,40 @@ __device__ __forceinline__ void partial_tile(
 
 template <bool GBf16, bool MPacked, bool VPacked>
 __global__ void __launch_bounds__(kBlock)
-k_adamw(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
-        uint32_t ntiles, StepScalars sc, const float *__restrict__ d_coef) {
+k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
+        const float *__restrict__ d_coef) {
   using Regs = TileRegs<GBf16, MPacked, VPacked>;
   using Ref = TileRef<GBf16, MPacked, VPacked>;
   const float coef = d_coef ? *d_coef : 1.0f;
   const uint32_t e0 = threadIdx.x * kAdamVec;
   uint32_t t = blockIdx.x;
   if (t >= ntiles) return;
+  const uint32_t last = ntiles - 1;
   Regs A, B;
-  Ref cur = tile_ref<GBf16, MPacked, VPacked>(td, tiles, t);
+  Ref cur = tile_ref<GBf16, MPacked, VPacked>(tiles[t]);
+  // the record of the next tile, read one iteration ahead (clamped to the
+  // last tile, so the scalar load is always in bounds)
+  StepTile rec = tiles[min(t + gridDim.x, last)];
   if (cur.full) issue_tile(A, cur, e0);
-  // one iteration: prefetch tile t + gridDim.x into Y, then finish tile t
-  // from X; two iterations per loop trip so X and Y alternate by name
+  // one iteration: issue every load of tile t + gridDim.x into Y, then the
+  // scalar load of the record after it, then compute and store tile t from
+  // X; two iterations per loop trip so X and Y alternate by name
   auto step = [&](Regs &X, Regs &Y) -> bool {
     const uint32_t tn = t + gridDim.x;
-    Ref nxt;
-    nxt.full = false;
-    nxt.lim = 0;
-    if (tn < ntiles) {
-      nxt = tile_ref<GBf16, MPacked, VPacked>(td, tiles, tn);
-      if (nxt.full) issue_tile(Y, nxt, e0);
-    }
+    const bool more = tn < ntiles;
+    const Ref nxt = tile_ref<GBf16, MPacked, VPacked>(rec);
+    if (more && nxt.full) issue_tile(Y, nxt, e0);
+    // only now the next record: scalar loads return out of order, so a wait
+    // for `rec` placed before the vector loads would also wait for this one
+    __builtin_amdgcn_sched_barrier(0);
+    rec = tiles[min(tn + gridDim.x, last)];
     if (cur.full)
       finish_tile(X, cur, e0, sc, coef);
     else
       partial_tile(cur, e0, sc, coef);
     cur = nxt;
     t = tn;
-    return t < ntiles;
+    return more;
   };
   while (step(A, B) && step(B, A)) {
   }
@@ -443,47 +439,54 @@ __device__ __forceinline__ double wave_sum(double x) {
 
 template <bool GBf16>
 __global__ void __launch_bounds__(kBlock)
-k_sumsq(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
-        uint32_t ntiles, float s, float max_norm, double *__restrict__ partials,
+k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
+        float max_norm, double *__restrict__ partials,
         unsigned int *__restrict__ ticket, float *__restrict__ d_norm,
         float *__restrict__ d_coef) {
   constexpr int V = kWide<GBf16>;
   constexpr int G = kTileElems / (kBlock * V);
-  // Two tiles per iteration (t and t + gridDim.x).  When both are full
-  // tiles of aligned tensors (the common case) all their loads are issued as
-  // raw 16-byte vectors before any is unpacked; otherwise each tile goes on
-  // its own, a tail tile through clamped one-element loads.
+  // Two tiles per iteration (t and t + gridDim.x).  Their records are read
+  // one iteration ahead (clamped to the last tile: always in bounds).  When
+  // both tiles are full tiles of aligned tensors (the common case) all their
+  // loads are issued as raw 16-byte vectors before any is unpacked;
+  // otherwise each tile goes on its own, a tail tile through clamped
+  // one-element loads.
   constexpr int U = 2;
+  const uint32_t last = ntiles ? ntiles - 1 : 0;
+  const uint32_t stride = U * gridDim.x;
+  const uint32_t e0 = threadIdx.x * V;
   double acc[G] = {};
-  for (uint32_t t0 = blockIdx.x; t0 < ntiles; t0 += U * gridDim.x) {
-    MTA_GLOBAL const elem_t<GBf16> *pg[U];
-    uint32_t lim[U];
-    bool vec[U];
+  GradTile rec[U];
+  if (ntiles) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      rec[u] = tiles[min(blockIdx.x + u * gridDim.x, last)];
+  }
+  for (uint32_t t0 = blockIdx.x; t0 < ntiles; t0 += stride) {
+    GradTile cur[U];
+    bool valid[U];
     bool all_full = true;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t t = t0 + u * gridDim.x;
-      pg[u] = nullptr;
-      lim[u] = 0;
-      vec[u] = false;
-      if (t < ntiles) {
-        const Tile tl = tiles[t];
-        const TensorDesc d = td[tl.tensor];
-        const int64_t base = static_cast<int64_t>(tl.index) * kTileElems;
-        pg[u] = gp<elem_t<GBf16>>(d.g, base);
-        lim[u] = tile_len(d.n, base);
-        vec[u] = d.vec != 0;
-      }
-      all_full = all_full && vec[u] && lim[u] == kTileElems;
+      cur[u] = rec[u];
+      valid[u] = t0 + u * gridDim.x < ntiles;
+      all_full = all_full && valid[u] && cur[u].vec &&
+                 cur[u].lim == kTileElems;
     }
-    const uint32_t e0 = threadIdx.x * V;
     if (all_full) {
       raw16_t<GBf16> r[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < G; ++j)
-          r[u][j] = load16b_raw<GBf16>(pg[u] + j * (kBlock * V), e0);
+          r[u][j] = load16b_raw<GBf16>(
+              gp<elem_t<GBf16>>(cur[u].g, j * (kBlock * V)), e0);
+      // the next records only after the vector loads (scalar loads return
+      // out of order: an earlier one would be waited for with these)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        rec[u] = tiles[min(t0 + stride + u * gridDim.x, last)];
       __builtin_amdgcn_sched_barrier(0);  // every load in flight first
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -498,21 +501,28 @@ k_sumsq(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
           }
         }
     } else {
-#pragma unroll 1
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        rec[u] = tiles[min(t0 + stride + u * gridDim.x, last)];
+      // unrolled: indexing cur[] with a loop variable would move the
+      // records out of scalar registers
+#pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (lim[u] == 0) continue;
+        if (!valid[u]) continue;
+        MTA_GLOBAL const elem_t<GBf16> *pg = gp<elem_t<GBf16>>(cur[u].g, 0);
+        const uint32_t lim = cur[u].lim;
         float x[G][V];
-        if (vec[u] && lim[u] == kTileElems) {
+        if (cur[u].vec && lim == kTileElems) {
 #pragma unroll
           for (int j = 0; j < G; ++j)
-            load16b<GBf16>(pg[u] + j * (kBlock * V), e0, x[j]);
+            load16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
         } else {
 #pragma unroll
           for (int j = 0; j < G; ++j)
 #pragma unroll
             for (int k = 0; k < V; ++k)
-              x[j][k] = load1_clamped<GBf16>(pg[u], e0 + j * (kBlock * V) + k,
-                                             lim[u]);
+              x[j][k] =
+                  load1_clamped<GBf16>(pg, e0 + j * (kBlock * V) + k, lim);
         }
 #pragma unroll
         for (int j = 0; j < G; ++j)
@@ -585,19 +595,17 @@ k_sumsq(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
 
 template <bool GBf16>
 __global__ void __launch_bounds__(kBlock)
-k_scale(const TensorDesc *__restrict__ td, const Tile *__restrict__ tiles,
-        uint32_t ntiles, float s) {
+k_scale(const GradTile *__restrict__ tiles, uint32_t ntiles, float s) {
   constexpr int V = kWide<GBf16>;
   constexpr int G = kTileElems / (kBlock * V);
   for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const Tile tl = tiles[t];
-    const TensorDesc d = td[tl.tensor];
-    const int64_t base = static_cast<int64_t>(tl.index) * kTileElems;
-    MTA_GLOBAL elem_t<GBf16> *__restrict__ pg = gp<elem_t<GBf16>>(d.g, base);
-    const uint32_t lim = tile_len(d.n, base);
+    const GradTile tl = tiles[t];
+    MTA_GLOBAL elem_t<GBf16> *__restrict__ pg =
+        gp<elem_t<GBf16>>(const_cast<void *>(tl.g), 0);
+    const uint32_t lim = tl.lim;
     const uint32_t e0 = threadIdx.x * V;
     float x[G][V];
-    if (d.vec && lim == kTileElems) {
+    if (tl.vec && lim == kTileElems) {
 #pragma unroll
       for (int j = 0; j < G; ++j) load16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
       __builtin_amdgcn_sched_barrier(0);  // all loads in flight first
@@ -637,7 +645,7 @@ template <bool G, bool M, bool V>
 hipError_t launch_adamw_t(const Work &wk, const StepScalars &sc,
                           const float *d_coef) {
   hipLaunchKernelGGL((k_adamw<G, M, V>), dim3(wk.grid), dim3(kBlock), 0,
-                     wk.stream, wk.td, wk.tiles, wk.ntiles, sc, d_coef);
+                     wk.stream, wk.stiles, wk.ntiles, sc, d_coef);
   return hipGetLastError();
 }
 
@@ -663,11 +671,11 @@ hipError_t launch_sumsq(int gtype, const Work &wk, float s, float max_norm,
                         NormScratch scr, float *d_norm, float *d_coef) {
   if (gtype)
     hipLaunchKernelGGL((k_sumsq<true>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.td, wk.tiles, wk.ntiles, s, max_norm,
+                       wk.stream, wk.gtiles, wk.ntiles, s, max_norm,
                        scr.partials, scr.ticket, d_norm, d_coef);
   else
     hipLaunchKernelGGL((k_sumsq<false>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.td, wk.tiles, wk.ntiles, s, max_norm,
+                       wk.stream, wk.gtiles, wk.ntiles, s, max_norm,
                        scr.partials, scr.ticket, d_norm, d_coef);
   return hipGetLastError();
 }
@@ -675,10 +683,10 @@ hipError_t launch_sumsq(int gtype, const Work &wk, float s, float max_norm,
 hipError_t launch_scale(int gtype, const Work &wk, float s) {
   if (gtype)
     hipLaunchKernelGGL((k_scale<true>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.td, wk.tiles, wk.ntiles, s);
+                       wk.stream, wk.gtiles, wk.ntiles, s);
   else
     hipLaunchKernelGGL((k_scale<false>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.td, wk.tiles, wk.ntiles, s);
+                       wk.stream, wk.gtiles, wk.ntiles, s);
   return hipGetLastError();
 }
 
