@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--cpu-steps", type=int, default=3,
                     help="oracle steps of the CPU baseline (0 = skip)")
+    ap.add_argument("--weight-copy", action="store_true",
+                    help="also write a bfloat16 copy of every updated weight "
+                         "(mta_list_set_weight_copies): +2 B/param")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB, 5 times: "
                          "the known-size kernel that scales the HBM byte "
@@ -124,6 +127,11 @@ def main():
     arena.fill_grads(1)
     L = M.MtaList([], entries=arena.entries(), gtype=wl.gtype, mkind=wl.mkind,
                   vkind=wl.vkind)
+    copies = None
+    if args.weight_copy:
+        copies = torch.empty(arena.total, dtype=torch.bfloat16, device="cuda")
+        L.set_weight_copies([copies[o:o + n] for o, n in
+                             zip(arena.offsets, wl.sizes)])
     info = L.info()
     norm_d = torch.zeros(1, device="cuda")
     coef_d = torch.zeros(1, device="cuda")
@@ -169,12 +177,15 @@ def main():
     assert torch.isfinite(norm_d).all() and torch.isfinite(coef_d).all()
 
     bpp = wl.bytes_per_param()
+    if args.weight_copy:
+        bpp["update"] += 2
     step_bytes = wl.n * (bpp["norm"] + bpp["update"])
     adamw_bytes = wl.n * bpp["update"]
     norm_bytes = wl.n * bpp["norm"]
     value = wl.n * args.steps / (host_s)
     achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name, "k_adamw")
+    traffic = (None if args.weight_copy
+               else measured_traffic(wl.name, "k_adamw"))
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) per "
                   "fused clip+AdamW step",
@@ -196,6 +207,7 @@ def main():
             "bytes_per_param": bpp["norm"] + bpp["update"],
             "tiles": info["tiles"], "grid_update": info["grid_update"],
             "grid_norm": info["grid_norm"], "parallelism": "single GPU",
+            "weight_copy": bool(args.weight_copy),
         },
         "step_gbs": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9,
         "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9

@@ -23,10 +23,11 @@
  *
  * Memory and ownership.  Every w, g, m, v pointer is device memory owned by
  * the caller (for example a PyTorch tensor's data pointer).  The library never
- * allocates, frees or resizes caller memory.  A list handle owns a small
- * device table (tensor descriptors and a tile table) and the scratch of the
- * norm reduction; it is created once and reused every step, so the caller's
- * buffers must stay at the same addresses for the handle's life.
+ * allocates, frees or resizes caller memory.  A list handle owns small device
+ * tables (one record per tile of up to 4096 elements: its buffer addresses,
+ * length and alignment) and the scratch of the norm reduction; it is created
+ * once and reused every step, so the caller's buffers must stay at the same
+ * addresses for the handle's life.
  *
  * Layouts.
  *   w            float32, n elements.
@@ -110,6 +111,7 @@ typedef struct {
   int32_t device;      /* HIP device the list lives on */
   int32_t vector_tensors; /* tensors that take the 16-byte vector path */
   int32_t gtype, mkind, vkind;
+  int32_t weight_copies;  /* tensors with an attached bfloat16 weight copy */
 } mta_list_info_t;
 
 /* Flags of mta_scale. */
@@ -118,8 +120,8 @@ typedef struct {
                                mta_adamw_step read f32(g * factor) in registers */
 
 /* Create a list handle over `count` (>= 0) tensors described by the host array
- * `tensors`.  Validates every entry, builds the tensor and tile tables and
- * copies them to the current device on `stream`, then waits for that copy.
+ * `tensors`.  Validates every entry, builds the tile tables and copies them
+ * to the current device on `stream`, then waits for that copy.
  * Allocates device memory (the only call that does).  On success *out owns the
  * handle; release it with mta_list_destroy. */
 int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
@@ -159,6 +161,21 @@ int mta_clip_norm(mta_list *list, float max_norm, float *d_norm, float *d_coef,
  * factor. */
 int mta_adamw_step(mta_list *list, const mta_adamw_hparams *hp, int64_t t,
                    const float *d_coef, void *stream);
+
+/* Attach bfloat16 copies of the weights: every later mta_adamw_step also
+ * writes w16[i][k] = bfloat16(w_new[k]) (nearest-even, NaN -> 0xFFFF) for
+ * each tensor i that has one, in the same launch ("Mica 7.7: a training step
+ * on the card, in every float type", section "float16 and bfloat16, whole":
+ * the weights stay float32 and a product reads them as bfloat16; "Precision
+ * and numerics", section "bf16 regions": nearest-even is the one cast).
+ * w16 is a host array of `count` device pointers in list order, each NULL (no
+ * copy for that tensor) or the caller-owned address of n bfloat16 elements,
+ * 2-byte aligned, overlapping no buffer of the list and no other copy.
+ * w16 == NULL detaches every copy.  Rewrites the device tile table on
+ * `stream` and waits for that upload; must not overlap a running step of
+ * this list.  On failure the previous copies stay attached. */
+int mta_list_set_weight_copies(mta_list *list, void *const *w16,
+                               void *stream);
 
 /* Host only, no device work: the seven float32 constants the AdamW kernel
  * receives for step t, in the order {step, bc2, c1, c2, b2, eps, dec}. */

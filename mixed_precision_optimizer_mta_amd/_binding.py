@@ -21,8 +21,9 @@ STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
 
 # every symbol include/mta.h declares
 EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
-           "mta_clip_norm", "mta_adamw_step", "mta_adamw_scalars",
-           "mta_list_info", "mta_last_error", "mta_abi_version")
+           "mta_clip_norm", "mta_adamw_step", "mta_list_set_weight_copies",
+           "mta_adamw_scalars", "mta_list_info", "mta_last_error",
+           "mta_abi_version")
 
 
 class mta_tensor(ctypes.Structure):
@@ -43,7 +44,7 @@ class mta_list_info_t(ctypes.Structure):
                 ("grid_update", ctypes.c_int32), ("grid_norm", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("vector_tensors", ctypes.c_int32),
                 ("gtype", ctypes.c_int32), ("mkind", ctypes.c_int32),
-                ("vkind", ctypes.c_int32)]
+                ("vkind", ctypes.c_int32), ("weight_copies", ctypes.c_int32)]
 
 
 class MtaError(RuntimeError):
@@ -77,6 +78,7 @@ def lib():
         L.mta_clip_norm.argtypes = [vp, f32, vp, vp, vp]
         L.mta_adamw_step.argtypes = [vp, ctypes.POINTER(mta_adamw_hparams),
                                      i64, vp, vp]
+        L.mta_list_set_weight_copies.argtypes = [vp, ctypes.POINTER(vp), vp]
         L.mta_adamw_scalars.argtypes = [ctypes.POINTER(mta_adamw_hparams),
                                         i64, ctypes.POINTER(ctypes.c_float)]
         L.mta_list_info.argtypes = [vp, ctypes.POINTER(mta_list_info_t)]
@@ -142,6 +144,17 @@ def mta_adamw_step(handle, hp, t, d_coef, stream=0):
     h = _hparams(hp)
     _check(lib().mta_adamw_step(handle, ctypes.byref(h), t, d_coef, stream),
            "mta_adamw_step")
+
+
+def mta_list_set_weight_copies(handle, w16, stream=0):
+    """w16: one device pointer (or None) per tensor of the list, or None to
+    detach every copy."""
+    if w16 is None:
+        arr = None
+    else:
+        arr = (ctypes.c_void_p * max(1, len(w16)))(*[p or None for p in w16])
+    _check(lib().mta_list_set_weight_copies(handle, arr, stream),
+           "mta_list_set_weight_copies")
 
 
 def mta_adamw_scalars(hp, t):

@@ -18,6 +18,8 @@
 #include "mta_internal.h"
 
 struct mta_list {
+  std::vector<mta_tensor> tensors;  // the caller's table, kept for rebuilds
+  std::vector<void *> w16;          // attached bfloat16 weight copies (or null)
   int device = 0;
   int gtype = 0, mkind = 0, vkind = 0;
   int64_t count = 0;
@@ -31,6 +33,7 @@ struct mta_list {
   mta::StepTile *d_stiles = nullptr;
   double *d_partials = nullptr;
   unsigned int *d_ticket = nullptr;
+  int weight_copies = 0;  // tensors with an attached bfloat16 copy
   bool deferred = false;  // a MTA_SCALE_DEFER factor is pending
   float deferred_s = 1.0f;
 };
@@ -152,6 +155,77 @@ struct Span {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Sorts the spans and fails on the first two that overlap.
+int check_overlaps(std::vector<Span> *spans) {
+  std::sort(spans->begin(), spans->end(),
+            [](const Span &a, const Span &b) { return a.lo < b.lo; });
+  static const char *names[5] = {"w", "g", "m", "v", "w16"};
+  for (size_t k = 1; k < spans->size(); ++k) {
+    const Span &a = (*spans)[k - 1], &b = (*spans)[k];
+    if (b.lo < a.hi)
+      return fail(MTA_EINVAL,
+                  "buffers overlap: tensor %lld %s and tensor %lld %s",
+                  static_cast<long long>(a.tensor), names[a.which],
+                  static_cast<long long>(b.tensor), names[b.which]);
+  }
+  return MTA_OK;
+}
+
+// The byte ranges of every buffer of the list's non-empty tensors.
+void list_spans(const mta_list *L, std::vector<Span> *spans) {
+  const uintptr_t sizes[4] = {4, L->gtype == MTA_BF16 ? 2u : 4u,
+                              L->mkind == MTA_MOM_BF16X2 ? 2u : 4u,
+                              L->vkind == MTA_MOM_BF16X2 ? 2u : 4u};
+  for (size_t i = 0; i < L->tensors.size(); ++i) {
+    const mta_tensor &x = L->tensors[i];
+    if (x.n == 0) continue;
+    const void *bufs[4] = {x.w, x.g, x.m, x.v};
+    for (int b = 0; b < 4; ++b) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(bufs[b]);
+      spans->push_back(Span{lo, lo + static_cast<uintptr_t>(x.n) * sizes[b],
+                            static_cast<int64_t>(i), b});
+    }
+  }
+}
+
+uintptr_t elem_size(int kind_is_16bit) { return kind_is_16bit ? 2 : 4; }
+
+// One StepTile per tile of every non-empty tensor, in list order.  w16 may be
+// empty (no copies) or hold one pointer per tensor.
+void build_step_tiles(const std::vector<mta_tensor> &tensors,
+                      const std::vector<void *> &w16, int gtype, int mkind,
+                      int vkind, std::vector<mta::StepTile> *out) {
+  const uintptr_t gsz = elem_size(gtype == MTA_BF16);
+  const uintptr_t msz = elem_size(mkind == MTA_MOM_BF16X2);
+  const uintptr_t vsz = elem_size(vkind == MTA_MOM_BF16X2);
+  out->clear();
+  for (size_t i = 0; i < tensors.size(); ++i) {
+    const mta_tensor &x = tensors[i];
+    void *copy = w16.empty() ? nullptr : w16[i];
+    const bool vec = aligned(x.w, 16) && aligned(x.g, 16) && aligned(x.m, 16) &&
+                     aligned(x.v, 16) && (!copy || aligned(copy, 16));
+    for (int64_t base = 0; base < x.n; base += mta::kTileElems) {
+      const int64_t left = x.n - base;
+      const uint32_t lim = static_cast<uint32_t>(
+          left < mta::kTileElems ? left : mta::kTileElems);
+      const uintptr_t b = static_cast<uintptr_t>(base);
+      const auto at = [b](const void *p, uintptr_t size) -> void * {
+        return p ? reinterpret_cast<char *>(const_cast<void *>(p)) + b * size
+                 : nullptr;
+      };
+      mta::StepTile st;
+      st.w = static_cast<float *>(at(x.w, 4));
+      st.g = at(x.g, gsz);
+      st.m = at(x.m, msz);
+      st.v = at(x.v, vsz);
+      st.lim = lim;
+      st.vec = vec ? 1u : 0u;
+      st.w16 = at(copy, 2);
+      out->push_back(st);
+    }
+  }
+}
+
 mta::Work work_of(const mta_list *L, int grid, void *stream) {
   mta::Work w;
   w.gtiles = L->d_gtiles;
@@ -199,6 +273,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
 
   std::vector<mta::GradTile> gtiles;
   std::vector<mta::StepTile> stiles;
+  std::vector<mta_tensor> kept;
   std::vector<Span> spans;
   int64_t elements = 0;
   int vec_tensors = 0;
@@ -238,45 +313,15 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
       // tile numbers and grid strides stay below 2^32 (no wrap-around)
       if (ntiles > (uint64_t{1} << 31)) return fail(MTA_EINVAL, "list too large");
     }
-    std::sort(spans.begin(), spans.end(),
-              [](const Span &a, const Span &b) { return a.lo < b.lo; });
-    static const char *names[4] = {"w", "g", "m", "v"};
-    for (size_t k = 1; k < spans.size(); ++k) {
-      if (spans[k].lo < spans[k - 1].hi)
-        return fail(MTA_EINVAL, "buffers overlap: tensor %lld %s and tensor %lld %s",
-                    static_cast<long long>(spans[k - 1].tensor),
-                    names[spans[k - 1].which],
-                    static_cast<long long>(spans[k].tensor),
-                    names[spans[k].which]);
-    }
+    int rc = check_overlaps(&spans);
+    if (rc) return rc;
     // one record per tile: buffer addresses offset to the tile's first
     // element, its length, and whether the vector path may be taken
-    gtiles.reserve(static_cast<size_t>(ntiles));
-    stiles.reserve(static_cast<size_t>(ntiles));
-    for (int64_t i = 0; i < count; ++i) {
-      const mta_tensor &x = tensors[i];
-      const bool vec = aligned(x.w, 16) && aligned(x.g, 16) &&
-                       aligned(x.m, 16) && aligned(x.v, 16);
-      for (int64_t base = 0; base < x.n; base += mta::kTileElems) {
-        const int64_t left = x.n - base;
-        const uint32_t lim = static_cast<uint32_t>(
-            left < mta::kTileElems ? left : mta::kTileElems);
-        const uintptr_t b = static_cast<uintptr_t>(base);
-        const auto at = [b](const void *p, uintptr_t size) {
-          return reinterpret_cast<char *>(const_cast<void *>(p)) + b * size;
-        };
-        gtiles.push_back(mta::GradTile{at(x.g, gsz), lim, vec ? 1u : 0u});
-        mta::StepTile st;
-        st.w = reinterpret_cast<float *>(at(x.w, 4));
-        st.g = at(x.g, gsz);
-        st.m = at(x.m, msz);
-        st.v = at(x.v, vsz);
-        st.lim = lim;
-        st.vec = vec ? 1u : 0u;
-        st.pad = 0;
-        stiles.push_back(st);
-      }
-    }
+    kept.assign(tensors, tensors + count);
+    build_step_tiles(kept, {}, gtype, mkind, vkind, &stiles);
+    gtiles.reserve(stiles.size());
+    for (const mta::StepTile &st : stiles)
+      gtiles.push_back(mta::GradTile{st.g, st.lim, aligned(st.g, 16) ? 1u : 0u});
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
   }
@@ -293,6 +338,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
 
   mta_list *L = new (std::nothrow) mta_list;
   if (!L) return fail(MTA_ENOMEM, "host allocation failed");
+  L->tensors = std::move(kept);
   L->device = dev;
   L->gtype = gtype;
   L->mkind = mkind;
@@ -363,6 +409,59 @@ int mta_list_destroy(mta_list *L) {
   return ok();
 }
 
+int mta_list_set_weight_copies(mta_list *L, void *const *w16, void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  std::vector<void *> copies;
+  int attached = 0;
+  try {
+    if (w16) {
+      std::vector<Span> spans;
+      list_spans(L, &spans);
+      copies.assign(w16, w16 + L->tensors.size());
+      for (size_t i = 0; i < copies.size(); ++i) {
+        const int64_t n = L->tensors[i].n;
+        if (!copies[i] || n == 0) {
+          copies[i] = nullptr;
+          continue;
+        }
+        if (!aligned(copies[i], 2))
+          return fail(MTA_EALIGN, "tensor %lld: weight copy not 2-byte aligned",
+                      static_cast<long long>(i));
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(copies[i]);
+        spans.push_back(Span{lo, lo + static_cast<uintptr_t>(n) * 2,
+                             static_cast<int64_t>(i), 4});
+        ++attached;
+      }
+      int rc = check_overlaps(&spans);
+      if (rc) return rc;
+      if (attached == 0) copies.clear();
+    }
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  int rc = check_device(L);
+  if (rc) return rc;
+  std::vector<mta::StepTile> stiles;
+  try {
+    build_step_tiles(L->tensors, copies, L->gtype, L->mkind, L->vkind,
+                     &stiles);
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (!stiles.empty())
+    e = hipMemcpyAsync(L->d_stiles, stiles.data(),
+                       stiles.size() * sizeof(mta::StepTile),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "uploading the tile table: %s", hipGetErrorString(e));
+  L->w16 = std::move(copies);
+  L->weight_copies = attached;
+  return ok();
+}
+
 int mta_list_info(const mta_list *L, mta_list_info_t *out) {
   if (!L || !out) return fail(MTA_EINVAL, "NULL argument");
   out->count = L->count;
@@ -376,6 +475,7 @@ int mta_list_info(const mta_list *L, mta_list_info_t *out) {
   out->gtype = L->gtype;
   out->mkind = L->mkind;
   out->vkind = L->vkind;
+  out->weight_copies = L->weight_copies;
   return ok();
 }
 

@@ -28,15 +28,16 @@ struct GradTile {
 };
 static_assert(sizeof(GradTile) == 16, "gradient tile layout");
 
-// k_adamw reads and writes all four buffers.
+// k_adamw reads and writes all four buffers, and writes the bfloat16 weight
+// copy when one is attached.
 struct StepTile {
   float *w;
   const void *g;
   void *m;
   void *v;
   uint32_t lim;  // elements in this tile, 1..kTileElems
-  uint32_t vec;  // 1: all four buffers 16-byte aligned
-  uint64_t pad;
+  uint32_t vec;  // 1: all buffers (w16 too, when present) 16-byte aligned
+  void *w16;     // bfloat16 copy of w at this tile, or nullptr
 };
 static_assert(sizeof(StepTile) == 48, "step tile layout");
 

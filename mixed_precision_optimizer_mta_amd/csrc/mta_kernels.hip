@@ -8,7 +8,9 @@
 //   k_adamw  AdamW over every (w, g, m, v) group (AdamWSteps, same section),
 //            with the element arithmetic of "BendTorch main.bend", section
 //            "Optimizers": adam_decay, adam_m, adam_v, adam_w, and the packed
-//            bfloat16 moments of adamh_l / adamhv_l (ph_of_bits, ph_to).
+//            bfloat16 moments of adamh_l / adamhv_l (ph_of_bits, ph_to); when
+//            a tensor has one, it also writes the bfloat16 copy of its new
+//            weights (Mica, section "float16 and bfloat16, whole").
 //   k_scale  ScaleTensors in place (same Mica section).
 //
 // Work is cut into tiles of kTileElems elements of one tensor.  The tile
@@ -266,6 +268,7 @@ struct TileRef {
   MTA_GLOBAL const elem_t<GBf16> *pg;
   MTA_GLOBAL elem_t<MPacked> *pm;
   MTA_GLOBAL elem_t<VPacked> *pv;
+  MTA_GLOBAL uint16_t *pw16;  // bfloat16 weight copy, or null
   uint32_t lim;
   bool full;
 };
@@ -278,6 +281,7 @@ __device__ __forceinline__ TileRef<GBf16, MPacked, VPacked> tile_ref(
   r.pg = gp<elem_t<GBf16>>(st.g, 0);
   r.pm = gp<elem_t<MPacked>>(st.m, 0);
   r.pv = gp<elem_t<VPacked>>(st.v, 0);
+  r.pw16 = gp<uint16_t>(st.w16, 0);
   r.lim = st.lim;
   r.full = st.vec && st.lim == kTileElems;
   return r;
@@ -316,6 +320,12 @@ __device__ __forceinline__ void finish_tile(
     store4<false>(T.pw, e, w);
     store4<MPacked>(T.pm, e, m);
     store4<VPacked>(T.pv, e, v);
+    if (T.pw16) {  // uniform: the tile has a bfloat16 weight copy
+      float h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) h[k] = round_bf16(w[k]);
+      store4<true>(T.pw16, e, h);
+    }
   }
 }
 
@@ -346,6 +356,7 @@ __device__ __forceinline__ void partial_tile(
         T.pw[e] = w[j][k];
         store1<MPacked>(T.pm, e, m[j][k]);
         store1<VPacked>(T.pv, e, v[j][k]);
+        if (T.pw16) store1<true>(T.pw16, e, round_bf16(w[j][k]));
       }
     }
 }

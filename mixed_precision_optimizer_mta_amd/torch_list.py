@@ -47,6 +47,7 @@ class MtaList:
                 entries.append((w.data_ptr(), g.data_ptr(), m.data_ptr(),
                                 v.data_ptr(), n))
         self.gtype, self.mkind, self.vkind = gtype, mkind, vkind
+        self.sizes = [int(e[4]) for e in entries]
         self.handle = B.mta_list_create(entries, gtype, mkind, vkind,
                                         current_stream())
 
@@ -66,6 +67,29 @@ class MtaList:
         B.mta_clip_norm(self.handle, max_norm,
                         None if norm_out is None else norm_out.data_ptr(),
                         coef_out.data_ptr(), current_stream())
+
+    def set_weight_copies(self, copies):
+        """copies: one bfloat16 GPU tensor (or None) per group, each with the
+        weight's numel, written with bfloat16(w) by every later AdamW step;
+        None detaches them all."""
+        ptrs = None
+        if copies is not None:
+            if len(copies) != len(self.sizes):
+                raise ValueError("one copy (or None) per tensor of the list")
+            ptrs = []
+            for c, n in zip(copies, self.sizes):
+                if c is None:
+                    ptrs.append(None)
+                    continue
+                if c.numel() != n:
+                    raise ValueError("a weight copy must have the weight's numel")
+                if c.dtype != torch.bfloat16 or not c.is_cuda or \
+                        not c.is_contiguous():
+                    raise TypeError("weight copies are contiguous bfloat16 "
+                                    "GPU tensors")
+                ptrs.append(c.data_ptr())
+            self._copies = list(copies)
+        B.mta_list_set_weight_copies(self.handle, ptrs, current_stream())
 
     def adamw_step(self, hparams, t, coef=None):
         if coef is not None and (coef.dtype != torch.float32 or

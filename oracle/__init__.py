@@ -69,6 +69,8 @@ def lib():
                                        ctypes.c_int, vp, ctypes.c_int, f32,
                                        f32, vp]
         L.mto_adamw_tensor.restype = None
+        L.mto_weight_copy.argtypes = [i64, vp, vp]
+        L.mto_weight_copy.restype = None
         _lib = L
     return _lib
 
@@ -199,11 +201,20 @@ def adamw_(w, g, m, v, gtype, mkind, vkind, sc, s=1.0, coef=1.0):
                            _ptr(sc, np.float32))
 
 
-class Tensor:
-    """One parameter group: weight, gradient and the two moments."""
+def weight_copy(w, out):
+    """bfloat16 copy of float32 weights (nearest-even, NaN -> 0xFFFF)."""
+    if out.size != w.size:
+        raise ValueError("copy buffer has the wrong size")
+    lib().mto_weight_copy(w.size, _ptr(w, np.float32), _ptr(out, np.uint16))
 
-    def __init__(self, w, g, m, v):
-        self.w, self.g, self.m, self.v = w, g, m, v
+
+class Tensor:
+    """One parameter group: weight, gradient and the two moments, and an
+    optional bfloat16 copy of the weight (numpy uint16, written after each
+    step when present)."""
+
+    def __init__(self, w, g, m, v, w16=None):
+        self.w, self.g, self.m, self.v, self.w16 = w, g, m, v, w16
 
     @property
     def n(self):
@@ -230,4 +241,6 @@ def step_(tensors, gtype, mkind, vkind, lr, beta1, beta2, eps, weight_decay,
     sc = scalars(lr, beta1, beta2, eps, weight_decay, t)
     for x in tensors:
         adamw_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c)
+        if getattr(x, "w16", None) is not None:
+            weight_copy(x.w, x.w16)
     return nrm, c

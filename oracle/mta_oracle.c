@@ -232,3 +232,15 @@ void mto_adamw_tensor(int64_t n, float *w, const void *g, int gtype, void *m,
     w[k] = wd + ((-step * m1) / denom);
   }
 }
+
+/* ---------------------------------------------------------------------- */
+/* bfloat16 copy of the updated weights ("Mica 7.7", section "float16 and */
+/* bfloat16, whole": weights stay float32 and a product reads them as     */
+/* bfloat16; "Precision and numerics": nearest-even is the one cast).     */
+/* out[k] = bfloat16(w[k]) by the same nearest-even rule as the moments.  */
+/* ---------------------------------------------------------------------- */
+
+void mto_weight_copy(int64_t n, const float *w, uint16_t *out) {
+  for (int64_t k = 0; k < n; ++k)
+    out[k] = (uint16_t)mto_bf16_of_bits(bits_of(w[k]));
+}

@@ -1,0 +1,105 @@
+"""GPU parity of the fused bfloat16 weight copy (mta_list_set_weight_copies):
+every AdamW step also writes bfloat16(w_new), nearest-even, NaN -> 0xFFFF,
+for the tensors that have a copy attached; bitwise against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_optimizer_mta_amd import MtaError, MtaList
+from mixed_precision_optimizer_mta_amd import workloads as WL
+
+from parity_util import compare, dev_bf16_bits, oracle_grads, oracle_state
+
+pytestmark = pytest.mark.gpu
+
+
+def run(wl, steps, offsets=None, copy_mask=None, copy_shift=0):
+    arena = WL.Arena(wl, "cuda", offsets)
+    arena.fill_weights()
+    # the copies live in their own bfloat16 arena, filled with a sentinel
+    copies = torch.full((arena.total + 8,), -7.0, dtype=torch.bfloat16,
+                        device="cuda")
+    sentinel = copies.clone()
+    mask = copy_mask or [True] * wl.count
+    views = [copies[o + copy_shift:o + copy_shift + n] if (k and n) else None
+             for o, n, k in zip(arena.offsets, wl.sizes, mask)]
+    L = MtaList([], entries=arena.entries(), gtype=wl.gtype, mkind=wl.mkind,
+                vkind=wl.vkind)
+    L.set_weight_copies(views)
+    assert L.info()["weight_copies"] == sum(1 for x in views if x is not None)
+    ost = oracle_state(arena)
+    for o, v in zip(ost, views):
+        o.w16 = None if v is None else np.zeros(v.numel(), np.uint16)
+    cd = torch.zeros(1, device="cuda")
+    for t in range(1, steps + 1):
+        arena.fill_grads(t)
+        for o, g in zip(ost, oracle_grads(arena)):
+            o.g = g
+        L.scale(wl.scale, defer=True)
+        L.clip_norm(wl.max_norm, None, cd)
+        L.adamw_step(wl.hparams, t, cd)
+        torch.cuda.synchronize()
+        O.step_(ost, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1, wl.beta2,
+                wl.eps, wl.weight_decay, t, s=wl.scale,
+                coef=np.float32(cd.item()))
+        assert compare(arena, ost) == {"w": 0, "m": 0, "v": 0}
+        for o, v in zip(ost, views):
+            if v is not None:
+                assert np.array_equal(dev_bf16_bits(v), o.w16)
+    # nothing outside the attached copies was written
+    written = torch.zeros(copies.numel(), dtype=torch.bool, device="cuda")
+    for o, n, v in zip(arena.offsets, wl.sizes, views):
+        if v is not None:
+            written[o + copy_shift:o + copy_shift + n] = True
+    same = copies.view(torch.int16) == sentinel.view(torch.int16)
+    assert bool((same | written).all())
+    # detach: a later step leaves the copies as they are
+    before = copies.clone()
+    L.set_weight_copies(None)
+    assert L.info()["weight_copies"] == 0
+    L.adamw_step(wl.hparams, steps + 1, cd)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), copies.view(torch.int16))
+    L.close()
+
+
+KINDS = [(g, m, v) for g in (0, 1) for m in (0, 1) for v in (0, 1)]
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind", KINDS)
+def test_weight_copy_every_kind(gtype, mkind, vkind):
+    sizes = [1, 7, 4095, 4096, 4097, 3 * 4096 + 5, 10000]
+    wl = WL.Workload("copies", sizes, gtype, mkind, vkind, steps=2,
+                     g_sigma=0.05, ident=21)
+    run(wl, 2)
+
+
+def test_weight_copy_partial_attach_and_unaligned_copies():
+    sizes = [5000, 4096, 33, 9000, 1]
+    wl = WL.Workload("copies2", sizes, 1, 1, 0, steps=2, ident=22)
+    # copies shifted by one element: 2 bytes off 16-byte alignment, so these
+    # tensors take the element path even though w, g, m, v are aligned
+    run(wl, 2, copy_mask=[True, False, True, True, False], copy_shift=1)
+
+
+def test_weight_copy_on_the_124m_list():
+    run(WL.get("gpt2_124m"), 2)
+
+
+def test_weight_copy_rejects_overlap_and_misalignment():
+    wl = WL.Workload("copies3", [100, 200], 0, 0, 0, steps=1, ident=23)
+    arena = WL.Arena(wl, "cuda")
+    L = MtaList([], entries=arena.entries(), gtype=0, mkind=0, vkind=0)
+    c = torch.zeros(400, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MtaError):                    # overlaps its own w
+        L.set_weight_copies([arena.view("w", 0).view(torch.bfloat16)[:100],
+                             None])
+    with pytest.raises(MtaError):                    # two copies overlap
+        L.set_weight_copies([c[0:100], c[50:250]])
+    from mixed_precision_optimizer_mta_amd import _binding as B
+    with pytest.raises(MtaError) as e:               # odd address
+        B.mta_list_set_weight_copies(L.handle, [c.data_ptr() + 1, None])
+    assert e.value.code == -2
+    assert L.info()["weight_copies"] == 0
+    L.close()

@@ -561,3 +561,37 @@ def test_nonfinite_gradient_propagates():
     assert O.clip_coef(1.0, np.float32(O.norm([g], O.F32))) == 0.0
     g = np.array([np.inf, 1.0, -np.inf], np.float32)
     assert O.norm([g], O.F32) == math.inf
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 weight copy ("Mica 7.7", float16 and bfloat16, whole: a product
+# reads the float32 weights as bfloat16; "Precision and numerics": the cast
+# is nearest-even)
+# ---------------------------------------------------------------------------
+
+def test_weight_copy_is_nearest_even_bfloat16():
+    rng = np.random.default_rng(12)
+    w = rng.normal(0, 0.02, 1 << 16).astype(np.float32)
+    w[:4] = [0.8671875, np.float32(1.00390625), -0.0, np.inf]
+    out = np.zeros(w.size, np.uint16)
+    O.weight_copy(w, out)
+    assert out[0] == 0x3F5E          # 0.8671875 = 1.1011110b * 2^-1, exact
+    assert out[1] == 0x3F80          # tie between 0x3F80 and 0x3F81: even
+    assert out[2] == 0x8000 and out[3] == 0x7F80
+    ref = torch.from_numpy(w.copy()).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out, ref)
+    w[5] = np.nan
+    O.weight_copy(w, out)
+    assert out[5] == 0xFFFF
+
+
+def test_step_writes_the_copy_of_the_new_weights():
+    row = _golden_rows("hand_steps.txt")[2]      # case B: w -> 0.8671875
+    w = np.array([1.0], np.float32)
+    g = np.array([float(Fraction(row[6]))], np.float32)
+    m, v = _mom_buf(O.MOM_BF16X2, 0.0), _mom_buf(O.MOM_BF16X2, 0.0)
+    t = O.Tensor(w, g, m, v, w16=np.zeros(1, np.uint16))
+    O.step_([t], O.F32, O.MOM_BF16X2, O.MOM_BF16X2, 0.125, 0.5, 0.75, 0.875,
+            0.5, 1)
+    assert float(t.w[0]) == 0.8671875 and t.w16[0] == 0x3F5E
