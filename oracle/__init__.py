@@ -36,7 +36,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 MOM_F32, MOM_BF16X2 = 0, 1
 
 _lib = None
@@ -71,6 +71,26 @@ def lib():
         L.mto_adamw_tensor.restype = None
         L.mto_weight_copy.argtypes = [i64, vp, vp]
         L.mto_weight_copy.restype = None
+        L.mto_f32_of_f16.argtypes = [ctypes.c_uint32]
+        L.mto_f32_of_f16.restype = f32
+        L.mto_f16_of_f32.argtypes = [f32]
+        L.mto_f16_of_f32.restype = ctypes.c_uint32
+        L.mto_f16_of_f32_array.argtypes = [i64, vp, vp]
+        L.mto_f16_of_f32_array.restype = None
+        L.mto_f32_of_f16_array.argtypes = [i64, vp, vp]
+        L.mto_f32_of_f16_array.restype = None
+        L.mto_pow_rn.argtypes = [f64, i64]
+        L.mto_pow_rn.restype = f64
+        L.mto_scalars_rn.argtypes = [f64, f64, f64, f64, f64, i64, vp]
+        L.mto_scalars_rn.restype = None
+        L.mto_inv_scale.argtypes = [f32]
+        L.mto_inv_scale.restype = f32
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        L.mto_amp_update.argtypes = [f32p, i32p, f32p,
+                                     ctypes.POINTER(ctypes.c_int64), f64, f64,
+                                     ctypes.c_int32]
+        L.mto_amp_update.restype = None
         _lib = L
     return _lib
 
@@ -84,7 +104,7 @@ def _ptr(a, dtype):
 
 
 def _grad_dtype(gtype):
-    return np.uint16 if gtype == BF16 else np.float32
+    return np.uint16 if gtype in (BF16, F16) else np.float32
 
 
 def _mom_dtype(kind):
@@ -244,3 +264,86 @@ def step_(tensors, gtype, mkind, vkind, lr, beta1, beta2, eps, weight_decay,
         if getattr(x, "w16", None) is not None:
             weight_copy(x.w, x.w16)
     return nrm, c
+
+
+# ---------------------------------------------------------------- float16
+
+def f32_of_f16(h):
+    """float16 bit patterns -> float32 (exact)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().mto_f32_of_f16_array(h.size, _ptr(h, np.uint16),
+                               _ptr(out, np.float32))
+    return out
+
+
+def f16_of_f32(x):
+    """float32 -> float16 bit patterns (nearest-even, NaN -> 0xFFFF)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().mto_f16_of_f32_array(x.size, _ptr(x, np.float32),
+                               _ptr(out, np.uint16))
+    return out
+
+
+# ---------------------------------------------------------------- AMP
+
+def pow_rn(b, t):
+    """b^t rounded once to the nearest float64."""
+    return float(lib().mto_pow_rn(float(b), int(t)))
+
+
+def scalars_rn(lr, beta1, beta2, eps, weight_decay, t):
+    """As scalars(), with 1 - b^t from the correctly rounded power (the form
+    the device computes from its own step counter)."""
+    if t < 1:
+        raise ValueError("t counts from 1")
+    out = np.zeros(7, dtype=np.float32)
+    lib().mto_scalars_rn(lr, beta1, beta2, eps, weight_decay, int(t),
+                         _ptr(out, np.float32))
+    return out
+
+
+def inv_scale(scale):
+    return np.float32(lib().mto_inv_scale(float(np.float32(scale))))
+
+
+class AmpState:
+    """The loss-scale state a caller keeps next to the tensors."""
+
+    def __init__(self, scale, step=0, tracker=0, found_inf=0.0):
+        self.scale = np.float32(scale)
+        self.step = int(step)
+        self.tracker = int(tracker)
+        self.found_inf = np.float32(found_inf)
+
+    def update(self, growth=2.0, backoff=0.5, interval=2000):
+        sc = ctypes.c_float(self.scale)
+        tr = ctypes.c_int32(self.tracker)
+        fi = ctypes.c_float(self.found_inf)
+        st = ctypes.c_int64(self.step)
+        lib().mto_amp_update(ctypes.byref(sc), ctypes.byref(tr),
+                             ctypes.byref(fi), ctypes.byref(st), growth,
+                             backoff, interval)
+        self.scale, self.tracker = np.float32(sc.value), tr.value
+        self.found_inf, self.step = np.float32(fi.value), st.value
+
+
+def amp_step_(tensors, gtype, mkind, vkind, amp, lr, beta1, beta2, eps,
+              weight_decay, max_norm, coef=None):
+    """One loss-scaled step: unscale by 1/S, joint norm, found_inf, clip,
+    and the AdamW update at t = step + 1 unless a gradient is not finite.
+    Does not call amp.update().  Returns (norm, coef, found_inf)."""
+    s = inv_scale(amp.scale)
+    nrm = norm([x.g for x in tensors], gtype, s)
+    found = not math.isfinite(nrm)
+    c = clip_coef(max_norm, np.float32(nrm)) if coef is None else \
+        np.float32(coef)
+    amp.found_inf = np.float32(1.0 if found else 0.0)
+    if not found:
+        sc = scalars_rn(lr, beta1, beta2, eps, weight_decay, amp.step + 1)
+        for x in tensors:
+            adamw_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c)
+            if getattr(x, "w16", None) is not None:
+                weight_copy(x.w, x.w16)
+    return nrm, c, found

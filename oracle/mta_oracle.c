@@ -43,6 +43,7 @@
 
 #define MTO_F32 0
 #define MTO_BF16 1
+#define MTO_F16 2
 #define MTO_MOM_F32 0
 #define MTO_MOM_BF16X2 1
 
@@ -100,9 +101,58 @@ static void packed_put(uint32_t *words, int64_t k, uint32_t h) {
   words[k >> 1] = w;
 }
 
-/* gradient element k as float32 (a bfloat16 gradient converts exactly) */
+/* ---------------------------------------------------------------------- */
+/* IEEE binary16 ("Mica 7.7": float16 stands beside float32 everywhere a  */
+/* float goes, and a float16 step needs its gradients unscaled)           */
+/* ---------------------------------------------------------------------- */
+
+/* float16 bits -> float32, exact: sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 is zero or subnormal (fraction * 2^-24), 31 is Inf
+ * or NaN (the fraction moves into the top of the float32 fraction). */
+float mto_f32_of_f16(uint32_t h) {
+  const uint32_t sign = (h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1Fu, f = h & 0x3FFu;
+  if (e == 0) {
+    const float mag = ldexpf((float)f, -24); /* exact: f < 2^10 */
+    return sign ? -mag : mag;
+  }
+  if (e == 31) return float_of(sign | 0x7F800000u | (f << 13));
+  return float_of(sign | ((e + 112u) << 23) | (f << 13));
+}
+
+/* float32 -> float16 bits, round to nearest, ties to even; overflow goes to
+ * Inf; any NaN becomes 0xFFFF (all ones, read by analogy with the
+ * bfloat16 rule). */
+uint32_t mto_f16_of_f32(float x) {
+  const uint32_t u = bits_of(x);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0xFFFFu;
+  if (a >= 0x477FF000u) return sign | 0x7C00u; /* |x| >= 65520 rounds up */
+  if (a < 0x38800000u) {                        /* below 2^-14: subnormal */
+    /* the subnormal step is 2^-24; |x| * 2^24 is exact in double and
+     * rint() rounds it to nearest, ties to even */
+    const double q = rint(ldexp((double)float_of(a), 24));
+    return sign | (uint32_t)q; /* q == 1024 is the smallest normal */
+  }
+  uint32_t h = ((a >> 23) - 112u) << 10 | ((a >> 13) & 0x3FFu);
+  const uint32_t rest = a & 0x1FFFu;
+  if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h += 1u;
+  return sign | h;
+}
+
+void mto_f16_of_f32_array(int64_t n, const float *in, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint16_t)mto_f16_of_f32(in[i]);
+}
+
+void mto_f32_of_f16_array(int64_t n, const uint16_t *in, float *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = mto_f32_of_f16(in[i]);
+}
+
+/* gradient element k as float32 (bfloat16 and float16 convert exactly) */
 static float grad_at(const void *g, int gtype, int64_t k) {
   if (gtype == MTO_BF16) return mto_f32_of_bf16(((const uint16_t *)g)[k]);
+  if (gtype == MTO_F16) return mto_f32_of_f16(((const uint16_t *)g)[k]);
   return ((const float *)g)[k];
 }
 
@@ -136,6 +186,10 @@ void mto_scale_tensor(int64_t n, void *g, int gtype, float s) {
       uint16_t *h = (uint16_t *)g;
       float x = mto_f32_of_bf16(h[k]) * s;
       h[k] = (uint16_t)mto_bf16_of_bits(bits_of(x));
+    } else if (gtype == MTO_F16) {
+      uint16_t *h = (uint16_t *)g;
+      float x = mto_f32_of_f16(h[k]) * s;
+      h[k] = (uint16_t)mto_f16_of_f32(x);
     } else {
       float *f = (float *)g;
       f[k] = f[k] * s;
@@ -243,4 +297,67 @@ void mto_adamw_tensor(int64_t n, float *w, const void *g, int gtype, void *m,
 void mto_weight_copy(int64_t n, const float *w, uint16_t *out) {
   for (int64_t k = 0; k < n; ++k)
     out[k] = (uint16_t)mto_bf16_of_bits(bits_of(w[k]));
+}
+
+/* ---------------------------------------------------------------------- */
+/* Dynamic loss scaling on the device (the AMP state a caller keeps in    */
+/* device memory).  Reading: PyTorch's GradScaler, as [Mica] promises     */
+/* PyTorch's numerics.                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* b^t rounded once to the nearest float64: square-and-multiply in
+ * __float128 (113-bit significand; the error of ~2*63 roundings stays near
+ * 2^-106 relative), then one rounding to double. */
+double mto_pow_rn(double b, int64_t t) {
+  __float128 r = 1, x = b;
+  uint64_t e = (uint64_t)t;
+  while (e) {
+    if (e & 1u) r *= x;
+    x *= x;
+    e >>= 1;
+  }
+  return (double)r;
+}
+
+/* The step constants from the device step counter: as mto_scalars, with
+ * 1 - b^t formed from the correctly rounded power. */
+void mto_scalars_rn(double lr, double b1, double b2, double eps, double wd,
+                    int64_t t, float out[7]) {
+  const double q1 = 1.0 - mto_pow_rn(b1, t);
+  const double q2 = 1.0 - mto_pow_rn(b2, t);
+  out[0] = (float)(lr / q1);
+  out[1] = (float)sqrt(q2);
+  out[2] = (float)(1.0 - b1);
+  out[3] = (float)(1.0 - b2);
+  out[4] = (float)b2;
+  out[5] = (float)eps;
+  out[6] = (float)(1.0 - lr * wd);
+}
+
+/* The unscale factor of a loss scale S: float32(1 / float64(S)). */
+float mto_inv_scale(float scale) { return (float)(1.0 / (double)scale); }
+
+/* After a step: a step with a non-finite unscaled gradient backs the scale
+ * off and resets the tracker; otherwise the step counts, the tracker grows,
+ * and every `interval` good steps the scale grows (when the grown scale is
+ * finite).  The found-inf flag is cleared for the next step.  Products are
+ * formed in float64 and rounded once to float32. */
+void mto_amp_update(float *scale, int32_t *tracker, float *found_inf,
+                    int64_t *step, double growth, double backoff,
+                    int32_t interval) {
+  if (*found_inf != 0.0f) {
+    *scale = (float)((double)*scale * backoff);
+    *tracker = 0;
+  } else {
+    *step += 1;
+    const int32_t good = *tracker + 1;
+    if (good == interval) {
+      const float grown = (float)((double)*scale * growth);
+      if (isfinite(grown)) *scale = grown;
+      *tracker = 0;
+    } else {
+      *tracker = good;
+    }
+  }
+  *found_inf = 0.0f;
 }

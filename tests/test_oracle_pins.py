@@ -595,3 +595,109 @@ def test_step_writes_the_copy_of_the_new_weights():
     O.step_([t], O.F32, O.MOM_BF16X2, O.MOM_BF16X2, 0.125, 0.5, 0.75, 0.875,
             0.5, 1)
     assert float(t.w[0]) == 0.8671875 and t.w16[0] == 0x3F5E
+
+
+# ---------------------------------------------------------------------------
+# float16 ("Mica 7.7": float16 beside float32 everywhere; the unscaling a
+# float16 step needs before its clip)
+# ---------------------------------------------------------------------------
+
+def test_f16_decode_all_patterns_match_numpy():
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    got = O.f32_of_f16(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_encode_nearest_even_matches_numpy():
+    # every float16 value, every midpoint between neighbours (ties), points
+    # just either side of the midpoints, and random float32 over the range
+    h = np.arange(0x7C00, dtype=np.uint32).astype(np.uint16)    # +0 .. max
+    v = h.view(np.float16).astype(np.float64)
+    mids = (v[:-1] + v[1:]) / 2                                # exact in f64
+    rng = np.random.default_rng(13)
+    xs = np.concatenate([
+        v, -v, mids, -mids,
+        np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+        np.nextafter(mids.astype(np.float32), np.float32(0)),
+        rng.normal(0, 1, 1 << 16) * 10.0 ** rng.uniform(-9, 5, 1 << 16),
+        [65504.0, 65519.99, 65520.0, 1e6, np.inf, -np.inf, 2.0 ** -25,
+         2.0 ** -25 * 1.0000001, 3 * 2.0 ** -25]]).astype(np.float32)
+    got = O.f16_of_f32(xs)
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    assert O.f16_of_f32(np.array([np.nan, -np.nan], np.float32)).tolist() == [
+        0xFFFF, 0xFFFF]
+
+
+# ---------------------------------------------------------------------------
+# loss scaling state (reading: PyTorch's GradScaler)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b", [0.9, 0.999, 0.95, 0.5, 0.123456789])
+def test_pow_rn_is_the_correctly_rounded_power(b):
+    for t in list(range(1, 40)) + [64, 127, 500, 1000]:
+        exact = Fraction(b) ** t
+        assert O.pow_rn(b, t) == float(exact), (b, t)   # Fraction rounds RN
+
+
+def test_scalars_rn_agree_with_the_host_form():
+    # the two forms differ only where libm's pow is not correctly rounded
+    diff = 0
+    for t in range(1, 3000):
+        a = O.scalars(3e-4, 0.9, 0.999, 1e-8, 0.1, t)
+        b = O.scalars_rn(3e-4, 0.9, 0.999, 1e-8, 0.1, t)
+        diff += int(np.any(a.view(np.uint32) != b.view(np.uint32)))
+    assert diff <= 3
+
+
+def test_amp_update_matches_torch_amp_update_scale():
+    rng = np.random.default_rng(14)
+    flags = rng.random(300) < 0.1
+    amp = O.AmpState(65536.0)
+    scale = torch.full((1,), 65536.0)
+    tracker = torch.zeros(1, dtype=torch.int32)
+    good = 0
+    for f in flags:
+        found = torch.full((1,), 1.0 if f else 0.0)
+        torch._amp_update_scale_(scale, tracker, found, 2.0, 0.5, 7)
+        amp.found_inf = np.float32(1.0 if f else 0.0)
+        amp.update(2.0, 0.5, 7)
+        good += int(not f)
+        assert amp.scale == np.float32(scale.item())
+        assert amp.tracker == int(tracker.item())
+        assert amp.step == good and amp.found_inf == 0.0
+
+
+def test_amp_update_keeps_the_scale_finite():
+    amp = O.AmpState(np.float32(3e38))
+    amp.update(2.0, 0.5, 1)                # 6e38 is not finite: no growth
+    assert amp.scale == np.float32(3e38) and amp.tracker == 0
+
+
+def test_amp_step_skips_on_non_finite_and_matches_plain_step_otherwise():
+    rng = np.random.default_rng(15)
+    n = 3000
+    g = (rng.normal(0, 1e-3, n) * 1024).astype(np.float32)
+    gh = O.f16_of_f32(g)
+    mk = lambda: O.Tensor(rng.normal(0, .02, n).astype(np.float32), gh.copy(),
+                          np.zeros(n, np.float32), np.zeros(n, np.float32))
+    a = mk()
+    b = O.Tensor(a.w.copy(), a.g.copy(), a.m.copy(), a.v.copy())
+    amp = O.AmpState(1024.0, step=4)
+    nrm, c, found = O.amp_step_([a], O.F16, 0, 0, amp, 3e-4, 0.9, 0.999,
+                                1e-8, 0.1, 1.0)
+    assert not found and amp.found_inf == 0.0
+    # the same step through the plain path: unscale by 1/1024, t = 5
+    O.step_([b], O.F16, 0, 0, 3e-4, 0.9, 0.999, 1e-8, 0.1, 5,
+            s=1.0 / 1024, max_norm=1.0)
+    assert np.array_equal(a.w, b.w) and np.array_equal(a.v, b.v)
+    # an Inf gradient: found_inf, nothing written
+    a.g[7] = 0x7C00
+    w0 = a.w.copy()
+    nrm, c, found = O.amp_step_([a], O.F16, 0, 0, amp, 3e-4, 0.9, 0.999,
+                                1e-8, 0.1, 1.0)
+    assert found and amp.found_inf == 1.0 and np.array_equal(a.w, w0)
