@@ -3,7 +3,8 @@
 One step = mta_clip_norm (joint norm + clip coefficient, one launch) and
 mta_adamw_step (AdamW over every tensor, one launch), plus the deferred
 unscale where the workload has one (no launch), over inputs resident in HBM.
-Prints one JSON line.
+A loss-scaled workload runs mta_amp_clip_norm, mta_amp_adamw_step and
+mta_amp_update (a one-thread launch) instead.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -52,9 +53,9 @@ def cpu_baseline(arena, wl, steps):
 
     import oracle as O
 
-    def host(t, bf16):
+    def host(t, bits16):
         t = t.detach().cpu()
-        if bf16:
+        if bits16:
             return t.view(torch.int16).numpy().view(np.uint16).copy()
         return t.numpy().copy()
 
@@ -63,18 +64,27 @@ def cpu_baseline(arena, wl, steps):
         m = host(arena.view("m", i), wl.mkind == 1)
         v = host(arena.view("v", i), wl.vkind == 1)
         ts.append(O.Tensor(host(arena.view("w", i), False),
-                           host(arena.view("g", i), wl.gtype == 1),
+                           host(arena.view("g", i), wl.gtype != 0),
                            O.pack_halves(m) if wl.mkind == 1 else m,
                            O.pack_halves(v) if wl.vkind == 1 else v))
     O.lib()
+    amp = O.AmpState(wl.amp_scale) if wl.amp else None
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
-        O.step_(ts, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1, wl.beta2,
-                wl.eps, wl.weight_decay, t, s=wl.scale, max_norm=wl.max_norm)
+        if amp is not None:
+            O.amp_step_(ts, wl.gtype, wl.mkind, wl.vkind, amp, wl.lr,
+                        wl.beta1, wl.beta2, wl.eps, wl.weight_decay,
+                        wl.max_norm)
+            amp.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
+        else:
+            O.step_(ts, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
+                    wl.beta2, wl.eps, wl.weight_decay, t, s=wl.scale,
+                    max_norm=wl.max_norm)
     dt = time.perf_counter() - t0
     return {"value": wl.n * steps / dt, "unit": "params/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{steps} whole steps (joint norm + clip + AdamW) of "
+            "sample": f"{steps} whole steps (joint norm + clip + AdamW"
+                      f"{' + loss-scale update' if amp else ''}) of "
                       f"the full {wl.n:,}-param list, one host thread, "
                       f"{dt:.2f} s"}
 
@@ -138,18 +148,27 @@ def main():
     stream = torch.cuda.current_stream()
     hp = wl.hparams
     defer = wl.scale != 1.0
+    amp = M.AmpState(wl.amp_scale) if wl.amp else None
 
     def step(t, ev=None):
         if defer:
             L.scale(wl.scale, defer=True)
         if ev is not None:
             ev[0].record(stream)
-        L.clip_norm(wl.max_norm, norm_d, coef_d)
+        if amp is not None:
+            L.amp_clip_norm(wl.max_norm, amp, norm_d, coef_d)
+        else:
+            L.clip_norm(wl.max_norm, norm_d, coef_d)
         if ev is not None:
             ev[1].record(stream)
-        L.adamw_step(hp, t, coef_d)
+        if amp is not None:
+            L.amp_adamw_step(hp, amp, coef_d)
+        else:
+            L.adamw_step(hp, t, coef_d)
         if ev is not None:
             ev[2].record(stream)
+        if amp is not None:      # one thread; not part of k_adamw's time
+            amp.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
 
     t = 0
     for _ in range(args.warmup):
@@ -175,6 +194,9 @@ def main():
     norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     adamw_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     assert torch.isfinite(norm_d).all() and torch.isfinite(coef_d).all()
+    if amp is not None:      # every timed step was taken, none skipped
+        st = amp.read()
+        assert st["step"] == t and st["found_inf"] == 0.0, st
 
     bpp = wl.bytes_per_param()
     if args.weight_copy:
@@ -202,7 +224,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "params": wl.n, "tensors": wl.count,
-            "grad": ["f32", "bf16"][wl.gtype],
+            "grad": ["f32", "bf16", "f16"][wl.gtype],
+            "loss_scaling": "dynamic (device state)" if wl.amp else "none",
             "m": ["f32", "bf16x2"][wl.mkind], "v": ["f32", "bf16x2"][wl.vkind],
             "bytes_per_param": bpp["norm"] + bpp["update"],
             "tiles": info["tiles"], "grid_update": info["grid_update"],

@@ -31,7 +31,8 @@
  *
  * Layouts.
  *   w            float32, n elements.
- *   g            float32 or bfloat16 (MTA_F32 / MTA_BF16, whole list), n elements.
+ *   g            float32, bfloat16 or IEEE float16 (MTA_F32 / MTA_BF16 /
+ *                MTA_F16, whole list), n elements.
  *   m, v         MTA_MOM_F32: float32, n elements.
  *                MTA_MOM_BF16X2: packed bfloat16, two per 32-bit word, element
  *                2k in the low half of word k ("BendTorch main.bend", PTree
@@ -70,7 +71,7 @@ extern "C" {
 
 typedef struct mta_list mta_list; /* opaque */
 
-typedef enum { MTA_F32 = 0, MTA_BF16 = 1 } mta_gtype;
+typedef enum { MTA_F32 = 0, MTA_BF16 = 1, MTA_F16 = 2 } mta_gtype;
 typedef enum { MTA_MOM_F32 = 0, MTA_MOM_BF16X2 = 1 } mta_mkind;
 
 typedef enum {
@@ -99,6 +100,23 @@ typedef struct {
 typedef struct {
   double lr, beta1, beta2, eps, weight_decay;
 } mta_adamw_hparams;
+
+/* Loss-scale state for float16 (or bfloat16) training with dynamic loss
+ * scaling, kept by the caller in DEVICE memory (24 bytes, 8-byte aligned) and
+ * read and written only by the device, so no step needs a host sync.  The
+ * gradients hold scale * (true gradient).  Reading of the pages' "the
+ * unscaling a float16 step needs before its clip" ("Mica 7.7", section "The
+ * whole model in one call"): PyTorch's GradScaler, whose numerics the pages
+ * promise.  Initialise scale (e.g. 65536), the other fields to 0. */
+typedef struct {
+  float scale;            /* loss scale */
+  float found_inf;        /* 1 when the last norm saw a non-finite unscaled
+                             gradient, else 0 (set by mta_amp_clip_norm,
+                             cleared by mta_amp_update) */
+  int32_t growth_tracker; /* good steps since the scale last changed */
+  int32_t reserved;
+  int64_t step;           /* AdamW steps taken; the next one is step + 1 */
+} mta_amp_state;
 
 /* Shape of a list handle, for callers and tests that want to see it. */
 typedef struct {
@@ -176,6 +194,39 @@ int mta_adamw_step(mta_list *list, const mta_adamw_hparams *hp, int64_t t,
  * this list.  On failure the previous copies stay attached. */
 int mta_list_set_weight_copies(mta_list *list, void *const *w16,
                                void *stream);
+
+/* Loss-scaled ClipGradNorms: as mta_clip_norm with the unscale factor
+ * s = float32(1 / float64(d_amp->scale)) read on the device, and one more
+ * output: d_amp->found_inf = 1 when the norm (of f32(g*s)) is not finite,
+ * that is when some unscaled gradient is Inf or NaN, else 0.  d_amp is a
+ * device pointer.  Not allowed while a host MTA_SCALE_DEFER factor is pending
+ * (MTA_ESTATE). */
+int mta_amp_clip_norm(mta_list *list, float max_norm, mta_amp_state *d_amp,
+                      float *d_norm, float *d_coef, void *stream);
+
+/* Loss-scaled AdamWSteps: one launch that does nothing when
+ * d_amp->found_inf is set; otherwise the step of mta_adamw_step with
+ * t = d_amp->step + 1 and the unscale factor float32(1/float64(scale)), both
+ * read on the device.  The device forms step = lr/(1-b1^t) and
+ * bc2 = sqrt(1-b2^t) in float64 with b^t rounded once to the nearest float64
+ * (the host form rounds b^t through libm's pow; the two agree except where
+ * pow is not correctly rounded).  d_amp is not modified: the step counter
+ * advances in mta_amp_update.  Same hyperparameter checks as
+ * mta_adamw_step. */
+int mta_amp_adamw_step(mta_list *list, const mta_adamw_hparams *hp,
+                       const mta_amp_state *d_amp, const float *d_coef,
+                       void *stream);
+
+/* After each loss-scaled step (PyTorch's GradScaler.update): one launch of
+ * one thread.  If found_inf: scale *= backoff_factor, growth_tracker = 0.
+ * Otherwise step += 1 and growth_tracker += 1; when it reaches
+ * growth_interval, scale *= growth_factor (kept only if finite) and
+ * growth_tracker = 0.  Products are formed in float64 and rounded to float32.
+ * found_inf is cleared.  Requires growth_factor > 1, 0 < backoff_factor < 1,
+ * growth_interval >= 1.  Needs no list. */
+int mta_amp_update(mta_amp_state *d_amp, double growth_factor,
+                   double backoff_factor, int32_t growth_interval,
+                   void *stream);
 
 /* Host only, no device work: the seven float32 constants the AdamW kernel
  * receives for step t, in the order {step, bc2, c1, c2, b2, eps, dec}. */

@@ -7,9 +7,10 @@ of the step, and nothing falls back to another implementation: if
 libmta.so is missing the first call raises.
 """
 from ._binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, MTA_BF16, MTA_F32, MTA_MOM_BF16X2, MTA_MOM_F32,
-    MTA_SCALE_DEFER, MTA_SCALE_INPLACE, MtaError, lib, mta_abi_version,
-    mta_adamw_scalars, mta_adamw_step, mta_clip_norm, mta_last_error,
+    EXPORTS, LIB_PATH, MTA_BF16, MTA_F16, MTA_F32, MTA_MOM_BF16X2,
+    MTA_MOM_F32, MTA_SCALE_DEFER, MTA_SCALE_INPLACE, MtaError, lib,
+    mta_abi_version, mta_adamw_scalars, mta_adamw_step, mta_amp_adamw_step,
+    mta_amp_clip_norm, mta_amp_update, mta_clip_norm, mta_last_error,
     mta_list_create, mta_list_destroy, mta_list_info,
     mta_list_set_weight_copies, mta_scale)
-from .torch_list import MtaList  # noqa: F401
+from .torch_list import AmpState, MtaList  # noqa: F401

@@ -10,7 +10,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmta.so")
 
-MTA_F32, MTA_BF16 = 0, 1
+MTA_F32, MTA_BF16, MTA_F16 = 0, 1, 2
 MTA_MOM_F32, MTA_MOM_BF16X2 = 0, 1
 MTA_SCALE_INPLACE, MTA_SCALE_DEFER = 1, 2
 
@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
 EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_clip_norm", "mta_adamw_step", "mta_list_set_weight_copies",
            "mta_adamw_scalars", "mta_list_info", "mta_last_error",
-           "mta_abi_version")
+           "mta_abi_version", "mta_amp_clip_norm", "mta_amp_adamw_step",
+           "mta_amp_update")
 
 
 class mta_tensor(ctypes.Structure):
@@ -36,6 +37,13 @@ class mta_adamw_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double)]
+
+
+class mta_amp_state(ctypes.Structure):
+    """Host image of the 24-byte device loss-scale state."""
+    _fields_ = [("scale", ctypes.c_float), ("found_inf", ctypes.c_float),
+                ("growth_tracker", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("step", ctypes.c_int64)]
 
 
 class mta_list_info_t(ctypes.Structure):
@@ -82,6 +90,12 @@ def lib():
         L.mta_adamw_scalars.argtypes = [ctypes.POINTER(mta_adamw_hparams),
                                         i64, ctypes.POINTER(ctypes.c_float)]
         L.mta_list_info.argtypes = [vp, ctypes.POINTER(mta_list_info_t)]
+        L.mta_amp_clip_norm.argtypes = [vp, f32, vp, vp, vp, vp]
+        L.mta_amp_adamw_step.argtypes = [vp,
+                                         ctypes.POINTER(mta_adamw_hparams),
+                                         vp, vp, vp]
+        L.mta_amp_update.argtypes = [vp, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_int32, vp]
         L.mta_last_error.argtypes = []
         L.mta_last_error.restype = ctypes.c_char_p
         L.mta_abi_version.argtypes = []
@@ -169,3 +183,20 @@ def mta_list_info(handle):
     info = mta_list_info_t()
     _check(lib().mta_list_info(handle, ctypes.byref(info)), "mta_list_info")
     return {name: getattr(info, name) for name, _ in mta_list_info_t._fields_}
+
+
+def mta_amp_clip_norm(handle, max_norm, d_amp, d_norm, d_coef, stream=0):
+    _check(lib().mta_amp_clip_norm(handle, max_norm, d_amp, d_norm, d_coef,
+                                   stream), "mta_amp_clip_norm")
+
+
+def mta_amp_adamw_step(handle, hp, d_amp, d_coef, stream=0):
+    h = _hparams(hp)
+    _check(lib().mta_amp_adamw_step(handle, ctypes.byref(h), d_amp, d_coef,
+                                    stream), "mta_amp_adamw_step")
+
+
+def mta_amp_update(d_amp, growth_factor, backoff_factor, growth_interval,
+                   stream=0):
+    _check(lib().mta_amp_update(d_amp, growth_factor, backoff_factor,
+                                growth_interval, stream), "mta_amp_update")

@@ -75,12 +75,12 @@ bool debug_sync() {
 // per CU that keeps two tiles of loads in flight (fewer concurrent streams,
 // better HBM page locality).  The norm pays one release fence and one ticket
 // atomic per workgroup, so it wants few workgroups, each with two tiles of
-// loads in flight: one per CU for float32 gradients, two for bfloat16 ones
+// loads in flight: one per CU for float32 gradients, two for 16-bit ones
 // (half the bytes per tile, so twice the workgroups for the same bytes in
 // flight).
 constexpr int kUpdateBlocksPerCu = 1;
 constexpr int kNormBlocksPerCuF32 = 1;
-constexpr int kNormBlocksPerCuBf16 = 2;
+constexpr int kNormBlocksPerCu16 = 2;
 
 int after_launch(hipError_t e, hipStream_t stream, const char *what) {
   if (e != hipSuccess)
@@ -147,6 +147,23 @@ void make_scalars(const mta_adamw_hparams &hp, int64_t t, float out[7]) {
   out[6] = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
 }
 
+// The kernel's scalar block for step t (t-independent entries are the same
+// for every t, so a loss-scaled step replaces only nstep, bc2 and s).
+mta::StepScalars step_scalars(const mta_adamw_hparams &hp, int64_t t) {
+  float c[7];
+  make_scalars(hp, t, c);
+  mta::StepScalars sc;
+  sc.nstep = -c[0];
+  sc.bc2 = c[1];
+  sc.c1 = c[2];
+  sc.c2 = c[3];
+  sc.b2 = c[4];
+  sc.eps = c[5];
+  sc.dec = c[6];
+  sc.s = 1.0f;
+  return sc;
+}
+
 struct Span {
   uintptr_t lo, hi;
   int64_t tensor;
@@ -173,7 +190,7 @@ int check_overlaps(std::vector<Span> *spans) {
 
 // The byte ranges of every buffer of the list's non-empty tensors.
 void list_spans(const mta_list *L, std::vector<Span> *spans) {
-  const uintptr_t sizes[4] = {4, L->gtype == MTA_BF16 ? 2u : 4u,
+  const uintptr_t sizes[4] = {4, L->gtype == MTA_F32 ? 4u : 2u,
                               L->mkind == MTA_MOM_BF16X2 ? 2u : 4u,
                               L->vkind == MTA_MOM_BF16X2 ? 2u : 4u};
   for (size_t i = 0; i < L->tensors.size(); ++i) {
@@ -195,7 +212,7 @@ uintptr_t elem_size(int kind_is_16bit) { return kind_is_16bit ? 2 : 4; }
 void build_step_tiles(const std::vector<mta_tensor> &tensors,
                       const std::vector<void *> &w16, int gtype, int mkind,
                       int vkind, std::vector<mta::StepTile> *out) {
-  const uintptr_t gsz = elem_size(gtype == MTA_BF16);
+  const uintptr_t gsz = elem_size(gtype != MTA_F32);
   const uintptr_t msz = elem_size(mkind == MTA_MOM_BF16X2);
   const uintptr_t vsz = elem_size(vkind == MTA_MOM_BF16X2);
   out->clear();
@@ -260,14 +277,14 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   if (count > 0 && !tensors) return fail(MTA_EINVAL, "tensors is NULL");
   if (count > static_cast<int64_t>(UINT32_MAX))
     return fail(MTA_EINVAL, "too many tensors");
-  if (gtype != MTA_F32 && gtype != MTA_BF16)
+  if (gtype != MTA_F32 && gtype != MTA_BF16 && gtype != MTA_F16)
     return fail(MTA_EDTYPE, "unknown gradient type %d", gtype);
   if (mkind != MTA_MOM_F32 && mkind != MTA_MOM_BF16X2)
     return fail(MTA_EDTYPE, "unknown m kind %d", mkind);
   if (vkind != MTA_MOM_F32 && vkind != MTA_MOM_BF16X2)
     return fail(MTA_EDTYPE, "unknown v kind %d", vkind);
 
-  const uintptr_t gsz = gtype == MTA_BF16 ? 2 : 4;
+  const uintptr_t gsz = gtype == MTA_F32 ? 4 : 2;
   const uintptr_t msz = mkind == MTA_MOM_BF16X2 ? 2 : 4;
   const uintptr_t vsz = vkind == MTA_MOM_BF16X2 ? 2 : 4;
 
@@ -350,7 +367,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
   const int bpc_n = env_int(
       "MTA_NORM_BLOCKS_PER_CU",
-      gtype == MTA_BF16 ? kNormBlocksPerCuBf16 : kNormBlocksPerCuF32, 1, 64);
+      gtype == MTA_F32 ? kNormBlocksPerCuF32 : kNormBlocksPerCu16, 1, 64);
   const int64_t tiles_or_one = std::max<int64_t>(1, L->ntiles);
   L->grid_update = static_cast<int>(
       std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_u));
@@ -518,7 +535,7 @@ int mta_clip_norm(mta_list *L, float max_norm, float *d_norm, float *d_coef,
   return after_launch(
       mta::launch_sumsq(L->gtype, wk, s, max_norm,
                         mta::NormScratch{L->d_partials, L->d_ticket}, d_norm,
-                        d_coef),
+                        d_coef, nullptr),
       wk.stream, "mta_clip_norm");
 }
 
@@ -531,21 +548,12 @@ int mta_adamw_step(mta_list *L, const mta_adamw_hparams *hp, int64_t t,
     return fail(MTA_EALIGN, "d_coef must be 4-byte aligned");
   rc = check_device(L);
   if (rc) return rc;
-  float c[7];
-  make_scalars(*hp, t, c);
-  mta::StepScalars sc;
-  sc.nstep = -c[0];
-  sc.bc2 = c[1];
-  sc.c1 = c[2];
-  sc.c2 = c[3];
-  sc.b2 = c[4];
-  sc.eps = c[5];
-  sc.dec = c[6];
+  mta::StepScalars sc = step_scalars(*hp, t);
   sc.s = L->deferred ? L->deferred_s : 1.0f;
   if (L->ntiles > 0) {
     const mta::Work wk = work_of(L, L->grid_update, stream);
-    const hipError_t e =
-        mta::launch_adamw(L->gtype, L->mkind, L->vkind, wk, sc, d_coef);
+    const hipError_t e = mta::launch_adamw(L->gtype, L->mkind, L->vkind, wk,
+                                           sc, d_coef, mta::AmpStep{});
     if (e != hipSuccess)  // nothing enqueued: the deferred factor stays
       return after_launch(e, wk.stream, "mta_adamw_step");
     L->deferred = false;
@@ -555,6 +563,81 @@ int mta_adamw_step(mta_list *L, const mta_adamw_hparams *hp, int64_t t,
   L->deferred = false;
   L->deferred_s = 1.0f;
   return ok();
+}
+
+int mta_amp_clip_norm(mta_list *L, float max_norm, mta_amp_state *d_amp,
+                      float *d_norm, float *d_coef, void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  if (!(max_norm > 0.0f))
+    return fail(MTA_EINVAL, "max_norm must be > 0 (got %g)",
+                static_cast<double>(max_norm));
+  if (!d_amp) return fail(MTA_EINVAL, "d_amp is NULL");
+  if (!d_coef) return fail(MTA_EINVAL, "d_coef is NULL");
+  if (!aligned(d_amp, 8))
+    return fail(MTA_EALIGN, "d_amp must be 8-byte aligned");
+  if (!aligned(d_coef, 4) || (d_norm && !aligned(d_norm, 4)))
+    return fail(MTA_EALIGN, "d_norm / d_coef must be 4-byte aligned");
+  if (L->deferred)
+    return fail(MTA_ESTATE,
+                "a host deferred scale factor is pending; a loss-scaled norm "
+                "takes its factor from the loss-scale state");
+  int rc = check_device(L);
+  if (rc) return rc;
+  const mta::Work wk = work_of(L, L->grid_norm, stream);
+  return after_launch(
+      mta::launch_sumsq(L->gtype, wk, 1.0f, max_norm,
+                        mta::NormScratch{L->d_partials, L->d_ticket}, d_norm,
+                        d_coef, d_amp),
+      wk.stream, "mta_amp_clip_norm");
+}
+
+int mta_amp_adamw_step(mta_list *L, const mta_adamw_hparams *hp,
+                       const mta_amp_state *d_amp, const float *d_coef,
+                       void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  int rc = check_hparams(hp, 1);
+  if (rc) return rc;
+  if (!d_amp) return fail(MTA_EINVAL, "d_amp is NULL");
+  if (!aligned(d_amp, 8))
+    return fail(MTA_EALIGN, "d_amp must be 8-byte aligned");
+  if (d_coef && !aligned(d_coef, 4))
+    return fail(MTA_EALIGN, "d_coef must be 4-byte aligned");
+  if (L->deferred)
+    return fail(MTA_ESTATE,
+                "a host deferred scale factor is pending; a loss-scaled step "
+                "takes its factor from the loss-scale state");
+  rc = check_device(L);
+  if (rc) return rc;
+  if (L->ntiles == 0) return ok();
+  // nstep, bc2 and s are formed by the kernel from the device state
+  const mta::StepScalars sc = step_scalars(*hp, 1);
+  const mta::Work wk = work_of(L, L->grid_update, stream);
+  return after_launch(
+      mta::launch_adamw(L->gtype, L->mkind, L->vkind, wk, sc, d_coef,
+                        mta::AmpStep{d_amp, hp->lr, hp->beta1, hp->beta2}),
+      wk.stream, "mta_amp_adamw_step");
+}
+
+int mta_amp_update(mta_amp_state *d_amp, double growth_factor,
+                   double backoff_factor, int32_t growth_interval,
+                   void *stream) {
+  if (!d_amp) return fail(MTA_EINVAL, "d_amp is NULL");
+  if (!aligned(d_amp, 8))
+    return fail(MTA_EALIGN, "d_amp must be 8-byte aligned");
+  if (!(std::isfinite(growth_factor) && growth_factor > 1.0))
+    return fail(MTA_EINVAL, "growth_factor must be finite and > 1 (got %g)",
+                growth_factor);
+  if (!(backoff_factor > 0.0 && backoff_factor < 1.0))
+    return fail(MTA_EINVAL, "backoff_factor must be in (0, 1) (got %g)",
+                backoff_factor);
+  if (growth_interval < 1)
+    return fail(MTA_EINVAL, "growth_interval must be >= 1 (got %d)",
+                static_cast<int>(growth_interval));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(mta::launch_amp_update(d_amp, growth_factor,
+                                             backoff_factor, growth_interval,
+                                             s),
+                      s, "mta_amp_update");
 }
 
 }  // extern "C"

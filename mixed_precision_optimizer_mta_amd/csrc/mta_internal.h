@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "../../include/mta.h"
+
 namespace mta {
 
 // A tile is the work of one workgroup iteration: up to kTileElems consecutive
@@ -62,10 +64,26 @@ struct NormScratch {
   unsigned int *ticket;
 };
 
+// Loss-scaled AdamW: with `state` set, the kernel skips the step when
+// state->found_inf is set, and otherwise takes t = state->step + 1 and the
+// unscale factor 1/state->scale from device memory, forming the
+// t-dependent constants itself from these float64 hyperparameters.
+static_assert(sizeof(mta_amp_state) == 24, "loss-scale state layout");
+
+struct AmpStep {
+  const mta_amp_state *state;  // nullptr: constants come from the host
+  double lr, beta1, beta2;
+};
+
 hipError_t launch_adamw(int gtype, int mkind, int vkind, const Work &work,
-                        const StepScalars &sc, const float *d_coef);
+                        const StepScalars &sc, const float *d_coef,
+                        const AmpStep &amp);
 hipError_t launch_sumsq(int gtype, const Work &work, float s, float max_norm,
-                        NormScratch scratch, float *d_norm, float *d_coef);
+                        NormScratch scratch, float *d_norm, float *d_coef,
+                        mta_amp_state *amp);
 hipError_t launch_scale(int gtype, const Work &work, float s);
+hipError_t launch_amp_update(mta_amp_state *state, double growth,
+                             double backoff, int32_t interval,
+                             hipStream_t stream);
 
 }  // namespace mta

@@ -1,38 +1,49 @@
 // mta_kernels.hip -- gfx950 kernels of the fused clip + multi-tensor AdamW step.
 //
-// Three kernels, each one launch over the whole tensor list:
-//   k_sumsq  joint sum of squares -> norm and clip coefficient (ClipGradNorms,
-//            "Mica 7.7: a training step on the card, in every float type",
-//            section "The whole model in one call"; the norm and coefficient
-//            stay in device memory, section "Values that stay on the card").
-//   k_adamw  AdamW over every (w, g, m, v) group (AdamWSteps, same section),
-//            with the element arithmetic of "BendTorch main.bend", section
-//            "Optimizers": adam_decay, adam_m, adam_v, adam_w, and the packed
-//            bfloat16 moments of adamh_l / adamhv_l (ph_of_bits, ph_to); when
-//            a tensor has one, it also writes the bfloat16 copy of its new
-//            weights (Mica, section "float16 and bfloat16, whole").
-//   k_scale  ScaleTensors in place (same Mica section).
+// Four kernels:
+//   k_sumsq       joint sum of squares -> norm and clip coefficient
+//                 (ClipGradNorms, "Mica 7.7: a training step on the card, in
+//                 every float type", section "The whole model in one call";
+//                 the norm and coefficient stay in device memory, section
+//                 "Values that stay on the card"); with a loss-scale state it
+//                 also reports whether any unscaled gradient is not finite.
+//   k_adamw       AdamW over every (w, g, m, v) group (AdamWSteps, same
+//                 section), with the element arithmetic of "BendTorch
+//                 main.bend", section "Optimizers": adam_decay, adam_m, adam_v,
+//                 adam_w, and the packed bfloat16 moments of adamh_l /
+//                 adamhv_l (ph_of_bits, ph_to); when a tensor has one, it also
+//                 writes the bfloat16 copy of its new weights (Mica, section
+//                 "float16 and bfloat16, whole").  With a loss-scale state it
+//                 skips a step whose gradients were not finite and takes the
+//                 step number from device memory.
+//   k_scale       ScaleTensors in place (same Mica section).
+//   k_amp_update  the loss-scale update after a step (one thread).
+// Each of the first three is one launch over the whole tensor list.
+//
+// Gradients are float32, bfloat16 or IEEE float16 (Mica: float16 and bfloat16
+// stand beside float32; a float16 step unscales before its clip).
 //
 // Work is cut into tiles of kTileElems elements of one tensor.  The tile
 // tables are built once per list on the host: each record holds the tile's
 // own buffer addresses, length and alignment, so one scalar load describes a
-// tile.  A persistent grid walks the tiles with a grid stride.  Inside a full tile of a 16-byte-aligned tensor every wave
-// instruction reads or writes one contiguous run of memory: lane l of group j
-// owns elements j*G + V*l .. j*G + V*l + V-1, where V is 4 for k_adamw (a
-// 16-byte access of a float32 buffer, 8 bytes of a bfloat16 one, so all four
-// buffers share one element mapping) and 16 bytes' worth for the single-buffer
-// kernels.  The tail tile of a tensor and the tiles of an unaligned tensor use
-// the same mapping with one-element accesses: loads clamped into the tile and
-// issued before any use, stores masked to the tile.
-// A lane owns whole elements, so a packed bfloat16 moment is written with
-// 8-byte or 16-bit stores and no 32-bit word is ever shared between lanes (no
-// read-modify-write of a neighbour's half).
+// tile.  A persistent grid walks the tiles with a grid stride.  Inside a full
+// tile of a 16-byte-aligned tensor every wave instruction reads or writes one
+// contiguous run of memory: lane l of group j owns elements j*G + V*l ..
+// j*G + V*l + V-1, where V is 4 for k_adamw (a 16-byte access of a float32
+// buffer, 8 bytes of a 16-bit one, so all buffers share one element mapping)
+// and 16 bytes' worth for the single-buffer kernels.  The tail tile of a
+// tensor and the tiles of an unaligned tensor use the same mapping with
+// one-element accesses: loads clamped into the tile and issued before any
+// use, stores masked to the tile.  A lane owns whole elements, so a packed
+// bfloat16 moment is written with 8-byte or 16-bit stores and no 32-bit word
+// is ever shared between lanes (no read-modify-write of a neighbour's half).
 //
 // Numerics: this file is compiled with -ffp-contract=off.  Every float32
 // operation of the AdamW update is rounded on its own, '/' and sqrtf are the
 // correctly rounded ones, and denormals are kept.  The only fused multiply-adds
-// are the explicit float64 fma of the norm's accumulation, which needs to be
-// accurate, not to follow a fixed rounding sequence.
+// are the explicit float64 fma of the norm's accumulation and of the
+// double-double power, which need to be accurate, not to follow a fixed
+// rounding sequence.
 #include <type_traits>
 
 #include "mta_internal.h"
@@ -40,8 +51,14 @@
 namespace mta {
 namespace {
 
+// Element types of a buffer (template argument D).
+constexpr int kF32 = 0;   // float32
+constexpr int kBF16 = 1;  // bfloat16 (packed moments are bfloat16 arrays)
+constexpr int kF16 = 2;   // IEEE binary16 (gradients only)
+
 // ---------------------------------------------------------------------------
-// bfloat16 <-> float32 ("BendTorch main.bend", Optimizers: ph_to, ph_of_bits)
+// 16-bit floats <-> float32 ("BendTorch main.bend", Optimizers: ph_to,
+// ph_of_bits for bfloat16)
 // ---------------------------------------------------------------------------
 
 // bfloat16 bits (low 16 bits of h) -> float32, exact.
@@ -61,6 +78,36 @@ __device__ __forceinline__ float round_bf16(float x) {
   return from_bf16(to_bf16(x));
 }
 
+// binary16 bits (low 16 bits of h) -> float32, exact (the hardware convert).
+__device__ __forceinline__ float from_f16(uint32_t h) {
+  return static_cast<float>(
+      __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu)));
+}
+
+// float32 -> binary16 bits, round to nearest, ties to even (the hardware
+// convert in the default rounding mode); any NaN -> 0xFFFF, as for bfloat16.
+// The empty asm pins x in a register as the float32 value it is: without it
+// the compiler fuses a producing multiply and this convert into one
+// mixed-precision fma with a +0 addend, which turns a -0 product into +0.
+__device__ __forceinline__ uint32_t to_f16(float x) {
+  __asm__("" : "+v"(x));
+  const uint32_t h =
+      __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  return (x != x) ? 0xFFFFu : h;
+}
+
+template <int D>
+__device__ __forceinline__ float decode16(uint32_t h) {
+  if constexpr (D == kBF16) return from_bf16(h & 0xFFFFu);
+  else return from_f16(h);
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t encode16(float x) {
+  if constexpr (D == kBF16) return to_bf16(x);
+  else return to_f16(x);
+}
+
 // Two bfloat16-exact float32 values (low halves zero) -> one packed word,
 // the even element in the low half.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -69,9 +116,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 // ---------------------------------------------------------------------------
 // Loads and stores through global-address-space pointers.  The buffers come
-// from the descriptor table, so without the cast the compiler cannot tell
-// them from LDS and would emit flat instructions.  Every tile has a uniform
-// base pointer (SGPRs) and each lane a 32-bit element offset, which maps to
+// from the tile records, so without the cast the compiler cannot tell them
+// from LDS and would emit flat instructions.  Every tile has a uniform base
+// pointer (SGPRs) and each lane a 32-bit element offset, which maps to
 // global_load/store with an SGPR base and a VGPR offset.  The vector accesses
 // carry the nontemporal hint: every byte is touched once per launch, and on
 // gfx950 the streaming hint measured faster for these contiguous-per-wave
@@ -83,9 +130,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Element type of a buffer: float32, or bfloat16 bits.
-template <bool Bf16>
-using elem_t = typename std::conditional<Bf16, uint16_t, float>::type;
+template <int D>
+using elem_t = typename std::conditional<D == kF32, float, uint16_t>::type;
 
 template <typename T>
 __device__ __forceinline__ MTA_GLOBAL T *gp(const void *p, int64_t elem) {
@@ -95,10 +141,10 @@ __device__ __forceinline__ MTA_GLOBAL T *gp(const void *p, int64_t elem) {
 // 4 consecutive elements at element offset e (a multiple of 4) of a
 // 16-byte-aligned tile base: a 16-byte store for float32, 8 bytes for
 // bfloat16 (values already bfloat16-exact; element 2k in the low half).
-template <bool Bf16>
-__device__ __forceinline__ void store4(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
+template <int D>
+__device__ __forceinline__ void store4(MTA_GLOBAL elem_t<D> *p, uint32_t e,
                                        const float (&x)[4]) {
-  if constexpr (Bf16)
+  if constexpr (D == kBF16)
     __builtin_nontemporal_store(u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])},
                                 (MTA_GLOBAL u32x2 *)(p + e));
   else
@@ -106,81 +152,49 @@ __device__ __forceinline__ void store4(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
                                 (MTA_GLOBAL f32x4 *)(p + e));
 }
 
-// 16 bytes per lane: 4 float32 or 8 bfloat16 elements at offset e.
-template <bool Bf16>
-constexpr int kWide = Bf16 ? 8 : 4;
+// 16 bytes per lane: 4 float32 or 8 16-bit elements at offset e, as one raw
+// vector, unpacked separately: a loop can issue every load of an iteration
+// before it unpacks any of them.
+template <int D>
+constexpr int kWide = D == kF32 ? 4 : 8;
 
-template <bool Bf16>
-__device__ __forceinline__ void load16b(MTA_GLOBAL const elem_t<Bf16> *p,
-                                        uint32_t e, float (&x)[kWide<Bf16>]) {
-  if constexpr (Bf16) {
-    const u32x4 a = __builtin_nontemporal_load((const MTA_GLOBAL u32x4 *)(p + e));
+template <int D>
+using raw16_t = typename std::conditional<D == kF32, f32x4, u32x4>::type;
+
+template <int D>
+__device__ __forceinline__ raw16_t<D> load16b_raw(MTA_GLOBAL const elem_t<D> *p,
+                                                 uint32_t e) {
+  return __builtin_nontemporal_load((const MTA_GLOBAL raw16_t<D> *)(p + e));
+}
+
+template <int D>
+__device__ __forceinline__ void unpack16b(const raw16_t<D> &a,
+                                          float (&x)[kWide<D>]) {
+  if constexpr (D == kF32) {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  } else {
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __uint_as_float(w[k] << 16);
-      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      x[2 * k] = decode16<D>(w[k]);
+      x[2 * k + 1] = decode16<D>(w[k] >> 16);
     }
-  } else {
-    const f32x4 a = __builtin_nontemporal_load((const MTA_GLOBAL f32x4 *)(p + e));
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   }
 }
 
-template <bool Bf16>
-__device__ __forceinline__ void store16b(MTA_GLOBAL elem_t<Bf16> *p,
-                                         uint32_t e,
-                                         const float (&x)[kWide<Bf16>]) {
-  if constexpr (Bf16)
-    __builtin_nontemporal_store(
-        u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]),
-              pack2(x[6], x[7])},
-        (MTA_GLOBAL u32x4 *)(p + e));
-  else
-    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]},
-                                (MTA_GLOBAL f32x4 *)(p + e));
-}
-
-// The same 16 bytes as one raw vector, unpacked separately: a loop can issue
-// every load of an iteration before it unpacks any of them.
-template <bool Bf16>
-using raw16_t = typename std::conditional<Bf16, u32x4, f32x4>::type;
-
-template <bool Bf16>
-__device__ __forceinline__ raw16_t<Bf16> load16b_raw(
-    MTA_GLOBAL const elem_t<Bf16> *p, uint32_t e) {
-  return __builtin_nontemporal_load((const MTA_GLOBAL raw16_t<Bf16> *)(p + e));
-}
-
-template <bool Bf16>
-__device__ __forceinline__ void unpack16b(const raw16_t<Bf16> &a,
-                                          float (&x)[kWide<Bf16>]) {
-  if constexpr (Bf16) {
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __uint_as_float(w[k] << 16);
-      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-    }
-  } else {
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  }
-}
-
-template <bool Bf16>
-__device__ __forceinline__ float load1(MTA_GLOBAL const elem_t<Bf16> *p,
+template <int D>
+__device__ __forceinline__ float load1(MTA_GLOBAL const elem_t<D> *p,
                                        uint32_t e) {
-  if constexpr (Bf16)
-    return from_bf16(p[e]);
-  else
-    return p[e];
+  if constexpr (D == kF32) return p[e];
+  else return decode16<D>(p[e]);
 }
 
-// Writes one element; for bfloat16 a 16-bit store of the (exact) value.
-template <bool Bf16>
-__device__ __forceinline__ void store1(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
+// Writes one element of a float32 or bfloat16 buffer; a bfloat16 value is
+// already bfloat16-exact and goes out as a 16-bit store.
+template <int D>
+__device__ __forceinline__ void store1(MTA_GLOBAL elem_t<D> *p, uint32_t e,
                                        float x) {
-  if constexpr (Bf16)
+  if constexpr (D == kBF16)
     p[e] = static_cast<uint16_t>(__float_as_uint(x) >> 16);
   else
     p[e] = x;
@@ -189,11 +203,47 @@ __device__ __forceinline__ void store1(MTA_GLOBAL elem_t<Bf16> *p, uint32_t e,
 // Element e of a tile of `lim` (>= 1) elements, or 0 past its end.  The
 // address is clamped to the tile's last element, so the load is always in
 // bounds and needs no branch: every such load of a loop issues back to back.
-template <bool Bf16>
-__device__ __forceinline__ float load1_clamped(MTA_GLOBAL const elem_t<Bf16> *p,
+template <int D>
+__device__ __forceinline__ float load1_clamped(MTA_GLOBAL const elem_t<D> *p,
                                                uint32_t e, uint32_t lim) {
-  const float x = load1<Bf16>(p, e < lim ? e : lim - 1);
+  const float x = load1<D>(p, e < lim ? e : lim - 1);
   return e < lim ? x : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// b^t rounded to the nearest float64, for step counts that live in device
+// memory: square-and-multiply in double-double (a float64 pair whose sum
+// carries ~106 bits; every product is exact to that width through fma), so
+// the result is the float64 nearest the true power unless it lies within
+// ~2^-100 (relative) of a rounding boundary.
+// ---------------------------------------------------------------------------
+
+struct DoubleDouble {
+  double hi, lo;  // |lo| <= ulp(hi)/2
+};
+
+__device__ __forceinline__ DoubleDouble dd_mul(DoubleDouble a,
+                                               DoubleDouble b) {
+  const double p = a.hi * b.hi;
+  double e = fma(a.hi, b.hi, -p);  // exact error of p
+  e = fma(a.hi, b.lo, e);
+  e = fma(a.lo, b.hi, e);
+  const double s = p + e;          // |e| << |p|: fast two-sum
+  return DoubleDouble{s, e - (s - p)};
+}
+
+__device__ double pow_rn(double b, int64_t t) {
+  DoubleDouble r{1.0, 0.0}, x{b, 0.0};
+  for (uint64_t k = static_cast<uint64_t>(t); k; k >>= 1) {
+    if (k & 1u) r = dd_mul(r, x);
+    x = dd_mul(x, x);
+  }
+  return r.hi;  // hi is the sum hi + lo rounded to nearest
+}
+
+// The unscale factor of a loss scale: float32(1 / float64(scale)).
+__device__ __forceinline__ float inv_scale(float scale) {
+  return static_cast<float>(1.0 / static_cast<double>(scale));
 }
 
 // ---------------------------------------------------------------------------
@@ -233,106 +283,114 @@ constexpr uint32_t kAdamStride = kBlock * kAdamVec;           // 1024
 // tile is computed, so no wait is needed between a tile's loads.
 
 // raw vectors of one lane's share of a full tile (4 accesses per buffer)
-template <bool Bf16>
-using raw4_t = typename std::conditional<Bf16, u32x2, f32x4>::type;
+template <int D>
+using raw4_t = typename std::conditional<D == kF32, f32x4, u32x2>::type;
 
-template <bool Bf16>
-__device__ __forceinline__ raw4_t<Bf16> load4_raw(MTA_GLOBAL const elem_t<Bf16> *p,
-                                                  uint32_t e) {
-  return __builtin_nontemporal_load((const MTA_GLOBAL raw4_t<Bf16> *)(p + e));
+template <int D>
+__device__ __forceinline__ raw4_t<D> load4_raw(MTA_GLOBAL const elem_t<D> *p,
+                                               uint32_t e) {
+  return __builtin_nontemporal_load((const MTA_GLOBAL raw4_t<D> *)(p + e));
 }
 
-template <bool Bf16>
-__device__ __forceinline__ void unpack4(const raw4_t<Bf16> &a, float (&x)[4]) {
-  if constexpr (Bf16) {
-    x[0] = __uint_as_float(a.x << 16);
-    x[1] = __uint_as_float(a.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(a.y << 16);
-    x[3] = __uint_as_float(a.y & 0xFFFF0000u);
-  } else {
+template <int D>
+__device__ __forceinline__ void unpack4(const raw4_t<D> &a, float (&x)[4]) {
+  if constexpr (D == kF32) {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  } else {
+    x[0] = decode16<D>(a.x);
+    x[1] = decode16<D>(a.x >> 16);
+    x[2] = decode16<D>(a.y);
+    x[3] = decode16<D>(a.y >> 16);
   }
 }
 
-template <bool GBf16, bool MPacked, bool VPacked>
+template <int G, bool MPacked, bool VPacked>
 struct TileRegs {
+  static constexpr int M = MPacked ? kBF16 : kF32;
+  static constexpr int V = VPacked ? kBF16 : kF32;
   f32x4 w[kAdamGroups];
-  raw4_t<GBf16> g[kAdamGroups];
-  raw4_t<MPacked> m[kAdamGroups];
-  raw4_t<VPacked> v[kAdamGroups];
+  raw4_t<G> g[kAdamGroups];
+  raw4_t<M> m[kAdamGroups];
+  raw4_t<V> v[kAdamGroups];
 };
 
-template <bool GBf16, bool MPacked, bool VPacked>
+template <int G, bool MPacked, bool VPacked>
 struct TileRef {
+  static constexpr int M = MPacked ? kBF16 : kF32;
+  static constexpr int V = VPacked ? kBF16 : kF32;
   MTA_GLOBAL float *pw;
-  MTA_GLOBAL const elem_t<GBf16> *pg;
-  MTA_GLOBAL elem_t<MPacked> *pm;
-  MTA_GLOBAL elem_t<VPacked> *pv;
+  MTA_GLOBAL const elem_t<G> *pg;
+  MTA_GLOBAL elem_t<M> *pm;
+  MTA_GLOBAL elem_t<V> *pv;
   MTA_GLOBAL uint16_t *pw16;  // bfloat16 weight copy, or null
   uint32_t lim;
   bool full;
 };
 
-template <bool GBf16, bool MPacked, bool VPacked>
-__device__ __forceinline__ TileRef<GBf16, MPacked, VPacked> tile_ref(
+template <int G, bool MPacked, bool VPacked>
+__device__ __forceinline__ TileRef<G, MPacked, VPacked> tile_ref(
     const StepTile &st) {
-  TileRef<GBf16, MPacked, VPacked> r;
+  using Ref = TileRef<G, MPacked, VPacked>;
+  Ref r;
   r.pw = gp<float>(st.w, 0);
-  r.pg = gp<elem_t<GBf16>>(st.g, 0);
-  r.pm = gp<elem_t<MPacked>>(st.m, 0);
-  r.pv = gp<elem_t<VPacked>>(st.v, 0);
+  r.pg = gp<elem_t<G>>(st.g, 0);
+  r.pm = gp<elem_t<Ref::M>>(st.m, 0);
+  r.pv = gp<elem_t<Ref::V>>(st.v, 0);
   r.pw16 = gp<uint16_t>(st.w16, 0);
   r.lim = st.lim;
   r.full = st.vec && st.lim == kTileElems;
   return r;
 }
 
-template <bool GBf16, bool MPacked, bool VPacked>
-__device__ __forceinline__ void issue_tile(
-    TileRegs<GBf16, MPacked, VPacked> &R,
-    const TileRef<GBf16, MPacked, VPacked> &T, uint32_t e0) {
+template <int G, bool MPacked, bool VPacked>
+__device__ __forceinline__ void issue_tile(TileRegs<G, MPacked, VPacked> &R,
+                                           const TileRef<G, MPacked, VPacked> &T,
+                                           uint32_t e0) {
+  using Ref = TileRef<G, MPacked, VPacked>;
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j) {
     const uint32_t e = e0 + j * kAdamStride;
-    R.w[j] = load4_raw<false>(T.pw, e);
-    R.g[j] = load4_raw<GBf16>(T.pg, e);
-    R.m[j] = load4_raw<MPacked>(T.pm, e);
-    R.v[j] = load4_raw<VPacked>(T.pv, e);
+    R.w[j] = load4_raw<kF32>(T.pw, e);
+    R.g[j] = load4_raw<G>(T.pg, e);
+    R.m[j] = load4_raw<Ref::M>(T.pm, e);
+    R.v[j] = load4_raw<Ref::V>(T.pv, e);
   }
 }
 
-template <bool GBf16, bool MPacked, bool VPacked>
+template <int G, bool MPacked, bool VPacked>
 __device__ __forceinline__ void finish_tile(
-    const TileRegs<GBf16, MPacked, VPacked> &R,
-    const TileRef<GBf16, MPacked, VPacked> &T, uint32_t e0,
-    const StepScalars &sc, float coef) {
+    const TileRegs<G, MPacked, VPacked> &R,
+    const TileRef<G, MPacked, VPacked> &T, uint32_t e0, const StepScalars &sc,
+    float coef) {
+  using Ref = TileRef<G, MPacked, VPacked>;
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j) {
     float w[4], g[4], m[4], v[4];
-    unpack4<false>(R.w[j], w);
-    unpack4<GBf16>(R.g[j], g);
-    unpack4<MPacked>(R.m[j], m);
-    unpack4<VPacked>(R.v[j], v);
+    unpack4<kF32>(R.w[j], w);
+    unpack4<G>(R.g[j], g);
+    unpack4<Ref::M>(R.m[j], m);
+    unpack4<Ref::V>(R.v[j], v);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       adamw_elem<MPacked, VPacked>(w[k], g[k], m[k], v[k], sc, coef);
     const uint32_t e = e0 + j * kAdamStride;
-    store4<false>(T.pw, e, w);
-    store4<MPacked>(T.pm, e, m);
-    store4<VPacked>(T.pv, e, v);
+    store4<kF32>(T.pw, e, w);
+    store4<Ref::M>(T.pm, e, m);
+    store4<Ref::V>(T.pv, e, v);
     if (T.pw16) {  // uniform: the tile has a bfloat16 weight copy
       float h[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) h[k] = round_bf16(w[k]);
-      store4<true>(T.pw16, e, h);
+      store4<kBF16>(T.pw16, e, h);
     }
   }
 }
 
-template <bool GBf16, bool MPacked, bool VPacked>
+template <int G, bool MPacked, bool VPacked>
 __device__ __forceinline__ void partial_tile(
-    const TileRef<GBf16, MPacked, VPacked> &T, uint32_t e0,
-    const StepScalars &sc, float coef) {
+    const TileRef<G, MPacked, VPacked> &T, uint32_t e0, const StepScalars &sc,
+    float coef) {
+  using Ref = TileRef<G, MPacked, VPacked>;
   float w[kAdamGroups][kAdamVec], g[kAdamGroups][kAdamVec],
       m[kAdamGroups][kAdamVec], v[kAdamGroups][kAdamVec];
 #pragma unroll
@@ -340,10 +398,10 @@ __device__ __forceinline__ void partial_tile(
 #pragma unroll
     for (int k = 0; k < kAdamVec; ++k) {
       const uint32_t e = e0 + j * kAdamStride + k;
-      w[j][k] = load1_clamped<false>(T.pw, e, T.lim);
-      g[j][k] = load1_clamped<GBf16>(T.pg, e, T.lim);
-      m[j][k] = load1_clamped<MPacked>(T.pm, e, T.lim);
-      v[j][k] = load1_clamped<VPacked>(T.pv, e, T.lim);
+      w[j][k] = load1_clamped<kF32>(T.pw, e, T.lim);
+      g[j][k] = load1_clamped<G>(T.pg, e, T.lim);
+      m[j][k] = load1_clamped<Ref::M>(T.pm, e, T.lim);
+      v[j][k] = load1_clamped<Ref::V>(T.pv, e, T.lim);
     }
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j)
@@ -354,26 +412,38 @@ __device__ __forceinline__ void partial_tile(
       const uint32_t e = e0 + j * kAdamStride + k;
       if (e < T.lim) {
         T.pw[e] = w[j][k];
-        store1<MPacked>(T.pm, e, m[j][k]);
-        store1<VPacked>(T.pv, e, v[j][k]);
-        if (T.pw16) store1<true>(T.pw16, e, round_bf16(w[j][k]));
+        store1<Ref::M>(T.pm, e, m[j][k]);
+        store1<Ref::V>(T.pv, e, v[j][k]);
+        if (T.pw16) store1<kBF16>(T.pw16, e, round_bf16(w[j][k]));
       }
     }
 }
 
-template <bool GBf16, bool MPacked, bool VPacked>
+template <int G, bool MPacked, bool VPacked>
 __global__ void __launch_bounds__(kBlock)
 k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
-        const float *__restrict__ d_coef) {
-  using Regs = TileRegs<GBf16, MPacked, VPacked>;
-  using Ref = TileRef<GBf16, MPacked, VPacked>;
+        const float *__restrict__ d_coef, AmpStep amp) {
+  using Regs = TileRegs<G, MPacked, VPacked>;
+  using Ref = TileRef<G, MPacked, VPacked>;
+  if (amp.state) {
+    // loss-scaled step: skipped when an unscaled gradient was not finite;
+    // otherwise t comes from the device counter and the two t-dependent
+    // constants are formed here, in float64, as the host forms them
+    if (amp.state->found_inf != 0.0f) return;
+    const int64_t t = amp.state->step + 1;
+    const double q1 = 1.0 - pow_rn(amp.beta1, t);
+    const double q2 = 1.0 - pow_rn(amp.beta2, t);
+    sc.nstep = -static_cast<float>(amp.lr / q1);
+    sc.bc2 = static_cast<float>(sqrt(q2));
+    sc.s = inv_scale(amp.state->scale);
+  }
   const float coef = d_coef ? *d_coef : 1.0f;
   const uint32_t e0 = threadIdx.x * kAdamVec;
   uint32_t t = blockIdx.x;
   if (t >= ntiles) return;
   const uint32_t last = ntiles - 1;
   Regs A, B;
-  Ref cur = tile_ref<GBf16, MPacked, VPacked>(tiles[t]);
+  Ref cur = tile_ref<G, MPacked, VPacked>(tiles[t]);
   // the record of the next tile, read one iteration ahead (clamped to the
   // last tile, so the scalar load is always in bounds)
   StepTile rec = tiles[min(t + gridDim.x, last)];
@@ -384,7 +454,7 @@ k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
   auto step = [&](Regs &X, Regs &Y) -> bool {
     const uint32_t tn = t + gridDim.x;
     const bool more = tn < ntiles;
-    const Ref nxt = tile_ref<GBf16, MPacked, VPacked>(rec);
+    const Ref nxt = tile_ref<G, MPacked, VPacked>(rec);
     if (more && nxt.full) issue_tile(Y, nxt, e0);
     // only now the next record: scalar loads return out of order, so a wait
     // for `rec` placed before the vector loads would also wait for this one
@@ -413,7 +483,8 @@ k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
 //   wave sums the partials in a fixed lane-strided order, takes the square
 //   root, forms the clip coefficient and writes both, then re-arms the ticket.
 // The grid and the tile order are fixed per list, so the result is the same
-// bits on every call.
+// bits on every call.  The float64 sum of the squares of float32 values
+// cannot overflow, so the total is finite exactly when every x is.
 // ---------------------------------------------------------------------------
 
 // DPP controls (gfx9 encoding): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -448,14 +519,15 @@ __device__ __forceinline__ double wave_sum(double x) {
          (readlane_f64(x, 32) + readlane_f64(x, 48));
 }
 
-template <bool GBf16>
+template <int D>
 __global__ void __launch_bounds__(kBlock)
 k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
         float max_norm, double *__restrict__ partials,
         unsigned int *__restrict__ ticket, float *__restrict__ d_norm,
-        float *__restrict__ d_coef) {
-  constexpr int V = kWide<GBf16>;
+        float *__restrict__ d_coef, mta_amp_state *__restrict__ amp) {
+  constexpr int V = kWide<D>;
   constexpr int G = kTileElems / (kBlock * V);
+  if (amp) s = inv_scale(amp->scale);  // loss-scaled: unscale by 1/scale
   // Two tiles per iteration (t and t + gridDim.x).  Their records are read
   // one iteration ahead (clamped to the last tile: always in bounds).  When
   // both tiles are full tiles of aligned tensors (the common case) all their
@@ -485,13 +557,13 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
                  cur[u].lim == kTileElems;
     }
     if (all_full) {
-      raw16_t<GBf16> r[U][G];
+      raw16_t<D> r[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < G; ++j)
-          r[u][j] = load16b_raw<GBf16>(
-              gp<elem_t<GBf16>>(cur[u].g, j * (kBlock * V)), e0);
+          r[u][j] = load16b_raw<D>(gp<elem_t<D>>(cur[u].g, j * (kBlock * V)),
+                                   e0);
       // the next records only after the vector loads (scalar loads return
       // out of order: an earlier one would be waited for with these)
       __builtin_amdgcn_sched_barrier(0);
@@ -504,7 +576,7 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           float x[V];
-          unpack16b<GBf16>(r[u][j], x);
+          unpack16b<D>(r[u][j], x);
 #pragma unroll
           for (int k = 0; k < V; ++k) {
             const double xs = static_cast<double>(x[k] * s);
@@ -520,20 +592,19 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!valid[u]) continue;
-        MTA_GLOBAL const elem_t<GBf16> *pg = gp<elem_t<GBf16>>(cur[u].g, 0);
+        MTA_GLOBAL const elem_t<D> *pg = gp<elem_t<D>>(cur[u].g, 0);
         const uint32_t lim = cur[u].lim;
         float x[G][V];
         if (cur[u].vec && lim == kTileElems) {
 #pragma unroll
           for (int j = 0; j < G; ++j)
-            load16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
+            unpack16b<D>(load16b_raw<D>(pg + j * (kBlock * V), e0), x[j]);
         } else {
 #pragma unroll
           for (int j = 0; j < G; ++j)
 #pragma unroll
             for (int k = 0; k < V; ++k)
-              x[j][k] =
-                  load1_clamped<GBf16>(pg, e0 + j * (kBlock * V) + k, lim);
+              x[j][k] = load1_clamped<D>(pg, e0 + j * (kBlock * V) + k, lim);
         }
 #pragma unroll
         for (int j = 0; j < G; ++j)
@@ -595,39 +666,48 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
     const float c = max_norm / (nrm + 1e-6f);
     if (d_norm) *d_norm = nrm;
     *d_coef = (c > 1.0f) ? 1.0f : c;
+    if (amp) amp->found_inf = isfinite(total) ? 0.0f : 1.0f;
     __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ---------------------------------------------------------------------------
-// ScaleTensors in place: g = g * s, a bfloat16 gradient rounded back to
-// nearest-even.
+// ScaleTensors in place: g = g * s, a 16-bit gradient rounded back to its
+// type (nearest-even; NaN -> 0xFFFF).
 // ---------------------------------------------------------------------------
 
-template <bool GBf16>
+template <int D>
 __global__ void __launch_bounds__(kBlock)
 k_scale(const GradTile *__restrict__ tiles, uint32_t ntiles, float s) {
-  constexpr int V = kWide<GBf16>;
+  constexpr int V = kWide<D>;
   constexpr int G = kTileElems / (kBlock * V);
   for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const GradTile tl = tiles[t];
-    MTA_GLOBAL elem_t<GBf16> *__restrict__ pg =
-        gp<elem_t<GBf16>>(const_cast<void *>(tl.g), 0);
+    MTA_GLOBAL elem_t<D> *__restrict__ pg =
+        gp<elem_t<D>>(const_cast<void *>(tl.g), 0);
     const uint32_t lim = tl.lim;
     const uint32_t e0 = threadIdx.x * V;
     float x[G][V];
     if (tl.vec && lim == kTileElems) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) load16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
-      __builtin_amdgcn_sched_barrier(0);  // all loads in flight first
+      for (int j = 0; j < G; ++j)
+        unpack16b<D>(load16b_raw<D>(pg + j * (kBlock * V), e0), x[j]);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
+        MTA_GLOBAL elem_t<D> *q = pg + j * (kBlock * V) + e0;
+        if constexpr (D == kF32) {
+          __builtin_nontemporal_store(
+              f32x4{x[j][0] * s, x[j][1] * s, x[j][2] * s, x[j][3] * s},
+              (MTA_GLOBAL f32x4 *)q);
+        } else {
+          uint32_t h[V];
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-          x[j][k] = x[j][k] * s;
-          if constexpr (GBf16) x[j][k] = round_bf16(x[j][k]);
+          for (int k = 0; k < V; ++k) h[k] = encode16<D>(x[j][k] * s);
+          __builtin_nontemporal_store(
+              u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                    h[4] | (h[5] << 16), h[6] | (h[7] << 16)},
+              (MTA_GLOBAL u32x4 *)q);
         }
-        store16b<GBf16>(pg + j * (kBlock * V), e0, x[j]);
       }
     } else {
       // tail tile or unaligned tensor: same mapping, clamped element loads
@@ -636,68 +716,128 @@ k_scale(const GradTile *__restrict__ tiles, uint32_t ntiles, float s) {
       for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int k = 0; k < V; ++k)
-          x[j][k] = load1_clamped<GBf16>(pg, e0 + j * (kBlock * V) + k, lim);
+          x[j][k] = load1_clamped<D>(pg, e0 + j * (kBlock * V) + k, lim);
 #pragma unroll
       for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int k = 0; k < V; ++k) {
           const uint32_t e = e0 + j * (kBlock * V) + k;
           if (e < lim) {
-            float y = x[j][k] * s;
-            if constexpr (GBf16) y = round_bf16(y);
-            store1<GBf16>(pg, e, y);
+            const float y = x[j][k] * s;
+            if constexpr (D == kF32)
+              pg[e] = y;
+            else
+              pg[e] = static_cast<uint16_t>(encode16<D>(y));
           }
         }
     }
   }
 }
 
-template <bool G, bool M, bool V>
+// ---------------------------------------------------------------------------
+// The loss-scale update after a step (reading: PyTorch's GradScaler.update):
+// a step with a non-finite unscaled gradient backs the scale off and resets
+// the tracker; otherwise the step counts, the tracker grows, and every
+// `interval` good steps the scale grows when the grown scale is finite.
+// Products in float64, rounded once to float32.  The flag is cleared.
+// ---------------------------------------------------------------------------
+
+__global__ void k_amp_update(mta_amp_state *__restrict__ st, double growth,
+                             double backoff, int32_t interval) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  if (st->found_inf != 0.0f) {
+    st->scale = static_cast<float>(static_cast<double>(st->scale) * backoff);
+    st->growth_tracker = 0;
+  } else {
+    st->step += 1;
+    const int32_t good = st->growth_tracker + 1;
+    if (good == interval) {
+      const float grown =
+          static_cast<float>(static_cast<double>(st->scale) * growth);
+      if (isfinite(grown)) st->scale = grown;
+      st->growth_tracker = 0;
+    } else {
+      st->growth_tracker = good;
+    }
+  }
+  st->found_inf = 0.0f;
+}
+
+template <int G, bool M, bool V>
 hipError_t launch_adamw_t(const Work &wk, const StepScalars &sc,
-                          const float *d_coef) {
+                          const float *d_coef, const AmpStep &amp) {
   hipLaunchKernelGGL((k_adamw<G, M, V>), dim3(wk.grid), dim3(kBlock), 0,
-                     wk.stream, wk.stiles, wk.ntiles, sc, d_coef);
+                     wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_adamw_g(int mkind, int vkind, const Work &wk,
+                          const StepScalars &sc, const float *d_coef,
+                          const AmpStep &amp) {
+  switch ((mkind << 1) | vkind) {
+    case 0: return launch_adamw_t<G, false, false>(wk, sc, d_coef, amp);
+    case 1: return launch_adamw_t<G, false, true>(wk, sc, d_coef, amp);
+    case 2: return launch_adamw_t<G, true, false>(wk, sc, d_coef, amp);
+    case 3: return launch_adamw_t<G, true, true>(wk, sc, d_coef, amp);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_sumsq_t(const Work &wk, float s, float max_norm,
+                          NormScratch scr, float *d_norm, float *d_coef,
+                          mta_amp_state *amp) {
+  hipLaunchKernelGGL((k_sumsq<D>), dim3(wk.grid), dim3(kBlock), 0, wk.stream,
+                     wk.gtiles, wk.ntiles, s, max_norm, scr.partials,
+                     scr.ticket, d_norm, d_coef, amp);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_scale_t(const Work &wk, float s) {
+  hipLaunchKernelGGL((k_scale<D>), dim3(wk.grid), dim3(kBlock), 0, wk.stream,
+                     wk.gtiles, wk.ntiles, s);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_adamw(int gtype, int mkind, int vkind, const Work &wk,
-                        const StepScalars &sc, const float *d_coef) {
-  const int key = (gtype << 2) | (mkind << 1) | vkind;
-  switch (key) {
-    case 0: return launch_adamw_t<false, false, false>(wk, sc, d_coef);
-    case 1: return launch_adamw_t<false, false, true>(wk, sc, d_coef);
-    case 2: return launch_adamw_t<false, true, false>(wk, sc, d_coef);
-    case 3: return launch_adamw_t<false, true, true>(wk, sc, d_coef);
-    case 4: return launch_adamw_t<true, false, false>(wk, sc, d_coef);
-    case 5: return launch_adamw_t<true, false, true>(wk, sc, d_coef);
-    case 6: return launch_adamw_t<true, true, false>(wk, sc, d_coef);
-    case 7: return launch_adamw_t<true, true, true>(wk, sc, d_coef);
+                        const StepScalars &sc, const float *d_coef,
+                        const AmpStep &amp) {
+  switch (gtype) {
+    case kF32: return launch_adamw_g<kF32>(mkind, vkind, wk, sc, d_coef, amp);
+    case kBF16: return launch_adamw_g<kBF16>(mkind, vkind, wk, sc, d_coef, amp);
+    case kF16: return launch_adamw_g<kF16>(mkind, vkind, wk, sc, d_coef, amp);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_sumsq(int gtype, const Work &wk, float s, float max_norm,
-                        NormScratch scr, float *d_norm, float *d_coef) {
-  if (gtype)
-    hipLaunchKernelGGL((k_sumsq<true>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.gtiles, wk.ntiles, s, max_norm,
-                       scr.partials, scr.ticket, d_norm, d_coef);
-  else
-    hipLaunchKernelGGL((k_sumsq<false>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.gtiles, wk.ntiles, s, max_norm,
-                       scr.partials, scr.ticket, d_norm, d_coef);
-  return hipGetLastError();
+                        NormScratch scr, float *d_norm, float *d_coef,
+                        mta_amp_state *amp) {
+  switch (gtype) {
+    case kF32: return launch_sumsq_t<kF32>(wk, s, max_norm, scr, d_norm, d_coef, amp);
+    case kBF16: return launch_sumsq_t<kBF16>(wk, s, max_norm, scr, d_norm, d_coef, amp);
+    case kF16: return launch_sumsq_t<kF16>(wk, s, max_norm, scr, d_norm, d_coef, amp);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_scale(int gtype, const Work &wk, float s) {
-  if (gtype)
-    hipLaunchKernelGGL((k_scale<true>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.gtiles, wk.ntiles, s);
-  else
-    hipLaunchKernelGGL((k_scale<false>), dim3(wk.grid), dim3(kBlock), 0,
-                       wk.stream, wk.gtiles, wk.ntiles, s);
+  switch (gtype) {
+    case kF32: return launch_scale_t<kF32>(wk, s);
+    case kBF16: return launch_scale_t<kBF16>(wk, s);
+    case kF16: return launch_scale_t<kF16>(wk, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_amp_update(mta_amp_state *st, double growth, double backoff,
+                             int32_t interval, hipStream_t stream) {
+  hipLaunchKernelGGL(k_amp_update, dim3(1), dim3(64), 0, stream, st, growth,
+                     backoff, interval);
   return hipGetLastError();
 }
 

@@ -5,11 +5,14 @@ Marshalling only.  It checks that the tensors are what the C ABI expects
 the current HIP stream, and owns the handle.  The tensors must keep their
 storage for the handle's life (the library holds their addresses).
 """
+import struct
+
 import torch
 
 from . import _binding as B
 
-_G = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16}
+_G = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
+      torch.float16: B.MTA_F16}
 _M = {torch.float32: B.MTA_MOM_F32, torch.bfloat16: B.MTA_MOM_BF16X2}
 
 
@@ -18,9 +21,9 @@ def current_stream():
 
 
 class MtaList:
-    """groups: sequence of (w, g, m, v) tensors.  w is float32; g float32 or
-    bfloat16; m and v float32 or bfloat16 (bfloat16 = packed moments); all
-    groups share the gradient type and each moment kind."""
+    """groups: sequence of (w, g, m, v) tensors.  w is float32; g float32,
+    bfloat16 or float16; m and v float32 or bfloat16 (bfloat16 = packed
+    moments); all groups share the gradient type and each moment kind."""
 
     def __init__(self, groups, entries=None, gtype=None, mkind=None,
                  vkind=None):
@@ -99,6 +102,26 @@ class MtaList:
                          None if coef is None else coef.data_ptr(),
                          current_stream())
 
+    def amp_clip_norm(self, max_norm, amp, norm_out, coef_out):
+        """Loss-scaled norm: unscales by 1/amp.scale on the device and sets
+        amp's found_inf flag."""
+        for t in (norm_out, coef_out):
+            if t is not None and (t.dtype != torch.float32 or not t.is_cuda):
+                raise TypeError("norm/coef outputs are float32 GPU tensors")
+        B.mta_amp_clip_norm(self.handle, max_norm, amp.ptr,
+                            None if norm_out is None else norm_out.data_ptr(),
+                            coef_out.data_ptr(), current_stream())
+
+    def amp_adamw_step(self, hparams, amp, coef=None):
+        """Loss-scaled AdamW step: t and 1/scale come from amp on the
+        device; no-op when its found_inf flag is set."""
+        if coef is not None and (coef.dtype != torch.float32 or
+                                 not coef.is_cuda):
+            raise TypeError("coef is a float32 GPU tensor")
+        B.mta_amp_adamw_step(self.handle, hparams, amp.ptr,
+                             None if coef is None else coef.data_ptr(),
+                             current_stream())
+
     def close(self):
         if self.handle is not None:
             B.mta_list_destroy(self.handle)
@@ -109,3 +132,37 @@ class MtaList:
             self.close()
         except Exception:
             pass
+
+
+class AmpState:
+    """The 24-byte device loss-scale state of include/mta.h (mta_amp_state):
+    scale, found_inf, growth_tracker, step.  Lives in device memory; reading
+    it back (``read``) synchronizes the stream."""
+
+    _FMT = "<ffiiq"
+
+    def __init__(self, scale=65536.0, step=0, growth_tracker=0,
+                 found_inf=0.0, device=None):
+        self.buf = torch.empty(3, dtype=torch.int64,
+                               device=device or torch.device("cuda"))
+        self.write(scale, step, growth_tracker, found_inf)
+
+    @property
+    def ptr(self):
+        return self.buf.data_ptr()
+
+    def write(self, scale, step=0, growth_tracker=0, found_inf=0.0):
+        raw = struct.pack(self._FMT, scale, found_inf, growth_tracker, 0, step)
+        host = torch.frombuffer(bytearray(raw), dtype=torch.int64)
+        self.buf.copy_(host)
+
+    def read(self):
+        raw = self.buf.cpu().numpy().tobytes()
+        scale, found_inf, tracker, _, step = struct.unpack(self._FMT, raw)
+        return {"scale": scale, "found_inf": found_inf,
+                "growth_tracker": tracker, "step": step}
+
+    def update(self, growth_factor=2.0, backoff_factor=0.5,
+               growth_interval=2000):
+        B.mta_amp_update(self.ptr, growth_factor, backoff_factor,
+                         growth_interval, current_stream())

@@ -2,8 +2,8 @@
 
 This module holds no optimizer arithmetic.  It only says which tensors a
 workload has, and fills weights and gradients with seeded normal draws
-(torch's generators, on the device the arena lives on; a bfloat16 gradient
-is torch's own float32 -> bfloat16 conversion of the drawn value).  Moments
+(torch's generators, on the device the arena lives on; a 16-bit gradient
+is torch's own float32 -> bfloat16 / float16 conversion of the drawn value).  Moments
 start at zero.  The tests and the benchmark feed the same bytes to the HIP
 library and to the CPU oracle.
 
@@ -17,6 +17,10 @@ Workloads (parameter counts are exact):
   gpt2_124m_bf16g  the same list with bfloat16 gradients holding
              65536 * N(0, 1e-3), unscaled by 2^-16 before the clip; f32
              moments; 100 steps.
+  gpt2_124m_f16amp  the same list with float16 gradients under dynamic loss
+             scaling: a device loss-scale state starting at 65536 (growth 2,
+             backoff 0.5, interval 2000), gradients holding 65536 *
+             N(0, 1e-3); f32 moments.
   gpt2_xl    GPT-2-XL-shaped list (vocab 50257, d 1600, 48 layers, d_ff
              6400), 434 tensors, 1,557,454,400 params; f32 g ~ N(0, 1e-3),
              packed bfloat16 m and v.
@@ -32,7 +36,7 @@ import numpy as np
 
 SEED = 20261202
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 MOM_F32, MOM_BF16X2 = 0, 1
 
 # element alignment of every tensor inside an arena: 128 elements is 512 B
@@ -61,6 +65,11 @@ class Workload:
     g_mult: float = 1.0         # gradient stored as g_mult * N(0, g_sigma)
     zero_grad: frozenset = field(default_factory=frozenset)
     ident: int = 0
+    amp: bool = False           # dynamic loss scaling with a device state
+    amp_scale: float = 65536.0  # its initial scale
+    amp_growth: float = 2.0
+    amp_backoff: float = 0.5
+    amp_interval: int = 2000
 
     @property
     def n(self):
@@ -78,7 +87,7 @@ class Workload:
     def bytes_per_param(self):
         """Algorithmic HBM bytes per parameter of one step: the norm reads g
         once; the update reads w, g, m, v and writes w, m, v."""
-        gb = 2 if self.gtype == BF16 else 4
+        gb = 4 if self.gtype == F32 else 2
         mb = 2 if self.mkind == MOM_BF16X2 else 4
         vb = 2 if self.vkind == MOM_BF16X2 else 4
         return {"norm": gb, "update": 4 + gb + mb + vb + 4 + mb + vb}
@@ -113,6 +122,10 @@ def get(name):
                         gpt2_sizes(50257, 768, 1024, 12, 3072), BF16, MOM_F32,
                         MOM_F32, steps=100, g_mult=65536.0,
                         scale=2.0 ** -16, ident=3)
+    if name == "gpt2_124m_f16amp":
+        return Workload("gpt2_124m_f16amp",
+                        gpt2_sizes(50257, 768, 1024, 12, 3072), F16, MOM_F32,
+                        MOM_F32, steps=20, g_mult=65536.0, amp=True, ident=6)
     if name == "gpt2_xl":
         return Workload("gpt2_xl", gpt2_sizes(50257, 1600, 1024, 48, 6400),
                         F32, MOM_BF16X2, MOM_BF16X2, steps=2, ident=4)
@@ -124,7 +137,8 @@ def get(name):
     raise KeyError(name)
 
 
-NAMES = ("tiny", "gpt2_124m", "gpt2_124m_bf16g", "gpt2_xl", "ragged")
+NAMES = ("tiny", "gpt2_124m", "gpt2_124m_bf16g", "gpt2_124m_f16amp",
+         "gpt2_xl", "ragged")
 
 
 def scaled_down(wl, sizes, name=None, zero_grad=None):
@@ -161,7 +175,8 @@ class Arena:
             total = -(-total // ALIGN_ELEMS) * ALIGN_ELEMS
         self.offsets = [int(o) for o in offsets]
         self.total = int(total) + ALIGN_ELEMS   # room for guard elements
-        gd = torch.bfloat16 if wl.gtype == BF16 else torch.float32
+        gd = {F32: torch.float32, BF16: torch.bfloat16,
+              F16: torch.float16}[wl.gtype]
         md = torch.bfloat16 if wl.mkind == MOM_BF16X2 else torch.float32
         vd = torch.bfloat16 if wl.vkind == MOM_BF16X2 else torch.float32
         self.w = torch.zeros(self.total, dtype=torch.float32,

@@ -60,7 +60,8 @@ def dev_bf16_bits(t):
 
 
 def grad_np(t, gtype):
-    return dev_bf16_bits(t) if gtype == WL.BF16 else dev_f32(t)
+    """Device gradient -> oracle layout (16-bit types: their bit patterns)."""
+    return dev_f32(t) if gtype == WL.F32 else dev_bf16_bits(t)
 
 
 def mom_np(t, kind):
@@ -160,3 +161,117 @@ def sample_positions(wl, offsets, nsample, seed=1):
     t = np.searchsorted(cum, r, side="right") - 1
     parts.append(offs[t] + (r - cum[t]))
     return np.unique(np.concatenate(parts))
+
+
+def make_list(arena):
+    from mixed_precision_optimizer_mta_amd import MtaList
+    wl = arena.wl
+    return MtaList([], entries=arena.entries(), gtype=wl.gtype,
+                   mkind=wl.mkind, vkind=wl.vkind)
+
+
+def _bits32(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+def check_amp_state(dev, ora, what=""):
+    """The device loss-scale state equals the oracle's, field by field
+    (the scale bit for bit)."""
+    got = (_bits32(dev["scale"]), _bits32(dev["found_inf"]),
+           dev["growth_tracker"], dev["step"])
+    want = (_bits32(ora.scale), _bits32(ora.found_inf), ora.tracker,
+            ora.step)
+    assert got == want, (what, dev, vars(ora))
+
+
+def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
+             check_guards=False, clip=True, inject=None):
+    """Run `steps` device steps in lockstep with the oracle; returns the
+    worst ulp distances seen.
+
+    A loss-scaled workload (wl.amp) runs mta_amp_clip_norm,
+    mta_amp_adamw_step and mta_amp_update against oracle.amp_step_ and
+    AmpState.update, and also checks the found_inf flag and the state after
+    every step.  inject: {step: [(arena position, value), ...]} written into
+    the gradients after they are drawn (positions must be sampled ones when
+    nsample is set, so the oracle sees them)."""
+    from mixed_precision_optimizer_mta_amd import AmpState
+    arena = WL.Arena(wl, "cuda", offsets)
+    arena.fill_weights()
+    L = make_list(arena)
+    idx = None
+    if nsample is not None:
+        idx = sample_positions(wl, arena.offsets, nsample)
+    ostate = oracle_state(arena, idx)
+    before = None
+    if check_guards:
+        before = {b: getattr(arena, b).clone() for b in "wmv"}
+    norm_d = torch.full((1,), -1.0, device="cuda")
+    coef_d = torch.full((1,), -1.0, device="cuda")
+    amp_d = amp_o = None
+    if wl.amp:
+        amp_d = AmpState(wl.amp_scale)
+        amp_o = O.AmpState(wl.amp_scale)
+    worst = {"w": 0, "m": 0, "v": 0}
+    skipped = 0
+    for t in range(1, steps + 1):
+        arena.fill_grads(t)
+        for pos, val in (inject or {}).get(t, []):
+            arena.g[pos] = val
+        for o, g in zip(ostate, oracle_grads(arena, idx)):
+            o.g = g
+        if wl.amp:
+            L.amp_clip_norm(wl.max_norm, amp_d, norm_d, coef_d)
+            found_d = amp_d.read()["found_inf"]
+            L.amp_adamw_step(wl.hparams, amp_d, coef_d)
+            amp_d.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
+        else:
+            if wl.scale != 1.0:
+                L.scale(wl.scale, defer=True)
+            if clip:
+                L.clip_norm(wl.max_norm, norm_d, coef_d)
+                L.adamw_step(wl.hparams, t, coef_d)
+            else:
+                L.adamw_step(wl.hparams, t, None)
+        torch.cuda.synchronize()
+        s = O.inv_scale(amp_o.scale) if wl.amp else wl.scale
+        coef = np.float32(1.0)
+        if clip:
+            ng = np.float32(norm_d.item())
+            coef = np.float32(coef_d.item())
+            if norm_steps is None or t in norm_steps:
+                gs = oracle_grads(arena) if idx is not None else \
+                    [o.g for o in ostate]
+                no = O.norm(gs, wl.gtype, s)
+                check_norm(ng, coef, no, wl.max_norm, f"{wl.name} t={t}")
+            else:
+                want = O.clip_coef(wl.max_norm, ng)
+                assert coef.view(np.uint32) == want.view(np.uint32)
+        if wl.amp:
+            _, _, found_o = O.amp_step_(
+                ostate, wl.gtype, wl.mkind, wl.vkind, amp_o, wl.lr,
+                wl.beta1, wl.beta2, wl.eps, wl.weight_decay, wl.max_norm,
+                coef=coef)
+            assert found_d == (1.0 if found_o else 0.0), (wl.name, t)
+            skipped += bool(found_o)
+            amp_o.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
+            check_amp_state(amp_d.read(), amp_o, f"{wl.name} t={t}")
+        else:
+            O.step_(ostate, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
+                    wl.beta2, wl.eps, wl.weight_decay, t, s=s, coef=coef)
+        got = compare(arena, ostate, idx, f"{wl.name} t={t}")
+        worst = {k: max(worst[k], got[k]) for k in worst}
+    if check_guards:
+        torch.cuda.synchronize()
+        inside = torch.zeros(arena.total, dtype=torch.bool, device="cuda")
+        for o, n in zip(arena.offsets, wl.sizes):
+            inside[o:o + n] = True
+        for b in "wmv":
+            now = getattr(arena, b)
+            ity = torch.int16 if now.dtype == torch.bfloat16 else torch.int32
+            diff = (now.view(ity) != before[b].view(ity)) & ~inside
+            assert not bool(diff.any()), f"{b} written outside its tensors"
+    L.close()
+    extra = f" amp: {skipped} skipped, state {amp_d.read()}" if wl.amp else ""
+    print(f"{wl.name}: steps={steps} worst ulp {worst}{extra}", flush=True)
+    return worst

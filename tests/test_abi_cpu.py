@@ -43,7 +43,7 @@ def _err(fn, *a):
 
 def test_create_rejects_bad_arguments_before_device_work():
     ok = (0x10000, 0x20000, 0x30000, 0x40000, 64)
-    assert _err(M.mta_list_create, [ok], 2, 0, 0) == -3            # gtype
+    assert _err(M.mta_list_create, [ok], 3, 0, 0) == -3            # gtype
     assert _err(M.mta_list_create, [ok], 0, 5, 0) == -3            # mkind
     assert _err(M.mta_list_create, [ok], 0, 0, -1) == -3           # vkind
     assert _err(M.mta_list_create, [(0x10000, 0, 0x30000, 0x40000, 64)],
@@ -54,6 +54,8 @@ def test_create_rejects_bad_arguments_before_device_work():
                                       64)], 0, 0, 0) == -2          # w align
     assert _err(M.mta_list_create, [(0x10000, 0x20001, 0x30000, 0x40000,
                                       64)], 1, 0, 0) == -2          # bf16 g
+    assert _err(M.mta_list_create, [(0x10000, 0x20001, 0x30000, 0x40000,
+                                      64)], 2, 0, 0) == -2          # f16 g
     # packed moments need only 2-byte alignment; f32 ones 4
     assert _err(M.mta_list_create, [(0x10000, 0x20000, 0x30002, 0x40000,
                                       64)], 0, 0, 0) == -2
@@ -82,7 +84,29 @@ def test_calls_on_a_null_handle_fail_cleanly():
     assert _err(M.mta_adamw_step, None, (1e-3, .9, .999, 1e-8, 0.), 1,
                 None) == -1
     assert _err(M.mta_scale, None, 0.5, M.MTA_SCALE_DEFER) == -1
+    assert _err(M.mta_amp_clip_norm, None, 1.0, 0x1000, None, 0x2000) == -1
+    assert _err(M.mta_amp_adamw_step, None, (1e-3, .9, .999, 1e-8, 0.),
+                0x1000, None) == -1
     M.mta_list_destroy(None)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 2.0, 0.5, 2000), -1),            # NULL state
+    ((0x1004, 2.0, 0.5, 2000), -2),          # state not 8-byte aligned
+    ((0x1000, 1.0, 0.5, 2000), -1),          # growth must be > 1
+    ((0x1000, float("inf"), 0.5, 2000), -1),
+    ((0x1000, 2.0, 1.0, 2000), -1),          # backoff must be < 1
+    ((0x1000, 2.0, 0.0, 2000), -1),          # and > 0
+    ((0x1000, 2.0, 0.5, 0), -1),             # interval >= 1
+])
+def test_amp_update_validation(args, code):
+    # every case fails in validation, before any device work
+    assert _err(M.mta_amp_update, *args) == code
+
+
+def test_amp_state_layout():
+    assert ctypes.sizeof(B.mta_amp_state) == 24
+    assert B.mta_amp_state.step.offset == 16
 
 
 @pytest.mark.parametrize("hp,t", [

@@ -5,7 +5,6 @@ in place), mta_clip_norm, mta_adamw_step -- and compares with the oracle
 element by element (lockstep protocol, see parity_util).  Small lists are
 compared in full; full-size lists at sampled positions plus the full norm.
 """
-import os
 
 import numpy as np
 import pytest
@@ -16,8 +15,8 @@ from mixed_precision_optimizer_mta_amd import workloads as WL
 
 pytestmark = pytest.mark.gpu
 
-from parity_util import (check_norm, compare, oracle_grads,  # noqa: E402
-                         oracle_state, sample_positions)
+from parity_util import (check_norm, compare, lockstep,  # noqa: E402
+                         make_list, oracle_grads, oracle_state)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -29,80 +28,12 @@ def _device():
     torch.cuda.synchronize()
 
 
-def make_list(arena):
-    from mixed_precision_optimizer_mta_amd import MtaList
-    wl = arena.wl
-    return MtaList([], entries=arena.entries(), gtype=wl.gtype,
-                   mkind=wl.mkind, vkind=wl.vkind)
-
-
-def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
-             check_guards=False, clip=True):
-    """Run `steps` device steps in lockstep with the oracle; returns the
-    worst ulp distances seen."""
-    arena = WL.Arena(wl, "cuda", offsets)
-    arena.fill_weights()
-    L = make_list(arena)
-    idx = None
-    if nsample is not None:
-        idx = sample_positions(wl, arena.offsets, nsample)
-    ostate = oracle_state(arena, idx)
-    before = None
-    if check_guards:
-        before = {b: getattr(arena, b).clone() for b in "wmv"}
-    norm_d = torch.full((1,), -1.0, device="cuda")
-    coef_d = torch.full((1,), -1.0, device="cuda")
-    worst = {"w": 0, "m": 0, "v": 0}
-    for t in range(1, steps + 1):
-        arena.fill_grads(t)
-        for o, g in zip(ostate, oracle_grads(arena, idx)):
-            o.g = g
-        if wl.scale != 1.0:
-            L.scale(wl.scale, defer=True)
-        if clip:
-            L.clip_norm(wl.max_norm, norm_d, coef_d)
-            L.adamw_step(wl.hparams, t, coef_d)
-        else:
-            L.adamw_step(wl.hparams, t, None)
-        torch.cuda.synchronize()
-        coef = np.float32(1.0)
-        if clip:
-            ng = np.float32(norm_d.item())
-            coef = np.float32(coef_d.item())
-            if norm_steps is None or t in norm_steps:
-                gs = oracle_grads(arena) if idx is not None else \
-                    [o.g for o in ostate]
-                no = O.norm(gs, wl.gtype, wl.scale)
-                check_norm(ng, coef, no, wl.max_norm, f"{wl.name} t={t}")
-            else:
-                want = O.clip_coef(wl.max_norm, ng)
-                assert coef.view(np.uint32) == want.view(np.uint32)
-        O.step_(ostate, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
-                wl.beta2, wl.eps, wl.weight_decay, t, s=wl.scale, coef=coef)
-        got = compare(arena, ostate, idx, f"{wl.name} t={t}")
-        worst = {k: max(worst[k], got[k]) for k in worst}
-    if check_guards:
-        torch.cuda.synchronize()
-        inside = torch.zeros(arena.total, dtype=torch.bool, device="cuda")
-        for o, n in zip(arena.offsets, wl.sizes):
-            inside[o:o + n] = True
-        for b in "wmv":
-            now = getattr(arena, b)
-            diff = (now.view(torch.int16 if now.dtype == torch.bfloat16
-                             else torch.int32) !=
-                    before[b].view(torch.int16 if now.dtype == torch.bfloat16
-                                   else torch.int32)) & ~inside
-            assert not bool(diff.any()), f"{b} written outside its tensors"
-    L.close()
-    print(f"{wl.name}: steps={steps} worst ulp {worst}", flush=True)
-    return worst
-
-
 # ---------------------------------------------------------------- small lists
 
 SMALL = {
     "gpt2_124m": WL.gpt2_sizes(1000, 64, 128, 2, 256),
     "gpt2_124m_bf16g": WL.gpt2_sizes(1000, 64, 128, 2, 256),
+    "gpt2_124m_f16amp": WL.gpt2_sizes(1000, 64, 128, 2, 256),
     "gpt2_xl": WL.gpt2_sizes(1000, 96, 64, 3, 384),
 }
 
@@ -131,7 +62,7 @@ def test_small_lists_lockstep(name):
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
-ALL_KINDS = [(g, m, v) for g in (0, 1) for m in (0, 1) for v in (0, 1)]
+ALL_KINDS = [(g, m, v) for g in (0, 1, 2) for m in (0, 1) for v in (0, 1)]
 
 
 @pytest.mark.parametrize("gtype,mkind,vkind", ALL_KINDS)
@@ -145,7 +76,7 @@ def test_edge_sizes_every_kind(gtype, mkind, vkind):
 
 
 @pytest.mark.parametrize("gtype,mkind,vkind", [(0, 0, 0), (1, 1, 0),
-                                               (1, 1, 1)])
+                                               (1, 1, 1), (2, 0, 1)])
 def test_unaligned_tensors_take_the_element_path(gtype, mkind, vkind):
     # element offsets of 1 (mod 8) break 16-byte alignment of every buffer
     sizes = [5000, 4096, 33, 9000]
@@ -232,7 +163,7 @@ def test_deferred_scale_equals_in_place_for_f32():
     assert torch.equal(w1, w2) and torch.equal(m1, m2) and torch.equal(v1, v2)
 
 
-@pytest.mark.parametrize("gtype", [0, 1])
+@pytest.mark.parametrize("gtype", [0, 1, 2])
 def test_in_place_scale_matches_oracle(gtype):
     sizes = [1, 4096 * 3, 4097, 77]
     wl = WL.Workload("scale", sizes, gtype, 0, 0, steps=1, g_sigma=50.0,

@@ -11,6 +11,8 @@ def test_parameter_counts():
     c2 = WL.get("gpt2_124m")
     assert c2.n == 124_419_840 and c2.count == 110
     assert WL.get("gpt2_124m_bf16g").n == c2.n
+    amp = WL.get("gpt2_124m_f16amp")
+    assert amp.n == c2.n and amp.gtype == WL.F16 and amp.amp
     c4 = WL.get("gpt2_xl")
     assert c4.n == 1_557_454_400 and c4.count == 434
     assert all(n % 2 == 0 for n in c4.sizes)
@@ -27,6 +29,8 @@ def test_bytes_per_param():
     assert WL.get("gpt2_124m").bytes_per_param() == {"norm": 4, "update": 28}
     assert WL.get("gpt2_124m_bf16g").bytes_per_param() == {"norm": 2,
                                                           "update": 26}
+    assert WL.get("gpt2_124m_f16amp").bytes_per_param() == {"norm": 2,
+                                                           "update": 26}
     assert WL.get("gpt2_xl").bytes_per_param() == {"norm": 4, "update": 20}
     assert WL.get("ragged").bytes_per_param() == {"norm": 2, "update": 22}
 
@@ -41,3 +45,11 @@ def test_seeded_inputs_reproduce_on_cpu():
     assert not bool(a.view("g", 1).any())
     assert bool(a.view("g", 2).any())
     assert all(o % WL.ALIGN_ELEMS == 0 for o in a.offsets)
+
+
+def test_float16_gradients_are_torch_conversions():
+    wl = WL.scaled_down(WL.get("gpt2_124m_f16amp"), [1000, 37])
+    a = WL.Arena(wl, "cpu")
+    a.fill_grads(2)
+    assert a.g.dtype == torch.float16
+    assert bool(torch.isfinite(a.g).all()) and float(a.g.abs().max()) > 100
