@@ -69,6 +69,17 @@ def lib():
                                        ctypes.c_int, vp, ctypes.c_int, f32,
                                        f32, vp]
         L.mto_adamw_tensor.restype = None
+        L.mto_adam_tensor.argtypes = [i64, vp, vp, ctypes.c_int, vp,
+                                      ctypes.c_int, vp, ctypes.c_int, f32,
+                                      f32, vp, ctypes.c_int, f32,
+                                      ctypes.c_int]
+        L.mto_adam_tensor.restype = None
+        L.mto_sgd_tensor.argtypes = [i64, vp, vp, ctypes.c_int, f32, f32,
+                                     f32, ctypes.c_int]
+        L.mto_sgd_tensor.restype = None
+        L.mto_momentum_tensor.argtypes = [i64, vp, vp, ctypes.c_int, vp, f32,
+                                          f32, f32, f32, ctypes.c_int]
+        L.mto_momentum_tensor.restype = None
         L.mto_weight_copy.argtypes = [i64, vp, vp]
         L.mto_weight_copy.restype = None
         L.mto_f32_of_f16.argtypes = [ctypes.c_uint32]
@@ -221,6 +232,49 @@ def adamw_(w, g, m, v, gtype, mkind, vkind, sc, s=1.0, coef=1.0):
                            _ptr(sc, np.float32))
 
 
+def adam_(w, g, m, v, gtype, mkind, vkind, sc, s=1.0, coef=1.0,
+          coupled=False, l2=0.0, zero=False):
+    """One Adam-family step over one tensor, in place on w, m, v (and g when
+    ``zero``).  coupled=False is AdamW (decay factor sc[6]); coupled=True is
+    Adam with g' = g + f32(w * l2) and no decay of w."""
+    n = w.size
+    if g.size != n:
+        raise ValueError("gradient size differs from the weight's")
+    for buf, kind in ((m, mkind), (v, vkind)):
+        want = packed_words(n) if kind == MOM_BF16X2 else n
+        if buf.size != want:
+            raise ValueError("moment buffer has the wrong size")
+    sc = np.ascontiguousarray(sc, dtype=np.float32)
+    lib().mto_adam_tensor(n, _ptr(w, np.float32), _ptr(g, _grad_dtype(gtype)),
+                          gtype, _ptr(m, _mom_dtype(mkind)), mkind,
+                          _ptr(v, _mom_dtype(vkind)), vkind,
+                          float(np.float32(s)), float(np.float32(coef)),
+                          _ptr(sc, np.float32), int(bool(coupled)),
+                          float(np.float32(l2)), int(bool(zero)))
+
+
+def sgd_(w, g, gtype, lr, s=1.0, coef=1.0, zero=False):
+    """SGD over one tensor: w <- w + (-lr) * f32(f32(g*s)*coef)."""
+    if g.size != w.size:
+        raise ValueError("gradient size differs from the weight's")
+    lib().mto_sgd_tensor(w.size, _ptr(w, np.float32),
+                         _ptr(g, _grad_dtype(gtype)), gtype,
+                         float(np.float32(s)), float(np.float32(coef)),
+                         float(np.float32(lr)), int(bool(zero)))
+
+
+def momentum_(w, g, buf, gtype, lr, mu, s=1.0, coef=1.0, zero=False):
+    """SGD with momentum over one tensor: buf <- buf*mu + g';
+    w <- w + (-lr)*buf (float32 buffer)."""
+    if g.size != w.size or buf.size != w.size:
+        raise ValueError("buffer sizes differ from the weight's")
+    lib().mto_momentum_tensor(w.size, _ptr(w, np.float32),
+                              _ptr(g, _grad_dtype(gtype)), gtype,
+                              _ptr(buf, np.float32), float(np.float32(s)),
+                              float(np.float32(coef)), float(np.float32(lr)),
+                              float(np.float32(mu)), int(bool(zero)))
+
+
 def weight_copy(w, out):
     """bfloat16 copy of float32 weights (nearest-even, NaN -> 0xFFFF)."""
     if out.size != w.size:
@@ -346,4 +400,76 @@ def amp_step_(tensors, gtype, mkind, vkind, amp, lr, beta1, beta2, eps,
             adamw_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c)
             if getattr(x, "w16", None) is not None:
                 weight_copy(x.w, x.w16)
+    return nrm, c, found
+
+
+# ---------------------------------------------------------------- optimizers
+
+OPT_KINDS = ("adamw", "adam", "sgd", "momentum")
+
+
+def _apply_opt(x, opt, gtype, mkind, vkind, sc, s, c, zero):
+    kind = opt["kind"]
+    if kind in ("adamw", "adam"):
+        adam_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c,
+              coupled=(kind == "adam"), l2=opt["weight_decay"], zero=zero)
+    elif kind == "sgd":
+        sgd_(x.w, x.g, gtype, opt["lr"], s, c, zero)
+    elif kind == "momentum":
+        momentum_(x.w, x.g, x.m, gtype, opt["lr"], opt["momentum"], s, c,
+                  zero)
+    else:
+        raise ValueError(f"unknown optimizer {kind!r}")
+    if getattr(x, "w16", None) is not None:
+        weight_copy(x.w, x.w16)
+
+
+def opt_step_(tensors, opt, gtype, mkind, vkind, t, s=1.0, max_norm=None,
+              coef=None, zero=False):
+    """The whole step over a tensor list for any optimizer of the
+    Optimizers section ("BendTorch main.bend"): opt is a dict with kind
+    ("adamw", "adam", "sgd", "momentum"), lr, beta1, beta2, eps,
+    weight_decay, momentum.  Unscale by s, clip by the joint norm when
+    max_norm is given (coef overrides the coefficient), update every group,
+    zero the gradients when asked.  Returns (norm_f64, coef_f32)."""
+    nrm = None
+    c = np.float32(1.0)
+    if max_norm is not None:
+        nrm = norm([x.g for x in tensors], gtype, s)
+        c = clip_coef(max_norm, np.float32(nrm))
+    if coef is not None:
+        c = np.float32(coef)
+    sc = None
+    if opt["kind"] in ("adamw", "adam"):
+        sc = scalars(opt["lr"], opt["beta1"], opt["beta2"], opt["eps"],
+                     opt["weight_decay"], t)
+    for x in tensors:
+        _apply_opt(x, opt, gtype, mkind, vkind, sc, s, c, zero)
+    return nrm, c
+
+
+def amp_opt_step_(tensors, opt, gtype, mkind, vkind, amp, max_norm,
+                  coef=None, zero=False):
+    """opt_step_ under a loss-scale state: unscale by 1/S; when the norm is
+    not finite the update is skipped (the gradients are still zeroed when
+    asked); otherwise Adam-family constants come from t = amp.step + 1 with
+    the correctly rounded power.  Does not call amp.update().  Returns
+    (norm, coef, found_inf)."""
+    s = inv_scale(amp.scale)
+    nrm = norm([x.g for x in tensors], gtype, s)
+    found = not math.isfinite(nrm)
+    c = clip_coef(max_norm, np.float32(nrm)) if coef is None else \
+        np.float32(coef)
+    amp.found_inf = np.float32(1.0 if found else 0.0)
+    if found:
+        if zero:
+            for x in tensors:
+                x.g[...] = 0
+        return nrm, c, found
+    sc = None
+    if opt["kind"] in ("adamw", "adam"):
+        sc = scalars_rn(opt["lr"], opt["beta1"], opt["beta2"], opt["eps"],
+                        opt["weight_decay"], amp.step + 1)
+    for x in tensors:
+        _apply_opt(x, opt, gtype, mkind, vkind, sc, s, c, zero)
     return nrm, c, found

@@ -35,7 +35,9 @@
  *     Neumaier compensation (effectively exact); the caller rounds it once.
  *   - Unscale and clip act in float32 registers: x = f32(g * s), then
  *     ge = f32(x * coef); gradients are not rewritten by the step.
- *   - The step does not zero the gradient (PyTorch's step does not).
+ *   - The step does not zero the gradient unless asked to (PyTorch's step
+ *     does not; every step loop of BendTorch's Optimizers section does, so
+ *     zeroing is an option of the step).
  */
 #include <math.h>
 #include <stdint.h>
@@ -246,16 +248,39 @@ float mto_clip_coef(float max_norm, float norm) {
 /* stored, rounded value.  The gradient is read, never written.            */
 /* ---------------------------------------------------------------------- */
 
-void mto_adamw_tensor(int64_t n, float *w, const void *g, int gtype, void *m,
-                      int mkind, void *v, int vkind, float s, float coef,
-                      const float sc[7]) {
+/* gradient element k set to +0 (every step loop of BendTorch's Optimizers
+   section writes 0.0 into the gradient after reading it) */
+static void grad_zero(void *g, int gtype, int64_t k) {
+  if (gtype == MTO_F32)
+    ((float *)g)[k] = 0.0f;
+  else
+    ((uint16_t *)g)[k] = 0; /* +0 in bfloat16 and in float16 */
+}
+
+/* The Adam family (BendTorch: adam_grad, adam_decay, adam_m, adam_v,
+   adam_w; the comment on the Opt type: `dec` picks AdamW's decoupled decay,
+   w *= 1 - lr*wd, over Adam's g += wd*w).
+   coupled = 0 (AdamW): the gradient is used as it is and w is decayed by
+   sc[6].  coupled = 1 (Adam): g' = ge + f32(w * l2) feeds both moments and w
+   is not decayed (sc[6] is not read).  zero != 0: the gradient element is
+   set to +0 after it is read. */
+void mto_adam_tensor(int64_t n, float *w, void *g, int gtype, void *m,
+                     int mkind, void *v, int vkind, float s, float coef,
+                     const float sc[7], int coupled, float l2, int zero) {
   const float step = sc[0], bc2 = sc[1], c1 = sc[2], c2 = sc[3];
   const float b2 = sc[4], eps = sc[5], dec = sc[6];
   for (int64_t k = 0; k < n; ++k) {
     float x = grad_at(g, gtype, k) * s; /* unscale */
     float ge = x * coef;                /* clip    */
+    if (zero) grad_zero(g, gtype, k);
 
-    float wd = w[k] * dec; /* adam_decay (AdamW) */
+    float wd;
+    if (coupled) {
+      ge = ge + (w[k] * l2); /* adam_grad (Adam) */
+      wd = w[k];             /* adam_decay (Adam): no decay */
+    } else {
+      wd = w[k] * dec;       /* adam_decay (AdamW) */
+    }
 
     float m0 = (mkind == MTO_MOM_BF16X2)
                    ? mto_f32_of_bf16(packed_get((const uint32_t *)m, k))
@@ -284,6 +309,49 @@ void mto_adamw_tensor(int64_t n, float *w, const void *g, int gtype, void *m,
 
     float denom = (sqrtf(v1) / bc2) + eps; /* adam_w */
     w[k] = wd + ((-step * m1) / denom);
+  }
+}
+
+/* AdamW with the gradient only read (the hot path's own form) */
+void mto_adamw_tensor(int64_t n, float *w, const void *g, int gtype, void *m,
+                      int mkind, void *v, int vkind, float s, float coef,
+                      const float sc[7]) {
+  mto_adam_tensor(n, w, (void *)g, gtype, m, mkind, v, vkind, s, coef, sc, 0,
+                  0.0f, 0);
+}
+
+/* ---------------------------------------------------------------------- */
+/* SGD (BendTorch sgd_l: w <- w + (-lr)*g, as PyTorch's p.add_(g,         */
+/* alpha=-lr)) on the unscaled, clipped gradient; lr is the float32 value. */
+/* ---------------------------------------------------------------------- */
+
+void mto_sgd_tensor(int64_t n, float *w, void *g, int gtype, float s,
+                    float coef, float lr, int zero) {
+  const float nlr = -lr;
+  for (int64_t k = 0; k < n; ++k) {
+    float x = grad_at(g, gtype, k) * s;
+    float ge = x * coef;
+    if (zero) grad_zero(g, gtype, k);
+    w[k] = w[k] + (nlr * ge);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* SGD with momentum (BendTorch mom_l: buf <- buf*mu + g; w <- w +        */
+/* (-lr)*buf, as PyTorch's SGD with momentum, no dampening, not Nesterov; */
+/* the buffer starts at zero).  buf is float32.                            */
+/* ---------------------------------------------------------------------- */
+
+void mto_momentum_tensor(int64_t n, float *w, void *g, int gtype, float *buf,
+                         float s, float coef, float lr, float mu, int zero) {
+  const float nlr = -lr;
+  for (int64_t k = 0; k < n; ++k) {
+    float x = grad_at(g, gtype, k) * s;
+    float ge = x * coef;
+    if (zero) grad_zero(g, gtype, k);
+    float nb = (buf[k] * mu) + ge;
+    buf[k] = nb;
+    w[k] = w[k] + (nlr * nb);
   }
 }
 

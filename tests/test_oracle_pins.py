@@ -701,3 +701,220 @@ def test_amp_step_skips_on_non_finite_and_matches_plain_step_otherwise():
     nrm, c, found = O.amp_step_([a], O.F16, 0, 0, amp, 3e-4, 0.9, 0.999,
                                 1e-8, 0.1, 1.0)
     assert found and amp.found_inf == 1.0 and np.array_equal(a.w, w0)
+
+
+# ---------------------------------------------------------------------------
+# the other optimizers of "BendTorch main.bend", Optimizers: Adam with
+# coupled decay (adam_grad / adam_decay with dec = False), SGD (sgd_l),
+# momentum SGD (mom_l), and the zeroed gradient every step loop leaves
+# ---------------------------------------------------------------------------
+
+def test_sgd_exact_dyadic_step():
+    # every product and sum below is exact in float32
+    w = np.array([1.0, -2.0, 0.75, 0.0], np.float32)
+    g = np.array([0.5, 0.25, -1.0, 3.0], np.float32)
+    O.sgd_(w, g, O.F32, lr=0.5, s=0.5, coef=0.5)      # g' = g / 4
+    assert w.tolist() == [1.0 - 0.0625, -2.0 - 0.03125, 0.75 + 0.125,
+                          -0.375]
+    assert g.tolist() == [0.5, 0.25, -1.0, 3.0]          # read only
+
+
+def test_sgd_against_torch_cpu():
+    rng = np.random.default_rng(31)
+    n, lr = 4096, 0.01
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(w.copy()))
+    opt = torch.optim.SGD([p], lr=lr, foreach=False)
+    for _ in range(10):
+        g = rng.normal(0, 1e-2, n).astype(np.float32)
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        w_prev = w.copy()
+        O.sgd_(w, g, O.F32, lr)
+        # torch's add with alpha may fuse the multiply: the two differ by
+        # the product's rounding, an ulp of the larger term at most
+        scale = np.maximum(np.abs(w_prev), np.abs(np.float32(lr) * g))
+        scale = np.maximum(scale, np.abs(w))       # the result's binade
+        assert np.all(np.abs(w - p.detach().numpy()) <= np.spacing(scale))
+        p.data.copy_(torch.from_numpy(w))          # restart from ours
+
+
+def test_momentum_geometric_series_is_exact():
+    # constant g = 1, mu = 1/2: buf_t = 2 (1 - 2^-t) and
+    # w_t = w0 - lr * sum_k buf_k, all exact dyadic numbers here
+    w = np.array([8.0], np.float32)
+    buf = np.zeros(1, np.float32)
+    g = np.ones(1, np.float32)
+    lr, mu = 0.25, 0.5
+    total = Fraction(0)
+    for t in range(1, 21):
+        O.momentum_(w, g, buf, O.F32, lr, mu)
+        bt = 2 * (1 - Fraction(1, 2 ** t))
+        total += bt
+        assert Fraction(float(buf[0])) == bt, t
+        assert Fraction(float(w[0])) == 8 - Fraction(1, 4) * total, t
+
+
+def test_momentum_against_torch_cpu():
+    rng = np.random.default_rng(32)
+    n, lr, mu = 4096, 0.01, 0.9
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    buf = np.zeros(n, np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(w.copy()))
+    opt = torch.optim.SGD([p], lr=lr, momentum=mu, foreach=False)
+    for t in range(10):
+        g = rng.normal(0, 1e-2, n).astype(np.float32)
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        w_prev, b_prev = w.copy(), buf.copy()
+        O.momentum_(w, g, buf, O.F32, lr, mu)
+        tb = opt.state[p]["momentum_buffer"].numpy()
+        # torch's first step clones g (ours: 0*mu + g, the same value); the
+        # later ones are buf*mu + g, as here, where an FMA would differ by
+        # the product's rounding; the weight update likewise
+        bscale = np.maximum(np.abs(b_prev * np.float32(mu)), np.abs(g))
+        bscale = np.maximum(bscale, np.abs(buf))
+        assert np.all(np.abs(buf - tb) <= np.spacing(bscale))
+        scale = np.maximum(np.abs(w_prev), np.abs(np.float32(lr) * buf))
+        scale = np.maximum(scale, np.abs(w))
+        assert np.all(np.abs(w - p.detach().numpy()) <= np.spacing(scale))
+        p.data.copy_(torch.from_numpy(w))
+        opt.state[p]["momentum_buffer"].copy_(torch.from_numpy(buf))
+
+
+def _adam_scalars(t, lr=3e-4, b1=0.9, b2=0.999, eps=1e-8, wd=0.1):
+    return O.scalars(lr, b1, b2, eps, wd, t)
+
+
+def test_adam_coupled_decay_first_step_direction():
+    # Adam's decay enters the gradient: g' = g + wd*w.  With w = 1,
+    # g = -0.1, wd = 0.5 the step follows g' = 0.4 and moves w DOWN by about
+    # lr; AdamW would move it up (g < 0) and decay it separately.
+    lr, wd = 1e-2, 0.5
+    sc = O.scalars(lr, 0.9, 0.999, 1e-8, wd, 1)
+    w = np.array([1.0], np.float32)
+    g = np.array([-0.1], np.float32)
+    m = np.zeros(1, np.float32)
+    v = np.zeros(1, np.float32)
+    O.adam_(w, g, m, v, O.F32, 0, 0, sc, coupled=True, l2=wd)
+    # first step from zero moments: w1 = w - lr * g'/(|g'| + eps), no decay
+    gp = -0.1 + 0.5
+    assert abs(float(w[0]) - (1.0 - lr * gp / (abs(gp) + 1e-8))) < 4e-7
+    assert abs(float(m[0]) - 0.1 * gp) < 1e-7
+    assert abs(float(v[0]) - 0.001 * gp * gp) < 1e-9
+    ww = np.array([1.0], np.float32)
+    O.adamw_(ww, g, np.zeros(1, np.float32), np.zeros(1, np.float32), O.F32,
+             0, 0, sc)
+    assert ww[0] > 1.0 - lr * wd and w[0] < 1.0 - 0.9 * lr
+
+
+def test_adam_with_zero_decay_equals_adamw_with_zero_decay():
+    rng = np.random.default_rng(33)
+    n = 3000
+    for t in (1, 2, 7):
+        w = rng.normal(0, 0.02, n).astype(np.float32)
+        g = rng.normal(0, 1e-3, n).astype(np.float32)
+        m = rng.normal(0, 1e-3, n).astype(np.float32)
+        v = np.abs(rng.normal(0, 1e-6, n)).astype(np.float32)
+        a = [x.copy() for x in (w, g, m, v)]
+        b = [x.copy() for x in (w, g, m, v)]
+        sc = O.scalars(3e-4, 0.9, 0.999, 1e-8, 0.0, t)
+        O.adam_(*a, O.F32, 0, 0, sc, coupled=True, l2=0.0)
+        O.adamw_(*b, O.F32, 0, 0, sc)
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_adam_against_torch_cpu():
+    rng = np.random.default_rng(34)
+    n, steps = 4096, 10
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.999, 1e-8, 0.1
+    w0 = rng.normal(0, 0.02, n).astype(np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.Adam([p], lr=lr, betas=(b1, b2), eps=eps,
+                           weight_decay=wd, foreach=False, fused=False)
+    w = w0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    for t in range(1, steps + 1):
+        g = rng.normal(0, 1e-2, n).astype(np.float32)
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        O.adam_(w, g, m, v, O.F32, 0, 0, O.scalars(lr, b1, b2, eps, wd, t),
+                coupled=True, l2=wd)
+    st = opt.state[p]
+    u = 2.0 ** -24
+    wscale = np.abs(w0) + steps * lr
+    assert np.all(np.abs(w - p.detach().numpy()) <=
+                  steps * (np.spacing(wscale) + 4 * u * lr))
+    assert np.all(np.abs(m - st["exp_avg"].numpy()) <=
+                  steps * 2 * u * (np.abs(st["exp_avg"].numpy()) + 1e-2))
+    assert ulp_dist(v, st["exp_avg_sq"].numpy()).max() <= 4
+
+
+@pytest.mark.parametrize("gtype", [O.F32, O.BF16, O.F16])
+@pytest.mark.parametrize("kind", O.OPT_KINDS)
+def test_zeroing_writes_plus_zero_and_changes_nothing_else(kind, gtype):
+    rng = np.random.default_rng(35)
+    n = 1001
+    opt = dict(kind=kind, lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8,
+               weight_decay=0.1 if kind.startswith("adam") else 0.0,
+               momentum=0.9)
+
+    def mk():
+        r = np.random.default_rng(36)
+        g = r.normal(0, 1e-2, n).astype(np.float32)
+        g[::7] = -0.0
+        if gtype == O.BF16:
+            g = O.bf16_of_f32(g)
+        elif gtype == O.F16:
+            g = O.f16_of_f32(g)
+        m = r.normal(0, 1e-3, n).astype(np.float32)
+        v = np.abs(r.normal(0, 1e-5, n)).astype(np.float32)
+        return O.Tensor(r.normal(0, .02, n).astype(np.float32), g, m, v)
+
+    a, b = mk(), mk()
+    O.opt_step_([a], opt, gtype, 0, 0, 3, s=0.5, max_norm=1.0, zero=False)
+    O.opt_step_([b], opt, gtype, 0, 0, 3, s=0.5, max_norm=1.0, zero=True)
+    assert not np.any(b.g.view(np.uint16 if gtype else np.uint32))
+    for x, y in ((a.w, b.w), (a.m, b.m), (a.v, b.v)):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert rng is not None
+
+
+@pytest.mark.parametrize("kind", O.OPT_KINDS)
+def test_amp_opt_step_skip_zeroes_only_the_gradient(kind):
+    n = 500
+    r = np.random.default_rng(37)
+    g = O.f16_of_f32((r.normal(0, 1e-3, n) * 1024).astype(np.float32))
+    g[3] = 0x7C00                                       # +Inf
+    x = O.Tensor(r.normal(0, .02, n).astype(np.float32), g,
+                 r.normal(0, 1e-3, n).astype(np.float32),
+                 np.abs(r.normal(0, 1e-5, n)).astype(np.float32))
+    before = [x.w.copy(), x.m.copy(), x.v.copy()]
+    amp = O.AmpState(1024.0, step=9)
+    opt = dict(kind=kind, lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8,
+               weight_decay=0.0, momentum=0.9)
+    nrm, c, found = O.amp_opt_step_([x], opt, O.F16, 0, 0, amp, 1.0,
+                                    zero=True)
+    assert found and amp.found_inf == 1.0 and not np.any(x.g)
+    for a, b in zip(before, (x.w, x.m, x.v)):
+        assert np.array_equal(a, b)
+
+
+def test_amp_opt_step_equals_plain_step_at_the_next_t():
+    n = 700
+    r = np.random.default_rng(38)
+    g = O.f16_of_f32((r.normal(0, 1e-3, n) * 256).astype(np.float32))
+    for kind in O.OPT_KINDS:
+        opt = dict(kind=kind, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                   weight_decay=0.05 if kind.startswith("adam") else 0.0,
+                   momentum=0.5)
+        mk = lambda: O.Tensor(np.full(n, 0.01, np.float32), g.copy(),
+                              np.full(n, 1e-4, np.float32),
+                              np.full(n, 1e-8, np.float32))
+        a, b = mk(), mk()
+        amp = O.AmpState(256.0, step=4)
+        O.amp_opt_step_([a], opt, O.F16, 0, 0, amp, 1.0)
+        O.opt_step_([b], opt, O.F16, 0, 0, 5, s=1.0 / 256, max_norm=1.0)
+        assert np.array_equal(a.w, b.w) and np.array_equal(a.m, b.m), kind
