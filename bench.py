@@ -45,9 +45,34 @@ def measured_traffic(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(arena, wl, steps):
+KERNEL_OF = {"adamw": "k_adamw", "adam": "k_adamw", "sgd": "k_sgd",
+             "momentum": "k_momentum"}
+
+
+def opt_of(wl, kind, zero):
+    """The update rule's configuration for a workload (SGD and momentum take
+    the workload's lr, no weight decay, momentum 0.9)."""
+    adam = kind in ("adamw", "adam")
+    return dict(kind=kind, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
+                eps=wl.eps, weight_decay=wl.weight_decay if adam else 0.0,
+                momentum=0.9, zero_grad=zero)
+
+
+def update_bytes(wl, kind, zero, copy):
+    """Algorithmic HBM bytes per parameter of one update launch."""
+    gb = 4 if wl.gtype == 0 else 2
+    mb = 2 if wl.mkind == 1 else 4
+    vb = 2 if wl.vkind == 1 else 4
+    b = {"adamw": wl.bytes_per_param()["update"],
+         "adam": wl.bytes_per_param()["update"],
+         "sgd": 4 + gb + 4,                       # read w, g; write w
+         "momentum": 4 + gb + mb + 4 + mb}[kind]  # + read/write buf
+    return b + (gb if zero else 0) + (2 if copy else 0)
+
+
+def cpu_baseline(arena, wl, steps, opt=None):
     """The oracle as it stands (single thread) on host copies of the same
-    list: `steps` whole steps (norm + AdamW)."""
+    list: `steps` whole steps (norm + update)."""
     import numpy as np
     import torch
 
@@ -69,9 +94,19 @@ def cpu_baseline(arena, wl, steps):
                            O.pack_halves(v) if wl.vkind == 1 else v))
     O.lib()
     amp = O.AmpState(wl.amp_scale) if wl.amp else None
+    general = opt is not None and (opt["kind"] != "adamw" or
+                                   opt["zero_grad"])
+    zero = bool(opt and opt["zero_grad"])
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
-        if amp is not None:
+        if general and amp is not None:
+            O.amp_opt_step_(ts, opt, wl.gtype, wl.mkind, wl.vkind, amp,
+                            wl.max_norm, zero=zero)
+            amp.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
+        elif general:
+            O.opt_step_(ts, opt, wl.gtype, wl.mkind, wl.vkind, t,
+                        s=wl.scale, max_norm=wl.max_norm, zero=zero)
+        elif amp is not None:
             O.amp_step_(ts, wl.gtype, wl.mkind, wl.vkind, amp, wl.lr,
                         wl.beta1, wl.beta2, wl.eps, wl.weight_decay,
                         wl.max_norm)
@@ -83,7 +118,8 @@ def cpu_baseline(arena, wl, steps):
     dt = time.perf_counter() - t0
     return {"value": wl.n * steps / dt, "unit": "params/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{steps} whole steps (joint norm + clip + AdamW"
+            "sample": f"{steps} whole steps (joint norm + clip + "
+                      f"{opt['kind'] if opt else 'adamw'} update"
                       f"{' + loss-scale update' if amp else ''}) of "
                       f"the full {wl.n:,}-param list, one host thread, "
                       f"{dt:.2f} s"}
@@ -100,6 +136,11 @@ def main():
     ap.add_argument("--weight-copy", action="store_true",
                     help="also write a bfloat16 copy of every updated weight "
                          "(mta_list_set_weight_copies): +2 B/param")
+    ap.add_argument("--opt", default="adamw",
+                    choices=["adamw", "adam", "sgd", "momentum"],
+                    help="update rule (mta_step); adamw runs mta_adamw_step")
+    ap.add_argument("--zero-grad", action="store_true",
+                    help="also zero every gradient in the update launch")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB, 5 times: "
                          "the known-size kernel that scales the HBM byte "
@@ -135,7 +176,12 @@ def main():
     arena = WL.Arena(wl, "cuda")
     arena.fill_weights()
     arena.fill_grads(1)
-    L = M.MtaList([], entries=arena.entries(), gtype=wl.gtype, mkind=wl.mkind,
+    opt = opt_of(wl, args.opt, args.zero_grad)
+    general = args.opt != "adamw" or args.zero_grad
+    has_m, has_v = args.opt != "sgd", args.opt in ("adamw", "adam")
+    ents = [(w, g, m if has_m else None, v if has_v else None, n)
+            for (w, g, m, v, n) in arena.entries()]
+    L = M.MtaList([], entries=ents, gtype=wl.gtype, mkind=wl.mkind,
                   vkind=wl.vkind)
     copies = None
     if args.weight_copy:
@@ -161,13 +207,17 @@ def main():
             L.clip_norm(wl.max_norm, norm_d, coef_d)
         if ev is not None:
             ev[1].record(stream)
-        if amp is not None:
+        if general and amp is not None:
+            L.amp_step(opt, amp, coef_d)
+        elif general:
+            L.step(opt, t, coef_d)
+        elif amp is not None:
             L.amp_adamw_step(hp, amp, coef_d)
         else:
             L.adamw_step(hp, t, coef_d)
         if ev is not None:
             ev[2].record(stream)
-        if amp is not None:      # one thread; not part of k_adamw's time
+        if amp is not None:      # one thread; not part of the update's time
             amp.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
 
     t = 0
@@ -198,16 +248,17 @@ def main():
         st = amp.read()
         assert st["step"] == t and st["found_inf"] == 0.0, st
 
-    bpp = wl.bytes_per_param()
-    if args.weight_copy:
-        bpp["update"] += 2
+    bpp = {"norm": wl.bytes_per_param()["norm"],
+           "update": update_bytes(wl, args.opt, args.zero_grad,
+                                  args.weight_copy)}
+    kernel = KERNEL_OF[args.opt]
     step_bytes = wl.n * (bpp["norm"] + bpp["update"])
     adamw_bytes = wl.n * bpp["update"]
     norm_bytes = wl.n * bpp["norm"]
     value = wl.n * args.steps / (host_s)
     achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
-    traffic = (None if args.weight_copy
-               else measured_traffic(wl.name, "k_adamw"))
+    traffic = (None if args.weight_copy or general
+               else measured_traffic(wl.name, kernel))
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) per "
                   "fused clip+AdamW step",
@@ -231,15 +282,16 @@ def main():
             "tiles": info["tiles"], "grid_update": info["grid_update"],
             "grid_norm": info["grid_norm"], "parallelism": "single GPU",
             "weight_copy": bool(args.weight_copy),
+            "optimizer": args.opt, "zero_grad": bool(args.zero_grad),
         },
         "step_gbs": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9,
         "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9
         / HBM_PEAK_GBS,
         "device_ms_per_step": ms_per_step,
-        "kernels_ms": {"k_sumsq": norm_ms, "k_adamw": adamw_ms},
+        "kernels_ms": {"k_sumsq": norm_ms, kernel: adamw_ms},
         "norm_gbs": norm_bytes / (norm_ms * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "k_adamw", "bound": "hbm", "achieved": achieved,
+            "kernel": kernel, "bound": "hbm", "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "bytes_per_launch": adamw_bytes,
@@ -247,7 +299,7 @@ def main():
     }
     L.close()
     if args.cpu_steps > 0:
-        out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)
     print(json.dumps(out), flush=True)
 
 

@@ -33,7 +33,11 @@
  *   w            float32, n elements.
  *   g            float32, bfloat16 or IEEE float16 (MTA_F32 / MTA_BF16 /
  *                MTA_F16, whole list), n elements.
- *   m, v         MTA_MOM_F32: float32, n elements.
+ *   m, v         the optimizer state.  Either may be NULL for every tensor of
+ *                a list (the choice is the same for all non-empty tensors):
+ *                a list for SGD needs neither, one for momentum SGD needs m
+ *                (float32), the Adam family needs both.
+ *                MTA_MOM_F32: float32, n elements.
  *                MTA_MOM_BF16X2: packed bfloat16, two per 32-bit word, element
  *                2k in the low half of word k ("BendTorch main.bend", PTree
  *                comment).  On this little-endian device that is byte for
@@ -130,7 +134,36 @@ typedef struct {
   int32_t vector_tensors; /* tensors that take the 16-byte vector path */
   int32_t gtype, mkind, vkind;
   int32_t weight_copies;  /* tensors with an attached bfloat16 weight copy */
+  int32_t state_buffers;  /* bit 0: the list has m; bit 1: it has v */
 } mta_list_info_t;
+
+/* The update rules of "BendTorch main.bend", section "Optimizers" (the Opt
+ * type and its comment; adam_grad, adam_decay, sgd_l, mom_l). */
+typedef enum {
+  MTA_OPT_ADAMW = 0,   /* decoupled decay: w' = w*(1 - lr*wd) */
+  MTA_OPT_ADAM = 1,    /* coupled decay (dec = false): g' = g + f32(w*wd) */
+  MTA_OPT_SGD = 2,     /* w = w + (-lr)*g */
+  MTA_OPT_MOMENTUM = 3 /* buf = buf*mu + g; w = w + (-lr)*buf (PyTorch's
+                          SGD momentum: no dampening, not Nesterov) */
+} mta_opt_kind;
+
+/* Flags of mta_opt. */
+#define MTA_STEP_ZERO_GRAD 1 /* write +0 into every gradient element after the
+                                step reads it, as every step loop of the
+                                Optimizers section does */
+
+/* One optimizer step's configuration.  Fields a rule does not use are
+ * ignored, except weight_decay, which must be 0 for SGD and momentum (their
+ * rules have no decay). */
+typedef struct {
+  int32_t kind;        /* mta_opt_kind */
+  int32_t flags;       /* MTA_STEP_ZERO_GRAD or 0 */
+  double lr;           /* all rules; finite, >= 0 */
+  double beta1, beta2; /* Adam family: 0 <= beta < 1 */
+  double eps;          /* Adam family: finite, >= 0 */
+  double weight_decay; /* Adam family: finite, >= 0 */
+  double momentum;     /* MTA_OPT_MOMENTUM: mu, finite, >= 0 */
+} mta_opt;
 
 /* Flags of mta_scale. */
 #define MTA_SCALE_INPLACE 1 /* launch now: g = g * factor, rounded to g's type */
@@ -180,6 +213,21 @@ int mta_clip_norm(mta_list *list, float max_norm, float *d_norm, float *d_coef,
 int mta_adamw_step(mta_list *list, const mta_adamw_hparams *hp, int64_t t,
                    const float *d_coef, void *stream);
 
+/* One step of any rule of mta_opt_kind: one launch over every tensor.
+ * Per element, ge = f32(f32(g*s) * coef) as in mta_adamw_step, then
+ *   MTA_OPT_ADAMW     the update of mta_adamw_step;
+ *   MTA_OPT_ADAM      ge' = ge + f32(w*wd) feeds m and v, and w is not
+ *                     decayed (w' = w); otherwise as AdamW;
+ *   MTA_OPT_SGD       w = w + f32(-lr)*ge;
+ *   MTA_OPT_MOMENTUM  m = (m*mu) + ge; w = w + f32(-lr)*m   (m float32);
+ * each operation rounded on its own; with MTA_STEP_ZERO_GRAD the gradient
+ * element is then set to +0.  Requires the state buffers of the rule
+ * (MTA_ESTATE when the list lacks them; MTA_EDTYPE for a packed momentum
+ * buffer).  t >= 1 (read by the Adam family only).  Clears a deferred scale
+ * factor, and writes the attached weight copies, as mta_adamw_step. */
+int mta_step(mta_list *list, const mta_opt *opt, int64_t t,
+             const float *d_coef, void *stream);
+
 /* Attach bfloat16 copies of the weights: every later mta_adamw_step also
  * writes w16[i][k] = bfloat16(w_new[k]) (nearest-even, NaN -> 0xFFFF) for
  * each tensor i that has one, in the same launch ("Mica 7.7: a training step
@@ -216,6 +264,16 @@ int mta_amp_clip_norm(mta_list *list, float max_norm, mta_amp_state *d_amp,
 int mta_amp_adamw_step(mta_list *list, const mta_adamw_hparams *hp,
                        const mta_amp_state *d_amp, const float *d_coef,
                        void *stream);
+
+/* Loss-scaled mta_step: one launch.  When d_amp->found_inf is set the
+ * update is skipped (w and the state untouched), but MTA_STEP_ZERO_GRAD
+ * still zeroes every gradient (a caller that zeroes every iteration expects
+ * it).  Otherwise the step of mta_step with the unscale factor
+ * float32(1/float64(scale)) and, for the Adam family, t = d_amp->step + 1,
+ * both read on the device as in mta_amp_adamw_step. */
+int mta_amp_step(mta_list *list, const mta_opt *opt,
+                 const mta_amp_state *d_amp, const float *d_coef,
+                 void *stream);
 
 /* After each loss-scaled step (PyTorch's GradScaler.update): one launch of
  * one thread.  If found_inf: scale *= backoff_factor, growth_tracker = 0.

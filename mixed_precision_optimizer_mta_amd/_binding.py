@@ -13,6 +13,10 @@ LIB_PATH = os.path.join(HERE, "libmta.so")
 MTA_F32, MTA_BF16, MTA_F16 = 0, 1, 2
 MTA_MOM_F32, MTA_MOM_BF16X2 = 0, 1
 MTA_SCALE_INPLACE, MTA_SCALE_DEFER = 1, 2
+MTA_OPT_ADAMW, MTA_OPT_ADAM, MTA_OPT_SGD, MTA_OPT_MOMENTUM = 0, 1, 2, 3
+OPT_KINDS = {"adamw": MTA_OPT_ADAMW, "adam": MTA_OPT_ADAM,
+             "sgd": MTA_OPT_SGD, "momentum": MTA_OPT_MOMENTUM}
+MTA_STEP_ZERO_GRAD = 1
 
 MTA_OK = 0
 STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
@@ -24,7 +28,7 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_clip_norm", "mta_adamw_step", "mta_list_set_weight_copies",
            "mta_adamw_scalars", "mta_list_info", "mta_last_error",
            "mta_abi_version", "mta_amp_clip_norm", "mta_amp_adamw_step",
-           "mta_amp_update")
+           "mta_amp_update", "mta_step", "mta_amp_step")
 
 
 class mta_tensor(ctypes.Structure):
@@ -37,6 +41,14 @@ class mta_adamw_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double)]
+
+
+class mta_opt(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double),
+                ("momentum", ctypes.c_double)]
 
 
 class mta_amp_state(ctypes.Structure):
@@ -52,7 +64,8 @@ class mta_list_info_t(ctypes.Structure):
                 ("grid_update", ctypes.c_int32), ("grid_norm", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("vector_tensors", ctypes.c_int32),
                 ("gtype", ctypes.c_int32), ("mkind", ctypes.c_int32),
-                ("vkind", ctypes.c_int32), ("weight_copies", ctypes.c_int32)]
+                ("vkind", ctypes.c_int32), ("weight_copies", ctypes.c_int32),
+                ("state_buffers", ctypes.c_int32)]
 
 
 class MtaError(RuntimeError):
@@ -96,6 +109,8 @@ def lib():
                                          vp, vp, vp]
         L.mta_amp_update.argtypes = [vp, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_int32, vp]
+        L.mta_step.argtypes = [vp, ctypes.POINTER(mta_opt), i64, vp, vp]
+        L.mta_amp_step.argtypes = [vp, ctypes.POINTER(mta_opt), vp, vp, vp]
         L.mta_last_error.argtypes = []
         L.mta_last_error.restype = ctypes.c_char_p
         L.mta_abi_version.argtypes = []
@@ -200,3 +215,28 @@ def mta_amp_update(d_amp, growth_factor, backoff_factor, growth_interval,
                    stream=0):
     _check(lib().mta_amp_update(d_amp, growth_factor, backoff_factor,
                                 growth_interval, stream), "mta_amp_update")
+
+
+def _opt(opt):
+    """An mta_opt from a dict: kind ("adamw", "adam", "sgd", "momentum" or
+    the enum value), lr, and the fields the rule reads; zero_grad (bool)."""
+    if isinstance(opt, mta_opt):
+        return opt
+    kind = opt["kind"]
+    kind = OPT_KINDS[kind] if isinstance(kind, str) else int(kind)
+    flags = MTA_STEP_ZERO_GRAD if opt.get("zero_grad") else 0
+    return mta_opt(kind, flags, opt.get("lr", 0.0), opt.get("beta1", 0.0),
+                   opt.get("beta2", 0.0), opt.get("eps", 0.0),
+                   opt.get("weight_decay", 0.0), opt.get("momentum", 0.0))
+
+
+def mta_step(handle, opt, t, d_coef, stream=0):
+    o = _opt(opt)
+    _check(lib().mta_step(handle, ctypes.byref(o), t, d_coef, stream),
+           "mta_step")
+
+
+def mta_amp_step(handle, opt, d_amp, d_coef, stream=0):
+    o = _opt(opt)
+    _check(lib().mta_amp_step(handle, ctypes.byref(o), d_amp, d_coef, stream),
+           "mta_amp_step")

@@ -25,8 +25,10 @@ struct mta_list {
   int64_t count = 0;
   int64_t elements = 0;
   uint32_t ntiles = 0;
-  int grid_update = 1;
+  int cus = 1;          // compute units of the device
+  int grid_update = 1;  // workgroups of an AdamW / scale launch
   int grid_norm = 1;
+  int state_buffers = 3;  // bit 0: tensors have m; bit 1: they have v
   int vector_tensors = 0;
   void *dev_block = nullptr;  // one allocation: tile tables, norm scratch
   mta::GradTile *d_gtiles = nullptr;
@@ -78,6 +80,8 @@ bool debug_sync() {
 // loads in flight: one per CU for float32 gradients, two for 16-bit ones
 // (half the bytes per tile, so twice the workgroups for the same bytes in
 // flight).
+// The same holds for the lighter SGD and momentum streams: on gpt2-124M-sized
+// lists one workgroup per CU measured 3-4% above two, three or four.
 constexpr int kUpdateBlocksPerCu = 1;
 constexpr int kNormBlocksPerCuF32 = 1;
 constexpr int kNormBlocksPerCu16 = 2;
@@ -152,7 +156,7 @@ void make_scalars(const mta_adamw_hparams &hp, int64_t t, float out[7]) {
 mta::StepScalars step_scalars(const mta_adamw_hparams &hp, int64_t t) {
   float c[7];
   make_scalars(hp, t, c);
-  mta::StepScalars sc;
+  mta::StepScalars sc{};
   sc.nstep = -c[0];
   sc.bc2 = c[1];
   sc.c1 = c[2];
@@ -198,6 +202,7 @@ void list_spans(const mta_list *L, std::vector<Span> *spans) {
     if (x.n == 0) continue;
     const void *bufs[4] = {x.w, x.g, x.m, x.v};
     for (int b = 0; b < 4; ++b) {
+      if (!bufs[b]) continue;  // a state buffer the list does not have
       const uintptr_t lo = reinterpret_cast<uintptr_t>(bufs[b]);
       spans->push_back(Span{lo, lo + static_cast<uintptr_t>(x.n) * sizes[b],
                             static_cast<int64_t>(i), b});
@@ -253,6 +258,134 @@ mta::Work work_of(const mta_list *L, int grid, void *stream) {
   return w;
 }
 
+const char *opt_name(int kind) {
+  switch (kind) {
+    case MTA_OPT_ADAMW: return "MTA_OPT_ADAMW";
+    case MTA_OPT_ADAM: return "MTA_OPT_ADAM";
+    case MTA_OPT_SGD: return "MTA_OPT_SGD";
+    case MTA_OPT_MOMENTUM: return "MTA_OPT_MOMENTUM";
+    default: return "?";
+  }
+}
+
+bool adam_family(int kind) {
+  return kind == MTA_OPT_ADAMW || kind == MTA_OPT_ADAM;
+}
+
+// Argument checks of one step of `o`'s rule (t is checked by the caller).
+int check_opt(const mta_opt *o, int64_t t) {
+  if (!o) return fail(MTA_EINVAL, "opt is NULL");
+  if (o->kind < MTA_OPT_ADAMW || o->kind > MTA_OPT_MOMENTUM)
+    return fail(MTA_EINVAL, "unknown optimizer kind %d", o->kind);
+  if (o->flags & ~MTA_STEP_ZERO_GRAD)
+    return fail(MTA_EINVAL, "unknown step flags 0x%x",
+                static_cast<unsigned>(o->flags));
+  if (adam_family(o->kind)) {
+    const mta_adamw_hparams hp{o->lr, o->beta1, o->beta2, o->eps,
+                               o->weight_decay};
+    return check_hparams(&hp, t);
+  }
+  if (!(std::isfinite(o->lr) && o->lr >= 0.0))
+    return fail(MTA_EINVAL, "lr must be finite and >= 0 (got %g)", o->lr);
+  if (o->weight_decay != 0.0)
+    return fail(MTA_EINVAL,
+                "%s has no weight decay: weight_decay must be 0 (got %g)",
+                opt_name(o->kind), o->weight_decay);
+  if (o->kind == MTA_OPT_MOMENTUM &&
+      !(std::isfinite(o->momentum) && o->momentum >= 0.0))
+    return fail(MTA_EINVAL, "momentum must be finite and >= 0 (got %g)",
+                o->momentum);
+  if (t < 1) return fail(MTA_EINVAL, "step t must be >= 1 (got %lld)",
+                         static_cast<long long>(t));
+  return MTA_OK;
+}
+
+// The kernel's scalar block for one step of `o`'s rule at step t.
+mta::StepScalars opt_scalars(const mta_opt &o, int64_t t) {
+  mta::StepScalars sc{};
+  if (adam_family(o.kind)) {
+    const mta_adamw_hparams hp{o.lr, o.beta1, o.beta2, o.eps,
+                               o.weight_decay};
+    sc = step_scalars(hp, t);
+    if (o.kind == MTA_OPT_ADAM) {
+      sc.dec = 1.0f;  // not read: Adam does not decay w
+      sc.l2 = static_cast<float>(o.weight_decay);
+    }
+  } else {
+    // w + (-lr)*g: lr is the float32 value, negated exactly
+    sc.nstep = -static_cast<float>(o.lr);
+    sc.mu = static_cast<float>(o.momentum);
+  }
+  sc.s = 1.0f;
+  sc.zero = (o.flags & MTA_STEP_ZERO_GRAD) ? 1u : 0u;
+  return sc;
+}
+
+
+// One step of any rule, plain (d_amp == nullptr: t and the deferred factor
+// from the host) or loss-scaled (t and 1/scale from the device state).
+int step_common(mta_list *L, const mta_opt *o, int64_t t, const float *d_coef,
+                const mta_amp_state *d_amp, void *stream, const char *what) {
+  int rc = check_opt(o, t);
+  if (rc) return rc;
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  const bool needs_m = o->kind != MTA_OPT_SGD;
+  const bool needs_v = adam_family(o->kind);
+  if ((needs_m && !(L->state_buffers & 1)) ||
+      (needs_v && !(L->state_buffers & 2)))
+    return fail(MTA_ESTATE, "%s needs the list's %s buffers, which it lacks",
+                opt_name(o->kind), needs_v ? "m and v" : "m");
+  if (o->kind == MTA_OPT_MOMENTUM && L->mkind != MTA_MOM_F32)
+    return fail(MTA_EDTYPE, "the momentum buffer (m) must be float32");
+  if (d_coef && !aligned(d_coef, 4))
+    return fail(MTA_EALIGN, "d_coef must be 4-byte aligned");
+  if (d_amp) {
+    if (!aligned(d_amp, 8))
+      return fail(MTA_EALIGN, "d_amp must be 8-byte aligned");
+    if (L->deferred)
+      return fail(MTA_ESTATE,
+                  "a host deferred scale factor is pending; a loss-scaled "
+                  "step takes its factor from the loss-scale state");
+  }
+  rc = check_device(L);
+  if (rc) return rc;
+  mta::StepScalars sc = opt_scalars(*o, t);
+  sc.s = (!d_amp && L->deferred) ? L->deferred_s : 1.0f;
+  const mta::AmpStep amp = d_amp
+      ? mta::AmpStep{d_amp, o->lr, o->beta1, o->beta2}
+      : mta::AmpStep{};
+  if (L->ntiles > 0) {
+    const mta::Work wk = work_of(L, L->grid_update, stream);
+    const hipError_t e = mta::launch_update(o->kind, L->gtype, L->mkind,
+                                            L->vkind, wk, sc, d_coef, amp);
+    if (e != hipSuccess)  // nothing enqueued: a deferred factor stays
+      return after_launch(e, wk.stream, what);
+    if (!d_amp) {
+      L->deferred = false;
+      L->deferred_s = 1.0f;
+    }
+    return after_launch(hipSuccess, wk.stream, what);
+  }
+  if (!d_amp) {
+    L->deferred = false;
+    L->deferred_s = 1.0f;
+  }
+  return ok();
+}
+
+mta_opt adamw_opt(const mta_adamw_hparams *hp) {
+  mta_opt o{};
+  o.kind = MTA_OPT_ADAMW;
+  if (hp) {
+    o.lr = hp->lr;
+    o.beta1 = hp->beta1;
+    o.beta2 = hp->beta2;
+    o.eps = hp->eps;
+    o.weight_decay = hp->weight_decay;
+  }
+  return o;
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +427,8 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   std::vector<Span> spans;
   int64_t elements = 0;
   int vec_tensors = 0;
+  int state = -1;  // m / v presence of the first non-empty tensor
+  int64_t state_from = -1;
   try {
     spans.reserve(static_cast<size_t>(count) * 4);
     uint64_t ntiles = 0;
@@ -305,9 +440,21 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
         return fail(MTA_EINVAL, "tensor %lld: n too large",
                     static_cast<long long>(i));
       if (x.n == 0) continue;
-      if (!x.w || !x.g || !x.m || !x.v)
-        return fail(MTA_EINVAL, "tensor %lld: a buffer pointer is NULL",
+      if (!x.w || !x.g)
+        return fail(MTA_EINVAL, "tensor %lld: w or g is NULL",
                     static_cast<long long>(i));
+      const int st = (x.m ? 1 : 0) | (x.v ? 2 : 0);
+      if (state < 0) {
+        state = st;
+        state_from = i;
+      } else if (st != state) {
+        return fail(MTA_EINVAL,
+                    "tensor %lld: its m / v buffers are not given the way "
+                    "tensor %lld's are (a list has the same state buffers "
+                    "on every tensor)",
+                    static_cast<long long>(i),
+                    static_cast<long long>(state_from));
+      }
       if (!aligned(x.w, 4) || !aligned(x.g, gsz) || !aligned(x.m, msz) ||
           !aligned(x.v, vsz))
         return fail(MTA_EALIGN,
@@ -320,6 +467,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
       const void *bufs[4] = {x.w, x.g, x.m, x.v};
       const uintptr_t sizes[4] = {4, gsz, msz, vsz};
       for (int b = 0; b < 4; ++b) {
+        if (!bufs[b]) continue;
         const uintptr_t lo = reinterpret_cast<uintptr_t>(bufs[b]);
         spans.push_back(Span{lo, lo + n * sizes[b], i, b});
       }
@@ -364,6 +512,8 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->elements = elements;
   L->ntiles = static_cast<uint32_t>(stiles.size());
   L->vector_tensors = vec_tensors;
+  L->cus = cus;
+  L->state_buffers = state < 0 ? 3 : state;  // no element: any rule works
   const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
   const int bpc_n = env_int(
       "MTA_NORM_BLOCKS_PER_CU",
@@ -493,6 +643,7 @@ int mta_list_info(const mta_list *L, mta_list_info_t *out) {
   out->mkind = L->mkind;
   out->vkind = L->vkind;
   out->weight_copies = L->weight_copies;
+  out->state_buffers = L->state_buffers;
   return ok();
 }
 
@@ -541,28 +692,14 @@ int mta_clip_norm(mta_list *L, float max_norm, float *d_norm, float *d_coef,
 
 int mta_adamw_step(mta_list *L, const mta_adamw_hparams *hp, int64_t t,
                    const float *d_coef, void *stream) {
-  if (!L) return fail(MTA_EINVAL, "list is NULL");
-  int rc = check_hparams(hp, t);
-  if (rc) return rc;
-  if (d_coef && !aligned(d_coef, 4))
-    return fail(MTA_EALIGN, "d_coef must be 4-byte aligned");
-  rc = check_device(L);
-  if (rc) return rc;
-  mta::StepScalars sc = step_scalars(*hp, t);
-  sc.s = L->deferred ? L->deferred_s : 1.0f;
-  if (L->ntiles > 0) {
-    const mta::Work wk = work_of(L, L->grid_update, stream);
-    const hipError_t e = mta::launch_adamw(L->gtype, L->mkind, L->vkind, wk,
-                                           sc, d_coef, mta::AmpStep{});
-    if (e != hipSuccess)  // nothing enqueued: the deferred factor stays
-      return after_launch(e, wk.stream, "mta_adamw_step");
-    L->deferred = false;
-    L->deferred_s = 1.0f;
-    return after_launch(hipSuccess, wk.stream, "mta_adamw_step");
-  }
-  L->deferred = false;
-  L->deferred_s = 1.0f;
-  return ok();
+  if (!hp) return fail(MTA_EINVAL, "hparams is NULL");
+  const mta_opt o = adamw_opt(hp);
+  return step_common(L, &o, t, d_coef, nullptr, stream, "mta_adamw_step");
+}
+
+int mta_step(mta_list *L, const mta_opt *opt, int64_t t, const float *d_coef,
+             void *stream) {
+  return step_common(L, opt, t, d_coef, nullptr, stream, "mta_step");
 }
 
 int mta_amp_clip_norm(mta_list *L, float max_norm, mta_amp_state *d_amp,
@@ -594,28 +731,16 @@ int mta_amp_clip_norm(mta_list *L, float max_norm, mta_amp_state *d_amp,
 int mta_amp_adamw_step(mta_list *L, const mta_adamw_hparams *hp,
                        const mta_amp_state *d_amp, const float *d_coef,
                        void *stream) {
-  if (!L) return fail(MTA_EINVAL, "list is NULL");
-  int rc = check_hparams(hp, 1);
-  if (rc) return rc;
+  if (!hp) return fail(MTA_EINVAL, "hparams is NULL");
   if (!d_amp) return fail(MTA_EINVAL, "d_amp is NULL");
-  if (!aligned(d_amp, 8))
-    return fail(MTA_EALIGN, "d_amp must be 8-byte aligned");
-  if (d_coef && !aligned(d_coef, 4))
-    return fail(MTA_EALIGN, "d_coef must be 4-byte aligned");
-  if (L->deferred)
-    return fail(MTA_ESTATE,
-                "a host deferred scale factor is pending; a loss-scaled step "
-                "takes its factor from the loss-scale state");
-  rc = check_device(L);
-  if (rc) return rc;
-  if (L->ntiles == 0) return ok();
-  // nstep, bc2 and s are formed by the kernel from the device state
-  const mta::StepScalars sc = step_scalars(*hp, 1);
-  const mta::Work wk = work_of(L, L->grid_update, stream);
-  return after_launch(
-      mta::launch_adamw(L->gtype, L->mkind, L->vkind, wk, sc, d_coef,
-                        mta::AmpStep{d_amp, hp->lr, hp->beta1, hp->beta2}),
-      wk.stream, "mta_amp_adamw_step");
+  const mta_opt o = adamw_opt(hp);
+  return step_common(L, &o, 1, d_coef, d_amp, stream, "mta_amp_adamw_step");
+}
+
+int mta_amp_step(mta_list *L, const mta_opt *opt, const mta_amp_state *d_amp,
+                 const float *d_coef, void *stream) {
+  if (!d_amp) return fail(MTA_EINVAL, "d_amp is NULL");
+  return step_common(L, opt, 1, d_coef, d_amp, stream, "mta_amp_step");
 }
 
 int mta_amp_update(mta_amp_state *d_amp, double growth_factor,

@@ -30,8 +30,10 @@ struct GradTile {
 };
 static_assert(sizeof(GradTile) == 16, "gradient tile layout");
 
-// k_adamw reads and writes all four buffers, and writes the bfloat16 weight
-// copy when one is attached.
+// The update kernels read and write the buffers their rule uses (w and g
+// always; m for momentum and the Adam family; v for the Adam family), and
+// write the bfloat16 weight copy when one is attached.  Unused buffers are
+// null.
 struct StepTile {
   float *w;
   const void *g;
@@ -43,11 +45,22 @@ struct StepTile {
 };
 static_assert(sizeof(StepTile) == 48, "step tile layout");
 
-// Per-call float32 constants of the AdamW step (formed on the host in float64,
-// rounded once).  nstep = -step: negation is exact, so (-step)*m is unchanged.
+// Update rules, numbered as mta_opt_kind.
+constexpr int kRuleAdamW = MTA_OPT_ADAMW;
+constexpr int kRuleAdam = MTA_OPT_ADAM;
+constexpr int kRuleSgd = MTA_OPT_SGD;
+constexpr int kRuleMomentum = MTA_OPT_MOMENTUM;
+
+// Per-call float32 constants of a step (formed on the host in float64,
+// rounded once).  Adam family: nstep = -step (negation is exact, so
+// (-step)*m is unchanged), bc2, c1, c2, b2, eps; dec is AdamW's decay
+// factor, l2 Adam's coupled decay.  SGD and momentum: nstep = -lr, mu.
 struct StepScalars {
   float nstep, bc2, c1, c2, b2, eps, dec;
-  float s;  // deferred unscale factor (1 when none)
+  float s;        // deferred unscale factor (1 when none)
+  float l2;       // Adam: g' = g + w*l2
+  float mu;       // momentum
+  uint32_t zero;  // 1: write +0 into every gradient element after reading it
 };
 
 struct Work {
@@ -64,10 +77,11 @@ struct NormScratch {
   unsigned int *ticket;
 };
 
-// Loss-scaled AdamW: with `state` set, the kernel skips the step when
-// state->found_inf is set, and otherwise takes t = state->step + 1 and the
-// unscale factor 1/state->scale from device memory, forming the
-// t-dependent constants itself from these float64 hyperparameters.
+// Loss-scaled step: with `state` set, the kernel skips the update when
+// state->found_inf is set (it still zeroes the gradients when asked), and
+// otherwise takes the unscale factor 1/state->scale and, for the Adam
+// family, t = state->step + 1 from device memory, forming the t-dependent
+// constants itself from these float64 hyperparameters.
 static_assert(sizeof(mta_amp_state) == 24, "loss-scale state layout");
 
 struct AmpStep {
@@ -75,9 +89,9 @@ struct AmpStep {
   double lr, beta1, beta2;
 };
 
-hipError_t launch_adamw(int gtype, int mkind, int vkind, const Work &work,
-                        const StepScalars &sc, const float *d_coef,
-                        const AmpStep &amp);
+hipError_t launch_update(int rule, int gtype, int mkind, int vkind,
+                         const Work &work, const StepScalars &sc,
+                         const float *d_coef, const AmpStep &amp);
 hipError_t launch_sumsq(int gtype, const Work &work, float s, float max_norm,
                         NormScratch scratch, float *d_norm, float *d_coef,
                         mta_amp_state *amp);

@@ -1,6 +1,7 @@
-// mta_kernels.hip -- gfx950 kernels of the fused clip + multi-tensor AdamW step.
+// mta_kernels.hip -- gfx950 kernels of the fused clip + multi-tensor optimizer
+// step.
 //
-// Four kernels:
+// Kernels:
 //   k_sumsq       joint sum of squares -> norm and clip coefficient
 //                 (ClipGradNorms, "Mica 7.7: a training step on the card, in
 //                 every float type", section "The whole model in one call";
@@ -15,7 +16,11 @@
 //                 writes the bfloat16 copy of its new weights (Mica, section
 //                 "float16 and bfloat16, whole").  With a loss-scale state it
 //                 skips a step whose gradients were not finite and takes the
-//                 step number from device memory.
+//                 step number from device memory.  The same kernel runs Adam
+//                 with coupled decay (adam_grad with dec = false).
+//   k_sgd, k_momentum  the SGD and momentum-SGD rules (sgd_l, mom_l), on the
+//                 same tile walk.  Every update kernel can also zero the
+//                 gradient after reading it, as every step loop there does.
 //   k_scale       ScaleTensors in place (same Mica section).
 //   k_amp_update  the loss-scale update after a step (one thread).
 // Each of the first three is one launch over the whole tensor list.
@@ -247,40 +252,64 @@ __device__ __forceinline__ float inv_scale(float scale) {
 }
 
 // ---------------------------------------------------------------------------
-// The AdamW element step ("BendTorch main.bend", Optimizers), with the
-// unscale (ScaleTensors) and the clip coefficient (ClipGradNorms) applied in
-// registers first.  Packed kinds round the new moment to bfloat16 and the
-// weight update reads the rounded value (adamh_l, adamhv_l).
+// The element step of each update rule ("BendTorch main.bend", Optimizers),
+// with the unscale (ScaleTensors) and the clip coefficient (ClipGradNorms)
+// applied in registers first.
+//   Adam family: adam_grad, adam_decay (AdamW decays w, Adam adds w*wd to the
+//   gradient), adam_m, adam_v, adam_w; packed kinds round the new moment to
+//   bfloat16 and the weight update reads the rounded value (adamh_l,
+//   adamhv_l).
+//   SGD: sgd_l.  Momentum: mom_l (float32 buffer in m).
 // ---------------------------------------------------------------------------
 
-template <bool MPacked, bool VPacked>
-__device__ __forceinline__ void adamw_elem(float &w, float g, float &m,
-                                           float &v, const StepScalars &sc,
-                                           float coef) {
+template <int R>
+constexpr bool kUsesM = R != kRuleSgd;
+template <int R>
+constexpr bool kUsesV = R == kRuleAdamW || R == kRuleAdam;
+
+template <int R, bool MPacked, bool VPacked>
+__device__ __forceinline__ void rule_elem(float &w, float g, float &m,
+                                          float &v, const StepScalars &sc,
+                                          float coef) {
   const float x = g * sc.s;                          // unscale
-  const float ge = x * coef;                         // clip
-  const float wd = w * sc.dec;                       // adam_decay (AdamW)
-  float m1 = m + sc.c1 * (ge - m);                   // adam_m (lerp form)
-  float v1 = (v * sc.b2) + ((sc.c2 * ge) * ge);      // adam_v
-  if constexpr (MPacked) m1 = round_bf16(m1);
-  if constexpr (VPacked) v1 = round_bf16(v1);
-  const float denom = (sqrtf(v1) / sc.bc2) + sc.eps; // adam_w
-  w = wd + ((sc.nstep * m1) / denom);
-  m = m1;
-  v = v1;
+  float ge = x * coef;                               // clip
+  if constexpr (R == kRuleSgd) {
+    w = w + (sc.nstep * ge);                         // sgd_l, nstep = -lr
+  } else if constexpr (R == kRuleMomentum) {
+    const float nb = (m * sc.mu) + ge;               // mom_l
+    m = nb;
+    w = w + (sc.nstep * nb);
+  } else {
+    float wd;
+    if constexpr (R == kRuleAdam) {
+      ge = ge + (w * sc.l2);                         // adam_grad (Adam)
+      wd = w;                                        // adam_decay (Adam)
+    } else {
+      wd = w * sc.dec;                               // adam_decay (AdamW)
+    }
+    float m1 = m + sc.c1 * (ge - m);                 // adam_m (lerp form)
+    float v1 = (v * sc.b2) + ((sc.c2 * ge) * ge);    // adam_v
+    if constexpr (MPacked) m1 = round_bf16(m1);
+    if constexpr (VPacked) v1 = round_bf16(v1);
+    const float denom = (sqrtf(v1) / sc.bc2) + sc.eps; // adam_w
+    w = wd + ((sc.nstep * m1) / denom);
+    m = m1;
+    v = v1;
+  }
 }
 
 constexpr int kAdamVec = 4;                                   // per access
 constexpr int kAdamGroups = kTileElems / (kBlock * kAdamVec); // 4
 constexpr uint32_t kAdamStride = kBlock * kAdamVec;           // 1024
 
-// k_adamw keeps two tiles in flight per lane: while it computes tile t from
-// one register set it has already issued every load of tile t + gridDim.x
-// into the other.  With one workgroup per CU (one wave per SIMD) this keeps
-// HBM busy through the ~1000 VALU instructions a lane spends on a tile; it
-// measured 3-5% above the single-buffered loop at any grid size on gfx950.
-// The register sets hold the raw loaded vectors; unpacking happens when a
-// tile is computed, so no wait is needed between a tile's loads.
+// The update kernels keep two tiles in flight per lane: while one computes
+// tile t from one register set it has already issued every load of tile
+// t + gridDim.x into the other.  With one workgroup per CU (one wave per
+// SIMD) this keeps HBM busy through the ~1000 VALU instructions a lane spends
+// on an AdamW tile; it measured 3-5% above the single-buffered loop at any
+// grid size on gfx950.  The register sets hold the raw loaded vectors;
+// unpacking happens when a tile is computed, so no wait is needed between a
+// tile's loads.
 
 // raw vectors of one lane's share of a full tile (4 accesses per buffer)
 template <int D>
@@ -304,14 +333,30 @@ __device__ __forceinline__ void unpack4(const raw4_t<D> &a, float (&x)[4]) {
   }
 }
 
-template <int G, bool MPacked, bool VPacked>
+// +0 into 4 consecutive gradient elements (16 or 8 bytes; all-zero bits are
+// +0 in every gradient type), or into one.
+template <int D>
+__device__ __forceinline__ void zero4(MTA_GLOBAL elem_t<D> *p, uint32_t e) {
+  if constexpr (D == kF32)
+    __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                (MTA_GLOBAL f32x4 *)(p + e));
+  else
+    __builtin_nontemporal_store(u32x2{0u, 0u}, (MTA_GLOBAL u32x2 *)(p + e));
+}
+
+template <int D>
+__device__ __forceinline__ void zero1(MTA_GLOBAL elem_t<D> *p, uint32_t e) {
+  p[e] = elem_t<D>(0);
+}
+
+template <int R, int G, bool MPacked, bool VPacked>
 struct TileRegs {
   static constexpr int M = MPacked ? kBF16 : kF32;
   static constexpr int V = VPacked ? kBF16 : kF32;
   f32x4 w[kAdamGroups];
   raw4_t<G> g[kAdamGroups];
-  raw4_t<M> m[kAdamGroups];
-  raw4_t<V> v[kAdamGroups];
+  raw4_t<M> m[kAdamGroups];  // unused (never written) when the rule has no m
+  raw4_t<V> v[kAdamGroups];  // likewise for v
 };
 
 template <int G, bool MPacked, bool VPacked>
@@ -319,7 +364,7 @@ struct TileRef {
   static constexpr int M = MPacked ? kBF16 : kF32;
   static constexpr int V = VPacked ? kBF16 : kF32;
   MTA_GLOBAL float *pw;
-  MTA_GLOBAL const elem_t<G> *pg;
+  MTA_GLOBAL elem_t<G> *pg;  // read, and written only when zeroing
   MTA_GLOBAL elem_t<M> *pm;
   MTA_GLOBAL elem_t<V> *pv;
   MTA_GLOBAL uint16_t *pw16;  // bfloat16 weight copy, or null
@@ -342,41 +387,42 @@ __device__ __forceinline__ TileRef<G, MPacked, VPacked> tile_ref(
   return r;
 }
 
-template <int G, bool MPacked, bool VPacked>
-__device__ __forceinline__ void issue_tile(TileRegs<G, MPacked, VPacked> &R,
-                                           const TileRef<G, MPacked, VPacked> &T,
-                                           uint32_t e0) {
+template <int R, int G, bool MPacked, bool VPacked>
+__device__ __forceinline__ void issue_tile(
+    TileRegs<R, G, MPacked, VPacked> &X, const TileRef<G, MPacked, VPacked> &T,
+    uint32_t e0) {
   using Ref = TileRef<G, MPacked, VPacked>;
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j) {
     const uint32_t e = e0 + j * kAdamStride;
-    R.w[j] = load4_raw<kF32>(T.pw, e);
-    R.g[j] = load4_raw<G>(T.pg, e);
-    R.m[j] = load4_raw<Ref::M>(T.pm, e);
-    R.v[j] = load4_raw<Ref::V>(T.pv, e);
+    X.w[j] = load4_raw<kF32>(T.pw, e);
+    X.g[j] = load4_raw<G>(T.pg, e);
+    if constexpr (kUsesM<R>) X.m[j] = load4_raw<Ref::M>(T.pm, e);
+    if constexpr (kUsesV<R>) X.v[j] = load4_raw<Ref::V>(T.pv, e);
   }
 }
 
-template <int G, bool MPacked, bool VPacked>
+template <int R, int G, bool MPacked, bool VPacked>
 __device__ __forceinline__ void finish_tile(
-    const TileRegs<G, MPacked, VPacked> &R,
+    const TileRegs<R, G, MPacked, VPacked> &X,
     const TileRef<G, MPacked, VPacked> &T, uint32_t e0, const StepScalars &sc,
     float coef) {
   using Ref = TileRef<G, MPacked, VPacked>;
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j) {
-    float w[4], g[4], m[4], v[4];
-    unpack4<kF32>(R.w[j], w);
-    unpack4<G>(R.g[j], g);
-    unpack4<Ref::M>(R.m[j], m);
-    unpack4<Ref::V>(R.v[j], v);
+    float w[4], g[4], m[4] = {}, v[4] = {};
+    unpack4<kF32>(X.w[j], w);
+    unpack4<G>(X.g[j], g);
+    if constexpr (kUsesM<R>) unpack4<Ref::M>(X.m[j], m);
+    if constexpr (kUsesV<R>) unpack4<Ref::V>(X.v[j], v);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      adamw_elem<MPacked, VPacked>(w[k], g[k], m[k], v[k], sc, coef);
+      rule_elem<R, MPacked, VPacked>(w[k], g[k], m[k], v[k], sc, coef);
     const uint32_t e = e0 + j * kAdamStride;
     store4<kF32>(T.pw, e, w);
-    store4<Ref::M>(T.pm, e, m);
-    store4<Ref::V>(T.pv, e, v);
+    if constexpr (kUsesM<R>) store4<Ref::M>(T.pm, e, m);
+    if constexpr (kUsesV<R>) store4<Ref::V>(T.pv, e, v);
+    if (sc.zero) zero4<G>(T.pg, e);  // uniform; after this lane's g load
     if (T.pw16) {  // uniform: the tile has a bfloat16 weight copy
       float h[4];
 #pragma unroll
@@ -386,13 +432,13 @@ __device__ __forceinline__ void finish_tile(
   }
 }
 
-template <int G, bool MPacked, bool VPacked>
+template <int R, int G, bool MPacked, bool VPacked>
 __device__ __forceinline__ void partial_tile(
     const TileRef<G, MPacked, VPacked> &T, uint32_t e0, const StepScalars &sc,
     float coef) {
   using Ref = TileRef<G, MPacked, VPacked>;
   float w[kAdamGroups][kAdamVec], g[kAdamGroups][kAdamVec],
-      m[kAdamGroups][kAdamVec], v[kAdamGroups][kAdamVec];
+      m[kAdamGroups][kAdamVec] = {}, v[kAdamGroups][kAdamVec] = {};
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j)
 #pragma unroll
@@ -400,41 +446,77 @@ __device__ __forceinline__ void partial_tile(
       const uint32_t e = e0 + j * kAdamStride + k;
       w[j][k] = load1_clamped<kF32>(T.pw, e, T.lim);
       g[j][k] = load1_clamped<G>(T.pg, e, T.lim);
-      m[j][k] = load1_clamped<Ref::M>(T.pm, e, T.lim);
-      v[j][k] = load1_clamped<Ref::V>(T.pv, e, T.lim);
+      if constexpr (kUsesM<R>)
+        m[j][k] = load1_clamped<Ref::M>(T.pm, e, T.lim);
+      if constexpr (kUsesV<R>)
+        v[j][k] = load1_clamped<Ref::V>(T.pv, e, T.lim);
     }
 #pragma unroll
   for (int j = 0; j < kAdamGroups; ++j)
 #pragma unroll
     for (int k = 0; k < kAdamVec; ++k) {
-      adamw_elem<MPacked, VPacked>(w[j][k], g[j][k], m[j][k], v[j][k], sc,
-                                   coef);
+      rule_elem<R, MPacked, VPacked>(w[j][k], g[j][k], m[j][k], v[j][k], sc,
+                                     coef);
       const uint32_t e = e0 + j * kAdamStride + k;
       if (e < T.lim) {
         T.pw[e] = w[j][k];
-        store1<Ref::M>(T.pm, e, m[j][k]);
-        store1<Ref::V>(T.pv, e, v[j][k]);
+        if constexpr (kUsesM<R>) store1<Ref::M>(T.pm, e, m[j][k]);
+        if constexpr (kUsesV<R>) store1<Ref::V>(T.pv, e, v[j][k]);
+        if (sc.zero) zero1<G>(T.pg, e);
         if (T.pw16) store1<kBF16>(T.pw16, e, round_bf16(w[j][k]));
       }
     }
 }
 
-template <int G, bool MPacked, bool VPacked>
-__global__ void __launch_bounds__(kBlock)
-k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
-        const float *__restrict__ d_coef, AmpStep amp) {
-  using Regs = TileRegs<G, MPacked, VPacked>;
+// +0 into every gradient element of the list: the whole work of a skipped
+// loss-scaled step that was asked to zero the gradients.
+template <int G>
+__device__ void zero_grad_tiles(const StepTile *__restrict__ tiles,
+                                uint32_t ntiles) {
+  const uint32_t e0 = threadIdx.x * kAdamVec;
+  for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const StepTile st = tiles[t];
+    MTA_GLOBAL elem_t<G> *pg = gp<elem_t<G>>(st.g, 0);
+    if (st.vec && st.lim == kTileElems) {
+#pragma unroll
+      for (int j = 0; j < kAdamGroups; ++j) zero4<G>(pg, e0 + j * kAdamStride);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kAdamGroups; ++j)
+#pragma unroll
+        for (int k = 0; k < kAdamVec; ++k) {
+          const uint32_t e = e0 + j * kAdamStride + k;
+          if (e < st.lim) zero1<G>(pg, e);
+        }
+    }
+  }
+}
+
+// The body of every update kernel: a persistent grid-stride walk of the
+// tile table with register double buffering.
+template <int R, int G, bool MPacked, bool VPacked>
+__device__ __forceinline__ void update_tiles(
+    const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
+    const float *__restrict__ d_coef, const AmpStep &amp) {
+  using Regs = TileRegs<R, G, MPacked, VPacked>;
   using Ref = TileRef<G, MPacked, VPacked>;
   if (amp.state) {
-    // loss-scaled step: skipped when an unscaled gradient was not finite;
-    // otherwise t comes from the device counter and the two t-dependent
-    // constants are formed here, in float64, as the host forms them
-    if (amp.state->found_inf != 0.0f) return;
-    const int64_t t = amp.state->step + 1;
-    const double q1 = 1.0 - pow_rn(amp.beta1, t);
-    const double q2 = 1.0 - pow_rn(amp.beta2, t);
-    sc.nstep = -static_cast<float>(amp.lr / q1);
-    sc.bc2 = static_cast<float>(sqrt(q2));
+    // loss-scaled step: skipped when an unscaled gradient was not finite
+    // (zeroing the gradients still happens when asked); otherwise the
+    // unscale factor, and for the Adam family t and the two t-dependent
+    // constants, come from the device state, formed in float64 as the host
+    // forms them
+    if (amp.state->found_inf != 0.0f) {
+      if (sc.zero) zero_grad_tiles<G>(tiles, ntiles);
+      return;
+    }
+    if constexpr (kUsesV<R>) {
+      const int64_t t = amp.state->step + 1;
+      const double q1 = 1.0 - pow_rn(amp.beta1, t);
+      const double q2 = 1.0 - pow_rn(amp.beta2, t);
+      sc.nstep = -static_cast<float>(amp.lr / q1);
+      sc.bc2 = static_cast<float>(sqrt(q2));
+    }
     sc.s = inv_scale(amp.state->scale);
   }
   const float coef = d_coef ? *d_coef : 1.0f;
@@ -463,13 +545,37 @@ k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
     if (cur.full)
       finish_tile(X, cur, e0, sc, coef);
     else
-      partial_tile(cur, e0, sc, coef);
+      partial_tile<R>(cur, e0, sc, coef);
     cur = nxt;
     t = tn;
     return more;
   };
   while (step(A, B) && step(B, A)) {
   }
+}
+
+// AdamW (L2 = false) and Adam with coupled decay (L2 = true).
+template <int G, bool MPacked, bool VPacked, bool L2>
+__global__ void __launch_bounds__(kBlock)
+k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
+        const float *__restrict__ d_coef, AmpStep amp) {
+  update_tiles<L2 ? kRuleAdam : kRuleAdamW, G, MPacked, VPacked>(
+      tiles, ntiles, sc, d_coef, amp);
+}
+
+template <int G>
+__global__ void __launch_bounds__(kBlock)
+k_sgd(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
+      const float *__restrict__ d_coef, AmpStep amp) {
+  update_tiles<kRuleSgd, G, false, false>(tiles, ntiles, sc, d_coef, amp);
+}
+
+template <int G>
+__global__ void __launch_bounds__(kBlock)
+k_momentum(const StepTile *__restrict__ tiles, uint32_t ntiles,
+           StepScalars sc, const float *__restrict__ d_coef, AmpStep amp) {
+  update_tiles<kRuleMomentum, G, false, false>(tiles, ntiles, sc, d_coef,
+                                               amp);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,24 +869,47 @@ __global__ void k_amp_update(mta_amp_state *__restrict__ st, double growth,
   st->found_inf = 0.0f;
 }
 
-template <int G, bool M, bool V>
+template <int G, bool M, bool V, bool L2>
 hipError_t launch_adamw_t(const Work &wk, const StepScalars &sc,
                           const float *d_coef, const AmpStep &amp) {
-  hipLaunchKernelGGL((k_adamw<G, M, V>), dim3(wk.grid), dim3(kBlock), 0,
+  hipLaunchKernelGGL((k_adamw<G, M, V, L2>), dim3(wk.grid), dim3(kBlock), 0,
                      wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool L2>
 hipError_t launch_adamw_g(int mkind, int vkind, const Work &wk,
                           const StepScalars &sc, const float *d_coef,
                           const AmpStep &amp) {
   switch ((mkind << 1) | vkind) {
-    case 0: return launch_adamw_t<G, false, false>(wk, sc, d_coef, amp);
-    case 1: return launch_adamw_t<G, false, true>(wk, sc, d_coef, amp);
-    case 2: return launch_adamw_t<G, true, false>(wk, sc, d_coef, amp);
-    case 3: return launch_adamw_t<G, true, true>(wk, sc, d_coef, amp);
+    case 0: return launch_adamw_t<G, false, false, L2>(wk, sc, d_coef, amp);
+    case 1: return launch_adamw_t<G, false, true, L2>(wk, sc, d_coef, amp);
+    case 2: return launch_adamw_t<G, true, false, L2>(wk, sc, d_coef, amp);
+    case 3: return launch_adamw_t<G, true, true, L2>(wk, sc, d_coef, amp);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <int G>
+hipError_t launch_update_g(int rule, int mkind, int vkind, const Work &wk,
+                           const StepScalars &sc, const float *d_coef,
+                           const AmpStep &amp) {
+  switch (rule) {
+    case kRuleAdamW:
+      return launch_adamw_g<G, false>(mkind, vkind, wk, sc, d_coef, amp);
+    case kRuleAdam:
+      return launch_adamw_g<G, true>(mkind, vkind, wk, sc, d_coef, amp);
+    case kRuleSgd:
+      hipLaunchKernelGGL((k_sgd<G>), dim3(wk.grid), dim3(kBlock), 0,
+                         wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
+      return hipGetLastError();
+    case kRuleMomentum:
+      if (mkind != 0) return hipErrorInvalidValue;  // float32 buffer only
+      hipLaunchKernelGGL((k_momentum<G>), dim3(wk.grid), dim3(kBlock), 0,
+                         wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
+      return hipGetLastError();
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
@@ -803,14 +932,18 @@ hipError_t launch_scale_t(const Work &wk, float s) {
 
 }  // namespace
 
-hipError_t launch_adamw(int gtype, int mkind, int vkind, const Work &wk,
-                        const StepScalars &sc, const float *d_coef,
-                        const AmpStep &amp) {
+hipError_t launch_update(int rule, int gtype, int mkind, int vkind,
+                         const Work &wk, const StepScalars &sc,
+                         const float *d_coef, const AmpStep &amp) {
   switch (gtype) {
-    case kF32: return launch_adamw_g<kF32>(mkind, vkind, wk, sc, d_coef, amp);
-    case kBF16: return launch_adamw_g<kBF16>(mkind, vkind, wk, sc, d_coef, amp);
-    case kF16: return launch_adamw_g<kF16>(mkind, vkind, wk, sc, d_coef, amp);
-    default: return hipErrorInvalidValue;
+    case kF32:
+      return launch_update_g<kF32>(rule, mkind, vkind, wk, sc, d_coef, amp);
+    case kBF16:
+      return launch_update_g<kBF16>(rule, mkind, vkind, wk, sc, d_coef, amp);
+    case kF16:
+      return launch_update_g<kF16>(rule, mkind, vkind, wk, sc, d_coef, amp);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 

@@ -23,7 +23,9 @@ def current_stream():
 class MtaList:
     """groups: sequence of (w, g, m, v) tensors.  w is float32; g float32,
     bfloat16 or float16; m and v float32 or bfloat16 (bfloat16 = packed
-    moments); all groups share the gradient type and each moment kind."""
+    moments), or None when the list's rule has no such state (SGD: neither,
+    momentum: no v); all groups share the gradient type and each moment
+    kind."""
 
     def __init__(self, groups, entries=None, gtype=None, mkind=None,
                  vkind=None):
@@ -33,22 +35,29 @@ class MtaList:
                 raise ValueError("empty list: pass gtype/mkind/vkind and "
                                  "entries=[] explicitly")
             g0, m0, v0 = self._keep[0][1], self._keep[0][2], self._keep[0][3]
-            gtype, mkind, vkind = _G[g0.dtype], _M[m0.dtype], _M[v0.dtype]
+
+            def kind(t):
+                return B.MTA_MOM_F32 if t is None else _M[t.dtype]
+
+            gtype, mkind, vkind = _G[g0.dtype], kind(m0), kind(v0)
             entries = []
             for w, g, m, v in self._keep:
                 for t in (w, g, m, v):
-                    if not t.is_cuda or not t.is_contiguous():
+                    if t is not None and (not t.is_cuda or
+                                          not t.is_contiguous()):
                         raise ValueError("tensors must be contiguous on the GPU")
                 if w.dtype != torch.float32:
                     raise TypeError("w must be float32")
-                if (_G.get(g.dtype), _M.get(m.dtype), _M.get(v.dtype)) != (
+                if (_G.get(g.dtype), kind(m), kind(v)) != (
                         gtype, mkind, vkind):
                     raise TypeError("all groups must share g, m, v dtypes")
                 n = w.numel()
-                if g.numel() != n or m.numel() != n or v.numel() != n:
+                if g.numel() != n or any(t is not None and t.numel() != n
+                                         for t in (m, v)):
                     raise ValueError("w, g, m, v must have the same numel")
-                entries.append((w.data_ptr(), g.data_ptr(), m.data_ptr(),
-                                v.data_ptr(), n))
+                entries.append((w.data_ptr(), g.data_ptr(),
+                                None if m is None else m.data_ptr(),
+                                None if v is None else v.data_ptr(), n))
         self.gtype, self.mkind, self.vkind = gtype, mkind, vkind
         self.sizes = [int(e[4]) for e in entries]
         self.handle = B.mta_list_create(entries, gtype, mkind, vkind,
@@ -101,6 +110,26 @@ class MtaList:
         B.mta_adamw_step(self.handle, hparams, t,
                          None if coef is None else coef.data_ptr(),
                          current_stream())
+
+    def step(self, opt, t, coef=None):
+        """One step of any rule: opt is a dict (kind "adamw" / "adam" /
+        "sgd" / "momentum", lr, beta1, beta2, eps, weight_decay, momentum,
+        zero_grad)."""
+        if coef is not None and (coef.dtype != torch.float32 or
+                                 not coef.is_cuda):
+            raise TypeError("coef is a float32 GPU tensor")
+        B.mta_step(self.handle, opt, t,
+                   None if coef is None else coef.data_ptr(),
+                   current_stream())
+
+    def amp_step(self, opt, amp, coef=None):
+        """Loss-scaled step of any rule (see step)."""
+        if coef is not None and (coef.dtype != torch.float32 or
+                                 not coef.is_cuda):
+            raise TypeError("coef is a float32 GPU tensor")
+        B.mta_amp_step(self.handle, opt, amp.ptr,
+                       None if coef is None else coef.data_ptr(),
+                       current_stream())
 
     def amp_clip_norm(self, max_norm, amp, norm_out, coef_out):
         """Loss-scaled norm: unscales by 1/amp.scale on the device and sets

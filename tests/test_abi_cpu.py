@@ -133,3 +133,34 @@ def test_scalars_match_the_oracle_bitwise(hp):
         want = O.scalars(*hp, t)
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (
             hp, t, got, want)
+
+
+@pytest.mark.parametrize("opt,t,msg", [
+    (dict(kind=7, lr=1e-3), 1, "unknown optimizer kind"),
+    (dict(kind="sgd", lr=1e-3, weight_decay=0.1), 1, "no weight decay"),
+    (dict(kind="momentum", lr=1e-3, weight_decay=0.1), 1, "no weight decay"),
+    (dict(kind="momentum", lr=1e-3, momentum=-0.5), 1, "momentum"),
+    (dict(kind="momentum", lr=1e-3, momentum=float("nan")), 1, "momentum"),
+    (dict(kind="sgd", lr=-1.0), 1, "lr"),
+    (dict(kind="sgd", lr=float("inf")), 1, "lr"),
+    (dict(kind="sgd", lr=1e-3), 0, "step t"),
+    (dict(kind="adam", lr=1e-3, beta1=1.0, beta2=0.999), 1, "beta1"),
+    (dict(kind="adamw", lr=1e-3, beta1=0.9, beta2=0.999, eps=-1.0), 1,
+     "eps"),
+])
+def test_step_validation_before_any_device_work(opt, t, msg):
+    # the optimizer is checked before the list: these fail on a NULL list
+    # with the optimizer's message
+    assert _err(M.mta_step, None, opt, t, None) == -1
+    assert msg in M.mta_last_error(), M.mta_last_error()
+
+
+def test_step_rejects_unknown_flags():
+    o = B.mta_opt(B.MTA_OPT_SGD, 0x10, 1e-3, 0, 0, 0, 0, 0)
+    assert _err(M.mta_step, None, o, 1, None) == -1
+    assert "flags" in M.mta_last_error()
+
+
+def test_opt_struct_layout():
+    assert ctypes.sizeof(B.mta_opt) == 56
+    assert B.mta_opt.lr.offset == 8 and B.mta_opt.momentum.offset == 48

@@ -1,0 +1,282 @@
+"""GPU parity of the other update rules of "BendTorch main.bend",
+Optimizers: Adam with coupled decay, SGD, momentum SGD, and the optional
+zeroing of the gradient, through mta_step / mta_amp_step, against
+oracle.opt_step_ / amp_opt_step_ element by element (lockstep: the device
+norm is checked against the oracle's and its coefficient fed to the
+oracle's step).  Lists for SGD carry no state buffers and lists for
+momentum no v, as a caller would hold them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_optimizer_mta_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+from parity_util import (bf16_ulp, check_amp_state, check_norm,  # noqa: E402
+                         dev_bf16_bits, dev_f32, f32_ulp, grad_np, mom_np,
+                         oracle_grads, sample_positions)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import mixed_precision_optimizer_mta_amd as M
+    M.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+EDGE = [0, 1, 2, 3, 7, 8, 9, 15, 17, 4095, 4096, 4097, 8191, 8193,
+        3 * 4096 + 5]
+
+
+def opt_for(kind, zero=False, lr=None):
+    adam = kind in ("adamw", "adam")
+    return dict(kind=kind, lr=lr if lr is not None else (3e-4 if adam
+                                                          else 0.05),
+                beta1=0.9, beta2=0.999, eps=1e-8,
+                weight_decay=0.1 if adam else 0.0, momentum=0.9,
+                zero_grad=zero)
+
+
+def uses(kind):
+    return kind != "sgd", kind in ("adamw", "adam")
+
+
+def make_rule_list(arena, kind):
+    from mixed_precision_optimizer_mta_amd import MtaList
+    wl = arena.wl
+    has_m, has_v = uses(kind)
+    ents = [(w, g, m if has_m else None, v if has_v else None, n)
+            for (w, g, m, v, n) in arena.entries()]
+    return MtaList([], entries=ents, gtype=wl.gtype, mkind=wl.mkind,
+                   vkind=wl.vkind)
+
+
+def oracle_rule_state(arena, kind, idx=None):
+    wl = arena.wl
+    has_m, has_v = uses(kind)
+    if idx is not None:
+        sel = torch.as_tensor(idx, device=arena.device)
+        views = [(arena.w[sel], arena.g[sel], arena.m[sel], arena.v[sel])]
+    else:
+        views = [tuple(arena.view(b, i) for b in "wgmv")
+                 for i in range(wl.count)]
+    out = []
+    for w, g, m, v in views:
+        out.append(O.Tensor(dev_f32(w), grad_np(g, wl.gtype),
+                            mom_np(m, wl.mkind) if has_m else None,
+                            mom_np(v, wl.vkind) if has_v else None))
+    return out
+
+
+def compare_rule(arena, ost, kind, idx=None, what=""):
+    """Bitwise comparison of w, g and the rule's state buffers."""
+    wl = arena.wl
+    has_m, has_v = uses(kind)
+    if idx is not None:
+        sel = torch.as_tensor(idx, device=arena.device)
+        views = [(arena.w[sel], arena.g[sel], arena.m[sel], arena.v[sel],
+                  len(idx))]
+    else:
+        views = [tuple(arena.view(b, i) for b in "wgmv") + (wl.sizes[i],)
+                 for i in range(wl.count)]
+    for (w, g, m, v, n), o in zip(views, ost):
+        if n == 0:
+            continue
+        assert f32_ulp(dev_f32(w), o.w).max() == 0, (what, "w")
+        assert np.array_equal(grad_np(g, wl.gtype), o.g), (what, "g")
+        for has, t, kind_, ob, name in ((has_m, m, wl.mkind, o.m, "m"),
+                                        (has_v, v, wl.vkind, o.v, "v")):
+            if not has:
+                continue
+            if kind_ == WL.MOM_BF16X2:
+                d = bf16_ulp(dev_bf16_bits(t), O.unpack_words(ob, n))
+            else:
+                d = f32_ulp(dev_f32(t), ob)
+            assert d.max() == 0, (what, name, int(d.max()))
+
+
+def rule_lockstep(wl, opt, steps, offsets=None, nsample=None,
+                  norm_steps=None, check_guards=False):
+    arena = WL.Arena(wl, "cuda", offsets)
+    arena.fill_weights()
+    kind, zero = opt["kind"], bool(opt.get("zero_grad"))
+    L = make_rule_list(arena, kind)
+    idx = None if nsample is None else sample_positions(wl, arena.offsets,
+                                                        nsample)
+    ost = oracle_rule_state(arena, kind, idx)
+    before = None
+    if check_guards:
+        before = {b: getattr(arena, b).clone() for b in "wgmv"}
+    nd = torch.full((1,), -1.0, device="cuda")
+    cd = torch.full((1,), -1.0, device="cuda")
+    for t in range(1, steps + 1):
+        arena.fill_grads(t)
+        if check_guards:
+            before["g"] = arena.g.clone()
+        for o, g in zip(ost, oracle_grads(arena, idx)):
+            o.g = g
+        full_g = None
+        if idx is not None and (norm_steps is None or t in norm_steps):
+            full_g = oracle_grads(arena)     # before a zeroing step runs
+        if wl.scale != 1.0:
+            L.scale(wl.scale, defer=True)
+        L.clip_norm(wl.max_norm, nd, cd)
+        L.step(opt, t, cd)
+        torch.cuda.synchronize()
+        ng, coef = np.float32(nd.item()), np.float32(cd.item())
+        if norm_steps is None or t in norm_steps:
+            # the oracle's step below may zero its copies: read them first
+            gs = [o.g for o in ost] if idx is None else full_g
+            check_norm(ng, coef, O.norm(gs, wl.gtype, wl.scale), wl.max_norm,
+                       f"{wl.name} {kind} t={t}")
+        O.opt_step_(ost, opt, wl.gtype, wl.mkind, wl.vkind, t, s=wl.scale,
+                    coef=coef, zero=zero)
+        compare_rule(arena, ost, kind, idx, f"{wl.name} {kind} t={t}")
+        if check_guards:
+            inside = torch.zeros(arena.total, dtype=torch.bool,
+                                 device="cuda")
+            for o, n in zip(arena.offsets, wl.sizes):
+                inside[o:o + n] = True
+            has_m, has_v = uses(kind)
+            for b in "wgmv":
+                now = getattr(arena, b)
+                ity = torch.int32 if now.dtype == torch.float32 else \
+                    torch.int16
+                diff = now.view(ity) != before[b].view(ity)
+                if b in "wg" or (b == "m" and has_m) or (b == "v" and has_v):
+                    diff = diff & ~inside    # only inside its tensors
+                assert not bool(diff.any()), f"{kind}: {b} written outside"
+    L.close()
+    print(f"{wl.name} {kind} zero={zero}: {steps} steps bitwise",
+          flush=True)
+
+
+RULE_CASES = [(k, g) for k in ("adam", "sgd", "momentum") for g in (0, 1, 2)]
+
+
+@pytest.mark.parametrize("zero", [False, True])
+@pytest.mark.parametrize("kind,gtype", RULE_CASES)
+def test_rules_edge_sizes(kind, gtype, zero):
+    wl = WL.Workload(f"edges_{kind}", EDGE, gtype, 0, 0, steps=3,
+                     g_sigma=0.3, scale=0.5 if gtype else 1.0, ident=31)
+    rule_lockstep(wl, opt_for(kind, zero), 3, check_guards=True)
+
+
+@pytest.mark.parametrize("mkind,vkind", [(1, 1), (1, 0), (0, 1)])
+def test_adam_packed_moments(mkind, vkind):
+    wl = WL.Workload("adam_packed", EDGE, 1, mkind, vkind, steps=3,
+                     g_sigma=0.3, ident=32)
+    rule_lockstep(wl, opt_for("adam", zero=True), 3, check_guards=True)
+
+
+def test_adamw_zero_grad_keeps_the_update():
+    wl = WL.Workload("adamw_zero", EDGE, 2, 1, 0, steps=3, g_sigma=0.3,
+                     scale=0.25, ident=33)
+    rule_lockstep(wl, opt_for("adamw", zero=True), 3, check_guards=True)
+
+
+@pytest.mark.parametrize("kind", ["adam", "sgd", "momentum"])
+def test_rules_unaligned_tensors(kind):
+    sizes = [5000, 4096, 33, 9000]
+    offsets, pos = [], 0
+    for n in sizes:
+        offsets.append(pos + 1)
+        pos += -(-(n + 1) // 8) * 8 + 8
+    wl = WL.Workload("unaligned_rules", sizes, 1, 0, 0, steps=2, ident=34)
+    rule_lockstep(wl, opt_for(kind, zero=True), 2, offsets=offsets,
+                  check_guards=True)
+
+
+def test_sgd_and_momentum_write_their_weight_copies():
+    for kind in ("sgd", "momentum"):
+        wl = WL.Workload("copies_rules", [4096 * 2 + 3, 100], 0, 0, 0,
+                         steps=1, ident=35)
+        arena = WL.Arena(wl, "cuda")
+        arena.fill_weights()
+        arena.fill_grads(1)
+        L = make_rule_list(arena, kind)
+        copies = torch.zeros(arena.total, dtype=torch.bfloat16,
+                             device="cuda")
+        L.set_weight_copies([copies[o:o + n] for o, n in
+                             zip(arena.offsets, wl.sizes)])
+        L.step(opt_for(kind), 1)
+        torch.cuda.synchronize()
+        for o, n in zip(arena.offsets, wl.sizes):
+            want = O.bf16_of_f32(dev_f32(arena.w[o:o + n]))
+            assert np.array_equal(dev_bf16_bits(copies[o:o + n]), want)
+        L.close()
+
+
+@pytest.mark.parametrize("kind", O.OPT_KINDS)
+def test_amp_rules_with_skip_and_zeroing(kind):
+    from mixed_precision_optimizer_mta_amd import AmpState
+    wl = WL.Workload("amp_rules", [4096 * 3 + 7, 999, 1], WL.F16, 0, 0,
+                     steps=6, g_mult=1024.0, ident=36)
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_weights()
+    L = make_rule_list(arena, kind)
+    ost = oracle_rule_state(arena, kind)
+    opt = opt_for(kind, zero=True)
+    amp_d, amp_o = AmpState(1024.0), O.AmpState(1024.0)
+    cd = torch.zeros(1, device="cuda")
+    nd = torch.zeros(1, device="cuda")
+    for t in range(1, 7):
+        arena.fill_grads(t)
+        if t in (2, 5):
+            arena.g[arena.offsets[1] + 9] = float("inf")
+        for o, g in zip(ost, oracle_grads(arena)):
+            o.g = g
+        L.amp_clip_norm(1.0, amp_d, nd, cd)
+        L.amp_step(opt, amp_d, cd)
+        amp_d.update(2.0, 0.5, 2)
+        torch.cuda.synchronize()
+        coef = np.float32(cd.item())
+        _, _, found = O.amp_opt_step_(ost, opt, wl.gtype, 0, 0, amp_o, 1.0,
+                                      coef=coef, zero=True)
+        assert found == (t in (2, 5))
+        amp_o.update(2.0, 0.5, 2)
+        check_amp_state(amp_d.read(), amp_o, f"{kind} t={t}")
+        compare_rule(arena, ost, kind, what=f"amp {kind} t={t}")
+    L.close()
+
+
+def test_state_buffer_checks():
+    from mixed_precision_optimizer_mta_amd import MtaError
+    wl = WL.Workload("checks", [100, 200], 0, 1, 0, steps=1, ident=37)
+    arena = WL.Arena(wl, "cuda")
+    sgd_list = make_rule_list(arena, "sgd")
+    assert sgd_list.info()["state_buffers"] == 0
+    for kind in ("adamw", "adam", "momentum"):
+        with pytest.raises(MtaError) as e:
+            sgd_list.step(opt_for(kind), 1)
+        assert e.value.code == -6, kind          # MTA_ESTATE
+    with pytest.raises(MtaError) as e:
+        sgd_list.adamw_step(opt_for("adamw"), 1)
+    assert e.value.code == -6
+    sgd_list.close()
+    mom_list = make_rule_list(arena, "momentum")  # packed m (mkind = 1)
+    assert mom_list.info()["state_buffers"] == 1
+    with pytest.raises(MtaError) as e:
+        mom_list.step(opt_for("momentum"), 1)
+    assert e.value.code == -3                    # MTA_EDTYPE
+    mom_list.close()
+    from mixed_precision_optimizer_mta_amd import MtaList
+    ents = arena.entries()
+    mixed = [ents[0], (ents[1][0], ents[1][1], None, None, ents[1][4])]
+    with pytest.raises(MtaError) as e:
+        MtaList([], entries=mixed, gtype=0, mkind=1, vkind=0)
+    assert e.value.code == -1
+
+
+@pytest.mark.parametrize("kind", ["adam", "sgd", "momentum"])
+def test_full_gpt2_124m_rules_sampled(kind):
+    wl = WL.get("gpt2_124m")
+    if kind != "adam":
+        wl.weight_decay = 0.0
+    rule_lockstep(wl, opt_for(kind, zero=(kind == "momentum")), 3,
+                  nsample=1 << 18, norm_steps={1, 3})
