@@ -58,6 +58,13 @@ def opt_of(wl, kind, zero):
                 momentum=0.9, zero_grad=zero)
 
 
+def traffic_key(wl, kind, zero):
+    """The key of a configuration in profiles/traffic.json."""
+    if kind == "adamw" and not zero:
+        return wl.name
+    return f"{wl.name}+{kind}" + ("+zero" if zero else "")
+
+
 def update_bytes(wl, kind, zero, copy):
     """Algorithmic HBM bytes per parameter of one update launch."""
     gb = 4 if wl.gtype == 0 else 2
@@ -257,8 +264,9 @@ def main():
     norm_bytes = wl.n * bpp["norm"]
     value = wl.n * args.steps / (host_s)
     achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
-    traffic = (None if args.weight_copy or general
-               else measured_traffic(wl.name, kernel))
+    traffic = (None if args.weight_copy
+               else measured_traffic(traffic_key(wl, args.opt, args.zero_grad),
+                                     kernel))
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) per "
                   "fused clip+AdamW step",
