@@ -148,6 +148,11 @@ def main():
                     help="update rule (mta_step); adamw runs mta_adamw_step")
     ap.add_argument("--zero-grad", action="store_true",
                     help="also zero every gradient in the update launch")
+    ap.add_argument("--graph", action="store_true",
+                    help="loss-scaled workloads only: after the eager pass, "
+                         "capture one whole step in a HIP graph and time K "
+                         "replays (value and ms_per_step then come from the "
+                         "replays; per-kernel times from the eager pass)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB, 5 times: "
                          "the known-size kernel that scales the HBM byte "
@@ -180,6 +185,11 @@ def main():
         return
     M.lib()
     wl = WL.get(args.workload)
+    if args.graph and not wl.amp:
+        print("--graph needs a loss-scaled workload (its step counter and "
+              "scale live on the device, so a captured step can be "
+              "replayed): e.g. --workload gpt2_124m_f16amp", file=sys.stderr)
+        sys.exit(2)
     arena = WL.Arena(wl, "cuda")
     arena.fill_weights()
     arena.fill_grads(1)
@@ -254,6 +264,30 @@ def main():
     if amp is not None:      # every timed step was taken, none skipped
         st = amp.read()
         assert st["step"] == t and st["found_inf"] == 0.0, st
+    if args.graph:
+        # one whole step captured once; every replay reads t and the scale
+        # from the device state, so replays are successive steps
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        h0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        host_s = time.perf_counter() - h0
+        dev_ms = start.elapsed_time(end)
+        ms_per_step = dev_ms / args.steps
+        st = amp.read()
+        assert st["step"] == t + args.warmup + args.steps, st
+        assert st["found_inf"] == 0.0, st
 
     bpp = {"norm": wl.bytes_per_param()["norm"],
            "update": update_bytes(wl, args.opt, args.zero_grad,
@@ -291,6 +325,7 @@ def main():
             "grid_norm": info["grid_norm"], "parallelism": "single GPU",
             "weight_copy": bool(args.weight_copy),
             "optimizer": args.opt, "zero_grad": bool(args.zero_grad),
+            "graph": bool(args.graph),
         },
         "step_gbs": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9,
         "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9
