@@ -20,6 +20,15 @@
  *                   bfloat16 moments as in adamh_l / adamhv_l; bias
  *                   correction step = lr/(1-b1^t), bc2 = sqrt(1-b2^t) as in
  *                   Opt.at and the Training section, t = 1 on the first step).
+ *   mta_step        any update rule of that "Optimizers" section (the Opt
+ *                   type): AdamW, Adam with coupled decay (adam_grad), SGD
+ *                   (sgd_l), momentum SGD (mom_l); optionally zeroing the
+ *                   gradient as every step loop there does.
+ *   mta_amp_*       the same steps under a dynamic loss scale kept in device
+ *                   memory (Mica: the unscaling a float16 step needs), with
+ *                   PyTorch's GradScaler rule for skipping and rescaling.
+ *   mta_list_set_weight_copies  bfloat16 copies of the new weights (Mica,
+ *                   section "float16 and bfloat16, whole").
  *
  * Memory and ownership.  Every w, g, m, v pointer is device memory owned by
  * the caller (for example a PyTorch tensor's data pointer).  The library never
@@ -128,7 +137,7 @@ typedef struct {
   int64_t elements;    /* sum of n */
   int64_t tiles;       /* work tiles (each covers up to tile_elems of one tensor) */
   int32_t tile_elems;  /* elements per tile */
-  int32_t grid_update; /* workgroups of the AdamW / scale launch */
+  int32_t grid_update; /* workgroups of an update / scale launch */
   int32_t grid_norm;   /* workgroups of the norm launch (= norm partials) */
   int32_t device;      /* HIP device the list lives on */
   int32_t vector_tensors; /* tensors that take the 16-byte vector path */
