@@ -77,6 +77,71 @@ def update_bytes(wl, kind, zero, copy):
     return b + (gb if zero else 0) + (2 if copy else 0)
 
 
+def ceiling(wl, reps=10):
+    """Best HBM rates of the ceiling probes (libmta_probe.so: no optimizer
+    arithmetic) on buffers of the workload's size: a stream with the update's
+    exact bytes (read w, g, m, v; write w, m, v), a read-only stream and a
+    copy, each over grids of 1, 2, 4 and 8 workgroups per CU."""
+    import ctypes
+
+    import torch
+
+    from mixed_precision_optimizer_mta_amd import build as MB
+    P = ctypes.CDLL(MB.PROBE_LIB)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    P.mta_probe_mix.argtypes = [vp, vp, vp, vp, i64, c_int, c_int, c_int,
+                                c_int, vp]
+    P.mta_probe_read.argtypes = [vp, i64, vp, c_int, vp]
+    P.mta_probe_copy.argtypes = [vp, vp, i64, c_int, vp]
+    n = -(-wl.n // 4096) * 4096
+    gb = 4 if wl.gtype == 0 else 2
+    mb = 2 if wl.mkind == 1 else 4
+    vb = 2 if wl.vkind == 1 else 4
+
+    def buf(b):
+        return torch.zeros(n, device="cuda",
+                           dtype=torch.float32 if b == 4 else torch.int16)
+
+    w, g, m, v = buf(4), buf(gb), buf(mb), buf(vb)
+    w2 = buf(4)
+    sink = torch.zeros(256, device="cuda")
+    s = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def best(launch, nbytes):
+        out = (0.0, 0)
+        for bpc in (1, 2, 4, 8):
+            grid = cus * bpc
+            for _ in range(2):
+                assert launch(grid) == 0
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(reps):
+                launch(grid)
+            b.record(s)
+            torch.cuda.synchronize()
+            gbs = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+            out = max(out, (gbs, bpc))
+        return out
+
+    sp = s.cuda_stream
+    mix = best(lambda gr: P.mta_probe_mix(w.data_ptr(), g.data_ptr(),
+                                          m.data_ptr(), v.data_ptr(), n, gb,
+                                          mb, vb, gr, sp),
+               n * (4 + gb + mb + vb + 4 + mb + vb))
+    rd = best(lambda gr: P.mta_probe_read(w.data_ptr(), n, sink.data_ptr(),
+                                          gr, sp), n * 4)
+    cp = best(lambda gr: P.mta_probe_copy(w.data_ptr(), w2.data_ptr(), n, gr,
+                                          sp), n * 8)
+    return {"probe": "libmta_probe.so, trivial arithmetic, best of 1/2/4/8 "
+                     "workgroups per CU",
+            "update_mix_gbs": mix[0], "update_mix_frac": mix[0] / HBM_PEAK_GBS,
+            "update_mix_blocks_per_cu": mix[1],
+            "read_gbs": rd[0], "read_frac": rd[0] / HBM_PEAK_GBS,
+            "copy_gbs": cp[0], "copy_frac": cp[0] / HBM_PEAK_GBS}
+
+
 def cpu_baseline(arena, wl, steps, opt=None):
     """The oracle as it stands (single thread) on host copies of the same
     list: `steps` whole steps (norm + update)."""
@@ -153,6 +218,9 @@ def main():
                          "capture one whole step in a HIP graph and time K "
                          "replays (value and ms_per_step then come from the "
                          "replays; per-kernel times from the eager pass)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the HBM ceiling probes (the update's byte "
+                         "mix with trivial arithmetic, read-only, copy)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB, 5 times: "
                          "the known-size kernel that scales the HBM byte "
@@ -341,6 +409,11 @@ def main():
         },
     }
     L.close()
+    if not args.no_ceiling and args.opt in ("adamw", "adam") and \
+            not args.zero_grad and not args.weight_copy:
+        c = ceiling(wl)
+        c["update_of_mix"] = achieved / c["update_mix_gbs"]
+        out["ceiling"] = c
     if args.cpu_steps > 0:
         out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)
     print(json.dumps(out), flush=True)

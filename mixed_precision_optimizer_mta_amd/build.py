@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmta.so")
 SOURCES = [os.path.join(CSRC, "mta_kernels.hip"),
            os.path.join(CSRC, "mta_host.cpp")]
+# HBM ceiling probes (measurement only; bench.py --ceiling loads them)
+PROBE_LIB = os.path.join(HERE, "libmta_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "mta_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -30,9 +33,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
 
 
 def build(verbose=False):
-    """Compile libmta.so; always recompiles.  Returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
+    """Compile libmta.so and the probe library; always recompiles.  Returns
+    libmta.so's path."""
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
+
+
+def _compile(lib, sources, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,8 +51,8 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
