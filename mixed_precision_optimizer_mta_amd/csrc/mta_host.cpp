@@ -555,6 +555,19 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
     e = hipMemcpyAsync(L->d_stiles, stiles.data(),
                        stiles.size() * sizeof(mta::StepTile),
                        hipMemcpyHostToDevice, s);
+  // every norm partial slot starts empty (the norm kernel re-arms them)
+  std::vector<uint64_t> empty_slots;
+  try {
+    empty_slots.assign(static_cast<size_t>(L->grid_norm), mta::kNormSlotEmpty);
+  } catch (const std::bad_alloc &) {
+    (void)hipFree(L->dev_block);
+    delete L;
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(L->d_partials, empty_slots.data(),
+                       empty_slots.size() * sizeof(uint64_t),
+                       hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(L->d_ticket, 0, 256, s);
   // the host vectors die with this call: wait for the copies
   if (e == hipSuccess) e = hipStreamSynchronize(s);

@@ -71,7 +71,11 @@ struct Work {
   hipStream_t stream;
 };
 
-// Norm scratch: one float64 partial per norm workgroup, then the ticket.
+// Norm scratch: one float64 partial slot per norm workgroup, then the
+// ticket.  A slot holds kNormSlotEmpty (the host fills them at list
+// creation) except between the storing workgroup and the finishing wave of
+// one launch, which re-arms it.
+constexpr uint64_t kNormSlotEmpty = 0xFFF0DEADBEEF0001ull;
 struct NormScratch {
   double *partials;
   unsigned int *ticket;

@@ -625,6 +625,15 @@ __device__ __forceinline__ double wave_sum(double x) {
          (readlane_f64(x, 32) + readlane_f64(x, 48));
 }
 
+// An empty partial slot: a negative signalling NaN.  No arithmetic result
+// has these bits (a NaN a float64 operation returns is quiet), so a stored
+// partial can never be mistaken for it.
+constexpr uint64_t kEmptySlot = kNormSlotEmpty;
+// Reloads of one slot before the finishing wave gives up on it (the sum then
+// carries the NaN of kEmptySlot).  A store made before the storing
+// workgroup's ticket is normally visible by the first load.
+constexpr uint32_t kSpinLimit = 1u << 16;
+
 template <int D>
 __global__ void __launch_bounds__(kBlock)
 k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
@@ -733,12 +742,17 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
   const double wsum = wave_sum(mine);
   if (lane == 0) wave_part[wave] = wsum;
   __syncthreads();
+  // Each partial slot is its own flag: an agent-scope atomic holding
+  // kEmptySlot until this workgroup's partial is stored into it.  No release
+  // fence is needed (a fence per workgroup costs ~47 ns, serialized across
+  // the grid); the ticket only elects the finishing workgroup.
+  uint64_t *const slots = reinterpret_cast<uint64_t *>(partials);
   if (threadIdx.x == 0) {
-    partials[blockIdx.x] = (wave_part[0] + wave_part[1]) +
-                           (wave_part[2] + wave_part[3]);
-    // release (agent scope): the partial is visible before the ticket moves;
-    // no acquire here, so the other workgroups keep their caches
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const double part = (wave_part[0] + wave_part[1]) +
+                        (wave_part[2] + wave_part[3]);
+    __hip_atomic_store(slots + blockIdx.x,
+                       static_cast<uint64_t>(__double_as_longlong(part)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned int prev = __hip_atomic_fetch_add(
         ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == gridDim.x - 1);
@@ -746,23 +760,38 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
   __syncthreads();
   if (!is_last) return;
 
-  // Stage 2: the finishing wave.
+  // Stage 2: the finishing wave.  Every other workgroup has stored its
+  // partial (each did so before taking its ticket), but a store may not be
+  // visible yet: lane l reads slots l, l+64, ... with atomic loads and
+  // reloads a slot that still holds kEmptySlot, at most kSpinLimit times,
+  // then sums them in that order and re-arms each slot for the next call.
+  // kEmptySlot is a NaN, so a partial that never arrived makes the norm NaN:
+  // loud, never silent.
   if (wave != 0) return;
-  // acquire (agent scope): every other workgroup's partial is visible
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // lane l sums partials l, l+64, l+128, ... in that order; each batch of
-  // eight loads is issued before the first add
   constexpr int kBatch = 8;
   double a = 0.0;
   for (uint32_t i0 = 0; i0 < gridDim.x; i0 += 64 * kBatch) {
-    double p[kBatch];
+    uint64_t raw[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const uint32_t i = i0 + q * 64 + lane;
-      p[q] = i < gridDim.x ? partials[i] : 0.0;
+      raw[q] = i < gridDim.x
+                   ? __hip_atomic_load(slots + i, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0ull;  // the bits of +0.0
     }
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) a += p[q];
+    for (int q = 0; q < kBatch; ++q) {
+      const uint32_t i = i0 + q * 64 + lane;
+      for (uint32_t spin = 0; raw[q] == kEmptySlot && spin < kSpinLimit;
+           ++spin)
+        raw[q] = __hip_atomic_load(slots + i, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      a += __longlong_as_double(static_cast<long long>(raw[q]));
+      if (i < gridDim.x)
+        __hip_atomic_store(slots + i, kEmptySlot, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   const double total = wave_sum(a);
   if (lane == 0) {
