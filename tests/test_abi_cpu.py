@@ -164,3 +164,37 @@ def test_step_rejects_unknown_flags():
 def test_opt_struct_layout():
     assert ctypes.sizeof(B.mta_opt) == 56
     assert B.mta_opt.lr.offset == 8 and B.mta_opt.momentum.offset == 48
+
+
+def test_last_error_is_per_host_thread():
+    # each thread's failing call leaves its own message; another thread's
+    # failure does not overwrite it
+    import threading
+    barrier = threading.Barrier(8)
+    results = {}
+
+    def worker(k):
+        barrier.wait()
+        lr = -1.0 - k            # a distinct invalid lr per thread
+        try:
+            M.mta_adamw_scalars((lr, 0.9, 0.999, 1e-8, 0.0), 1)
+        except M.MtaError:
+            pass
+        barrier.wait()           # every thread has failed by now
+        results[k] = M.mta_last_error()
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for k in range(8):
+        assert f"(got {-1.0 - k:g})" in results[k], (k, results[k])
+
+
+def test_success_clears_the_last_error():
+    with pytest.raises(M.MtaError):
+        M.mta_adamw_scalars((-1.0, 0.9, 0.999, 1e-8, 0.0), 1)
+    assert M.mta_last_error() != ""
+    M.mta_adamw_scalars((1e-3, 0.9, 0.999, 1e-8, 0.0), 1)
+    assert M.mta_last_error() == ""
