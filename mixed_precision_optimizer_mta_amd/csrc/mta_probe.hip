@@ -37,7 +37,6 @@ __device__ __forceinline__ pf4 mix(pf4 a, pf4 b) { return a + b; }
 __device__ __forceinline__ pu2 mix(pu2 a, pf4 b) {
   return a + pu2{__float_as_uint(b.x), __float_as_uint(b.y)};
 }
-__device__ __forceinline__ pu2 mix(pu2 a, pu2 b) { return a + b; }
 __device__ __forceinline__ pf4 mix(pf4 a, pu2 b) {
   return a + pf4{__uint_as_float(b.x), __uint_as_float(b.y), 0.0f, 0.0f};
 }
