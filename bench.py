@@ -203,8 +203,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gpt2_124m")
-    ap.add_argument("--cpu-steps", type=int, default=3,
-                    help="oracle steps of the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-steps", type=int, default=30,
+                    help="oracle steps of the CPU baseline (0 = skip); the "
+                         "default is about 11 s of one host core on the "
+                         "124M list")
     ap.add_argument("--weight-copy", action="store_true",
                     help="also write a bfloat16 copy of every updated weight "
                          "(mta_list_set_weight_copies): +2 B/param")
