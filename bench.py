@@ -142,6 +142,80 @@ def ceiling(wl, reps=10):
             "copy_gbs": cp[0], "copy_frac": cp[0] / HBM_PEAK_GBS}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_parallel(arena, wl, steps, threads):
+    """The same oracle functions, unchanged, run by `threads` host threads
+    over disjoint element ranges of the list (AdamW, deferred unscale, joint
+    clip): each thread's float64 sum-of-squares state for its ranges, the
+    states summed in thread order, then every thread's AdamW on its ranges.
+    Plain AdamW workloads only."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    def host(t, bits16):
+        t = t.detach().cpu()
+        if bits16:
+            return t.view(torch.int16).numpy().view(np.uint16).copy()
+        return t.numpy().copy()
+
+    chunk = max(4096, (wl.n // (threads * 8)) // 2 * 2)  # even: packed words
+    parts = []
+    for i in range(wl.count):
+        n = wl.sizes[i]
+        if n == 0:
+            continue
+        w = host(arena.view("w", i), False)
+        g = host(arena.view("g", i), wl.gtype != 0)
+        m = host(arena.view("m", i), wl.mkind == 1)
+        v = host(arena.view("v", i), wl.vkind == 1)
+        m = O.pack_halves(m) if wl.mkind == 1 else m
+        v = O.pack_halves(v) if wl.vkind == 1 else v
+        for a in range(0, n, chunk):
+            b = min(n, a + chunk)
+            mm = m[a // 2:(b + 1) // 2] if wl.mkind == 1 else m[a:b]
+            vv = v[a // 2:(b + 1) // 2] if wl.vkind == 1 else v[a:b]
+            parts.append(O.Tensor(w[a:b], g[a:b], mm, vv))
+    groups = [parts[k::threads] for k in range(threads)]
+    O.lib()
+    pool = ThreadPoolExecutor(threads)
+    t0 = time.perf_counter()
+    for t in range(1, steps + 1):
+        sums = list(pool.map(
+            lambda grp: O.sumsq([x.g for x in grp], wl.gtype, wl.scale),
+            groups))
+        nrm = float(np.sqrt(sum(sums)))
+        c = O.clip_coef(wl.max_norm, np.float32(nrm))
+        sc = O.scalars(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, t)
+
+        def update(grp):
+            for x in grp:
+                O.adamw_(x.w, x.g, x.m, x.v, wl.gtype, wl.mkind, wl.vkind,
+                         sc, wl.scale, c)
+        list(pool.map(update, groups))
+    dt = time.perf_counter() - t0
+    pool.shutdown()
+    return {"value": wl.n * steps / dt, "unit": "params/s", "cores": threads,
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"{steps} whole steps of the full {wl.n:,}-param "
+                      f"list, the oracle's own functions over disjoint "
+                      f"ranges of {chunk:,} elements on {threads} host "
+                      f"threads, {dt:.2f} s"}
+
+
 def cpu_baseline(arena, wl, steps, opt=None):
     """The oracle as it stands (single thread) on host copies of the same
     list: `steps` whole steps (norm + update)."""
@@ -189,7 +263,7 @@ def cpu_baseline(arena, wl, steps, opt=None):
                     max_norm=wl.max_norm)
     dt = time.perf_counter() - t0
     return {"value": wl.n * steps / dt, "unit": "params/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{steps} whole steps (joint norm + clip + "
                       f"{opt['kind'] if opt else 'adamw'} update"
                       f"{' + loss-scale update' if amp else ''}) of "
@@ -330,6 +404,10 @@ def main():
     ms_per_step = dev_ms / args.steps
     norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     adamw_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(q * len(per_step)))]
     assert torch.isfinite(norm_d).all() and torch.isfinite(coef_d).all()
     if amp is not None:      # every timed step was taken, none skipped
         st = amp.read()
@@ -401,6 +479,7 @@ def main():
         "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9
         / HBM_PEAK_GBS,
         "device_ms_per_step": ms_per_step,
+        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "kernels_ms": {"k_sumsq": norm_ms, kernel: adamw_ms},
         "norm_gbs": norm_bytes / (norm_ms * 1e-3) / 1e9,
         "roofline": {
@@ -418,6 +497,10 @@ def main():
         out["ceiling"] = c
     if args.cpu_steps > 0:
         out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)
+        if not general and not wl.amp and not args.weight_copy:
+            threads = max(1, min(16, os.cpu_count() or 1))
+            out["cpu_baseline_parallel"] = cpu_baseline_parallel(
+                arena, wl, args.cpu_steps, threads)
     print(json.dumps(out), flush=True)
 
 

@@ -282,3 +282,53 @@ def test_full_ragged_sampled():
     wl = WL.get("ragged")
     worst = lockstep(wl, wl.steps, nsample=1 << 20)
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+@pytest.mark.parametrize("name", ["gpt2_124m", "gpt2_124m_bf16g", "gpt2_xl",
+                                  "ragged"])
+def test_independent_mode_report(name):
+    """Informational run: the oracle uses its own clip coefficient, from
+    f32 of its own norm, instead of the device's.  The device and oracle
+    norms agree to well within 1e-6, so the runs stay within a few ulp;
+    the distances are printed."""
+    from parity_util import bf16_ulp, dev_bf16_bits, dev_f32, f32_ulp
+    wl = small(name)
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_weights()
+    L = make_list(arena)
+    ostate = oracle_state(arena)
+    nd = torch.zeros(1, device="cuda")
+    cd = torch.zeros(1, device="cuda")
+    worst = {"w": 0, "m": 0, "v": 0, "coef": 0}
+    for t in range(1, 6):
+        arena.fill_grads(t)
+        for o, g in zip(ostate, oracle_grads(arena)):
+            o.g = g
+        if wl.scale != 1.0:
+            L.scale(wl.scale, defer=True)
+        L.clip_norm(wl.max_norm, nd, cd)
+        L.adamw_step(wl.hparams, t, cd)
+        torch.cuda.synchronize()
+        _, c_own = O.step_(ostate, wl.gtype, wl.mkind, wl.vkind, wl.lr,
+                           wl.beta1, wl.beta2, wl.eps, wl.weight_decay, t,
+                           s=wl.scale, max_norm=wl.max_norm)
+        worst["coef"] = max(worst["coef"], int(f32_ulp(
+            np.array([cd.item()], np.float32),
+            np.array([c_own], np.float32)).max()))
+        for i, o in enumerate(ostate):
+            n = wl.sizes[i]
+            if n == 0:
+                continue
+            worst["w"] = max(worst["w"], int(f32_ulp(
+                dev_f32(arena.view("w", i)), o.w).max()))
+            for b, kind, ob in (("m", wl.mkind, o.m), ("v", wl.vkind, o.v)):
+                dv = arena.view(b, i)
+                if kind == WL.MOM_BF16X2:
+                    d = bf16_ulp(dev_bf16_bits(dv), O.unpack_words(ob, n))
+                else:
+                    d = f32_ulp(dev_f32(dv), ob)
+                worst[b] = max(worst[b], int(d.max()))
+    L.close()
+    print(f"independent mode {name}: worst {worst}", flush=True)
+    assert worst["coef"] <= 8 and worst["w"] <= 4, worst
+    assert worst["m"] <= 64 and worst["v"] <= 64, worst
