@@ -73,15 +73,12 @@ bool debug_sync() {
 
 // Workgroups per compute unit of the persistent launches.  A workgroup is
 // four wave64s; the grid walks the tile table with a grid stride.  Measured
-// on gfx950 (MI355X): the update streams best with one long-lived workgroup
-// per CU that keeps two tiles of loads in flight (fewer concurrent streams,
-// better HBM page locality).  The norm pays one release fence and one ticket
-// atomic per workgroup, so it wants few workgroups, each with two tiles of
-// loads in flight: one per CU for float32 gradients, two for 16-bit ones
-// (half the bytes per tile, so twice the workgroups for the same bytes in
-// flight).
-// The same holds for the lighter SGD and momentum streams: on gpt2-124M-sized
-// lists one workgroup per CU measured 3-4% above two, three or four.
+// on gfx950 (MI355X): every update rule streams best with one long-lived
+// workgroup per CU that keeps two tiles of loads in flight (fewer concurrent
+// streams, better HBM page locality; two, three or four per CU measured
+// 3-9% slower).  The norm keeps two tiles of loads in flight per workgroup:
+// one workgroup per CU for float32 gradients, two for 16-bit ones (half the
+// bytes per tile, so twice the workgroups for the same bytes in flight).
 constexpr int kUpdateBlocksPerCu = 1;
 constexpr int kNormBlocksPerCuF32 = 1;
 constexpr int kNormBlocksPerCu16 = 2;

@@ -20,7 +20,7 @@ constexpr int kTileElems = 4096;  // 16 elements per thread
 // its buffers' addresses already offset to the tile's first element, the
 // number of elements in it, and whether all of them are 16-byte aligned.  One
 // scalar load of the record is all a workgroup needs before it can issue the
-// tile's vector loads (no second, dependent lookup of a tensor descriptor).
+// tile's vector loads (no second, dependent lookup of a per-tensor record).
 
 // k_sumsq and k_scale read only the gradient.
 struct GradTile {
