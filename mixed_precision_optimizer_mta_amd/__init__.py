@@ -15,3 +15,4 @@ from ._binding import (  # noqa: F401
     mta_last_error, mta_list_create, mta_list_destroy, mta_list_info,
     mta_list_set_weight_copies, mta_scale, mta_step)
 from .torch_list import AmpState, MtaList  # noqa: F401
+from .optim import MtaOptimizer  # noqa: F401

@@ -1,0 +1,170 @@
+"""MtaOptimizer: a torch.optim-style front end over the C ABI.
+
+Marshalling only, like MtaList: it allocates the state buffers a rule needs
+(float32, or bfloat16 for packed Adam-family moments), keeps them in
+``self.state`` under PyTorch's names (exp_avg, exp_avg_sq, momentum_buffer)
+so ``state_dict()`` / ``load_state_dict()`` work, and drives one list per
+parameter group.  A step is:
+
+  * with ``max_norm``: one mta_clip_norm over every gradient of every group
+    (a list with no state buffers), the joint norm and coefficient left in
+    device tensors (``last_norm``, ``last_coef``);
+  * one mta_step per parameter group with that coefficient.
+
+Every step of the arithmetic runs in libmta.  Parameters are float32 CUDA
+tensors; their gradients share one type (float32, bfloat16 or float16).  The
+device tables are rebuilt whenever a parameter, gradient or state buffer
+moved (``zero_grad(set_to_none=True)`` lets PyTorch reallocate gradients;
+``zero_grad=True`` here instead zeroes them inside the update launch).
+"""
+import torch
+
+from . import _binding as B
+from .torch_list import MtaList
+
+_KINDS = ("adamw", "adam", "sgd", "momentum")
+
+
+class MtaOptimizer(torch.optim.Optimizer):
+    """kind: "adamw" (decoupled decay), "adam" (coupled decay), "sgd",
+    "momentum" (SGD with momentum, no dampening, not Nesterov)."""
+
+    def __init__(self, params, kind="adamw", lr=1e-3, betas=(0.9, 0.999),
+                 eps=1e-8, weight_decay=0.0, momentum=0.0, max_norm=None,
+                 packed_moments=False, zero_grad=False):
+        if kind not in _KINDS:
+            raise ValueError(f"kind must be one of {_KINDS}")
+        if packed_moments and kind not in ("adamw", "adam"):
+            raise ValueError("packed moments are for the Adam family")
+        defaults = dict(lr=lr, betas=tuple(betas), eps=eps,
+                        weight_decay=weight_decay, momentum=momentum)
+        super().__init__(params, defaults)
+        self.kind = kind
+        self.max_norm = max_norm
+        self.packed = bool(packed_moments)
+        self.zero_grad_in_step = bool(zero_grad)
+        self._lists = {}       # group index -> (pointer key, MtaList)
+        self._norm_list = None  # (pointer key, MtaList)
+        self.last_norm = None
+        self.last_coef = None
+
+    # -- state buffers ----------------------------------------------------
+    def _state_buffers(self, p):
+        st = self.state[p]
+        mdt = torch.bfloat16 if self.packed else torch.float32
+        if self.kind in ("adamw", "adam"):
+            if "exp_avg" not in st:
+                st["exp_avg"] = torch.zeros_like(p, dtype=mdt)
+                st["exp_avg_sq"] = torch.zeros_like(p, dtype=mdt)
+                st["step"] = 0
+            for name in ("exp_avg", "exp_avg_sq"):
+                # load_state_dict casts floating state to the parameter's
+                # dtype; a bfloat16 moment comes back exactly
+                if st[name].dtype != mdt:
+                    st[name] = st[name].to(mdt).contiguous()
+            return st["exp_avg"], st["exp_avg_sq"]
+        if self.kind == "momentum":
+            if "momentum_buffer" not in st:
+                st["momentum_buffer"] = torch.zeros_like(p)
+                st["step"] = 0
+            return st["momentum_buffer"], None
+        st.setdefault("step", 0)
+        return None, None
+
+    @staticmethod
+    def _check(p):
+        if p.dtype != torch.float32 or not p.is_cuda or \
+                not p.is_contiguous():
+            raise TypeError("parameters must be contiguous float32 CUDA "
+                            "tensors")
+        g = p.grad
+        if g is None or not g.is_cuda or not g.is_contiguous():
+            raise ValueError("every parameter needs a contiguous CUDA "
+                             "gradient before step()")
+
+    def _group_list(self, k, params):
+        groups, key = [], []
+        for p in params:
+            m, v = self._state_buffers(p)
+            groups.append((p, p.grad, m, v))
+            key.append((p.data_ptr(), p.grad.data_ptr(),
+                        None if m is None else m.data_ptr(),
+                        None if v is None else v.data_ptr(), p.numel(),
+                        p.grad.dtype))
+        key = tuple(key)
+        cached = self._lists.get(k)
+        if cached is None or cached[0] != key:
+            if cached is not None:
+                cached[1].close()
+            g0 = groups[0][1]
+            gtype = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
+                     torch.float16: B.MTA_F16}[g0.dtype]
+            mk = B.MTA_MOM_BF16X2 if self.packed else B.MTA_MOM_F32
+            L = MtaList([], entries=[(p.data_ptr(), g.data_ptr(),
+                                      None if m is None else m.data_ptr(),
+                                      None if v is None else v.data_ptr(),
+                                      p.numel()) for p, g, m, v in groups],
+                        gtype=gtype, mkind=mk, vkind=mk)
+            L._keep = groups
+            self._lists[k] = (key, L)
+        return self._lists[k][1]
+
+    def _joint_norm_list(self, all_params):
+        key = tuple((p.data_ptr(), p.grad.data_ptr(), p.numel(),
+                     p.grad.dtype) for p in all_params)
+        if self._norm_list is None or self._norm_list[0] != key:
+            if self._norm_list is not None:
+                self._norm_list[1].close()
+            gtype = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
+                     torch.float16: B.MTA_F16}[all_params[0].grad.dtype]
+            L = MtaList([], entries=[(p.data_ptr(), p.grad.data_ptr(), None,
+                                      None, p.numel()) for p in all_params],
+                        gtype=gtype, mkind=B.MTA_MOM_F32, vkind=B.MTA_MOM_F32)
+            L._keep = [(p, p.grad) for p in all_params]
+            self._norm_list = (key, L)
+        return self._norm_list[1]
+
+    # -- the step ---------------------------------------------------------
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        groups = [[p for p in g["params"] if p.grad is not None]
+                  for g in self.param_groups]
+        all_params = [p for ps in groups for p in ps]
+        if not all_params:
+            return loss
+        for p in all_params:
+            self._check(p)
+        if len({p.grad.dtype for p in all_params}) != 1:
+            raise TypeError("all gradients must share one dtype")
+        coef = None
+        if self.max_norm is not None:
+            dev = all_params[0].device
+            if self.last_norm is None or self.last_norm.device != dev:
+                self.last_norm = torch.zeros(1, device=dev)
+                self.last_coef = torch.zeros(1, device=dev)
+            self._joint_norm_list(all_params).clip_norm(
+                float(self.max_norm), self.last_norm, self.last_coef)
+            coef = self.last_coef
+        for k, (group, ps) in enumerate(zip(self.param_groups, groups)):
+            if not ps:
+                continue
+            L = self._group_list(k, ps)
+            steps = {int(self.state[p]["step"]) for p in ps}
+            if len(steps) != 1:
+                raise RuntimeError(
+                    "the parameters of one group have taken different "
+                    "numbers of steps; one launch applies one t to a group")
+            t = steps.pop() + 1
+            for p in ps:
+                self.state[p]["step"] = t
+            b1, b2 = group["betas"]
+            L.step(dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
+                        eps=group["eps"],
+                        weight_decay=group["weight_decay"],
+                        momentum=group["momentum"],
+                        zero_grad=self.zero_grad_in_step), t, coef)
+        return loss

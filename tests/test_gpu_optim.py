@@ -1,0 +1,155 @@
+"""MtaOptimizer, the torch.optim-style front end: a real torch model's
+parameters and autograd gradients, one joint clip over every parameter
+group, one launch per group.  Checked bit for bit against the oracle
+(lockstep on the device coefficient) and within rounding against
+torch.optim.AdamW + clip_grad_norm_; state_dict round trips continue
+exactly; reallocated gradients rebuild the tables."""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import mixed_precision_optimizer_mta_amd as M
+    M.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _model(seed=0):
+    torch.manual_seed(seed)
+    return torch.nn.Sequential(
+        torch.nn.Linear(300, 513), torch.nn.GELU(),
+        torch.nn.Linear(513, 257), torch.nn.GELU(),
+        torch.nn.Linear(257, 10)).cuda()
+
+
+def _grads(model, step):
+    torch.manual_seed(1000 + step)
+    x = torch.randn(64, 300, device="cuda")
+    y = torch.randint(0, 10, (64,), device="cuda")
+    loss = torch.nn.functional.cross_entropy(model(x), y)
+    model.zero_grad(set_to_none=False)
+    loss.backward()
+
+
+def _host(t):
+    return t.detach().cpu().numpy().copy()
+
+
+@pytest.mark.parametrize("kind", ["adamw", "adam", "sgd", "momentum"])
+def test_matches_the_oracle_bitwise(kind):
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model()
+    params = list(model.parameters())
+    adam = kind in ("adamw", "adam")
+    groups = [{"params": params[:2], "lr": 1e-3 if adam else 0.05},
+              {"params": params[2:], "lr": 3e-4 if adam else 0.02,
+               "weight_decay": 0.0}]
+    wd = 0.05 if adam else 0.0
+    opt = MtaOptimizer(groups, kind=kind, betas=(0.9, 0.99), eps=1e-8,
+                       weight_decay=wd, momentum=0.9, max_norm=0.5)
+    ost = [[O.Tensor(_host(p), None, np.zeros(p.numel(), np.float32),
+                     np.zeros(p.numel(), np.float32)) for p in g["params"]]
+           for g in groups]
+    for t in range(1, 5):
+        _grads(model, t)
+        for g, og in zip(groups, ost):
+            for p, o in zip(g["params"], og):
+                o.g = _host(p.grad).ravel()
+                o.w = o.w.ravel()
+        opt.step()
+        torch.cuda.synchronize()
+        coef = np.float32(opt.last_coef.item())
+        allg = [o.g for og in ost for o in og]
+        nrm = O.norm(allg, O.F32)
+        assert abs(float(opt.last_norm.item()) - nrm) <= 1e-6 * nrm
+        assert coef == O.clip_coef(0.5, np.float32(opt.last_norm.item()))
+        for g, og in zip(groups, ost):
+            o_opt = dict(kind=kind, lr=g["lr"], beta1=0.9, beta2=0.99,
+                         eps=1e-8, weight_decay=g.get("weight_decay", wd),
+                         momentum=0.9)
+            O.opt_step_(og, o_opt, O.F32, 0, 0, t, coef=coef)
+            for p, o in zip(g["params"], og):
+                assert np.array_equal(_host(p).ravel().view(np.uint32),
+                                      o.w.view(np.uint32)), (kind, t)
+
+
+def test_close_to_torch_adamw_with_clip():
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    a = _model(3)
+    b = copy.deepcopy(a)
+    opt_a = MtaOptimizer(a.parameters(), kind="adamw", lr=1e-3,
+                         weight_decay=0.1, max_norm=1.0)
+    opt_b = torch.optim.AdamW(b.parameters(), lr=1e-3, weight_decay=0.1,
+                              foreach=False)
+    for t in range(1, 6):
+        _grads(a, t)
+        _grads(b, t)
+        opt_a.step()
+        torch.nn.utils.clip_grad_norm_(b.parameters(), 1.0, foreach=False)
+        opt_b.step()
+    for pa, pb in zip(a.parameters(), b.parameters()):
+        assert torch.allclose(pa, pb, rtol=1e-5, atol=1e-7), \
+            (pa - pb).abs().max().item()
+
+
+def test_state_dict_round_trip_continues_exactly():
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    for packed in (False, True):
+        ref = _model(5)
+        opt_ref = MtaOptimizer(ref.parameters(), kind="adamw", lr=1e-3,
+                               weight_decay=0.1, max_norm=1.0,
+                               packed_moments=packed)
+        for t in range(1, 7):
+            _grads(ref, t)
+            opt_ref.step()
+        run = _model(5)
+        opt = MtaOptimizer(run.parameters(), kind="adamw", lr=1e-3,
+                           weight_decay=0.1, max_norm=1.0,
+                           packed_moments=packed)
+        for t in range(1, 4):
+            _grads(run, t)
+            opt.step()
+        saved = copy.deepcopy(opt.state_dict())
+        run2 = copy.deepcopy(run)
+        opt2 = MtaOptimizer(run2.parameters(), kind="adamw", lr=1e-3,
+                            weight_decay=0.1, max_norm=1.0,
+                            packed_moments=packed)
+        opt2.load_state_dict(saved)
+        for t in range(4, 7):
+            _grads(run2, t)
+            opt2.step()
+        torch.cuda.synchronize()
+        for pa, pb in zip(ref.parameters(), run2.parameters()):
+            assert torch.equal(pa, pb), packed
+
+
+def test_reallocated_gradients_and_fused_zeroing():
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    a = _model(7)
+    b = copy.deepcopy(a)
+    opt_a = MtaOptimizer(a.parameters(), kind="momentum", lr=0.05,
+                         momentum=0.9, max_norm=1.0)
+    opt_b = MtaOptimizer(b.parameters(), kind="momentum", lr=0.05,
+                         momentum=0.9, max_norm=1.0, zero_grad=True)
+    for t in range(1, 5):
+        for p in a.parameters():
+            p.grad = None            # PyTorch allocates fresh gradients
+        _grads(a, t)
+        _grads(b, t)
+        opt_a.step()
+        opt_b.step()
+        torch.cuda.synchronize()
+        for p in b.parameters():     # zeroed inside the update launch
+            assert not bool(p.grad.any())
+    for pa, pb in zip(a.parameters(), b.parameters()):
+        assert torch.equal(pa, pb)
