@@ -11,6 +11,14 @@ parameter group.  A step is:
     device tensors (``last_norm``, ``last_coef``);
   * one mta_step per parameter group with that coefficient.
 
+With ``loss_scale`` (an initial scale) the step is loss-scaled on the
+device: ``opt.loss_scale`` is a one-element float32 device view of the
+current scale (multiply the loss by it before backward), the joint norm
+unscales by 1/scale and sets the found-inf flag, every group's update is
+skipped on overflow, and the scale then grows or backs off (PyTorch's
+GradScaler rule) -- no host synchronization anywhere.  The step counter
+lives in ``opt.amp`` (an AmpState), not in ``self.state``.
+
 Every step of the arithmetic runs in libmta.  Parameters are float32 CUDA
 tensors; their gradients share one type (float32, bfloat16 or float16).  The
 device tables are rebuilt whenever a parameter, gradient or state buffer
@@ -31,7 +39,9 @@ class MtaOptimizer(torch.optim.Optimizer):
 
     def __init__(self, params, kind="adamw", lr=1e-3, betas=(0.9, 0.999),
                  eps=1e-8, weight_decay=0.0, momentum=0.0, max_norm=None,
-                 packed_moments=False, zero_grad=False):
+                 packed_moments=False, zero_grad=False, loss_scale=None,
+                 growth_factor=2.0, backoff_factor=0.5,
+                 growth_interval=2000):
         if kind not in _KINDS:
             raise ValueError(f"kind must be one of {_KINDS}")
         if packed_moments and kind not in ("adamw", "adam"):
@@ -47,6 +57,15 @@ class MtaOptimizer(torch.optim.Optimizer):
         self._norm_list = None  # (pointer key, MtaList)
         self.last_norm = None
         self.last_coef = None
+        self.amp = None
+        self.loss_scale = None
+        if loss_scale is not None:
+            from .torch_list import AmpState
+            self.amp = AmpState(float(loss_scale))
+            # the scale is the state's first 4 bytes
+            self.loss_scale = self.amp.buf.view(torch.float32)[:1]
+            self._amp_rule = (float(growth_factor), float(backoff_factor),
+                              int(growth_interval))
 
     # -- state buffers ----------------------------------------------------
     def _state_buffers(self, p):
@@ -141,18 +160,32 @@ class MtaOptimizer(torch.optim.Optimizer):
         if len({p.grad.dtype for p in all_params}) != 1:
             raise TypeError("all gradients must share one dtype")
         coef = None
-        if self.max_norm is not None:
+        if self.max_norm is not None or self.amp is not None:
             dev = all_params[0].device
             if self.last_norm is None or self.last_norm.device != dev:
                 self.last_norm = torch.zeros(1, device=dev)
                 self.last_coef = torch.zeros(1, device=dev)
-            self._joint_norm_list(all_params).clip_norm(
-                float(self.max_norm), self.last_norm, self.last_coef)
+            NL = self._joint_norm_list(all_params)
+            cap = float("inf") if self.max_norm is None else \
+                float(self.max_norm)
+            if self.amp is not None:
+                NL.amp_clip_norm(cap, self.amp, self.last_norm,
+                                 self.last_coef)
+            else:
+                NL.clip_norm(cap, self.last_norm, self.last_coef)
             coef = self.last_coef
         for k, (group, ps) in enumerate(zip(self.param_groups, groups)):
             if not ps:
                 continue
             L = self._group_list(k, ps)
+            b1, b2 = group["betas"]
+            rule = dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
+                        eps=group["eps"], weight_decay=group["weight_decay"],
+                        momentum=group["momentum"],
+                        zero_grad=self.zero_grad_in_step)
+            if self.amp is not None:
+                L.amp_step(rule, self.amp, coef)
+                continue
             steps = {int(self.state[p]["step"]) for p in ps}
             if len(steps) != 1:
                 raise RuntimeError(
@@ -161,10 +194,7 @@ class MtaOptimizer(torch.optim.Optimizer):
             t = steps.pop() + 1
             for p in ps:
                 self.state[p]["step"] = t
-            b1, b2 = group["betas"]
-            L.step(dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
-                        eps=group["eps"],
-                        weight_decay=group["weight_decay"],
-                        momentum=group["momentum"],
-                        zero_grad=self.zero_grad_in_step), t, coef)
+            L.step(rule, t, coef)
+        if self.amp is not None:
+            self.amp.update(*self._amp_rule)
         return loss

@@ -153,3 +153,42 @@ def test_reallocated_gradients_and_fused_zeroing():
             assert not bool(p.grad.any())
     for pa, pb in zip(a.parameters(), b.parameters()):
         assert torch.equal(pa, pb)
+
+
+def test_loss_scaled_front_end_matches_the_oracle_and_skips_overflow():
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model(11)
+    params = list(model.parameters())
+    opt = MtaOptimizer(params, kind="adamw", lr=1e-3, weight_decay=0.1,
+                       max_norm=1.0, loss_scale=256.0, growth_interval=2)
+    assert opt.loss_scale.item() == 256.0
+    amp_o = O.AmpState(256.0)
+    ost = [O.Tensor(_host(p).ravel(), None, np.zeros(p.numel(), np.float32),
+                    np.zeros(p.numel(), np.float32)) for p in params]
+    for t in range(1, 7):
+        torch.manual_seed(2000 + t)
+        x = torch.randn(32, 300, device="cuda")
+        y = torch.randint(0, 10, (32,), device="cuda")
+        model.zero_grad(set_to_none=False)
+        loss = torch.nn.functional.cross_entropy(model(x), y)
+        (loss * opt.loss_scale).backward()     # no host read of the scale
+        if t == 4:
+            params[0].grad[0, 0] = float("inf")
+        for p, o in zip(params, ost):
+            o.g = _host(p.grad).ravel()
+        opt.step()
+        torch.cuda.synchronize()
+        coef = np.float32(opt.last_coef.item())
+        _, _, found = O.amp_opt_step_(
+            ost, dict(kind="adamw", lr=1e-3, beta1=0.9, beta2=0.999,
+                      eps=1e-8, weight_decay=0.1, momentum=0.0),
+            O.F32, 0, 0, amp_o, 1.0, coef=coef)
+        assert found == (t == 4)
+        amp_o.update(2.0, 0.5, 2)
+        st = opt.amp.read()
+        assert (np.float32(st["scale"]), st["step"], st["growth_tracker"]) \
+            == (amp_o.scale, amp_o.step, amp_o.tracker), (t, st)
+        for p, o in zip(params, ost):
+            assert np.array_equal(_host(p).ravel().view(np.uint32),
+                                  o.w.view(np.uint32)), t
+    assert opt.amp.read()["step"] == 5
