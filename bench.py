@@ -353,7 +353,8 @@ def main():
     norm_d = torch.zeros(1, device="cuda")
     coef_d = torch.zeros(1, device="cuda")
     stream = torch.cuda.current_stream()
-    hp = wl.hparams
+    hp = M._binding.mta_adamw_hparams(wl.lr, wl.beta1, wl.beta2, wl.eps,
+                                      wl.weight_decay)
     defer = wl.scale != 1.0
     amp = M.AmpState(wl.amp_scale) if wl.amp else None
 
@@ -387,8 +388,12 @@ def main():
         step(t)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
+    # per-kernel events on an evenly spaced sample of ~50 timed steps: each
+    # record costs the host a few microseconds, which a launch-bound list
+    # (tiny) would otherwise pay every step
+    every = max(1, args.steps // 50)
+    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for k in range(0, args.steps, every)}
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -396,15 +401,15 @@ def main():
     start.record(stream)
     for k in range(args.steps):
         t += 1
-        step(t, evs[k])
+        step(t, evs.get(k))
     end.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
     dev_ms = start.elapsed_time(end)
     ms_per_step = dev_ms / args.steps
-    norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    adamw_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs.values()) / len(evs)
+    adamw_ms = sum(e[1].elapsed_time(e[2]) for e in evs.values()) / len(evs)
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs.values())
 
     def pct(q):
         return per_step[min(len(per_step) - 1, int(q * len(per_step)))]
