@@ -62,7 +62,10 @@
  * Streams.  Every device call enqueues its work on the caller's hipStream_t
  * (passed as void*, NULL = the null stream) and returns without waiting.  A
  * list is used on one stream at a time: the norm scratch is shared by all
- * calls on the list, so calls on one list that overlap in time race.
+ * calls on the list, so calls on one list that overlap in time race.  A list
+ * handle also holds host state (a pending deferred scale factor, attached
+ * weight copies), so one list is driven by one host thread at a time;
+ * different lists are independent on every count.
  *
  * Errors.  Functions return MTA_OK (0) or a negative mta_status.  On failure
  * nothing has been enqueued and mta_last_error() (per host thread) says why.
