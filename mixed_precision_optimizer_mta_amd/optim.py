@@ -19,6 +19,14 @@ skipped on overflow, and the scale then grows or backs off (PyTorch's
 GradScaler rule) -- no host synchronization anywhere.  The step counter
 lives in ``opt.amp`` (an AmpState), not in ``self.state``.
 
+``capturable=True`` keeps the step counter on the device without loss
+scaling (a state whose scale is 1 and never grows: the unscale multiplies by
+exactly 1), so ``step()`` can be captured in a HIP graph and replayed; the
+one difference from the plain step is that a non-finite gradient skips the
+update instead of spreading NaN.  Run one eager step first (it builds the
+device tables, which allocates), and keep the gradients' storage across
+replays (``zero_grad=True`` zeroes them inside the update launch).
+
 Every step of the arithmetic runs in libmta.  Parameters are float32 CUDA
 tensors; their gradients share one type (float32, bfloat16 or float16).  The
 device tables are rebuilt whenever a parameter, gradient or state buffer
@@ -41,7 +49,7 @@ class MtaOptimizer(torch.optim.Optimizer):
                  eps=1e-8, weight_decay=0.0, momentum=0.0, max_norm=None,
                  packed_moments=False, zero_grad=False, loss_scale=None,
                  growth_factor=2.0, backoff_factor=0.5,
-                 growth_interval=2000):
+                 growth_interval=2000, capturable=False):
         if kind not in _KINDS:
             raise ValueError(f"kind must be one of {_KINDS}")
         if packed_moments and kind not in ("adamw", "adam"):
@@ -59,6 +67,10 @@ class MtaOptimizer(torch.optim.Optimizer):
         self.last_coef = None
         self.amp = None
         self.loss_scale = None
+        if loss_scale is None and capturable:
+            # a device step counter without loss scaling: scale 1 that never
+            # grows within 2^31 - 1 good steps
+            loss_scale, growth_interval = 1.0, 2 ** 31 - 1
         if loss_scale is not None:
             from .torch_list import AmpState
             self.amp = AmpState(float(loss_scale))

@@ -192,3 +192,59 @@ def test_loss_scaled_front_end_matches_the_oracle_and_skips_overflow():
             assert np.array_equal(_host(p).ravel().view(np.uint32),
                                   o.w.view(np.uint32)), t
     assert opt.amp.read()["step"] == 5
+
+
+def test_capturable_step_replays_like_eager_steps():
+    # the optimizer step captured once in a HIP graph; gradients are made
+    # eagerly into the same storage before every replay
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    a = _model(13)
+    b = copy.deepcopy(a)
+    kw = dict(kind="adamw", lr=1e-3, weight_decay=0.1, max_norm=1.0,
+              capturable=True, zero_grad=True)
+    opt_a, opt_b = MtaOptimizer(a.parameters(), **kw), \
+        MtaOptimizer(b.parameters(), **kw)
+    _grads(a, 1)
+    _grads(b, 1)
+    opt_a.step()                   # eager: builds the tables
+    opt_b.step()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        opt_a.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for t in range(2, 8):
+        _grads(a, t)
+        _grads(b, t)
+        torch.cuda.synchronize()
+        graph.replay()
+        opt_b.step()
+        torch.cuda.synchronize()
+        for pa, pb in zip(a.parameters(), b.parameters()):
+            assert torch.equal(pa, pb), t
+            assert not bool(pa.grad.any())
+        assert opt_a.amp.read() == opt_b.amp.read()
+    assert opt_a.amp.read()["step"] == 7
+    assert opt_a.loss_scale.item() == 1.0
+
+
+def test_capturable_matches_the_plain_step_on_finite_gradients():
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    a = _model(17)
+    b = copy.deepcopy(a)
+    opt_a = MtaOptimizer(a.parameters(), kind="adam", lr=1e-3,
+                         weight_decay=0.05, max_norm=0.7, capturable=True)
+    opt_b = MtaOptimizer(b.parameters(), kind="adam", lr=1e-3,
+                         weight_decay=0.05, max_norm=0.7)
+    for t in range(1, 6):
+        _grads(a, t)
+        _grads(b, t)
+        opt_a.step()
+        opt_b.step()
+    torch.cuda.synchronize()
+    # the device step constants use the correctly rounded power, the host
+    # ones libm's pow; they agree at these t, so the runs are identical
+    for pa, pb in zip(a.parameters(), b.parameters()):
+        assert torch.equal(pa, pb)
