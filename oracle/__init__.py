@@ -275,20 +275,28 @@ def momentum_(w, g, buf, gtype, lr, mu, s=1.0, coef=1.0, zero=False):
                               float(np.float32(mu)), int(bool(zero)))
 
 
-def weight_copy(w, out):
-    """bfloat16 copy of float32 weights (nearest-even, NaN -> 0xFFFF)."""
+def weight_copy(w, out, ctype=BF16):
+    """16-bit copy of float32 weights: bfloat16 (ctype BF16, the default) or
+    IEEE float16 (ctype F16), nearest-even, NaN -> 0xFFFF."""
     if out.size != w.size:
         raise ValueError("copy buffer has the wrong size")
-    lib().mto_weight_copy(w.size, _ptr(w, np.float32), _ptr(out, np.uint16))
+    if ctype == F16:
+        out[...] = f16_of_f32(w)
+    elif ctype == BF16:
+        lib().mto_weight_copy(w.size, _ptr(w, np.float32),
+                              _ptr(out, np.uint16))
+    else:
+        raise ValueError("a weight copy is bfloat16 or float16")
 
 
 class Tensor:
     """One parameter group: weight, gradient and the two moments, and an
-    optional bfloat16 copy of the weight (numpy uint16, written after each
-    step when present)."""
+    optional 16-bit copy of the weight (numpy uint16, bfloat16 or float16
+    by w16_type, written after each step when present)."""
 
-    def __init__(self, w, g, m, v, w16=None):
+    def __init__(self, w, g, m, v, w16=None, w16_type=BF16):
         self.w, self.g, self.m, self.v, self.w16 = w, g, m, v, w16
+        self.w16_type = w16_type
 
     @property
     def n(self):
@@ -316,7 +324,7 @@ def step_(tensors, gtype, mkind, vkind, lr, beta1, beta2, eps, weight_decay,
     for x in tensors:
         adamw_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c)
         if getattr(x, "w16", None) is not None:
-            weight_copy(x.w, x.w16)
+            weight_copy(x.w, x.w16, getattr(x, "w16_type", BF16))
     return nrm, c
 
 
@@ -399,7 +407,7 @@ def amp_step_(tensors, gtype, mkind, vkind, amp, lr, beta1, beta2, eps,
         for x in tensors:
             adamw_(x.w, x.g, x.m, x.v, gtype, mkind, vkind, sc, s, c)
             if getattr(x, "w16", None) is not None:
-                weight_copy(x.w, x.w16)
+                weight_copy(x.w, x.w16, getattr(x, "w16_type", BF16))
     return nrm, c, found
 
 
@@ -421,7 +429,7 @@ def _apply_opt(x, opt, gtype, mkind, vkind, sc, s, c, zero):
     else:
         raise ValueError(f"unknown optimizer {kind!r}")
     if getattr(x, "w16", None) is not None:
-        weight_copy(x.w, x.w16)
+        weight_copy(x.w, x.w16, getattr(x, "w16_type", BF16))
 
 
 def opt_step_(tensors, opt, gtype, mkind, vkind, t, s=1.0, max_norm=None,

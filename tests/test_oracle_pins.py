@@ -918,3 +918,33 @@ def test_amp_opt_step_equals_plain_step_at_the_next_t():
         O.amp_opt_step_([a], opt, O.F16, 0, 0, amp, 1.0)
         O.opt_step_([b], opt, O.F16, 0, 0, 5, s=1.0 / 256, max_norm=1.0)
         assert np.array_equal(a.w, b.w) and np.array_equal(a.m, b.m), kind
+
+
+def test_float16_weight_copy_is_numpys_nearest_even():
+    # "float16 and bfloat16, whole": a float16 step's product reads the
+    # float32 weights as float16; the copy is numpy's conversion bit for bit
+    rng = np.random.default_rng(41)
+    w = np.concatenate([rng.normal(0, 0.02, 50000),
+                        rng.normal(0, 1e4, 5000),
+                        [65504.0, 65520.0, 1e-8, -0.0, np.inf]]).astype(
+                            np.float32)
+    out = np.zeros(w.size, np.uint16)
+    O.weight_copy(w, out, O.F16)
+    with np.errstate(over="ignore"):
+        want = w.astype(np.float16).view(np.uint16)
+    assert np.array_equal(out, want)
+    nan = np.array([np.nan], np.float32)
+    o1 = np.zeros(1, np.uint16)
+    O.weight_copy(nan, o1, O.F16)
+    assert o1[0] == 0xFFFF
+
+
+def test_step_writes_a_float16_copy_when_asked():
+    rng = np.random.default_rng(42)
+    n = 1001
+    x = O.Tensor(rng.normal(0, 0.02, n).astype(np.float32),
+                 rng.normal(0, 1e-3, n).astype(np.float32),
+                 np.zeros(n, np.float32), np.zeros(n, np.float32),
+                 np.zeros(n, np.uint16), O.F16)
+    O.step_([x], O.F32, 0, 0, 3e-4, 0.9, 0.999, 1e-8, 0.1, 1)
+    assert np.array_equal(x.w16, x.w.astype(np.float16).view(np.uint16))
