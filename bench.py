@@ -281,9 +281,11 @@ def main():
                     help="oracle steps of the CPU baseline (0 = skip); the "
                          "default is about 11 s of one host core on the "
                          "124M list")
-    ap.add_argument("--weight-copy", action="store_true",
-                    help="also write a bfloat16 copy of every updated weight "
-                         "(mta_list_set_weight_copies): +2 B/param")
+    ap.add_argument("--weight-copy", nargs="?", const="bf16", default=None,
+                    choices=["bf16", "f16"],
+                    help="also write a 16-bit copy (bfloat16 by default, or "
+                         "float16) of every updated weight "
+                         "(mta_list_set_weight_copies_as): +2 B/param")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -346,7 +348,8 @@ def main():
                   vkind=wl.vkind)
     copies = None
     if args.weight_copy:
-        copies = torch.empty(arena.total, dtype=torch.bfloat16, device="cuda")
+        cdt = torch.float16 if args.weight_copy == "f16" else torch.bfloat16
+        copies = torch.empty(arena.total, dtype=cdt, device="cuda")
         L.set_weight_copies([copies[o:o + n] for o, n in
                              zip(arena.offsets, wl.sizes)])
     info = L.info()
@@ -476,7 +479,7 @@ def main():
             "bytes_per_param": bpp["norm"] + bpp["update"],
             "tiles": info["tiles"], "grid_update": info["grid_update"],
             "grid_norm": info["grid_norm"], "parallelism": "single GPU",
-            "weight_copy": bool(args.weight_copy),
+            "weight_copy": args.weight_copy,
             "optimizer": args.opt, "zero_grad": bool(args.zero_grad),
             "graph": bool(args.graph),
         },

@@ -27,8 +27,9 @@
  *   mta_amp_*       the same steps under a dynamic loss scale kept in device
  *                   memory (Mica: the unscaling a float16 step needs), with
  *                   PyTorch's GradScaler rule for skipping and rescaling.
- *   mta_list_set_weight_copies  bfloat16 copies of the new weights (Mica,
- *                   section "float16 and bfloat16, whole").
+ *   mta_list_set_weight_copies  bfloat16 (or, by mta_list_set_weight_copies_as,
+ *                   float16) copies of the new weights (Mica, section
+ *                   "float16 and bfloat16, whole").
  *
  * Memory and ownership.  Every w, g, m, v pointer is device memory owned by
  * the caller (for example a PyTorch tensor's data pointer).  The library never
@@ -145,8 +146,10 @@ typedef struct {
   int32_t device;      /* HIP device the list lives on */
   int32_t vector_tensors; /* tensors that take the 16-byte vector path */
   int32_t gtype, mkind, vkind;
-  int32_t weight_copies;  /* tensors with an attached bfloat16 weight copy */
+  int32_t weight_copies;  /* tensors with an attached 16-bit weight copy */
   int32_t state_buffers;  /* bit 0: the list has m; bit 1: it has v */
+  int32_t weight_copy_type; /* MTA_BF16 or MTA_F16: the copies' format */
+  int32_t reserved;
 } mta_list_info_t;
 
 /* The update rules of "BendTorch main.bend", section "Optimizers" (the Opt
@@ -254,6 +257,16 @@ int mta_step(mta_list *list, const mta_opt *opt, int64_t t,
  * this list.  On failure the previous copies stay attached. */
 int mta_list_set_weight_copies(mta_list *list, void *const *w16,
                                void *stream);
+
+/* As mta_list_set_weight_copies, with the copies' format: copy_type MTA_BF16
+ * (the same call) or MTA_F16, IEEE binary16 (Mica, section "float16 and
+ * bfloat16, whole": the two 16-bit types stand side by side, and a float16
+ * step reads its weights as float16).  A float16 copy is the nearest-even
+ * binary16 value, +-Inf beyond its range (|w| >= 65520), with NaN -> 0xFFFF.
+ * One format per list; the call sets it for every attached copy.
+ * MTA_EDTYPE for any other copy_type (nothing changes then). */
+int mta_list_set_weight_copies_as(mta_list *list, void *const *w16,
+                                  int32_t copy_type, void *stream);
 
 /* Loss-scaled ClipGradNorms: as mta_clip_norm with the unscale factor
  * s = float32(1 / float64(d_amp->scale)) read on the device, and one more

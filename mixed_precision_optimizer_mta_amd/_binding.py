@@ -28,7 +28,8 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_clip_norm", "mta_adamw_step", "mta_list_set_weight_copies",
            "mta_adamw_scalars", "mta_list_info", "mta_last_error",
            "mta_abi_version", "mta_amp_clip_norm", "mta_amp_adamw_step",
-           "mta_amp_update", "mta_step", "mta_amp_step")
+           "mta_amp_update", "mta_step", "mta_amp_step",
+           "mta_list_set_weight_copies_as")
 
 
 class mta_tensor(ctypes.Structure):
@@ -65,7 +66,9 @@ class mta_list_info_t(ctypes.Structure):
                 ("device", ctypes.c_int32), ("vector_tensors", ctypes.c_int32),
                 ("gtype", ctypes.c_int32), ("mkind", ctypes.c_int32),
                 ("vkind", ctypes.c_int32), ("weight_copies", ctypes.c_int32),
-                ("state_buffers", ctypes.c_int32)]
+                ("state_buffers", ctypes.c_int32),
+                ("weight_copy_type", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class MtaError(RuntimeError):
@@ -100,6 +103,8 @@ def lib():
         L.mta_adamw_step.argtypes = [vp, ctypes.POINTER(mta_adamw_hparams),
                                      i64, vp, vp]
         L.mta_list_set_weight_copies.argtypes = [vp, ctypes.POINTER(vp), vp]
+        L.mta_list_set_weight_copies_as.argtypes = [vp, ctypes.POINTER(vp),
+                                                    ctypes.c_int32, vp]
         L.mta_adamw_scalars.argtypes = [ctypes.POINTER(mta_adamw_hparams),
                                         i64, ctypes.POINTER(ctypes.c_float)]
         L.mta_list_info.argtypes = [vp, ctypes.POINTER(mta_list_info_t)]
@@ -175,15 +180,24 @@ def mta_adamw_step(handle, hp, t, d_coef, stream=0):
            "mta_adamw_step")
 
 
+def _copy_array(w16):
+    if w16 is None:
+        return None
+    return (ctypes.c_void_p * max(1, len(w16)))(*[p or None for p in w16])
+
+
 def mta_list_set_weight_copies(handle, w16, stream=0):
     """w16: one device pointer (or None) per tensor of the list, or None to
     detach every copy."""
-    if w16 is None:
-        arr = None
-    else:
-        arr = (ctypes.c_void_p * max(1, len(w16)))(*[p or None for p in w16])
-    _check(lib().mta_list_set_weight_copies(handle, arr, stream),
+    _check(lib().mta_list_set_weight_copies(handle, _copy_array(w16), stream),
            "mta_list_set_weight_copies")
+
+
+def mta_list_set_weight_copies_as(handle, w16, copy_type, stream=0):
+    """As mta_list_set_weight_copies; copy_type MTA_BF16 or MTA_F16."""
+    _check(lib().mta_list_set_weight_copies_as(handle, _copy_array(w16),
+                                               copy_type, stream),
+           "mta_list_set_weight_copies_as")
 
 
 def mta_adamw_scalars(hp, t):

@@ -19,7 +19,7 @@
 
 struct mta_list {
   std::vector<mta_tensor> tensors;  // the caller's table, kept for rebuilds
-  std::vector<void *> w16;          // attached bfloat16 weight copies (or null)
+  std::vector<void *> w16;          // attached 16-bit weight copies (or null)
   int device = 0;
   int gtype = 0, mkind = 0, vkind = 0;
   int64_t count = 0;
@@ -35,7 +35,8 @@ struct mta_list {
   mta::StepTile *d_stiles = nullptr;
   double *d_partials = nullptr;
   unsigned int *d_ticket = nullptr;
-  int weight_copies = 0;  // tensors with an attached bfloat16 copy
+  int weight_copies = 0;  // tensors with an attached 16-bit copy
+  int copy_type = MTA_BF16;  // format of the copies: MTA_BF16 or MTA_F16
   bool deferred = false;  // a MTA_SCALE_DEFER factor is pending
   float deferred_s = 1.0f;
 };
@@ -348,6 +349,7 @@ int step_common(mta_list *L, const mta_opt *o, int64_t t, const float *d_coef,
   if (rc) return rc;
   mta::StepScalars sc = opt_scalars(*o, t);
   sc.s = (!d_amp && L->deferred) ? L->deferred_s : 1.0f;
+  sc.copy_f16 = L->copy_type == MTA_F16 ? 1u : 0u;
   const mta::AmpStep amp = d_amp
       ? mta::AmpStep{d_amp, o->lr, o->beta1, o->beta2}
       : mta::AmpStep{};
@@ -587,7 +589,15 @@ int mta_list_destroy(mta_list *L) {
 }
 
 int mta_list_set_weight_copies(mta_list *L, void *const *w16, void *stream) {
+  return mta_list_set_weight_copies_as(L, w16, MTA_BF16, stream);
+}
+
+int mta_list_set_weight_copies_as(mta_list *L, void *const *w16,
+                                  int32_t copy_type, void *stream) {
   if (!L) return fail(MTA_EINVAL, "list is NULL");
+  if (copy_type != MTA_BF16 && copy_type != MTA_F16)
+    return fail(MTA_EDTYPE, "a weight copy is bfloat16 or float16, not %d",
+                static_cast<int>(copy_type));
   std::vector<void *> copies;
   int attached = 0;
   try {
@@ -636,6 +646,7 @@ int mta_list_set_weight_copies(mta_list *L, void *const *w16, void *stream) {
     return fail(MTA_EHIP, "uploading the tile table: %s", hipGetErrorString(e));
   L->w16 = std::move(copies);
   L->weight_copies = attached;
+  L->copy_type = copy_type;
   return ok();
 }
 
@@ -654,6 +665,8 @@ int mta_list_info(const mta_list *L, mta_list_info_t *out) {
   out->vkind = L->vkind;
   out->weight_copies = L->weight_copies;
   out->state_buffers = L->state_buffers;
+  out->weight_copy_type = L->copy_type;
+  out->reserved = 0;
   return ok();
 }
 

@@ -32,7 +32,7 @@ static_assert(sizeof(GradTile) == 16, "gradient tile layout");
 
 // The update kernels read and write the buffers their rule uses (w and g
 // always; m for momentum and the Adam family; v for the Adam family), and
-// write the bfloat16 weight copy when one is attached.  Unused buffers are
+// write the 16-bit weight copy when one is attached.  Unused buffers are
 // null.
 struct StepTile {
   float *w;
@@ -41,7 +41,7 @@ struct StepTile {
   void *v;
   uint32_t lim;  // elements in this tile, 1..kTileElems
   uint32_t vec;  // 1: all buffers (w16 too, when present) 16-byte aligned
-  void *w16;     // bfloat16 copy of w at this tile, or nullptr
+  void *w16;     // 16-bit copy of w at this tile, or nullptr
 };
 static_assert(sizeof(StepTile) == 48, "step tile layout");
 
@@ -61,6 +61,7 @@ struct StepScalars {
   float l2;       // Adam: g' = g + w*l2
   float mu;       // momentum
   uint32_t zero;  // 1: write +0 into every gradient element after reading it
+  uint32_t copy_f16;  // weight copies are float16 (else bfloat16)
 };
 
 struct Work {

@@ -388,7 +388,7 @@ struct TileRef {
   MTA_GLOBAL elem_t<G> *pg;  // read, and written only when zeroing
   MTA_GLOBAL elem_t<M> *pm;
   MTA_GLOBAL elem_t<V> *pv;
-  MTA_GLOBAL uint16_t *pw16;  // bfloat16 weight copy, or null
+  MTA_GLOBAL uint16_t *pw16;  // 16-bit weight copy, or null
   uint32_t lim;
   bool full;
 };
@@ -423,6 +423,28 @@ __device__ __forceinline__ void issue_tile(
   }
 }
 
+// The 16-bit weight copy ("Mica 7.7", section "float16 and bfloat16,
+// whole"): bfloat16 or float16 codes of the new float32 weights, nearest-even,
+// NaN -> 0xFFFF.  f16 is uniform (a list has one copy format).
+__device__ __forceinline__ uint32_t encode_copy(float x, uint32_t f16) {
+  return f16 ? to_f16(x) : to_bf16(x);
+}
+
+__device__ __forceinline__ void store_copy4(MTA_GLOBAL uint16_t *p,
+                                            uint32_t e, const float (&w)[4],
+                                            uint32_t f16) {
+  uint32_t h[4];
+  if (f16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h[k] = to_f16(w[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h[k] = to_bf16(w[k]);
+  }
+  __builtin_nontemporal_store(u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)},
+                              (MTA_GLOBAL u32x2 *)(p + e));
+}
+
 template <int R, int G, bool MPacked, bool VPacked>
 __device__ __forceinline__ void finish_tile(
     const TileRegs<R, G, MPacked, VPacked> &X,
@@ -444,12 +466,7 @@ __device__ __forceinline__ void finish_tile(
     if constexpr (kUsesM<R>) store4<Ref::M>(T.pm, e, m);
     if constexpr (kUsesV<R>) store4<Ref::V>(T.pv, e, v);
     if (sc.zero) zero4<G>(T.pg, e);  // uniform; after this lane's g load
-    if (T.pw16) {  // uniform: the tile has a bfloat16 weight copy
-      float h[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) h[k] = round_bf16(w[k]);
-      store4<kBF16>(T.pw16, e, h);
-    }
+    if (T.pw16) store_copy4(T.pw16, e, w, sc.copy_f16);  // uniform
   }
 }
 
@@ -484,7 +501,7 @@ __device__ __forceinline__ void partial_tile(
         if constexpr (kUsesM<R>) store1<Ref::M>(T.pm, e, m[j][k]);
         if constexpr (kUsesV<R>) store1<Ref::V>(T.pv, e, v[j][k]);
         if (sc.zero) zero1<G>(T.pg, e);
-        if (T.pw16) store1<kBF16>(T.pw16, e, round_bf16(w[j][k]));
+        if (T.pw16) T.pw16[e] = encode_copy(w[j][k], sc.copy_f16);
       }
     }
 }

@@ -89,10 +89,11 @@ class MtaList:
                         coef_out.data_ptr(), current_stream())
 
     def set_weight_copies(self, copies):
-        """copies: one bfloat16 GPU tensor (or None) per group, each with the
-        weight's numel, written with bfloat16(w) by every later AdamW step;
-        None detaches them all."""
+        """copies: one bfloat16 or float16 GPU tensor (or None) per group,
+        each with the weight's numel and all of one dtype, written with the
+        16-bit rounding of w by every later step; None detaches them all."""
         ptrs = None
+        ctype = B.MTA_BF16
         if copies is not None:
             if len(copies) != len(self.sizes):
                 raise ValueError("one copy (or None) per tensor of the list")
@@ -103,13 +104,20 @@ class MtaList:
                     continue
                 if c.numel() != n:
                     raise ValueError("a weight copy must have the weight's numel")
-                if c.dtype != torch.bfloat16 or not c.is_cuda or \
-                        not c.is_contiguous():
+                if c.dtype not in (torch.bfloat16, torch.float16) or \
+                        not c.is_cuda or not c.is_contiguous():
                     raise TypeError("weight copies are contiguous bfloat16 "
-                                    "GPU tensors")
+                                    "or float16 GPU tensors")
                 ptrs.append(c.data_ptr())
-            self._copies = list(copies)
-        B.mta_list_set_weight_copies(self.handle, ptrs, current_stream())
+            dts = {c.dtype for c in copies if c is not None}
+            if len(dts) > 1:
+                raise TypeError("the weight copies of a list share one dtype")
+            if dts == {torch.float16}:
+                ctype = B.MTA_F16
+        B.mta_list_set_weight_copies_as(self.handle, ptrs, ctype,
+                                        current_stream())
+        # the list holds raw addresses: keep the tensors alive with it
+        self._copies = None if copies is None else list(copies)
 
     def adamw_step(self, hparams, t, coef=None):
         if coef is not None and (coef.dtype != torch.float32 or

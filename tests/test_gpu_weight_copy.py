@@ -1,6 +1,7 @@
-"""GPU parity of the fused bfloat16 weight copy (mta_list_set_weight_copies):
-every AdamW step also writes bfloat16(w_new), nearest-even, NaN -> 0xFFFF,
-for the tensors that have a copy attached; bitwise against the oracle."""
+"""GPU parity of the fused 16-bit weight copy (mta_list_set_weight_copies,
+mta_list_set_weight_copies_as): every AdamW step also writes bfloat16(w_new)
+or float16(w_new), nearest-even, NaN -> 0xFFFF, for the tensors that have a
+copy attached; bitwise against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -14,11 +15,16 @@ from parity_util import compare, dev_bf16_bits, oracle_grads, oracle_state
 pytestmark = pytest.mark.gpu
 
 
-def run(wl, steps, offsets=None, copy_mask=None, copy_shift=0):
+def run(wl, steps, offsets=None, copy_mask=None, copy_shift=0,
+        dtype=torch.bfloat16, plant=None):
+    """plant: {(tensor, element): weight value} written before the first
+    step."""
     arena = WL.Arena(wl, "cuda", offsets)
     arena.fill_weights()
-    # the copies live in their own bfloat16 arena, filled with a sentinel
-    copies = torch.full((arena.total + 8,), -7.0, dtype=torch.bfloat16,
+    for (i, k), val in (plant or {}).items():
+        arena.w[arena.offsets[i] + k] = val
+    # the copies live in their own 16-bit arena, filled with a sentinel
+    copies = torch.full((arena.total + 8,), -7.0, dtype=dtype,
                         device="cuda")
     sentinel = copies.clone()
     mask = copy_mask or [True] * wl.count
@@ -27,10 +33,14 @@ def run(wl, steps, offsets=None, copy_mask=None, copy_shift=0):
     L = MtaList([], entries=arena.entries(), gtype=wl.gtype, mkind=wl.mkind,
                 vkind=wl.vkind)
     L.set_weight_copies(views)
-    assert L.info()["weight_copies"] == sum(1 for x in views if x is not None)
+    ctype = O.F16 if dtype == torch.float16 else O.BF16
+    info = L.info()
+    assert info["weight_copies"] == sum(1 for x in views if x is not None)
+    assert info["weight_copy_type"] == ctype
     ost = oracle_state(arena)
     for o, v in zip(ost, views):
         o.w16 = None if v is None else np.zeros(v.numel(), np.uint16)
+        o.w16_type = ctype
     cd = torch.zeros(1, device="cuda")
     for t in range(1, steps + 1):
         arena.fill_grads(t)
@@ -64,27 +74,49 @@ def run(wl, steps, offsets=None, copy_mask=None, copy_shift=0):
     L.close()
 
 
-KINDS = [(g, m, v) for g in (0, 1) for m in (0, 1) for v in (0, 1)]
+KINDS = [(g, m, v) for g in (0, 1) for m in (0, 1) for v in (0, 1)] + \
+    [(2, 0, 0), (2, 1, 1)]
+COPY = [torch.bfloat16, torch.float16]
 
 
+@pytest.mark.parametrize("dtype", COPY, ids=["bf16", "f16"])
 @pytest.mark.parametrize("gtype,mkind,vkind", KINDS)
-def test_weight_copy_every_kind(gtype, mkind, vkind):
+def test_weight_copy_every_kind(gtype, mkind, vkind, dtype):
     sizes = [1, 7, 4095, 4096, 4097, 3 * 4096 + 5, 10000]
     wl = WL.Workload("copies", sizes, gtype, mkind, vkind, steps=2,
                      g_sigma=0.05, ident=21)
-    run(wl, 2)
+    run(wl, 2, dtype=dtype)
 
 
-def test_weight_copy_partial_attach_and_unaligned_copies():
+@pytest.mark.parametrize("dtype", COPY, ids=["bf16", "f16"])
+def test_weight_copy_partial_attach_and_unaligned_copies(dtype):
     sizes = [5000, 4096, 33, 9000, 1]
     wl = WL.Workload("copies2", sizes, 1, 1, 0, steps=2, ident=22)
     # copies shifted by one element: 2 bytes off 16-byte alignment, so these
     # tensors take the element path even though w, g, m, v are aligned
-    run(wl, 2, copy_mask=[True, False, True, True, False], copy_shift=1)
+    run(wl, 2, copy_mask=[True, False, True, True, False], copy_shift=1,
+        dtype=dtype)
 
 
-def test_weight_copy_on_the_124m_list():
-    run(WL.get("gpt2_124m"), 2)
+@pytest.mark.parametrize("dtype", COPY, ids=["bf16", "f16"])
+def test_weight_copy_of_extreme_weights(dtype):
+    # weights at and past the float16 range, subnormal in float16, signed
+    # zeros and NaN, in a vector tile and in a ragged tail
+    sizes = [4096, 4100]
+    wl = WL.Workload("copies4", sizes, 0, 0, 0, steps=2, ident=24)
+    vals = [65504.0, 65519.0, 65520.0, 70000.0, -1e6, 3e38, 6e-8, 1e-7,
+            2.9e-8, -0.0, 0.0, float("nan"), float("inf"), -float("inf"),
+            1.00048828125, 2049.0]
+    plant = {}
+    for i, base in ((0, 0), (1, 0), (1, 4084)):  # the last: 12 + 4 in the tail
+        for k, x in enumerate(vals):
+            plant[(i, base + k)] = x
+    run(wl, 2, dtype=dtype, plant=plant)
+
+
+@pytest.mark.parametrize("dtype", COPY, ids=["bf16", "f16"])
+def test_weight_copy_on_the_124m_list(dtype):
+    run(WL.get("gpt2_124m"), 2, dtype=dtype)
 
 
 def test_weight_copy_rejects_overlap_and_misalignment():
@@ -101,5 +133,12 @@ def test_weight_copy_rejects_overlap_and_misalignment():
     with pytest.raises(MtaError) as e:               # odd address
         B.mta_list_set_weight_copies(L.handle, [c.data_ptr() + 1, None])
     assert e.value.code == -2
+    h = torch.zeros(300, dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):                   # mixed copy dtypes
+        L.set_weight_copies([c[0:100], h[0:200]])
+    with pytest.raises(MtaError) as e:               # no such copy format
+        B.mta_list_set_weight_copies_as(L.handle, [c.data_ptr(), None], 0)
+    assert e.value.code == -3
     assert L.info()["weight_copies"] == 0
+    assert L.info()["weight_copy_type"] == B.MTA_BF16
     L.close()
