@@ -27,11 +27,23 @@ update instead of spreading NaN.  Run one eager step first (it builds the
 device tables, which allocates), and keep the gradients' storage across
 replays (``zero_grad=True`` zeroes them inside the update launch).
 
+``master_weights=True`` is for a model kept in bfloat16 or float16: the
+optimizer holds a float32 master copy of every parameter (``state[p]
+["master_weight"]``), the update runs on the masters with the model's 16-bit
+gradients, and the same launch writes the 16-bit rounding of each new master
+into the parameter itself (the list's weight copies).  The model's forward
+and backward then read and produce 16-bit values only, while the weights
+accumulate updates in float32.
+
 Every step of the arithmetic runs in libmta.  Parameters are float32 CUDA
-tensors; their gradients share one type (float32, bfloat16 or float16).  The
-device tables are rebuilt whenever a parameter, gradient or state buffer
-moved (``zero_grad(set_to_none=True)`` lets PyTorch reallocate gradients;
+tensors (or, with master_weights, all bfloat16 or all float16); their
+gradients share one type (float32, bfloat16 or float16).  The device tables
+are rebuilt whenever a parameter, gradient or state buffer moved
+(``zero_grad(set_to_none=True)`` lets PyTorch reallocate gradients;
 ``zero_grad=True`` here instead zeroes them inside the update launch).
+``load_state_dict`` keeps every state tensor in the dtype it was saved in
+(PyTorch's default would cast float32 masters and moments to a 16-bit
+parameter's dtype).
 """
 import torch
 
@@ -49,7 +61,8 @@ class MtaOptimizer(torch.optim.Optimizer):
                  eps=1e-8, weight_decay=0.0, momentum=0.0, max_norm=None,
                  packed_moments=False, zero_grad=False, loss_scale=None,
                  growth_factor=2.0, backoff_factor=0.5,
-                 growth_interval=2000, capturable=False):
+                 growth_interval=2000, capturable=False,
+                 master_weights=False):
         if kind not in _KINDS:
             raise ValueError(f"kind must be one of {_KINDS}")
         if packed_moments and kind not in ("adamw", "adam"):
@@ -61,6 +74,7 @@ class MtaOptimizer(torch.optim.Optimizer):
         self.max_norm = max_norm
         self.packed = bool(packed_moments)
         self.zero_grad_in_step = bool(zero_grad)
+        self.master_weights = bool(master_weights)
         self._lists = {}       # group index -> (pointer key, MtaList)
         self._norm_list = None  # (pointer key, MtaList)
         self.last_norm = None
@@ -80,6 +94,15 @@ class MtaOptimizer(torch.optim.Optimizer):
                               int(growth_interval))
 
     # -- state buffers ----------------------------------------------------
+    def master(self, p):
+        """The float32 weight the update runs on: p itself, or its master."""
+        if not self.master_weights:
+            return p
+        st = self.state[p]
+        if "master_weight" not in st:
+            st["master_weight"] = p.detach().float().contiguous()
+        return st["master_weight"]
+
     def _state_buffers(self, p):
         st = self.state[p]
         mdt = torch.bfloat16 if self.packed else torch.float32
@@ -102,12 +125,17 @@ class MtaOptimizer(torch.optim.Optimizer):
         st.setdefault("step", 0)
         return None, None
 
-    @staticmethod
-    def _check(p):
-        if p.dtype != torch.float32 or not p.is_cuda or \
+    def _check(self, p):
+        if self.master_weights:
+            if p.dtype not in (torch.bfloat16, torch.float16) or \
+                    not p.is_cuda or not p.is_contiguous():
+                raise TypeError("with master_weights, parameters must be "
+                                "contiguous bfloat16 or float16 CUDA "
+                                "tensors")
+        elif p.dtype != torch.float32 or not p.is_cuda or \
                 not p.is_contiguous():
             raise TypeError("parameters must be contiguous float32 CUDA "
-                            "tensors")
+                            "tensors (16-bit ones need master_weights=True)")
         g = p.grad
         if g is None or not g.is_cuda or not g.is_contiguous():
             raise ValueError("every parameter needs a contiguous CUDA "
@@ -117,11 +145,12 @@ class MtaOptimizer(torch.optim.Optimizer):
         groups, key = [], []
         for p in params:
             m, v = self._state_buffers(p)
-            groups.append((p, p.grad, m, v))
-            key.append((p.data_ptr(), p.grad.data_ptr(),
+            w = self.master(p)
+            groups.append((w, p.grad, m, v))
+            key.append((w.data_ptr(), p.grad.data_ptr(),
                         None if m is None else m.data_ptr(),
                         None if v is None else v.data_ptr(), p.numel(),
-                        p.grad.dtype))
+                        p.grad.dtype, p.data_ptr()))
         key = tuple(key)
         cached = self._lists.get(k)
         if cached is None or cached[0] != key:
@@ -137,21 +166,28 @@ class MtaOptimizer(torch.optim.Optimizer):
                                       p.numel()) for p, g, m, v in groups],
                         gtype=gtype, mkind=mk, vkind=mk)
             L._keep = groups
+            if self.master_weights:
+                # the parameters are the list's 16-bit weight copies
+                L.set_weight_copies([p.detach() for p in params])
             self._lists[k] = (key, L)
         return self._lists[k][1]
 
     def _joint_norm_list(self, all_params):
-        key = tuple((p.data_ptr(), p.grad.data_ptr(), p.numel(),
-                     p.grad.dtype) for p in all_params)
+        # the norm reads only the gradients; w is the float32 weight the
+        # list's validation sizes as 4 bytes per element
+        ws = [self.master(p) for p in all_params]
+        key = tuple((w.data_ptr(), p.grad.data_ptr(), p.numel(),
+                     p.grad.dtype) for w, p in zip(ws, all_params))
         if self._norm_list is None or self._norm_list[0] != key:
             if self._norm_list is not None:
                 self._norm_list[1].close()
             gtype = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
                      torch.float16: B.MTA_F16}[all_params[0].grad.dtype]
-            L = MtaList([], entries=[(p.data_ptr(), p.grad.data_ptr(), None,
-                                      None, p.numel()) for p in all_params],
+            L = MtaList([], entries=[(w.data_ptr(), p.grad.data_ptr(), None,
+                                      None, p.numel())
+                                     for w, p in zip(ws, all_params)],
                         gtype=gtype, mkind=B.MTA_MOM_F32, vkind=B.MTA_MOM_F32)
-            L._keep = [(p, p.grad) for p in all_params]
+            L._keep = [(w, p.grad) for w, p in zip(ws, all_params)]
             self._norm_list = (key, L)
         return self._norm_list[1]
 
@@ -171,6 +207,10 @@ class MtaOptimizer(torch.optim.Optimizer):
             self._check(p)
         if len({p.grad.dtype for p in all_params}) != 1:
             raise TypeError("all gradients must share one dtype")
+        if self.master_weights and \
+                len({p.dtype for p in all_params}) != 1:
+            raise TypeError("with master_weights, all parameters must share "
+                            "one dtype")
         coef = None
         if self.max_norm is not None or self.amp is not None:
             dev = all_params[0].device
@@ -210,3 +250,23 @@ class MtaOptimizer(torch.optim.Optimizer):
         if self.amp is not None:
             self.amp.update(*self._amp_rule)
         return loss
+
+    # -- checkpoints ------------------------------------------------------
+    def load_state_dict(self, state_dict):
+        """As torch.optim.Optimizer.load_state_dict, except that every state
+        tensor comes back in the dtype it was saved in (masters and float32
+        moments of a 16-bit parameter stay float32)."""
+        super().load_state_dict(state_dict)
+        ids = [i for g in state_dict["param_groups"] for i in g["params"]]
+        params = [p for g in self.param_groups for p in g["params"]]
+        saved = state_dict["state"]
+        for i, p in zip(ids, params):
+            for name, val in saved.get(i, {}).items():
+                if torch.is_tensor(val) and name != "step":
+                    self.state[p][name] = val.to(
+                        device=p.device, dtype=val.dtype,
+                        copy=True).contiguous()
+        # every table is rebuilt on the next step
+        for _, L in self._lists.values():
+            L.close()
+        self._lists = {}

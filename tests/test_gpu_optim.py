@@ -248,3 +248,108 @@ def test_capturable_matches_the_plain_step_on_finite_gradients():
     # ones libm's pow; they agree at these t, so the runs are identical
     for pa, pb in zip(a.parameters(), b.parameters()):
         assert torch.equal(pa, pb)
+
+
+def _bits16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(
+        np.uint16).ravel().copy()
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16],
+                         ids=["bf16", "f16"])
+def test_master_weights_match_the_oracle_bitwise(dt):
+    # a 16-bit model: float32 masters in the optimizer, 16-bit gradients,
+    # and the new masters' 16-bit rounding written into the parameters by
+    # the update launch; float16 runs loss-scaled with an overflow at t = 4
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model(13).to(dt)
+    params = list(model.parameters())
+    gt = O.BF16 if dt == torch.bfloat16 else O.F16
+    scaled = dt == torch.float16
+    opt = MtaOptimizer(params, kind="adamw", lr=1e-3, weight_decay=0.1,
+                       max_norm=1.0, master_weights=True,
+                       loss_scale=1024.0 if scaled else None,
+                       growth_interval=2)
+    rule = dict(kind="adamw", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                weight_decay=0.1, momentum=0.0)
+    ost = [O.Tensor(_host(p.float()).ravel(), None,
+                    np.zeros(p.numel(), np.float32),
+                    np.zeros(p.numel(), np.float32),
+                    np.zeros(p.numel(), np.uint16), gt) for p in params]
+    amp_o = O.AmpState(1024.0) if scaled else None
+    for t in range(1, 7):
+        torch.manual_seed(3000 + t)
+        x = torch.randn(32, 300, device="cuda", dtype=dt)
+        y = torch.randint(0, 10, (32,), device="cuda")
+        model.zero_grad(set_to_none=False)
+        loss = torch.nn.functional.cross_entropy(model(x).float(), y)
+        (loss * opt.loss_scale if scaled else loss).backward()
+        if scaled and t == 4:
+            params[2].grad[1, 1] = float("inf")
+        for p, o in zip(params, ost):
+            assert p.grad.dtype == dt
+            o.g = _bits16(p.grad)
+        before = [_bits16(p) for p in params]
+        opt.step()
+        torch.cuda.synchronize()
+        coef = np.float32(opt.last_coef.item())
+        if scaled:
+            _, _, found = O.amp_opt_step_(ost, rule, gt, 0, 0, amp_o, 1.0,
+                                          coef=coef)
+            assert found == (t == 4)
+            amp_o.update(2.0, 0.5, 2)
+            assert opt.amp.read()["step"] == amp_o.step
+        else:
+            nrm = O.norm([o.g for o in ost], gt)
+            assert abs(float(opt.last_norm.item()) - nrm) <= 1e-6 * nrm
+            O.opt_step_(ost, rule, gt, 0, 0, t, coef=coef)
+        for p, o, b in zip(params, ost, before):
+            w = opt.state[p]["master_weight"]
+            assert w.dtype == torch.float32
+            assert np.array_equal(_host(w).ravel().view(np.uint32),
+                                  o.w.view(np.uint32)), (t, "master")
+            assert np.array_equal(_bits16(p), o.w16), (t, "parameter")
+            if scaled and t == 4:
+                assert np.array_equal(_bits16(p), b)   # skipped step
+
+
+def test_master_weights_state_dict_keeps_float32_state():
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+
+    def make():
+        m = _model(17).to(torch.bfloat16)
+        return m, MtaOptimizer(m.parameters(), kind="adamw", lr=1e-3,
+                               weight_decay=0.1, max_norm=1.0,
+                               master_weights=True)
+
+    def grads(m, t):
+        torch.manual_seed(4000 + t)
+        x = torch.randn(16, 300, device="cuda", dtype=torch.bfloat16)
+        y = torch.randint(0, 10, (16,), device="cuda")
+        m.zero_grad(set_to_none=False)
+        torch.nn.functional.cross_entropy(m(x).float(), y).backward()
+
+    ref, opt_ref = make()
+    for t in range(1, 7):
+        grads(ref, t)
+        opt_ref.step()
+    run, opt = make()
+    for t in range(1, 4):
+        grads(run, t)
+        opt.step()
+    saved = copy.deepcopy(opt.state_dict())
+    run2 = copy.deepcopy(run)
+    opt2 = MtaOptimizer(run2.parameters(), kind="adamw", lr=1e-3,
+                        weight_decay=0.1, max_norm=1.0, master_weights=True)
+    opt2.load_state_dict(saved)
+    for p in run2.parameters():
+        for name in ("master_weight", "exp_avg", "exp_avg_sq"):
+            assert opt2.state[p][name].dtype == torch.float32, name
+    for t in range(4, 7):
+        grads(run2, t)
+        opt2.step()
+    torch.cuda.synchronize()
+    for pa, pb in zip(ref.parameters(), run2.parameters()):
+        assert torch.equal(pa.view(torch.int16), pb.view(torch.int16))
+        assert torch.equal(opt_ref.state[pa]["master_weight"],
+                           opt2.state[pb]["master_weight"])

@@ -29,3 +29,14 @@ def test_step_without_gradients_is_a_no_op():
     opt = MtaOptimizer(ps, kind="sgd", lr=0.1)
     assert opt.step() is None
     assert torch.equal(ps[0].detach(), torch.zeros(10))
+
+
+def test_master_weights_refuse_float32_and_mixed_parameters():
+    ps = _params()
+    ps[0].grad = torch.zeros(10)
+    with pytest.raises(TypeError):       # float32 parameters, CPU too
+        MtaOptimizer(ps, master_weights=True).step()
+    h = [torch.nn.Parameter(torch.zeros(10, dtype=torch.bfloat16))]
+    h[0].grad = torch.zeros(10, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):       # 16-bit without master weights
+        MtaOptimizer(h).step()
