@@ -277,6 +277,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--layout", default="padded", choices=["padded", "flat"],
+                    help="padded: every tensor starts 16-byte aligned in "
+                         "each buffer; flat: tensors back to back in one "
+                         "buffer per kind, as a flat parameter / gradient "
+                         "buffer holds them (a tensor may start anywhere)")
     ap.add_argument("--cpu-steps", type=int, default=30,
                     help="oracle steps of the CPU baseline (0 = skip); the "
                          "default is about 11 s of one host core on the "
@@ -336,7 +341,12 @@ def main():
               "scale live on the device, so a captured step can be "
               "replayed): e.g. --workload gpt2_124m_f16amp", file=sys.stderr)
         sys.exit(2)
-    arena = WL.Arena(wl, "cuda")
+    offsets = None
+    if args.layout == "flat":
+        offsets = [0]
+        for n in wl.sizes[:-1]:
+            offsets.append(offsets[-1] + n)
+    arena = WL.Arena(wl, "cuda", offsets)
     arena.fill_weights()
     arena.fill_grads(1)
     opt = opt_of(wl, args.opt, args.zero_grad)
@@ -454,7 +464,7 @@ def main():
     norm_bytes = wl.n * bpp["norm"]
     value = wl.n * args.steps / (host_s)
     achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
-    traffic = (None if args.weight_copy
+    traffic = (None if args.weight_copy or args.layout != "padded"
                else measured_traffic(traffic_key(wl, args.opt, args.zero_grad),
                                      kernel))
     out = {
@@ -473,6 +483,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "params": wl.n, "tensors": wl.count,
+            "layout": args.layout, "vector_tensors": info["vector_tensors"],
             "grad": ["f32", "bf16", "f16"][wl.gtype],
             "loss_scaling": "dynamic (device state)" if wl.amp else "none",
             "m": ["f32", "bf16x2"][wl.mkind], "v": ["f32", "bf16x2"][wl.vkind],

@@ -57,7 +57,13 @@
  *                needs 2n bytes.
  *   Alignment    float32 buffers 4 bytes, bfloat16 buffers 2 bytes.  A tensor
  *                whose buffers are all 16-byte aligned takes the 16-byte
- *                vector path; any other tensor is processed element by element.
+ *                vector path.  One whose buffers all become aligned together
+ *                after its first h elements (tensors at the same element
+ *                offset of flat buffers, for instance) has those h elements
+ *                processed one by one and the rest on the vector path: h < 64
+ *                where that reaches a 128-byte boundary in every buffer, else
+ *                h < 8 to 16 bytes.  Any other tensor is processed element by
+ *                element.
  *   Buffers of one list must not overlap (checked at create).
  *
  * Streams.  Every device call enqueues its work on the caller's hipStream_t
@@ -144,7 +150,8 @@ typedef struct {
   int32_t grid_update; /* workgroups of an update / scale launch */
   int32_t grid_norm;   /* workgroups of the norm launch (= norm partials) */
   int32_t device;      /* HIP device the list lives on */
-  int32_t vector_tensors; /* tensors that take the 16-byte vector path */
+  int32_t vector_tensors; /* tensors that take the 16-byte vector path
+                             (after a head of under 64 elements) */
   int32_t gtype, mkind, vkind;
   int32_t weight_copies;  /* tensors with an attached 16-bit weight copy */
   int32_t state_buffers;  /* bit 0: the list has m; bit 1: it has v */

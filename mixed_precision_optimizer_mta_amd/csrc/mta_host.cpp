@@ -210,8 +210,47 @@ void list_spans(const mta_list *L, std::vector<Span> *spans) {
 
 uintptr_t elem_size(int kind_is_16bit) { return kind_is_16bit ? 2 : 4; }
 
+// Elements to take off the front of a tensor so that every buffer it has is
+// aligned from there on: the smallest h < 64 that puts all of them on a
+// 128-byte cache-line boundary, else the smallest h < 8 that makes all of
+// them 16-byte aligned, else -1 (their misalignments disagree).  Elements
+// are 2 or 4 bytes and each buffer is aligned to its element size, so a
+// buffer's offset mod 128 repeats every 64 elements and mod 16 every 8.
+// Line-aligned tiles keep every wave's stores to whole cache lines, as in
+// a tensor that starts on one.
+int64_t vector_peel(const mta_tensor &x, int gtype, int mkind, int vkind) {
+  const void *bufs[4] = {x.w, x.g, x.m, x.v};
+  const uintptr_t sizes[4] = {4, elem_size(gtype != MTA_F32),
+                              elem_size(mkind == MTA_MOM_BF16X2),
+                              elem_size(vkind == MTA_MOM_BF16X2)};
+  const auto first = [&](uintptr_t period, uintptr_t align) -> int64_t {
+    for (uintptr_t h = 0; h < period; ++h) {
+      bool ok = true;
+      for (int b = 0; b < 4 && ok; ++b)
+        ok = !bufs[b] ||
+             (reinterpret_cast<uintptr_t>(bufs[b]) + h * sizes[b]) % align ==
+                 0;
+      if (ok) return static_cast<int64_t>(h);
+    }
+    return -1;
+  };
+  const int64_t line = first(64, 128);
+  return line >= 0 ? line : first(8, 16);
+}
+
+// Tiles of a tensor of n > 0 elements with vector_peel h: a head tile of h
+// elements when 0 < h < n, then whole tiles from there.
+uint64_t tiles_of(int64_t n, int64_t h) {
+  const uint64_t head = (h > 0) ? static_cast<uint64_t>(h < n ? h : n) : 0;
+  const uint64_t rest = static_cast<uint64_t>(n) - head;
+  return (head ? 1 : 0) + (rest + mta::kTileElems - 1) / mta::kTileElems;
+}
+
 // One StepTile per tile of every non-empty tensor, in list order.  w16 may be
-// empty (no copies) or hold one pointer per tensor.
+// empty (no copies) or hold one pointer per tensor.  The tile cuts depend on
+// w, g, m, v only, so attaching copies never changes the tile count; a copy
+// that is not 16-byte aligned at the vector tiles' starts sends the tensor
+// down the element path.
 void build_step_tiles(const std::vector<mta_tensor> &tensors,
                       const std::vector<void *> &w16, int gtype, int mkind,
                       int vkind, std::vector<mta::StepTile> *out) {
@@ -221,13 +260,14 @@ void build_step_tiles(const std::vector<mta_tensor> &tensors,
   out->clear();
   for (size_t i = 0; i < tensors.size(); ++i) {
     const mta_tensor &x = tensors[i];
+    if (x.n == 0) continue;
     void *copy = w16.empty() ? nullptr : w16[i];
-    const bool vec = aligned(x.w, 16) && aligned(x.g, 16) && aligned(x.m, 16) &&
-                     aligned(x.v, 16) && (!copy || aligned(copy, 16));
-    for (int64_t base = 0; base < x.n; base += mta::kTileElems) {
-      const int64_t left = x.n - base;
-      const uint32_t lim = static_cast<uint32_t>(
-          left < mta::kTileElems ? left : mta::kTileElems);
+    const int64_t peel = vector_peel(x, gtype, mkind, vkind);
+    const int64_t head = peel > 0 ? std::min(peel, x.n) : 0;
+    const bool vec =
+        peel >= 0 &&
+        (!copy || (reinterpret_cast<uintptr_t>(copy) + head * 2) % 16 == 0);
+    const auto push = [&](int64_t base, int64_t lim, bool v) {
       const uintptr_t b = static_cast<uintptr_t>(base);
       const auto at = [b](const void *p, uintptr_t size) -> void * {
         return p ? reinterpret_cast<char *>(const_cast<void *>(p)) + b * size
@@ -238,10 +278,15 @@ void build_step_tiles(const std::vector<mta_tensor> &tensors,
       st.g = at(x.g, gsz);
       st.m = at(x.m, msz);
       st.v = at(x.v, vsz);
-      st.lim = lim;
-      st.vec = vec ? 1u : 0u;
+      st.lim = static_cast<uint32_t>(lim);
+      st.vec = v ? 1u : 0u;
       st.w16 = at(copy, 2);
       out->push_back(st);
+    };
+    if (head > 0) push(0, head, false);
+    for (int64_t base = head; base < x.n; base += mta::kTileElems) {
+      const int64_t left = x.n - base;
+      push(base, left < mta::kTileElems ? left : mta::kTileElems, vec);
     }
   }
 }
@@ -459,9 +504,8 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
         return fail(MTA_EALIGN,
                     "tensor %lld: a buffer is not aligned to its element size",
                     static_cast<long long>(i));
-      const bool vec = aligned(x.w, 16) && aligned(x.g, 16) &&
-                       aligned(x.m, 16) && aligned(x.v, 16);
-      vec_tensors += vec ? 1 : 0;
+      const int64_t peel = vector_peel(x, gtype, mkind, vkind);
+      vec_tensors += (peel >= 0 && peel < x.n) ? 1 : 0;
       const uintptr_t n = static_cast<uintptr_t>(x.n);
       const void *bufs[4] = {x.w, x.g, x.m, x.v};
       const uintptr_t sizes[4] = {4, gsz, msz, vsz};
@@ -471,9 +515,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
         spans.push_back(Span{lo, lo + n * sizes[b], i, b});
       }
       elements += x.n;
-      const uint64_t nt = (static_cast<uint64_t>(x.n) + mta::kTileElems - 1) /
-                          mta::kTileElems;
-      ntiles += nt;
+      ntiles += tiles_of(x.n, peel);
       // tile numbers and grid strides stay below 2^32 (no wrap-around)
       if (ntiles > (uint64_t{1} << 31)) return fail(MTA_EINVAL, "list too large");
     }
@@ -635,6 +677,8 @@ int mta_list_set_weight_copies_as(mta_list *L, void *const *w16,
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
   }
+  if (stiles.size() != L->ntiles)  // the cuts depend on w, g, m, v only
+    return fail(MTA_EINVAL, "internal: the tile count changed");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (!stiles.empty())

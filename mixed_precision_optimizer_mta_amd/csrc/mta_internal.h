@@ -11,8 +11,11 @@
 namespace mta {
 
 // A tile is the work of one workgroup iteration: up to kTileElems consecutive
-// elements of one tensor, starting at a multiple of kTileElems.  Tiles never
-// straddle tensors, so every vector access inside a tile stays in one buffer.
+// elements of one tensor.  Tiles never straddle tensors, so every vector
+// access inside a tile stays in one buffer.  A tensor's tiles start at
+// multiples of kTileElems, or, when its buffers reach alignment together only
+// after its first h (1..63) elements, at 0 (a head tile of h elements) and
+// then at h + multiples of kTileElems.
 constexpr int kBlock = 256;       // threads per workgroup (4 wave64s)
 constexpr int kTileElems = 4096;  // 16 elements per thread
 

@@ -158,10 +158,15 @@ def _seed(wl, buffer, step):
 class Arena:
     """Flat buffers w, g, m, v for a whole list on one device; tensor i
     occupies elements [off[i], off[i] + n[i]) of each (same element offsets
-    for every buffer kind)."""
+    for every buffer kind; g_shift, 0..ALIGN_ELEMS-1, moves every gradient
+    that many elements further, to give g a different alignment from the
+    other buffers)."""
 
-    def __init__(self, wl, device, offsets=None):
+    def __init__(self, wl, device, offsets=None, g_shift=0):
         import torch
+        if not 0 <= g_shift < ALIGN_ELEMS:
+            raise ValueError("g_shift must be in [0, ALIGN_ELEMS)")
+        self.g_shift = int(g_shift)
         self.wl = wl
         self.device = torch.device(device)
         if offsets is None:
@@ -187,6 +192,8 @@ class Arena:
 
     def view(self, buf, i):
         o, n = self.offsets[i], self.wl.sizes[i]
+        if buf == "g":
+            o += self.g_shift
         return getattr(self, buf)[o:o + n]
 
     def entries(self):
@@ -194,7 +201,8 @@ class Arena:
         out = []
         for i, n in enumerate(self.wl.sizes):
             o = self.offsets[i]
-            out.append((self.w[o:].data_ptr(), self.g[o:].data_ptr(),
+            out.append((self.w[o:].data_ptr(),
+                        self.g[o + self.g_shift:].data_ptr(),
                         self.m[o:].data_ptr(), self.v[o:].data_ptr(), n))
         return out
 

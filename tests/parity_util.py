@@ -163,6 +163,32 @@ def sample_positions(wl, offsets, nsample, seed=1):
     return np.unique(np.concatenate(parts))
 
 
+def expected_tiles(entries, gtype, mkind, vkind):
+    """(tiles, vector tensors) a list of these (w, g, m, v, n) entries must
+    have: a tensor whose present buffers all reach a 128-byte boundary
+    after its first h elements, or else all reach 16-byte alignment (the
+    smallest such h, found by trying every h up to 127, then up to 15), is
+    cut into a head of h elements, if h > 0, and then 4096-element tiles;
+    any other tensor into 4096-element tiles from 0."""
+    sz = [4, 4 if gtype == WL.F32 else 2,
+          2 if mkind == WL.MOM_BF16X2 else 4,
+          2 if vkind == WL.MOM_BF16X2 else 4]
+    tiles = vec = 0
+    for w, g, m, v, n in entries:
+        if n == 0:
+            continue
+        bufs = [(p, s) for p, s in zip((w, g, m, v), sz) if p]
+        h = next((h for h in range(128)
+                  if all((p + h * s) % 128 == 0 for p, s in bufs)), None)
+        if h is None:
+            h = next((h for h in range(16)
+                      if all((p + h * s) % 16 == 0 for p, s in bufs)), None)
+        head = min(h, n) if h else 0
+        tiles += (1 if head else 0) + -(-(n - head) // 4096)
+        vec += h is not None and h < n
+    return tiles, vec
+
+
 def make_list(arena):
     from mixed_precision_optimizer_mta_amd import MtaList
     wl = arena.wl
@@ -185,7 +211,7 @@ def check_amp_state(dev, ora, what=""):
 
 
 def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
-             check_guards=False, clip=True, inject=None):
+             check_guards=False, clip=True, inject=None, g_shift=0):
     """Run `steps` device steps in lockstep with the oracle; returns the
     worst ulp distances seen.
 
@@ -196,7 +222,8 @@ def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
     the gradients after they are drawn (positions must be sampled ones when
     nsample is set, so the oracle sees them)."""
     from mixed_precision_optimizer_mta_amd import AmpState
-    arena = WL.Arena(wl, "cuda", offsets)
+    assert not (g_shift and nsample is not None), "sampling reads g unshifted"
+    arena = WL.Arena(wl, "cuda", offsets, g_shift=g_shift)
     arena.fill_weights()
     L = make_list(arena)
     idx = None

@@ -101,8 +101,9 @@ def compare_rule(arena, ost, kind, idx=None, what=""):
 
 
 def rule_lockstep(wl, opt, steps, offsets=None, nsample=None,
-                  norm_steps=None, check_guards=False):
-    arena = WL.Arena(wl, "cuda", offsets)
+                  norm_steps=None, check_guards=False, g_shift=0):
+    assert not (g_shift and nsample is not None)
+    arena = WL.Arena(wl, "cuda", offsets, g_shift=g_shift)
     arena.fill_weights()
     kind, zero = opt["kind"], bool(opt.get("zero_grad"))
     L = make_rule_list(arena, kind)
@@ -138,12 +139,13 @@ def rule_lockstep(wl, opt, steps, offsets=None, nsample=None,
                     coef=coef, zero=zero)
         compare_rule(arena, ost, kind, idx, f"{wl.name} {kind} t={t}")
         if check_guards:
-            inside = torch.zeros(arena.total, dtype=torch.bool,
-                                 device="cuda")
-            for o, n in zip(arena.offsets, wl.sizes):
-                inside[o:o + n] = True
             has_m, has_v = uses(kind)
             for b in "wgmv":
+                sh = arena.g_shift if b == "g" else 0
+                inside = torch.zeros(arena.total, dtype=torch.bool,
+                                     device="cuda")
+                for o, n in zip(arena.offsets, wl.sizes):
+                    inside[o + sh:o + sh + n] = True
                 now = getattr(arena, b)
                 ity = torch.int32 if now.dtype == torch.float32 else \
                     torch.int16
@@ -182,7 +184,8 @@ def test_adamw_zero_grad_keeps_the_update():
 
 @pytest.mark.parametrize("kind", ["adam", "sgd", "momentum"])
 def test_rules_unaligned_tensors(kind):
-    sizes = [5000, 4096, 33, 9000]
+    # every buffer 1 element (mod 8) off: a head tile, then vector tiles
+    sizes = [5000, 4096, 33, 9000, 5]
     offsets, pos = [], 0
     for n in sizes:
         offsets.append(pos + 1)
@@ -190,6 +193,15 @@ def test_rules_unaligned_tensors(kind):
     wl = WL.Workload("unaligned_rules", sizes, 1, 0, 0, steps=2, ident=34)
     rule_lockstep(wl, opt_for(kind, zero=True), 2, offsets=offsets,
                   check_guards=True)
+
+
+@pytest.mark.parametrize("kind", ["adam", "sgd", "momentum"])
+def test_rules_disagreeing_misalignments(kind):
+    # g one element off w (and m, v): the element path throughout
+    sizes = [5000, 4096, 33, 9000]
+    wl = WL.Workload("unaligned_rules2", sizes, 1, 0, 0, steps=2, ident=35)
+    rule_lockstep(wl, opt_for(kind, zero=True), 2, check_guards=True,
+                  g_shift=1)
 
 
 def test_sgd_and_momentum_write_their_weight_copies():

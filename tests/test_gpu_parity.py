@@ -15,8 +15,8 @@ from mixed_precision_optimizer_mta_amd import workloads as WL
 
 pytestmark = pytest.mark.gpu
 
-from parity_util import (check_norm, compare, lockstep,  # noqa: E402
-                         make_list, oracle_grads, oracle_state)
+from parity_util import (check_norm, compare, expected_tiles,  # noqa: E402
+                         lockstep, make_list, oracle_grads, oracle_state)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -75,11 +75,16 @@ def test_edge_sizes_every_kind(gtype, mkind, vkind):
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
-@pytest.mark.parametrize("gtype,mkind,vkind", [(0, 0, 0), (1, 1, 0),
-                                               (1, 1, 1), (2, 0, 1)])
-def test_unaligned_tensors_take_the_element_path(gtype, mkind, vkind):
-    # element offsets of 1 (mod 8) break 16-byte alignment of every buffer
-    sizes = [5000, 4096, 33, 9000]
+UNALIGNED_KINDS = [(0, 0, 0), (1, 1, 0), (1, 1, 1), (2, 0, 1)]
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind", UNALIGNED_KINDS)
+def test_unaligned_tensors_peel_a_head_then_vectorize(gtype, mkind, vkind):
+    # element offsets of 1 (mod 8) put every buffer 4 or 2 bytes off 16-byte
+    # alignment, all by the same element count: a head of up to 63 elements
+    # brings every buffer to a cache-line boundary, and the rest of the
+    # tensor runs on the vector path
+    sizes = [5000, 4096, 33, 9000, 7, 3]
     offsets, pos = [], 0
     for n in sizes:
         offsets.append(pos + 1)             # 1 (mod 8): 4 or 2 bytes off
@@ -88,7 +93,48 @@ def test_unaligned_tensors_take_the_element_path(gtype, mkind, vkind):
                      ident=12)
     arena = WL.Arena(wl, "cuda", offsets)
     L = make_list(arena)
-    assert L.info()["vector_tensors"] == 0
+    info = L.info()
+    assert (info["tiles"], info["vector_tensors"]) == \
+        expected_tiles(arena.entries(), gtype, mkind, vkind)
+    assert info["vector_tensors"] == 4      # 7 and 3: all head
+    assert info["tiles"] == 3 + 2 + 2 + 4 + 1 + 1
+    L.close()
+    worst = lockstep(wl, 2, offsets=offsets, check_guards=True)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind", UNALIGNED_KINDS)
+def test_disagreeing_misalignments_take_the_element_path(gtype, mkind, vkind):
+    # g one element further than w, m, v: no head length aligns both
+    sizes = [5000, 4096, 33, 9000]
+    wl = WL.Workload("unaligned2", sizes, gtype, mkind, vkind, steps=2,
+                     ident=14)
+    arena = WL.Arena(wl, "cuda", g_shift=1)
+    L = make_list(arena)
+    info = L.info()
+    assert info["vector_tensors"] == 0
+    assert info["tiles"] == 2 + 1 + 1 + 3
+    L.close()
+    worst = lockstep(wl, 2, check_guards=True, g_shift=1)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+@pytest.mark.parametrize("gtype,mkind,vkind", [(0, 0, 0), (1, 1, 0),
+                                               (2, 1, 1)])
+def test_flat_buffer_layout(gtype, mkind, vkind):
+    # tensors back to back in one buffer per kind, as a flat parameter
+    # buffer holds them: every start offset mod 8 occurs
+    rng = np.random.default_rng(15)
+    sizes = [int(x) for x in rng.integers(1, 12000, size=40)]
+    offsets = np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
+    wl = WL.Workload("flat", sizes, gtype, mkind, vkind, steps=2,
+                     g_sigma=0.05, ident=16)
+    arena = WL.Arena(wl, "cuda", offsets)
+    L = make_list(arena)
+    info = L.info()
+    assert (info["tiles"], info["vector_tensors"]) == \
+        expected_tiles(arena.entries(), gtype, mkind, vkind)
+    assert info["vector_tensors"] >= sum(1 for n in sizes if n >= 64)
     L.close()
     worst = lockstep(wl, 2, offsets=offsets, check_guards=True)
     assert worst == {"w": 0, "m": 0, "v": 0}, worst

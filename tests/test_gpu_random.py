@@ -20,6 +20,7 @@ from mixed_precision_optimizer_mta_amd import workloads as WL
 pytestmark = pytest.mark.gpu
 
 from parity_util import (bf16_ulp, check_amp_state, check_norm,  # noqa: E402
+                         expected_tiles,
                          dev_bf16_bits, dev_f32, f32_ulp, grad_np, mom_np,
                          oracle_grads)
 
@@ -88,6 +89,9 @@ def run_case(c):
     ents = [(w, g, m if has_m else None, v if has_v else None, n)
             for (w, g, m, v, n) in arena.entries()]
     L = MtaList([], entries=ents, gtype=gtype, mkind=mkind, vkind=vkind)
+    info = L.info()
+    assert (info["tiles"], info["vector_tensors"]) == \
+        expected_tiles(ents, gtype, mkind, vkind)
     copies = None
     picked = [p and c["copies"] for p in c["pick"]]
     if c["copies"]:

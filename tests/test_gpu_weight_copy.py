@@ -99,6 +99,18 @@ def test_weight_copy_partial_attach_and_unaligned_copies(dtype):
 
 
 @pytest.mark.parametrize("dtype", COPY, ids=["bf16", "f16"])
+def test_weight_copy_at_the_weights_flat_offsets(dtype):
+    # tensors and copies at the same odd element offsets: the copies stay
+    # aligned with the other buffers after the head, so the vector path
+    # writes them; shifted one element more, the element path does
+    sizes = [5000, 4096, 33, 9000, 5]
+    offsets = np.concatenate([[3], 3 + np.cumsum(sizes)[:-1]]).tolist()
+    wl = WL.Workload("copies5", sizes, 1, 1, 0, steps=2, ident=25)
+    run(wl, 2, offsets=offsets, dtype=dtype)
+    run(wl, 2, offsets=offsets, copy_shift=1, dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", COPY, ids=["bf16", "f16"])
 def test_weight_copy_of_extreme_weights(dtype):
     # weights at and past the float16 range, subnormal in float16, signed
     # zeros and NaN, in a vector tile and in a ragged tail
