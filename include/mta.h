@@ -156,7 +156,10 @@ typedef struct {
   int32_t weight_copies;  /* tensors with an attached 16-bit weight copy */
   int32_t state_buffers;  /* bit 0: the list has m; bit 1: it has v */
   int32_t weight_copy_type; /* MTA_BF16 or MTA_F16: the copies' format */
-  int32_t reserved;
+  int32_t norm_kept_tiles;  /* the list's last tiles, whose gradients the
+                               norm reads with cache-allocating loads so
+                               that the update finds them in the device's
+                               memory-side cache (a cache policy only) */
 } mta_list_info_t;
 
 /* The update rules of "BendTorch main.bend", section "Optimizers" (the Opt

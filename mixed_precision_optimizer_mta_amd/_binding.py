@@ -68,7 +68,7 @@ class mta_list_info_t(ctypes.Structure):
                 ("vkind", ctypes.c_int32), ("weight_copies", ctypes.c_int32),
                 ("state_buffers", ctypes.c_int32),
                 ("weight_copy_type", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("norm_kept_tiles", ctypes.c_int32)]
 
 
 class MtaError(RuntimeError):

@@ -25,6 +25,7 @@ struct mta_list {
   int64_t count = 0;
   int64_t elements = 0;
   uint32_t ntiles = 0;
+  uint32_t keep_from = 0;  // first tile the norm reads with allocating loads
   int cus = 1;          // compute units of the device
   int grid_update = 1;  // workgroups of an AdamW / scale launch
   int grid_norm = 1;
@@ -83,6 +84,17 @@ bool debug_sync() {
 constexpr int kUpdateBlocksPerCu = 1;
 constexpr int kNormBlocksPerCuF32 = 1;
 constexpr int kNormBlocksPerCu16 = 2;
+
+// Gradient bytes, at the end of the list, that the norm reads with
+// allocating loads so that the memory-side cache (256 MiB on MI355X) still
+// holds them when the update reads them again; the update's own accesses
+// stream past it.  Only for lists whose gradients total at most
+// kNormKeepListMiB: in a longer list the update moves many GB before it
+// reaches those tiles, they no longer hit, and the allocating loads only
+// slow the norm.  MTA_NORM_KEEP_MIB sets the budget for any list at list
+// creation (0: every norm load streams).
+constexpr int kNormKeepMiB = 256;
+constexpr int64_t kNormKeepListMiB = 1024;
 
 int after_launch(hipError_t e, hipStream_t stream, const char *what) {
   if (e != hipSuccess)
@@ -296,6 +308,7 @@ mta::Work work_of(const mta_list *L, int grid, void *stream) {
   w.gtiles = L->d_gtiles;
   w.stiles = L->d_stiles;
   w.ntiles = L->ntiles;
+  w.keep_from = L->keep_from;
   w.grid = grid;
   w.stream = static_cast<hipStream_t>(stream);
   return w;
@@ -469,6 +482,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   std::vector<mta::StepTile> stiles;
   std::vector<mta_tensor> kept;
   std::vector<Span> spans;
+  uint32_t keep_from = 0;
   int64_t elements = 0;
   int vec_tensors = 0;
   int state = -1;  // m / v presence of the first non-empty tensor
@@ -528,6 +542,21 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
     gtiles.reserve(stiles.size());
     for (const mta::StepTile &st : stiles)
       gtiles.push_back(mta::GradTile{st.g, st.lim, aligned(st.g, 16) ? 1u : 0u});
+    // the last tiles, up to the keep budget
+    const int keep_default =
+        elements * static_cast<int64_t>(gsz) <= (kNormKeepListMiB << 20)
+            ? kNormKeepMiB
+            : 0;
+    uint64_t budget = static_cast<uint64_t>(env_int(
+                          "MTA_NORM_KEEP_MIB", keep_default, 0, 1 << 20))
+                      << 20;
+    keep_from = static_cast<uint32_t>(gtiles.size());
+    while (keep_from > 0) {
+      const uint64_t bytes = uint64_t{gtiles[keep_from - 1].lim} * gsz;
+      if (bytes > budget) break;
+      budget -= bytes;
+      --keep_from;
+    }
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
   }
@@ -552,6 +581,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->count = count;
   L->elements = elements;
   L->ntiles = static_cast<uint32_t>(stiles.size());
+  L->keep_from = keep_from;
   L->vector_tensors = vec_tensors;
   L->cus = cus;
   L->state_buffers = state < 0 ? 3 : state;  // no element: any rule works
@@ -710,7 +740,7 @@ int mta_list_info(const mta_list *L, mta_list_info_t *out) {
   out->weight_copies = L->weight_copies;
   out->state_buffers = L->state_buffers;
   out->weight_copy_type = L->copy_type;
-  out->reserved = 0;
+  out->norm_kept_tiles = static_cast<int32_t>(L->ntiles - L->keep_from);
   return ok();
 }
 

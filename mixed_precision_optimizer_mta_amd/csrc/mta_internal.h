@@ -71,6 +71,7 @@ struct Work {
   const GradTile *gtiles;
   const StepTile *stiles;
   uint32_t ntiles;
+  uint32_t keep_from;  // k_sumsq: first tile read with allocating loads
   int grid;
   hipStream_t stream;
 };

@@ -172,6 +172,15 @@ __device__ __forceinline__ raw16_t<D> load16b_raw(MTA_GLOBAL const elem_t<D> *p,
   return __builtin_nontemporal_load((const MTA_GLOBAL raw16_t<D> *)(p + e));
 }
 
+// Keep = true: the same load without the streaming hint, so the line is
+// allocated in the caches on its way in (the norm's kept tiles, below).
+template <int D, bool Keep>
+__device__ __forceinline__ raw16_t<D> load16b(MTA_GLOBAL const elem_t<D> *p,
+                                             uint32_t e) {
+  if constexpr (Keep) return *((const MTA_GLOBAL raw16_t<D> *)(p + e));
+  else return load16b_raw<D>(p, e);
+}
+
 template <int D>
 __device__ __forceinline__ void unpack16b(const raw16_t<D> &a,
                                           float (&x)[kWide<D>]) {
@@ -672,34 +681,28 @@ constexpr uint64_t kEmptySlot = kNormSlotEmpty;
 // workgroup's ticket is normally visible by the first load.
 constexpr uint32_t kSpinLimit = 1u << 16;
 
-template <int D>
-__global__ void __launch_bounds__(kBlock)
-k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
-        float max_norm, double *__restrict__ partials,
-        unsigned int *__restrict__ ticket, float *__restrict__ d_norm,
-        float *__restrict__ d_coef, mta_amp_state *__restrict__ amp) {
+// One grid-stride walk of k_sumsq over tile pairs (t0, t0 + gridDim.x),
+// from t0 while t0 < end: two tiles per iteration, their records read one
+// iteration ahead (clamped to the last tile: always in bounds).  When both
+// tiles are full tiles of aligned tensors (the common case) all their loads
+// are issued as raw 16-byte vectors before any is unpacked; otherwise each
+// tile goes on its own, a tail tile through clamped one-element loads.
+// Keep selects the vector loads' cache policy; the kernel runs one walk of
+// each kind, one after the other, so each is its own loop (the compiler
+// would merge two policies behind one branch into one load and drop the
+// streaming hint).
+template <int D, bool Keep>
+__device__ __forceinline__ void sumsq_walk(
+    const GradTile *__restrict__ tiles, uint32_t ntiles, uint32_t end,
+    uint32_t &t0, GradTile (&rec)[2],
+    double (&acc)[kTileElems / (kBlock * kWide<D>)], float s) {
   constexpr int V = kWide<D>;
   constexpr int G = kTileElems / (kBlock * V);
-  if (amp) s = inv_scale(amp->scale);  // loss-scaled: unscale by 1/scale
-  // Two tiles per iteration (t and t + gridDim.x).  Their records are read
-  // one iteration ahead (clamped to the last tile: always in bounds).  When
-  // both tiles are full tiles of aligned tensors (the common case) all their
-  // loads are issued as raw 16-byte vectors before any is unpacked;
-  // otherwise each tile goes on its own, a tail tile through clamped
-  // one-element loads.
   constexpr int U = 2;
   const uint32_t last = ntiles ? ntiles - 1 : 0;
   const uint32_t stride = U * gridDim.x;
   const uint32_t e0 = threadIdx.x * V;
-  double acc[G] = {};
-  const uint32_t first = stream_of_block();
-  GradTile rec[U];
-  if (ntiles) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      rec[u] = tiles[min(first + u * gridDim.x, last)];
-  }
-  for (uint32_t t0 = first; t0 < ntiles; t0 += stride) {
+  for (; t0 < end; t0 += stride) {
     GradTile cur[U];
     bool valid[U];
     bool all_full = true;
@@ -716,8 +719,8 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < G; ++j)
-          r[u][j] = load16b_raw<D>(gp<elem_t<D>>(cur[u].g, j * (kBlock * V)),
-                                   e0);
+          r[u][j] = load16b<D, Keep>(gp<elem_t<D>>(cur[u].g, j * (kBlock * V)),
+                                     e0);
       // the next records only after the vector loads (scalar loads return
       // out of order: an earlier one would be waited for with these)
       __builtin_amdgcn_sched_barrier(0);
@@ -752,7 +755,7 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
         if (cur[u].vec && lim == kTileElems) {
 #pragma unroll
           for (int j = 0; j < G; ++j)
-            unpack16b<D>(load16b_raw<D>(pg + j * (kBlock * V), e0), x[j]);
+            unpack16b<D>(load16b<D, Keep>(pg + j * (kBlock * V), e0), x[j]);
         } else {
 #pragma unroll
           for (int j = 0; j < G; ++j)
@@ -770,6 +773,40 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
       }
     }
   }
+}
+
+// Tiles from keep_from on are the list's last gradient bytes, up to what
+// the device's memory-side cache holds: the norm reads them with allocating
+// loads so the update launch that follows, which reads the same gradients
+// last, finds them there instead of in HBM.  Earlier tiles stream.
+template <int D>
+__global__ void __launch_bounds__(kBlock)
+k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles,
+        uint32_t keep_from, float s, float max_norm,
+        double *__restrict__ partials, unsigned int *__restrict__ ticket,
+        float *__restrict__ d_norm, float *__restrict__ d_coef,
+        mta_amp_state *__restrict__ amp) {
+  constexpr int V = kWide<D>;
+  constexpr int G = kTileElems / (kBlock * V);
+  if (amp) s = inv_scale(amp->scale);  // loss-scaled: unscale by 1/scale
+  constexpr int U = 2;
+  const uint32_t last = ntiles ? ntiles - 1 : 0;
+  double acc[G] = {};
+  uint32_t t0 = stream_of_block();
+  GradTile rec[U];
+  if (ntiles) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      rec[u] = tiles[min(t0 + u * gridDim.x, last)];
+  }
+  // a pair streams when both its tiles lie before keep_from (a tile past
+  // the end counts as before it)
+  const uint32_t reach = (U - 1) * gridDim.x;
+  const uint32_t split = keep_from >= ntiles  ? ntiles
+                         : keep_from > reach ? keep_from - reach
+                                             : 0;
+  sumsq_walk<D, false>(tiles, ntiles, min(split, ntiles), t0, rec, acc, s);
+  sumsq_walk<D, true>(tiles, ntiles, ntiles, t0, rec, acc, s);
   double mine = acc[0];
 #pragma unroll
   for (int j = 1; j < G; ++j) mine += acc[j];
@@ -986,8 +1023,8 @@ hipError_t launch_sumsq_t(const Work &wk, float s, float max_norm,
                           NormScratch scr, float *d_norm, float *d_coef,
                           mta_amp_state *amp) {
   hipLaunchKernelGGL((k_sumsq<D>), dim3(wk.grid), dim3(kBlock), 0, wk.stream,
-                     wk.gtiles, wk.ntiles, s, max_norm, scr.partials,
-                     scr.ticket, d_norm, d_coef, amp);
+                     wk.gtiles, wk.ntiles, wk.keep_from, s, max_norm,
+                     scr.partials, scr.ticket, d_norm, d_coef, amp);
   return hipGetLastError();
 }
 

@@ -378,3 +378,53 @@ def test_independent_mode_report(name):
     print(f"independent mode {name}: worst {worst}", flush=True)
     assert worst["coef"] <= 8 and worst["w"] <= 4, worst
     assert worst["m"] <= 64 and worst["v"] <= 64, worst
+
+
+def test_norm_cache_policy_changes_no_bits(monkeypatch):
+    # the norm's kept tiles (allocating loads) are a cache policy only:
+    # every tile kept, none kept, or the default cut give the same norm,
+    # coefficient and update, bit for bit
+    wl = small("gpt2_124m")
+    wl = WL.scaled_down(wl, wl.sizes)
+    results = []
+    for keep in (None, "0", "100000"):
+        if keep is None:
+            monkeypatch.delenv("MTA_NORM_KEEP_MIB", raising=False)
+        else:
+            monkeypatch.setenv("MTA_NORM_KEEP_MIB", keep)
+        arena = WL.Arena(wl, "cuda")
+        arena.fill_weights()
+        arena.fill_grads(1)
+        L = make_list(arena)
+        info = L.info()
+        if keep == "0":
+            assert info["norm_kept_tiles"] == 0
+        else:                      # a small list: kept whole by default
+            assert info["norm_kept_tiles"] == info["tiles"]
+        nd = torch.zeros(1, device="cuda")
+        cd = torch.zeros(1, device="cuda")
+        L.clip_norm(wl.max_norm, nd, cd)
+        L.adamw_step(wl.hparams, 1, cd)
+        torch.cuda.synchronize()
+        results.append((nd.view(torch.int32).item(),
+                        cd.view(torch.int32).item(),
+                        arena.w.view(torch.int32).clone()))
+        L.close()
+    for r in results[1:]:
+        assert r[:2] == results[0][:2]
+        assert torch.equal(r[2], results[0][2])
+
+
+def test_norm_keeps_the_last_256_mib_of_the_124m_list(monkeypatch):
+    monkeypatch.delenv("MTA_NORM_KEEP_MIB", raising=False)
+    wl = WL.get("gpt2_124m")
+    arena = WL.Arena(wl, "cuda")
+    L = make_list(arena)
+    info = L.info()
+    kept = info["norm_kept_tiles"]
+    # float32 gradients of 498 MB: the last 256 MiB worth of tiles (a few
+    # of them bias tiles shorter than 4096 elements)
+    assert 0 < kept < info["tiles"]
+    assert (256 << 20) - 4096 * 4 < kept * 4096 * 4 <= (256 << 20) + \
+        64 * 4096 * 4
+    L.close()
