@@ -291,6 +291,14 @@ def main():
                     help="also write a 16-bit copy (bfloat16 by default, or "
                          "float16) of every updated weight "
                          "(mta_list_set_weight_copies_as): +2 B/param")
+    ap.add_argument("--scale-inplace", action="store_true",
+                    help="workloads with an unscale factor s (not loss-"
+                         "scaled): apply it with an in-place mta_scale "
+                         "launch (k_scale: reads and writes g) instead of "
+                         "deferring it into the norm and the update; the "
+                         "factor alternates s, 1/s from step to step so "
+                         "the gradients keep their values (s is a power of "
+                         "two)")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -336,6 +344,11 @@ def main():
         return
     M.lib()
     wl = WL.get(args.workload)
+    if args.scale_inplace and (wl.amp or wl.scale == 1.0):
+        print("--scale-inplace needs a workload with a fixed unscale factor "
+              "(not loss-scaled): e.g. --workload gpt2_124m_bf16g",
+              file=sys.stderr)
+        sys.exit(2)
     if args.graph and not wl.amp:
         print("--graph needs a loss-scaled workload (its step counter and "
               "scale live on the device, so a captured step can be "
@@ -368,10 +381,15 @@ def main():
     stream = torch.cuda.current_stream()
     hp = M._binding.mta_adamw_hparams(wl.lr, wl.beta1, wl.beta2, wl.eps,
                                       wl.weight_decay)
-    defer = wl.scale != 1.0
+    inplace = bool(args.scale_inplace)
+    defer = wl.scale != 1.0 and not inplace
     amp = M.AmpState(wl.amp_scale) if wl.amp else None
 
     def step(t, ev=None):
+        if ev is not None and inplace:
+            ev[3].record(stream)
+        if inplace:
+            L.scale(wl.scale if t % 2 else 1.0 / wl.scale, defer=False)
         if defer:
             L.scale(wl.scale, defer=True)
         if ev is not None:
@@ -405,7 +423,7 @@ def main():
     # record costs the host a few microseconds, which a launch-bound list
     # (tiny) would otherwise pay every step
     every = max(1, args.steps // 50)
-    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for k in range(0, args.steps, every)}
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -422,7 +440,10 @@ def main():
     ms_per_step = dev_ms / args.steps
     norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs.values()) / len(evs)
     adamw_ms = sum(e[1].elapsed_time(e[2]) for e in evs.values()) / len(evs)
-    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs.values())
+    first = 3 if inplace else 0
+    per_step = sorted(e[first].elapsed_time(e[2]) for e in evs.values())
+    scale_ms = (sum(e[3].elapsed_time(e[0]) for e in evs.values()) /
+                len(evs)) if inplace else None
 
     def pct(q):
         return per_step[min(len(per_step) - 1, int(q * len(per_step)))]
@@ -459,12 +480,14 @@ def main():
            "update": update_bytes(wl, args.opt, args.zero_grad,
                                   args.weight_copy)}
     kernel = KERNEL_OF[args.opt]
-    step_bytes = wl.n * (bpp["norm"] + bpp["update"])
+    scale_bytes = wl.n * 2 * (4 if wl.gtype == WL.F32 else 2) if inplace \
+        else 0
+    step_bytes = wl.n * (bpp["norm"] + bpp["update"]) + scale_bytes
     adamw_bytes = wl.n * bpp["update"]
     norm_bytes = wl.n * bpp["norm"]
     value = wl.n * args.steps / (host_s)
     achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
-    traffic = (None if args.weight_copy or args.layout != "padded"
+    traffic = (None if args.weight_copy or args.layout != "padded" or inplace
                else measured_traffic(traffic_key(wl, args.opt, args.zero_grad),
                                      kernel))
     out = {
@@ -487,7 +510,10 @@ def main():
             "grad": ["f32", "bf16", "f16"][wl.gtype],
             "loss_scaling": "dynamic (device state)" if wl.amp else "none",
             "m": ["f32", "bf16x2"][wl.mkind], "v": ["f32", "bf16x2"][wl.vkind],
-            "bytes_per_param": bpp["norm"] + bpp["update"],
+            "unscale": ("in place (k_scale)" if inplace else "deferred"
+                        if defer else "none"),
+            "bytes_per_param": bpp["norm"] + bpp["update"] +
+            scale_bytes // wl.n,
             "tiles": info["tiles"], "grid_update": info["grid_update"],
             "grid_norm": info["grid_norm"], "parallelism": "single GPU",
             "weight_copy": args.weight_copy,
@@ -499,8 +525,11 @@ def main():
         / HBM_PEAK_GBS,
         "device_ms_per_step": ms_per_step,
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-        "kernels_ms": {"k_sumsq": norm_ms, kernel: adamw_ms},
+        "kernels_ms": {"k_sumsq": norm_ms, kernel: adamw_ms,
+                       **({"k_scale": scale_ms} if inplace else {})},
         "norm_gbs": norm_bytes / (norm_ms * 1e-3) / 1e9,
+        **({"scale_gbs": scale_bytes / (scale_ms * 1e-3) / 1e9}
+           if inplace else {}),
         "roofline": {
             "kernel": kernel, "bound": "hbm", "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s",

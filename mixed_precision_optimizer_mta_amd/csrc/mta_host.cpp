@@ -762,7 +762,8 @@ int mta_scale(mta_list *L, float factor, int flags, void *stream) {
   int rc = check_device(L);
   if (rc) return rc;
   if (L->ntiles == 0) return ok();
-  const mta::Work wk = work_of(L, L->grid_update, stream);
+  // the norm's grid: the same two-tile walk over the gradient alone
+  const mta::Work wk = work_of(L, L->grid_norm, stream);
   return after_launch(mta::launch_scale(L->gtype, wk, factor), wk.stream,
                       "mta_scale");
 }

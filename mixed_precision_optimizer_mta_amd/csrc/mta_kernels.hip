@@ -887,60 +887,127 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles,
 // type (nearest-even; NaN -> 0xFFFF).
 // ---------------------------------------------------------------------------
 
+// g = f32(g * s), rounded back to g's type, for one tile of a full,
+// aligned tensor whose loads are already in r.
+template <int D>
+__device__ __forceinline__ void scale_store_tile(
+    MTA_GLOBAL elem_t<D> *pg, const raw16_t<D> (&r)[kTileElems /
+                                                   (kBlock * kWide<D>)],
+    uint32_t e0, float s) {
+  constexpr int V = kWide<D>;
+  constexpr int G = kTileElems / (kBlock * V);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float x[V];
+    unpack16b<D>(r[j], x);
+    MTA_GLOBAL elem_t<D> *q = pg + j * (kBlock * V) + e0;
+    if constexpr (D == kF32) {
+      __builtin_nontemporal_store(
+          f32x4{x[0] * s, x[1] * s, x[2] * s, x[3] * s},
+          (MTA_GLOBAL f32x4 *)q);
+    } else {
+      uint32_t h[V];
+#pragma unroll
+      for (int k = 0; k < V; ++k) h[k] = encode16<D>(x[k] * s);
+      __builtin_nontemporal_store(
+          u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                h[4] | (h[5] << 16), h[6] | (h[7] << 16)},
+          (MTA_GLOBAL u32x4 *)q);
+    }
+  }
+}
+
+// The same for any tile: clamped element loads (all issued first) and
+// masked element stores, or the vector path for a full aligned tile.
+template <int D>
+__device__ __forceinline__ void scale_any_tile(const GradTile &tl, uint32_t e0,
+                                               float s) {
+  constexpr int V = kWide<D>;
+  constexpr int G = kTileElems / (kBlock * V);
+  MTA_GLOBAL elem_t<D> *pg = gp<elem_t<D>>(const_cast<void *>(tl.g), 0);
+  const uint32_t lim = tl.lim;
+  if (tl.vec && lim == kTileElems) {
+    raw16_t<D> r[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) r[j] = load16b_raw<D>(pg + j * (kBlock * V), e0);
+    scale_store_tile<D>(pg, r, e0, s);
+    return;
+  }
+  float x[G][V];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      x[j][k] = load1_clamped<D>(pg, e0 + j * (kBlock * V) + k, lim);
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const uint32_t e = e0 + j * (kBlock * V) + k;
+      if (e < lim) {
+        const float y = x[j][k] * s;
+        if constexpr (D == kF32)
+          pg[e] = y;
+        else
+          pg[e] = static_cast<uint16_t>(encode16<D>(y));
+      }
+    }
+}
+
+// Two tiles per iteration (t and t + gridDim.x), records read one iteration
+// ahead, every load of a pair of full tiles issued before any store: as
+// k_sumsq's walk, so that enough bytes are in flight to cover HBM latency.
 template <int D>
 __global__ void __launch_bounds__(kBlock)
 k_scale(const GradTile *__restrict__ tiles, uint32_t ntiles, float s) {
   constexpr int V = kWide<D>;
   constexpr int G = kTileElems / (kBlock * V);
-  for (uint32_t t = stream_of_block(); t < ntiles; t += gridDim.x) {
-    const GradTile tl = tiles[t];
-    MTA_GLOBAL elem_t<D> *__restrict__ pg =
-        gp<elem_t<D>>(const_cast<void *>(tl.g), 0);
-    const uint32_t lim = tl.lim;
-    const uint32_t e0 = threadIdx.x * V;
-    float x[G][V];
-    if (tl.vec && lim == kTileElems) {
+  constexpr int U = 2;
+  const uint32_t last = ntiles ? ntiles - 1 : 0;
+  const uint32_t stride = U * gridDim.x;
+  const uint32_t e0 = threadIdx.x * V;
+  const uint32_t first = stream_of_block();
+  GradTile rec[U];
+  if (ntiles) {
 #pragma unroll
-      for (int j = 0; j < G; ++j)
-        unpack16b<D>(load16b_raw<D>(pg + j * (kBlock * V), e0), x[j]);
+    for (int u = 0; u < U; ++u)
+      rec[u] = tiles[min(first + u * gridDim.x, last)];
+  }
+  for (uint32_t t0 = first; t0 < ntiles; t0 += stride) {
+    GradTile cur[U];
+    bool valid[U];
+    bool all_full = true;
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        MTA_GLOBAL elem_t<D> *q = pg + j * (kBlock * V) + e0;
-        if constexpr (D == kF32) {
-          __builtin_nontemporal_store(
-              f32x4{x[j][0] * s, x[j][1] * s, x[j][2] * s, x[j][3] * s},
-              (MTA_GLOBAL f32x4 *)q);
-        } else {
-          uint32_t h[V];
+    for (int u = 0; u < U; ++u) {
+      cur[u] = rec[u];
+      valid[u] = t0 + u * gridDim.x < ntiles;
+      all_full = all_full && valid[u] && cur[u].vec &&
+                 cur[u].lim == kTileElems;
+    }
+    if (all_full) {
+      raw16_t<D> r[U][G];
 #pragma unroll
-          for (int k = 0; k < V; ++k) h[k] = encode16<D>(x[j][k] * s);
-          __builtin_nontemporal_store(
-              u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                    h[4] | (h[5] << 16), h[6] | (h[7] << 16)},
-              (MTA_GLOBAL u32x4 *)q);
-        }
-      }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          r[u][j] = load16b_raw<D>(
+              gp<elem_t<D>>(cur[u].g, j * (kBlock * V)), e0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        rec[u] = tiles[min(t0 + stride + u * gridDim.x, last)];
+      __builtin_amdgcn_sched_barrier(0);  // every load in flight first
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        scale_store_tile<D>(gp<elem_t<D>>(const_cast<void *>(cur[u].g), 0),
+                            r[u], e0, s);
     } else {
-      // tail tile or unaligned tensor: same mapping, clamped element loads
-      // (all issued first) and masked element stores
 #pragma unroll
-      for (int j = 0; j < G; ++j)
+      for (int u = 0; u < U; ++u)
+        rec[u] = tiles[min(t0 + stride + u * gridDim.x, last)];
 #pragma unroll
-        for (int k = 0; k < V; ++k)
-          x[j][k] = load1_clamped<D>(pg, e0 + j * (kBlock * V) + k, lim);
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          const uint32_t e = e0 + j * (kBlock * V) + k;
-          if (e < lim) {
-            const float y = x[j][k] * s;
-            if constexpr (D == kF32)
-              pg[e] = y;
-            else
-              pg[e] = static_cast<uint16_t>(encode16<D>(y));
-          }
-        }
+      for (int u = 0; u < U; ++u)
+        if (valid[u]) scale_any_tile<D>(cur[u], e0, s);
     }
   }
 }

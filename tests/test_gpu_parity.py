@@ -230,6 +230,39 @@ def test_in_place_scale_matches_oracle(gtype):
     L.close()
 
 
+@pytest.mark.parametrize("gtype", [0, 1, 2])
+def test_in_place_scale_full_tile_pairs_and_flat_offsets(gtype):
+    # enough tiles that every workgroup walks pairs of full tiles, plus
+    # tensors at odd flat offsets (peeled heads) and ragged tails; nothing
+    # outside the tensors is written
+    sizes = [4096 * 2200 + 5, 3, 4096 * 3 + 1, 300]
+    offsets = [1]
+    for n in sizes[:-1]:
+        offsets.append(offsets[-1] + n)
+    wl = WL.Workload("scale2", sizes, gtype, 0, 0, steps=1, g_sigma=50.0,
+                     ident=17)
+    arena = WL.Arena(wl, "cuda", offsets)
+    arena.fill_grads(1)
+    ity = torch.int32 if gtype == 0 else torch.int16
+    before = arena.g.view(ity).clone()
+    gs = oracle_grads(arena)
+    L = make_list(arena)
+    assert L.info()["tiles"] > 4 * 512 >= 2 * L.info()["grid_norm"]
+    for s in (0.3, 2.0 ** 20):
+        L.scale(s, defer=False)
+        torch.cuda.synchronize()
+        for g in gs:
+            O.scale_(g, gtype, s)
+        for a, b in zip(oracle_grads(arena), gs):
+            assert np.array_equal(a.view(np.uint16 if gtype else np.uint32),
+                                  b.view(np.uint16 if gtype else np.uint32))
+    inside = torch.zeros(arena.total, dtype=torch.bool, device="cuda")
+    for o, n in zip(offsets, sizes):
+        inside[o:o + n] = True
+    assert not bool(((arena.g.view(ity) != before) & ~inside).any())
+    L.close()
+
+
 def test_deferred_scale_state_machine():
     from mixed_precision_optimizer_mta_amd import MtaError
     wl = WL.Workload("defer", [100], 1, 0, 0, steps=1, ident=16)
