@@ -353,3 +353,49 @@ def test_master_weights_state_dict_keeps_float32_state():
         assert torch.equal(pa.view(torch.int16), pb.view(torch.int16))
         assert torch.equal(opt_ref.state[pa]["master_weight"],
                            opt2.state[pb]["master_weight"])
+
+
+def test_master_weights_loss_scaled_step_replays_in_a_graph():
+    # a float16 model, float32 masters, device loss scaling: the whole
+    # optimizer step captured once and replayed matches eager steps bit for
+    # bit (masters, parameters and the scale state)
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    a = _model(19).to(torch.float16)
+    b = copy.deepcopy(a)
+    kw = dict(kind="adamw", lr=1e-3, weight_decay=0.1, max_norm=1.0,
+              master_weights=True, loss_scale=512.0, growth_interval=3,
+              zero_grad=True)
+    opt_a, opt_b = MtaOptimizer(a.parameters(), **kw), \
+        MtaOptimizer(b.parameters(), **kw)
+
+    def grads(m, opt, t):
+        torch.manual_seed(5000 + t)
+        x = torch.randn(16, 300, device="cuda", dtype=torch.float16)
+        y = torch.randint(0, 10, (16,), device="cuda")
+        loss = torch.nn.functional.cross_entropy(m(x).float(), y)
+        (loss * opt.loss_scale).backward()
+
+    for m, o in ((a, opt_a), (b, opt_b)):
+        grads(m, o, 1)
+        o.step()                   # eager: builds the tables and masters
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        opt_a.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for t in range(2, 9):
+        grads(a, opt_a, t)
+        grads(b, opt_b, t)
+        torch.cuda.synchronize()
+        graph.replay()
+        opt_b.step()
+        torch.cuda.synchronize()
+        for pa, pb in zip(a.parameters(), b.parameters()):
+            assert torch.equal(pa.view(torch.int16), pb.view(torch.int16)), t
+            assert torch.equal(opt_a.state[pa]["master_weight"],
+                               opt_b.state[pb]["master_weight"]), t
+            assert not bool(pa.grad.any())
+        assert opt_a.amp.read() == opt_b.amp.read()
+    assert opt_a.amp.read()["step"] >= 6
