@@ -329,6 +329,19 @@ int mta_adamw_scalars(const mta_adamw_hparams *hp, int64_t t, float out[7]);
 /* Host only: describe a handle. */
 int mta_list_info(const mta_list *list, mta_list_info_t *out);
 
+/* Host only: the shape mta_list_create would give a list of these tensors,
+ * without creating one.  The same argument, alignment and overlap checks
+ * and the same errors as mta_list_create; on success *out holds count,
+ * elements, tiles, tile_elems, vector_tensors, gtype, mkind, vkind,
+ * state_buffers and norm_kept_tiles as the list would have them (weight
+ * copies none, weight_copy_type MTA_BF16).  The device-dependent fields
+ * are not set: grid_update = grid_norm = 0, device = -1.  The pointers are
+ * compared, never dereferenced; no HIP call is made, so it also runs on a
+ * host with no GPU (a caller can check how a flat-buffer layout cuts into
+ * vector tiles before allocating it). */
+int mta_list_plan(const mta_tensor *tensors, int64_t count, int gtype,
+                  int mkind, int vkind, mta_list_info_t *out);
+
 /* Message for the last failure on the calling host thread ("" if none). */
 const char *mta_last_error(void);
 

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     mta_abi_version, mta_adamw_scalars, mta_adamw_step, mta_amp_adamw_step,
     mta_amp_clip_norm, mta_amp_step, mta_amp_update, mta_clip_norm,
     mta_last_error, mta_list_create, mta_list_destroy, mta_list_info,
-    mta_list_set_weight_copies, mta_scale, mta_step)
+    mta_list_plan, mta_list_set_weight_copies, mta_list_set_weight_copies_as,
+    mta_scale, mta_step)
 from .torch_list import AmpState, MtaList  # noqa: F401
 from .optim import MtaOptimizer  # noqa: F401

@@ -29,7 +29,7 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_adamw_scalars", "mta_list_info", "mta_last_error",
            "mta_abi_version", "mta_amp_clip_norm", "mta_amp_adamw_step",
            "mta_amp_update", "mta_step", "mta_amp_step",
-           "mta_list_set_weight_copies_as")
+           "mta_list_set_weight_copies_as", "mta_list_plan")
 
 
 class mta_tensor(ctypes.Structure):
@@ -108,6 +108,9 @@ def lib():
         L.mta_adamw_scalars.argtypes = [ctypes.POINTER(mta_adamw_hparams),
                                         i64, ctypes.POINTER(ctypes.c_float)]
         L.mta_list_info.argtypes = [vp, ctypes.POINTER(mta_list_info_t)]
+        L.mta_list_plan.argtypes = [ctypes.POINTER(mta_tensor), i64, c_int,
+                                    c_int, c_int,
+                                    ctypes.POINTER(mta_list_info_t)]
         L.mta_amp_clip_norm.argtypes = [vp, f32, vp, vp, vp, vp]
         L.mta_amp_adamw_step.argtypes = [vp,
                                          ctypes.POINTER(mta_adamw_hparams),
@@ -148,12 +151,17 @@ def _hparams(hp):
     return mta_adamw_hparams(*hp)
 
 
-def mta_list_create(tensors, gtype, mkind, vkind, stream=0):
-    """tensors: sequence of (w_ptr, g_ptr, m_ptr, v_ptr, n).  Returns the
-    opaque handle (an int)."""
+def _tensor_table(tensors):
     arr = (mta_tensor * max(1, len(tensors)))()
     for i, (w, g, m, v, n) in enumerate(tensors):
         arr[i] = mta_tensor(w, g, m, v, n)
+    return arr
+
+
+def mta_list_create(tensors, gtype, mkind, vkind, stream=0):
+    """tensors: sequence of (w_ptr, g_ptr, m_ptr, v_ptr, n).  Returns the
+    opaque handle (an int)."""
+    arr = _tensor_table(tensors)
     out = ctypes.c_void_p()
     rc = lib().mta_list_create(arr, len(tensors), gtype, mkind, vkind,
                                stream, ctypes.byref(out))
@@ -211,6 +219,16 @@ def mta_adamw_scalars(hp, t):
 def mta_list_info(handle):
     info = mta_list_info_t()
     _check(lib().mta_list_info(handle, ctypes.byref(info)), "mta_list_info")
+    return {name: getattr(info, name) for name, _ in mta_list_info_t._fields_}
+
+
+def mta_list_plan(tensors, gtype, mkind, vkind):
+    """The shape mta_list_create would give these (w, g, m, v, n) entries
+    (pointers as ints, m / v may be None); no device is touched."""
+    info = mta_list_info_t()
+    _check(lib().mta_list_plan(_tensor_table(tensors), len(tensors), gtype,
+                               mkind, vkind, ctypes.byref(info)),
+           "mta_list_plan")
     return {name: getattr(info, name) for name, _ in mta_list_info_t._fields_}
 
 

@@ -443,26 +443,20 @@ mta_opt adamw_opt(const mta_adamw_hparams *hp) {
   return o;
 }
 
-}  // namespace
+// Everything mta_list_create decides before it touches a device: argument
+// checks, overlap checks, the tile tables and the norm's kept tiles.
+struct Plan {
+  std::vector<mta_tensor> kept;
+  std::vector<mta::GradTile> gtiles;
+  std::vector<mta::StepTile> stiles;
+  int64_t elements = 0;
+  int vec_tensors = 0;
+  int state = -1;
+  uint32_t keep_from = 0;
+};
 
-extern "C" {
-
-int mta_abi_version(void) { return MTA_ABI_VERSION; }
-
-const char *mta_last_error(void) { return g_err; }
-
-int mta_adamw_scalars(const mta_adamw_hparams *hp, int64_t t, float out[7]) {
-  int rc = check_hparams(hp, t);
-  if (rc) return rc;
-  if (!out) return fail(MTA_EINVAL, "out is NULL");
-  make_scalars(*hp, t, out);
-  return ok();
-}
-
-int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
-                    int mkind, int vkind, void *stream, mta_list **out) {
-  if (!out) return fail(MTA_EINVAL, "out is NULL");
-  *out = nullptr;
+int plan_list(const mta_tensor *tensors, int64_t count, int gtype, int mkind,
+              int vkind, Plan *plan) {
   if (count < 0) return fail(MTA_EINVAL, "count must be >= 0");
   if (count > 0 && !tensors) return fail(MTA_EINVAL, "tensors is NULL");
   if (count > static_cast<int64_t>(UINT32_MAX))
@@ -478,14 +472,14 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   const uintptr_t msz = mkind == MTA_MOM_BF16X2 ? 2 : 4;
   const uintptr_t vsz = vkind == MTA_MOM_BF16X2 ? 2 : 4;
 
-  std::vector<mta::GradTile> gtiles;
-  std::vector<mta::StepTile> stiles;
-  std::vector<mta_tensor> kept;
+  std::vector<mta::GradTile> &gtiles = plan->gtiles;
+  std::vector<mta::StepTile> &stiles = plan->stiles;
+  std::vector<mta_tensor> &kept = plan->kept;
   std::vector<Span> spans;
-  uint32_t keep_from = 0;
-  int64_t elements = 0;
-  int vec_tensors = 0;
-  int state = -1;  // m / v presence of the first non-empty tensor
+  uint32_t &keep_from = plan->keep_from;
+  int64_t &elements = plan->elements;
+  int &vec_tensors = plan->vec_tensors;
+  int &state = plan->state;  // m / v presence of the first non-empty tensor
   int64_t state_from = -1;
   try {
     spans.reserve(static_cast<size_t>(count) * 4);
@@ -560,6 +554,34 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
   }
+  return MTA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mta_abi_version(void) { return MTA_ABI_VERSION; }
+
+const char *mta_last_error(void) { return g_err; }
+
+int mta_adamw_scalars(const mta_adamw_hparams *hp, int64_t t, float out[7]) {
+  int rc = check_hparams(hp, t);
+  if (rc) return rc;
+  if (!out) return fail(MTA_EINVAL, "out is NULL");
+  make_scalars(*hp, t, out);
+  return ok();
+}
+
+int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
+                    int mkind, int vkind, void *stream, mta_list **out) {
+  if (!out) return fail(MTA_EINVAL, "out is NULL");
+  *out = nullptr;
+  Plan plan;
+  const int rc = plan_list(tensors, count, gtype, mkind, vkind, &plan);
+  if (rc) return rc;
+  std::vector<mta::GradTile> &gtiles = plan.gtiles;
+  std::vector<mta::StepTile> &stiles = plan.stiles;
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -573,18 +595,18 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
 
   mta_list *L = new (std::nothrow) mta_list;
   if (!L) return fail(MTA_ENOMEM, "host allocation failed");
-  L->tensors = std::move(kept);
+  L->tensors = std::move(plan.kept);
   L->device = dev;
   L->gtype = gtype;
   L->mkind = mkind;
   L->vkind = vkind;
   L->count = count;
-  L->elements = elements;
+  L->elements = plan.elements;
   L->ntiles = static_cast<uint32_t>(stiles.size());
-  L->keep_from = keep_from;
-  L->vector_tensors = vec_tensors;
+  L->keep_from = plan.keep_from;
+  L->vector_tensors = plan.vec_tensors;
   L->cus = cus;
-  L->state_buffers = state < 0 ? 3 : state;  // no element: any rule works
+  L->state_buffers = plan.state < 0 ? 3 : plan.state;  // no element: any rule
   const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
   const int bpc_n = env_int(
       "MTA_NORM_BLOCKS_PER_CU",
@@ -721,6 +743,33 @@ int mta_list_set_weight_copies_as(mta_list *L, void *const *w16,
   L->w16 = std::move(copies);
   L->weight_copies = attached;
   L->copy_type = copy_type;
+  return ok();
+}
+
+int mta_list_plan(const mta_tensor *tensors, int64_t count, int gtype,
+                  int mkind, int vkind, mta_list_info_t *out) {
+  if (!out) return fail(MTA_EINVAL, "out is NULL");
+  Plan plan;
+  try {
+    const int rc = plan_list(tensors, count, gtype, mkind, vkind, &plan);
+    if (rc) return rc;
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  *out = mta_list_info_t{};
+  out->count = count;
+  out->elements = plan.elements;
+  out->tiles = static_cast<int64_t>(plan.stiles.size());
+  out->tile_elems = mta::kTileElems;
+  out->device = -1;  // no device: grid_update and grid_norm stay 0
+  out->vector_tensors = plan.vec_tensors;
+  out->gtype = gtype;
+  out->mkind = mkind;
+  out->vkind = vkind;
+  out->state_buffers = plan.state < 0 ? 3 : plan.state;
+  out->weight_copy_type = MTA_BF16;
+  out->norm_kept_tiles =
+      static_cast<int32_t>(plan.stiles.size() - plan.keep_from);
   return ok();
 }
 
