@@ -1,15 +1,19 @@
 """Seeded random parity sweep: every knob of the library at once.
 
 Each case draws a tensor list (counts, sizes from empty through tail tiles to
-several tiles, aligned or shifted off 16-byte alignment), a gradient type,
-moment kinds, an update rule, gradient zeroing, a deferred unscale or a
-device loss scale, bfloat16 weight copies on a random subset of tensors, a
-clip threshold (from always clipping to never) and occasionally a non-finite
-gradient, then runs two lockstep steps through the C ABI against the oracle
+several tiles; aligned, shifted off 16-byte alignment, or back to back in
+flat buffers; sometimes the gradient shifted against the other buffers), a
+gradient type, moment kinds, an update rule, gradient zeroing, a deferred
+unscale or a device loss scale, bfloat16 or float16 weight copies on a
+random subset of tensors, a clip threshold (from always clipping to never)
+and occasionally a non-finite gradient, then runs two lockstep steps
+through the C ABI against the oracle
 and compares every buffer bit for bit (w, g, the rule's state buffers, the
 copies), the norm (1e-6 relative), the clip coefficient (exact) and, under
 loss scaling, the whole device state.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -63,6 +67,9 @@ def draw_case(seed):
         bad_step=int(rng.choice([0, 0, 0, 0, 1, 2])),
         shifts=[int(x) for x in rng.integers(0, 8, count)],
         pick=[bool(x) for x in rng.random(count) < 0.6],
+        copy_f16=bool(rng.random() < 0.5),
+        flat=bool(rng.random() < 0.5),
+        g_shift=int(rng.choice([0, 0, 0, 0, 0, 1, 2, 5])),
     )
     return c
 
@@ -79,12 +86,16 @@ def run_case(c):
                      max_norm=c["max_norm"], amp=c["amp"], amp_scale=256.0,
                      amp_interval=2, ident=50 + c["seed"] % 1000)
     offsets = None
-    if not c["aligned"]:
+    if not c["aligned"] and c["flat"]:
+        offsets = [c["shifts"][0]]          # back to back
+        for n in c["sizes"][:-1]:
+            offsets.append(offsets[-1] + n)
+    elif not c["aligned"]:
         offsets, pos = [], 0
         for n, sh in zip(c["sizes"], c["shifts"]):
             offsets.append(pos + sh)
             pos += -(-(n + sh) // 8) * 8 + 8
-    arena = WL.Arena(wl, "cuda", offsets)
+    arena = WL.Arena(wl, "cuda", offsets, g_shift=c["g_shift"])
     arena.fill_weights()
     ents = [(w, g, m if has_m else None, v if has_v else None, n)
             for (w, g, m, v, n) in arena.entries()]
@@ -95,7 +106,8 @@ def run_case(c):
     copies = None
     picked = [p and c["copies"] for p in c["pick"]]
     if c["copies"]:
-        copies = torch.zeros(arena.total, dtype=torch.bfloat16, device="cuda")
+        copies = torch.zeros(arena.total, dtype=torch.float16 if
+                             c["copy_f16"] else torch.bfloat16, device="cuda")
         L.set_weight_copies([copies[o:o + n] if p else None for o, n, p in
                              zip(arena.offsets, wl.sizes, picked)])
     opt = dict(kind=kind, lr=1e-3 if adam else 0.05, beta1=0.9, beta2=0.99,
@@ -107,7 +119,8 @@ def run_case(c):
         ost.append(O.Tensor(dev_f32(views[0]), grad_np(views[1], gtype),
                             mom_np(views[2], mkind) if has_m else None,
                             mom_np(views[3], vkind) if has_v else None,
-                            np.zeros(n, np.uint16) if picked[i] else None))
+                            np.zeros(n, np.uint16) if picked[i] else None,
+                            O.F16 if c["copy_f16"] else O.BF16))
     amp_d = AmpState(wl.amp_scale) if c["amp"] else None
     amp_o = O.AmpState(wl.amp_scale) if c["amp"] else None
     nd = torch.full((1,), -1.0, device="cuda")
@@ -117,7 +130,7 @@ def run_case(c):
         arena.fill_grads(t)
         if t == c["bad_step"] and nonempty:
             i = nonempty[c["seed"] % len(nonempty)]
-            arena.g[arena.offsets[i] + wl.sizes[i] // 2] = float("inf")
+            arena.view("g", i)[wl.sizes[i] // 2] = float("inf")
         for o, g in zip(ost, oracle_grads(arena)):
             o.g = g
         if c["amp"]:
@@ -166,6 +179,8 @@ def run_case(c):
     L.close()
 
 
-@pytest.mark.parametrize("seed", range(160))
+# MTA_RANDOM_CASES widens the sweep for a one-off run
+@pytest.mark.parametrize(
+    "seed", range(int(os.environ.get("MTA_RANDOM_CASES", "600"))))
 def test_random_case(seed):
     run_case(draw_case(seed))
