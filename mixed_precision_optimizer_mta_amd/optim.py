@@ -255,7 +255,9 @@ class MtaOptimizer(torch.optim.Optimizer):
     def load_state_dict(self, state_dict):
         """As torch.optim.Optimizer.load_state_dict, except that every state
         tensor comes back in the dtype it was saved in (masters and float32
-        moments of a 16-bit parameter stay float32)."""
+        moments of a 16-bit parameter stay float32).  The state buffers are
+        new allocations and the device tables are rebuilt on the next step:
+        capture a graph of step() again after loading."""
         super().load_state_dict(state_dict)
         ids = [i for g in state_dict["param_groups"] for i in g["params"]]
         params = [p for g in self.param_groups for p in g["params"]]

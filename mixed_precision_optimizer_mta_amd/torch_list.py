@@ -68,6 +68,7 @@ class MtaList:
                                 None if v is None else v.data_ptr(), n))
         self.gtype, self.mkind, self.vkind = gtype, mkind, vkind
         self.sizes = [int(e[4]) for e in entries]
+        self.device = torch.cuda.current_device()
         self.handle = B.mta_list_create(entries, gtype, mkind, vkind,
                                         current_stream())
 
@@ -168,7 +169,11 @@ class MtaList:
                              current_stream())
 
     def close(self):
+        """Free the handle's device tables once the device is done with
+        them: mta_list_destroy requires every stream that used the list to
+        be synchronized, and work launched earlier may still be queued."""
         if self.handle is not None:
+            torch.cuda.synchronize(self.device)
             B.mta_list_destroy(self.handle)
             self.handle = None
 
