@@ -192,14 +192,31 @@ def scale_(g, gtype, s):
 
 # ---------------------------------------------------------------- norm
 
-def sumsq(grads, gtype, s=1.0):
-    """Joint sum of squares of f32(g*s) over a list of gradient arrays."""
+def joint_sumsq(parts):
+    """Joint sum of squares over several gradient lists, each with its own
+    gradient type and unscale factor: parts = [(grads, gtype, s), ...].
+    The one cap of ClipGradNorms is over the joint length of every gradient
+    the step names ("Mica 7.7", "The whole model in one call"), whatever
+    type each is stored in (under bfloat16, a high-numerics parameter keeps
+    a float32 gradient: "Precision and numerics", Parameters).  Every
+    f32(g*s)^2 goes into one compensated float64 sum, in list order."""
     state = np.zeros(2, dtype=np.float64)
     L = lib()
-    for g in grads:
-        L.mto_sumsq_accumulate(g.size, _ptr(g, _grad_dtype(gtype)), gtype,
-                               float(s), _ptr(state, np.float64))
+    for grads, gtype, s in parts:
+        for g in grads:
+            L.mto_sumsq_accumulate(g.size, _ptr(g, _grad_dtype(gtype)),
+                                   gtype, float(s), _ptr(state, np.float64))
     return float(state[0] + state[1])
+
+
+def joint_norm(parts):
+    """L2 norm of joint_sumsq(parts) (float64, effectively exact)."""
+    return math.sqrt(joint_sumsq(parts))
+
+
+def sumsq(grads, gtype, s=1.0):
+    """Joint sum of squares of f32(g*s) over a list of gradient arrays."""
+    return joint_sumsq([(grads, gtype, s)])
 
 
 def norm(grads, gtype, s=1.0):

@@ -948,3 +948,32 @@ def test_step_writes_a_float16_copy_when_asked():
                  np.zeros(n, np.uint16), O.F16)
     O.step_([x], O.F32, 0, 0, 3e-4, 0.9, 0.999, 1e-8, 0.1, 1)
     assert np.array_equal(x.w16, x.w.astype(np.float16).view(np.uint16))
+
+
+def test_joint_norm_over_mixed_gradient_types_is_the_exact_norm():
+    # brute force: exact rational sum of the squares of f32(g*s) over a
+    # float32 list, a bfloat16 list and a float16 list, each with its own
+    # unscale factor; the oracle's compensated float64 sum must be the
+    # correctly rounded sum to within a couple of float64 ulps
+    from fractions import Fraction
+    rng = np.random.default_rng(51)
+    a = [rng.normal(0, 3, 40).astype(np.float32),
+         rng.normal(0, 1e-3, 7).astype(np.float32)]
+    b = [O.bf16_of_f32(rng.normal(0, 50, 33).astype(np.float32))]
+    c = [O.f16_of_f32(rng.normal(0, 2, 21).astype(np.float32))]
+    parts = [(a, O.F32, 1.0), (b, O.BF16, 2.0 ** -6), (c, O.F16, 0.3)]
+    exact = Fraction(0)
+    for grads, gtype, s in parts:
+        for g in grads:
+            x = g if gtype == O.F32 else (O.f32_of_bf16(g) if gtype == O.BF16
+                                          else O.f32_of_f16(g))
+            xs = (x.astype(np.float32) * np.float32(s)).astype(np.float32)
+            exact += sum(Fraction(float(v)) ** 2 for v in xs)
+    got = O.joint_sumsq(parts)
+    assert abs(Fraction(got) - exact) <= exact * Fraction(1, 2 ** 51)
+    # one type throughout: the joint sum is the plain sum of the
+    # concatenation, bit for bit (the same terms in the same order)
+    assert O.joint_sumsq([(a[:1], O.F32, 1.0), (a[1:], O.F32, 1.0)]) == \
+        O.sumsq(a, O.F32)
+    # a missing part changes the result: every part is counted
+    assert O.joint_sumsq(parts[:2]) < got
