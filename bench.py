@@ -299,6 +299,11 @@ def main():
                          "factor alternates s, 1/s from step to step so "
                          "the gradients keep their values (s is a power of "
                          "two)")
+    ap.add_argument("--joint-norm", type=int, default=1, metavar="K",
+                    help="clip over the joint norm of K lists (the tensors "
+                         "cut into K runs of consecutive tensors, norms "
+                         "chained by mta_clip_norm_joint) instead of one; "
+                         "the update stays one list")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -344,6 +349,10 @@ def main():
         return
     M.lib()
     wl = WL.get(args.workload)
+    if args.joint_norm > 1 and args.scale_inplace:
+        print("--joint-norm with --scale-inplace is not measured",
+              file=sys.stderr)
+        sys.exit(2)
     if args.scale_inplace and (wl.amp or wl.scale == 1.0):
         print("--scale-inplace needs a workload with a fixed unscale factor "
               "(not loss-scaled): e.g. --workload gpt2_124m_bf16g",
@@ -376,6 +385,15 @@ def main():
         L.set_weight_copies([copies[o:o + n] for o, n in
                              zip(arena.offsets, wl.sizes)])
     info = L.info()
+    norm_lists = [L]
+    if args.joint_norm > 1:
+        k = args.joint_norm
+        cuts = [round(i * len(ents) / k) for i in range(k + 1)]
+        norm_lists = [M.MtaList([], entries=[e[:2] + (None, None, e[4])
+                                             for e in ents[a:b]],
+                                gtype=wl.gtype, mkind=wl.mkind,
+                                vkind=wl.vkind)
+                      for a, b in zip(cuts, cuts[1:]) if b > a]
     norm_d = torch.zeros(1, device="cuda")
     coef_d = torch.zeros(1, device="cuda")
     stream = torch.cuda.current_stream()
@@ -384,6 +402,11 @@ def main():
     inplace = bool(args.scale_inplace)
     defer = wl.scale != 1.0 and not inplace
     amp = M.AmpState(wl.amp_scale) if wl.amp else None
+    if defer and len(norm_lists) > 1:
+        # norm-only lists never step, so a deferred factor set once stays
+        # pending and applies to every later norm
+        for x in norm_lists:
+            x.scale(wl.scale, defer=True)
 
     def step(t, ev=None):
         if ev is not None and inplace:
@@ -394,7 +417,10 @@ def main():
             L.scale(wl.scale, defer=True)
         if ev is not None:
             ev[0].record(stream)
-        if amp is not None:
+        if len(norm_lists) > 1:
+            M.clip_norm_joint(norm_lists, wl.max_norm, norm_d, coef_d,
+                              amp=amp)
+        elif amp is not None:
             L.amp_clip_norm(wl.max_norm, amp, norm_d, coef_d)
         else:
             L.clip_norm(wl.max_norm, norm_d, coef_d)
@@ -519,6 +545,7 @@ def main():
             "weight_copy": args.weight_copy,
             "optimizer": args.opt, "zero_grad": bool(args.zero_grad),
             "graph": bool(args.graph),
+            "joint_norm_lists": len(norm_lists),
         },
         "step_gbs": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9,
         "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9
@@ -538,6 +565,8 @@ def main():
         },
     }
     L.close()
+    for x in norm_lists[1:] if len(norm_lists) > 1 else []:
+        x.close()
     if not args.no_ceiling and args.opt in ("adamw", "adam") and \
             not args.zero_grad and not args.weight_copy:
         c = ceiling(wl)

@@ -226,6 +226,23 @@ int mta_scale(mta_list *list, float factor, int flags, void *stream);
 int mta_clip_norm(mta_list *list, float max_norm, float *d_norm, float *d_coef,
                   void *stream);
 
+/* ClipGradNorms over several lists: one cap over the joint length of every
+ * gradient of every list ("Mica 7.7", section "The whole model in one
+ * call"), each list keeping its own gradient type and its own pending
+ * deferred factor (a bfloat16 program whose high-numerics parameters keep
+ * float32 gradients: "Precision and numerics", Parameters).  One launch per
+ * list, in order on `stream`; each adds its float64 sum of squares to the
+ * running total (kept in lists[0]'s handle, so a list's total is never
+ * rounded to float32 on the way) and writes the norm and coef of the total
+ * so far, so the last launch leaves the joint ones in *d_norm and *d_coef.
+ * nlists >= 1; no list may appear twice (MTA_EINVAL); all on the current
+ * device.  nlists == 1 is mta_clip_norm.  Every list's mta_adamw_step (or
+ * mta_step) then takes the same d_coef.  Like every call on a list, not
+ * concurrent with other work on these lists. */
+int mta_clip_norm_joint(mta_list *const *lists, int64_t nlists,
+                        float max_norm, float *d_norm, float *d_coef,
+                        void *stream);
+
 /* AdamWSteps: one launch over every tensor of the list, step number t >= 1.
  * Per element, in float32 with every operation rounded on its own:
  *   ge = f32(f32(g*s) * coef)        (coef = *d_coef, or 1 when d_coef is NULL)
@@ -287,6 +304,14 @@ int mta_list_set_weight_copies_as(mta_list *list, void *const *w16,
  * (MTA_ESTATE). */
 int mta_amp_clip_norm(mta_list *list, float max_norm, mta_amp_state *d_amp,
                       float *d_norm, float *d_coef, void *stream);
+
+/* Loss-scaled ClipGradNorms over several lists: mta_clip_norm_joint with
+ * the factor and the found-inf flag of mta_amp_clip_norm (found_inf = 1
+ * when the joint norm is not finite).  No list may have a host
+ * MTA_SCALE_DEFER factor pending (MTA_ESTATE). */
+int mta_amp_clip_norm_joint(mta_list *const *lists, int64_t nlists,
+                            float max_norm, mta_amp_state *d_amp,
+                            float *d_norm, float *d_coef, void *stream);
 
 /* Loss-scaled AdamWSteps: one launch that does nothing when
  * d_amp->found_inf is set; otherwise the step of mta_adamw_step with

@@ -11,9 +11,10 @@ from ._binding import (  # noqa: F401
     MTA_MOM_F32, MTA_OPT_ADAM, MTA_OPT_ADAMW, MTA_OPT_MOMENTUM, MTA_OPT_SGD,
     MTA_SCALE_DEFER, MTA_SCALE_INPLACE, MTA_STEP_ZERO_GRAD, MtaError, lib,
     mta_abi_version, mta_adamw_scalars, mta_adamw_step, mta_amp_adamw_step,
-    mta_amp_clip_norm, mta_amp_step, mta_amp_update, mta_clip_norm,
+    mta_amp_clip_norm, mta_amp_clip_norm_joint, mta_amp_step, mta_amp_update,
+    mta_clip_norm, mta_clip_norm_joint,
     mta_last_error, mta_list_create, mta_list_destroy, mta_list_info,
     mta_list_plan, mta_list_set_weight_copies, mta_list_set_weight_copies_as,
     mta_scale, mta_step)
-from .torch_list import AmpState, MtaList  # noqa: F401
+from .torch_list import AmpState, MtaList, clip_norm_joint  # noqa: F401
 from .optim import MtaOptimizer  # noqa: F401

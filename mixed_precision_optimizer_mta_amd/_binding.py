@@ -29,7 +29,8 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_adamw_scalars", "mta_list_info", "mta_last_error",
            "mta_abi_version", "mta_amp_clip_norm", "mta_amp_adamw_step",
            "mta_amp_update", "mta_step", "mta_amp_step",
-           "mta_list_set_weight_copies_as", "mta_list_plan")
+           "mta_list_set_weight_copies_as", "mta_list_plan",
+           "mta_clip_norm_joint", "mta_amp_clip_norm_joint")
 
 
 class mta_tensor(ctypes.Structure):
@@ -100,6 +101,10 @@ def lib():
         L.mta_list_destroy.argtypes = [vp]
         L.mta_scale.argtypes = [vp, f32, c_int, vp]
         L.mta_clip_norm.argtypes = [vp, f32, vp, vp, vp]
+        L.mta_clip_norm_joint.argtypes = [ctypes.POINTER(vp), i64, f32, vp,
+                                          vp, vp]
+        L.mta_amp_clip_norm_joint.argtypes = [ctypes.POINTER(vp), i64, f32,
+                                              vp, vp, vp, vp]
         L.mta_adamw_step.argtypes = [vp, ctypes.POINTER(mta_adamw_hparams),
                                      i64, vp, vp]
         L.mta_list_set_weight_copies.argtypes = [vp, ctypes.POINTER(vp), vp]
@@ -182,6 +187,17 @@ def mta_clip_norm(handle, max_norm, d_norm, d_coef, stream=0):
            "mta_clip_norm")
 
 
+def _handles(handles):
+    return (ctypes.c_void_p * max(1, len(handles)))(*handles)
+
+
+def mta_clip_norm_joint(handles, max_norm, d_norm, d_coef, stream=0):
+    """handles: list handles in the order their norms are summed."""
+    _check(lib().mta_clip_norm_joint(_handles(handles), len(handles),
+                                     max_norm, d_norm, d_coef, stream),
+           "mta_clip_norm_joint")
+
+
 def mta_adamw_step(handle, hp, t, d_coef, stream=0):
     h = _hparams(hp)
     _check(lib().mta_adamw_step(handle, ctypes.byref(h), t, d_coef, stream),
@@ -235,6 +251,13 @@ def mta_list_plan(tensors, gtype, mkind, vkind):
 def mta_amp_clip_norm(handle, max_norm, d_amp, d_norm, d_coef, stream=0):
     _check(lib().mta_amp_clip_norm(handle, max_norm, d_amp, d_norm, d_coef,
                                    stream), "mta_amp_clip_norm")
+
+
+def mta_amp_clip_norm_joint(handles, max_norm, d_amp, d_norm, d_coef,
+                            stream=0):
+    _check(lib().mta_amp_clip_norm_joint(_handles(handles), len(handles),
+                                         max_norm, d_amp, d_norm, d_coef,
+                                         stream), "mta_amp_clip_norm_joint")
 
 
 def mta_amp_adamw_step(handle, hp, d_amp, d_coef, stream=0):

@@ -36,6 +36,7 @@ struct mta_list {
   mta::StepTile *d_stiles = nullptr;
   double *d_partials = nullptr;
   unsigned int *d_ticket = nullptr;
+  double *d_acc = nullptr;  // running total of a norm over several lists
   int weight_copies = 0;  // tensors with an attached 16-bit copy
   int copy_type = MTA_BF16;  // format of the copies: MTA_BF16 or MTA_F16
   bool deferred = false;  // a MTA_SCALE_DEFER factor is pending
@@ -312,6 +313,55 @@ mta::Work work_of(const mta_list *L, int grid, void *stream) {
   w.grid = grid;
   w.stream = static_cast<hipStream_t>(stream);
   return w;
+}
+
+// Argument checks of a norm over `nlists` lists (one list: mta_clip_norm).
+int check_joint(mta_list *const *lists, int64_t nlists, float max_norm,
+                const float *d_norm, const float *d_coef) {
+  if (!lists || nlists < 1) return fail(MTA_EINVAL, "no lists");
+  if (!(max_norm > 0.0f))
+    return fail(MTA_EINVAL, "max_norm must be > 0 (got %g)",
+                static_cast<double>(max_norm));
+  if (!d_coef) return fail(MTA_EINVAL, "d_coef is NULL");
+  if (!aligned(d_coef, 4) || (d_norm && !aligned(d_norm, 4)))
+    return fail(MTA_EALIGN, "d_norm / d_coef must be 4-byte aligned");
+  for (int64_t i = 0; i < nlists; ++i) {
+    if (!lists[i])
+      return nlists == 1 ? fail(MTA_EINVAL, "list is NULL")
+                         : fail(MTA_EINVAL, "list %lld is NULL",
+                                static_cast<long long>(i));
+    for (int64_t j = 0; j < i; ++j)
+      if (lists[j] == lists[i])  // its gradients would count twice
+        return fail(MTA_EINVAL, "list %lld appears twice",
+                    static_cast<long long>(i));
+  }
+  for (int64_t i = 0; i < nlists; ++i) {
+    const int rc = check_device(lists[i]);
+    if (rc) return rc;
+  }
+  return MTA_OK;
+}
+
+// One norm launch per list, in order: each adds the running float64 total
+// in lists[0]'s accumulator slot and writes the norm and coefficient of the
+// total so far; the last launch's are the joint result.  d_amp set: the
+// loss-scaled norm (unscale factor from the state, found_inf).
+int joint_norm(mta_list *const *lists, int64_t nlists, float max_norm,
+               mta_amp_state *d_amp, float *d_norm, float *d_coef,
+               void *stream, const char *what) {
+  double *const acc = lists[0]->d_acc;
+  for (int64_t i = 0; i < nlists; ++i) {
+    mta_list *L = lists[i];
+    const mta::Work wk = work_of(L, L->grid_norm, stream);
+    const float s = (!d_amp && L->deferred) ? L->deferred_s : 1.0f;
+    const mta::NormScratch scr{L->d_partials, L->d_ticket,
+                               i > 0 ? acc : nullptr,
+                               i + 1 < nlists ? acc : nullptr};
+    const hipError_t e = mta::launch_sumsq(L->gtype, wk, s, max_norm, scr,
+                                           d_norm, d_coef, d_amp);
+    if (e != hipSuccess) return after_launch(e, wk.stream, what);
+  }
+  return after_launch(hipSuccess, static_cast<hipStream_t>(stream), what);
 }
 
 const char *opt_name(int kind) {
@@ -637,6 +687,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->d_stiles = reinterpret_cast<mta::StepTile *>(base + off_st);
   L->d_partials = reinterpret_cast<double *>(base + off_part);
   L->d_ticket = reinterpret_cast<unsigned int *>(base + off_ticket);
+  L->d_acc = reinterpret_cast<double *>(base + off_ticket + 8);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   e = hipSuccess;
@@ -819,22 +870,16 @@ int mta_scale(mta_list *L, float factor, int flags, void *stream) {
 
 int mta_clip_norm(mta_list *L, float max_norm, float *d_norm, float *d_coef,
                   void *stream) {
-  if (!L) return fail(MTA_EINVAL, "list is NULL");
-  if (!(max_norm > 0.0f))
-    return fail(MTA_EINVAL, "max_norm must be > 0 (got %g)",
-                static_cast<double>(max_norm));
-  if (!d_coef) return fail(MTA_EINVAL, "d_coef is NULL");
-  if (!aligned(d_coef, 4) || (d_norm && !aligned(d_norm, 4)))
-    return fail(MTA_EALIGN, "d_norm / d_coef must be 4-byte aligned");
-  int rc = check_device(L);
+  return mta_clip_norm_joint(&L, 1, max_norm, d_norm, d_coef, stream);
+}
+
+int mta_clip_norm_joint(mta_list *const *lists, int64_t nlists,
+                        float max_norm, float *d_norm, float *d_coef,
+                        void *stream) {
+  int rc = check_joint(lists, nlists, max_norm, d_norm, d_coef);
   if (rc) return rc;
-  const mta::Work wk = work_of(L, L->grid_norm, stream);
-  const float s = L->deferred ? L->deferred_s : 1.0f;
-  return after_launch(
-      mta::launch_sumsq(L->gtype, wk, s, max_norm,
-                        mta::NormScratch{L->d_partials, L->d_ticket}, d_norm,
-                        d_coef, nullptr),
-      wk.stream, "mta_clip_norm");
+  return joint_norm(lists, nlists, max_norm, nullptr, d_norm, d_coef, stream,
+                    nlists == 1 ? "mta_clip_norm" : "mta_clip_norm_joint");
 }
 
 int mta_adamw_step(mta_list *L, const mta_adamw_hparams *hp, int64_t t,
@@ -851,28 +896,28 @@ int mta_step(mta_list *L, const mta_opt *opt, int64_t t, const float *d_coef,
 
 int mta_amp_clip_norm(mta_list *L, float max_norm, mta_amp_state *d_amp,
                       float *d_norm, float *d_coef, void *stream) {
-  if (!L) return fail(MTA_EINVAL, "list is NULL");
-  if (!(max_norm > 0.0f))
-    return fail(MTA_EINVAL, "max_norm must be > 0 (got %g)",
-                static_cast<double>(max_norm));
+  return mta_amp_clip_norm_joint(&L, 1, max_norm, d_amp, d_norm, d_coef,
+                                 stream);
+}
+
+int mta_amp_clip_norm_joint(mta_list *const *lists, int64_t nlists,
+                            float max_norm, mta_amp_state *d_amp,
+                            float *d_norm, float *d_coef, void *stream) {
   if (!d_amp) return fail(MTA_EINVAL, "d_amp is NULL");
-  if (!d_coef) return fail(MTA_EINVAL, "d_coef is NULL");
   if (!aligned(d_amp, 8))
     return fail(MTA_EALIGN, "d_amp must be 8-byte aligned");
-  if (!aligned(d_coef, 4) || (d_norm && !aligned(d_norm, 4)))
-    return fail(MTA_EALIGN, "d_norm / d_coef must be 4-byte aligned");
-  if (L->deferred)
-    return fail(MTA_ESTATE,
-                "a host deferred scale factor is pending; a loss-scaled norm "
-                "takes its factor from the loss-scale state");
-  int rc = check_device(L);
+  int rc = check_joint(lists, nlists, max_norm, d_norm, d_coef);
   if (rc) return rc;
-  const mta::Work wk = work_of(L, L->grid_norm, stream);
-  return after_launch(
-      mta::launch_sumsq(L->gtype, wk, 1.0f, max_norm,
-                        mta::NormScratch{L->d_partials, L->d_ticket}, d_norm,
-                        d_coef, d_amp),
-      wk.stream, "mta_amp_clip_norm");
+  for (int64_t i = 0; i < nlists; ++i)
+    if (lists[i]->deferred)
+      return fail(MTA_ESTATE,
+                  "list %lld: a host deferred scale factor is pending; a "
+                  "loss-scaled norm takes its factor from the loss-scale "
+                  "state",
+                  static_cast<long long>(i));
+  return joint_norm(lists, nlists, max_norm, d_amp, d_norm, d_coef, stream,
+                    nlists == 1 ? "mta_amp_clip_norm"
+                                : "mta_amp_clip_norm_joint");
 }
 
 int mta_amp_adamw_step(mta_list *L, const mta_adamw_hparams *hp,

@@ -84,6 +84,11 @@ constexpr uint64_t kNormSlotEmpty = 0xFFF0DEADBEEF0001ull;
 struct NormScratch {
   double *partials;
   unsigned int *ticket;
+  // A norm over several lists launches one norm per list: each adds the
+  // float64 total the previous one left in *acc_in (null for the first)
+  // and leaves its own in *acc_out (null when there is no later list).
+  const double *acc_in;
+  double *acc_out;
 };
 
 // Loss-scaled step: with `state` set, the kernel skips the update when

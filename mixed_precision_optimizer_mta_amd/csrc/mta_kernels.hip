@@ -784,8 +784,8 @@ __global__ void __launch_bounds__(kBlock)
 k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles,
         uint32_t keep_from, float s, float max_norm,
         double *__restrict__ partials, unsigned int *__restrict__ ticket,
-        float *__restrict__ d_norm, float *__restrict__ d_coef,
-        mta_amp_state *__restrict__ amp) {
+        const double *acc_in, double *acc_out, float *__restrict__ d_norm,
+        float *__restrict__ d_coef, mta_amp_state *__restrict__ amp) {
   constexpr int V = kWide<D>;
   constexpr int G = kTileElems / (kBlock * V);
   if (amp) s = inv_scale(amp->scale);  // loss-scaled: unscale by 1/scale
@@ -869,8 +869,12 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  const double total = wave_sum(a);
+  double total = wave_sum(a);
   if (lane == 0) {
+    // a norm over several lists: the earlier lists' total comes first
+    // (acc_in and acc_out may be one address: read, then written)
+    if (acc_in) total = *acc_in + total;
+    if (acc_out) *acc_out = total;
     const float nrm = static_cast<float>(sqrt(total));
     // PyTorch's clip_grad_norm_: max / (norm + 1e-6), clamped at 1; the
     // comparison lets a NaN through and an infinite norm gives 0.
@@ -1091,7 +1095,8 @@ hipError_t launch_sumsq_t(const Work &wk, float s, float max_norm,
                           mta_amp_state *amp) {
   hipLaunchKernelGGL((k_sumsq<D>), dim3(wk.grid), dim3(kBlock), 0, wk.stream,
                      wk.gtiles, wk.ntiles, wk.keep_from, s, max_norm,
-                     scr.partials, scr.ticket, d_norm, d_coef, amp);
+                     scr.partials, scr.ticket, scr.acc_in, scr.acc_out,
+                     d_norm, d_coef, amp);
   return hipGetLastError();
 }
 

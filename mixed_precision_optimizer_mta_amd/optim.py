@@ -4,12 +4,14 @@ Marshalling only, like MtaList: it allocates the state buffers a rule needs
 (float32, or bfloat16 for packed Adam-family moments), keeps them in
 ``self.state`` under PyTorch's names (exp_avg, exp_avg_sq, momentum_buffer)
 so ``state_dict()`` / ``load_state_dict()`` work, and drives one list per
-parameter group.  A step is:
+parameter group and gradient dtype.  A step is:
 
-  * with ``max_norm``: one mta_clip_norm over every gradient of every group
-    (a list with no state buffers), the joint norm and coefficient left in
-    device tensors (``last_norm``, ``last_coef``);
-  * one mta_step per parameter group with that coefficient.
+  * with ``max_norm``: one clip over the joint norm of every gradient of
+    every group (mta_clip_norm_joint over one norm list per gradient dtype,
+    lists with no state buffers), the norm and coefficient left in device
+    tensors (``last_norm``, ``last_coef``);
+  * one mta_step per parameter group and gradient dtype with that
+    coefficient.
 
 With ``loss_scale`` (an initial scale) the step is loss-scaled on the
 device: ``opt.loss_scale`` is a one-element float32 device view of the
@@ -28,16 +30,19 @@ device tables, which allocates), and keep the gradients' storage across
 replays (``zero_grad=True`` zeroes them inside the update launch).
 
 ``master_weights=True`` is for a model kept in bfloat16 or float16: the
-optimizer holds a float32 master copy of every parameter (``state[p]
+optimizer holds a float32 master copy of every 16-bit parameter (``state[p]
 ["master_weight"]``), the update runs on the masters with the model's 16-bit
 gradients, and the same launch writes the 16-bit rounding of each new master
 into the parameter itself (the list's weight copies).  The model's forward
 and backward then read and produce 16-bit values only, while the weights
-accumulate updates in float32.
+accumulate updates in float32.  A parameter the model keeps in float32 (one
+whose uses need full precision) is its own master and takes no copy; its
+float32 gradient joins the same joint clip.
 
 Every step of the arithmetic runs in libmta.  Parameters are float32 CUDA
-tensors (or, with master_weights, all bfloat16 or all float16); their
-gradients share one type (float32, bfloat16 or float16).  The device tables
+tensors (with master_weights, also bfloat16 or float16 ones); gradients are
+float32, bfloat16 or float16, a 16-bit parameter's in its own dtype.  The
+device tables
 are rebuilt whenever a parameter, gradient or state buffer moved
 (``zero_grad(set_to_none=True)`` lets PyTorch reallocate gradients;
 ``zero_grad=True`` here instead zeroes them inside the update launch).
@@ -48,9 +53,11 @@ parameter's dtype).
 import torch
 
 from . import _binding as B
-from .torch_list import MtaList
+from .torch_list import MtaList, clip_norm_joint
 
 _KINDS = ("adamw", "adam", "sgd", "momentum")
+_GTYPE = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
+          torch.float16: B.MTA_F16}
 
 
 class MtaOptimizer(torch.optim.Optimizer):
@@ -75,8 +82,8 @@ class MtaOptimizer(torch.optim.Optimizer):
         self.packed = bool(packed_moments)
         self.zero_grad_in_step = bool(zero_grad)
         self.master_weights = bool(master_weights)
-        self._lists = {}       # group index -> (pointer key, MtaList)
-        self._norm_list = None  # (pointer key, MtaList)
+        self._lists = {}       # (group, grad dtype) -> (pointer key, MtaList)
+        self._norm_cache = {}  # grad dtype -> (pointer key, MtaList)
         self.last_norm = None
         self.last_coef = None
         self.amp = None
@@ -95,8 +102,9 @@ class MtaOptimizer(torch.optim.Optimizer):
 
     # -- state buffers ----------------------------------------------------
     def master(self, p):
-        """The float32 weight the update runs on: p itself, or its master."""
-        if not self.master_weights:
+        """The float32 weight the update runs on: p itself (a float32
+        parameter), or the master of a 16-bit one."""
+        if p.dtype == torch.float32:
             return p
         st = self.state[p]
         if "master_weight" not in st:
@@ -119,7 +127,8 @@ class MtaOptimizer(torch.optim.Optimizer):
             return st["exp_avg"], st["exp_avg_sq"]
         if self.kind == "momentum":
             if "momentum_buffer" not in st:
-                st["momentum_buffer"] = torch.zeros_like(p)
+                st["momentum_buffer"] = torch.zeros_like(
+                    p, dtype=torch.float32)
                 st["step"] = 0
             return st["momentum_buffer"], None
         st.setdefault("step", 0)
@@ -127,11 +136,11 @@ class MtaOptimizer(torch.optim.Optimizer):
 
     def _check(self, p):
         if self.master_weights:
-            if p.dtype not in (torch.bfloat16, torch.float16) or \
-                    not p.is_cuda or not p.is_contiguous():
+            if p.dtype not in _GTYPE or not p.is_cuda or \
+                    not p.is_contiguous():
                 raise TypeError("with master_weights, parameters must be "
-                                "contiguous bfloat16 or float16 CUDA "
-                                "tensors")
+                                "contiguous float32, bfloat16 or float16 "
+                                "CUDA tensors")
         elif p.dtype != torch.float32 or not p.is_cuda or \
                 not p.is_contiguous():
             raise TypeError("parameters must be contiguous float32 CUDA "
@@ -142,6 +151,8 @@ class MtaOptimizer(torch.optim.Optimizer):
                              "gradient before step()")
 
     def _group_list(self, k, params):
+        """The update list of parameter group k's params (all with one
+        gradient dtype; k is (group index, dtype))."""
         groups, key = [], []
         for p in params:
             m, v = self._state_buffers(p)
@@ -156,40 +167,50 @@ class MtaOptimizer(torch.optim.Optimizer):
         if cached is None or cached[0] != key:
             if cached is not None:
                 cached[1].close()
-            g0 = groups[0][1]
-            gtype = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
-                     torch.float16: B.MTA_F16}[g0.dtype]
             mk = B.MTA_MOM_BF16X2 if self.packed else B.MTA_MOM_F32
-            L = MtaList([], entries=[(p.data_ptr(), g.data_ptr(),
+            L = MtaList([], entries=[(w.data_ptr(), g.data_ptr(),
                                       None if m is None else m.data_ptr(),
                                       None if v is None else v.data_ptr(),
-                                      p.numel()) for p, g, m, v in groups],
-                        gtype=gtype, mkind=mk, vkind=mk)
+                                      w.numel()) for w, g, m, v in groups],
+                        gtype=_GTYPE[groups[0][1].dtype], mkind=mk, vkind=mk)
             L._keep = groups
-            if self.master_weights:
-                # the parameters are the list's 16-bit weight copies
-                L.set_weight_copies([p.detach() for p in params])
+            if any(p.dtype != torch.float32 for p in params):
+                # 16-bit parameters are the list's weight copies (a float32
+                # one among them is its own weight and takes none)
+                L.set_weight_copies([None if p.dtype == torch.float32
+                                     else p.detach() for p in params])
             self._lists[k] = (key, L)
         return self._lists[k][1]
 
-    def _joint_norm_list(self, all_params):
-        # the norm reads only the gradients; w is the float32 weight the
-        # list's validation sizes as 4 bytes per element
-        ws = [self.master(p) for p in all_params]
-        key = tuple((w.data_ptr(), p.grad.data_ptr(), p.numel(),
-                     p.grad.dtype) for w, p in zip(ws, all_params))
-        if self._norm_list is None or self._norm_list[0] != key:
-            if self._norm_list is not None:
-                self._norm_list[1].close()
-            gtype = {torch.float32: B.MTA_F32, torch.bfloat16: B.MTA_BF16,
-                     torch.float16: B.MTA_F16}[all_params[0].grad.dtype]
-            L = MtaList([], entries=[(w.data_ptr(), p.grad.data_ptr(), None,
-                                      None, p.numel())
-                                     for w, p in zip(ws, all_params)],
-                        gtype=gtype, mkind=B.MTA_MOM_F32, vkind=B.MTA_MOM_F32)
-            L._keep = [(w, p.grad) for w, p in zip(ws, all_params)]
-            self._norm_list = (key, L)
-        return self._norm_list[1]
+    def _norm_lists(self, all_params):
+        """One norm list per gradient dtype (float32, bfloat16, float16
+        order); the clip is over their joint norm."""
+        out, keys = [], []
+        for dt in _GTYPE:
+            ps = [p for p in all_params if p.grad.dtype == dt]
+            if not ps:
+                continue
+            # the norm reads only the gradients; w is the float32 weight
+            # the list's validation sizes as 4 bytes per element
+            ws = [self.master(p) for p in ps]
+            key = tuple((w.data_ptr(), p.grad.data_ptr(), p.numel())
+                        for w, p in zip(ws, ps))
+            cached = self._norm_cache.get(dt)
+            if cached is None or cached[0] != key:
+                if cached is not None:
+                    cached[1].close()
+                L = MtaList([], entries=[(w.data_ptr(), p.grad.data_ptr(),
+                                          None, None, p.numel())
+                                         for w, p in zip(ws, ps)],
+                            gtype=_GTYPE[dt], mkind=B.MTA_MOM_F32,
+                            vkind=B.MTA_MOM_F32)
+                L._keep = [(w, p.grad) for w, p in zip(ws, ps)]
+                self._norm_cache[dt] = (key, L)
+            out.append(self._norm_cache[dt][1])
+            keys.append(dt)
+        for dt in [d for d in self._norm_cache if d not in keys]:
+            self._norm_cache.pop(dt)[1].close()
+        return out
 
     # -- the step ---------------------------------------------------------
     @torch.no_grad()
@@ -205,51 +226,49 @@ class MtaOptimizer(torch.optim.Optimizer):
             return loss
         for p in all_params:
             self._check(p)
-        if len({p.grad.dtype for p in all_params}) != 1:
-            raise TypeError("all gradients must share one dtype")
-        if self.master_weights and \
-                len({p.dtype for p in all_params}) != 1:
-            raise TypeError("with master_weights, all parameters must share "
-                            "one dtype")
+            if p.grad.dtype not in _GTYPE:
+                raise TypeError("gradients are float32, bfloat16 or float16")
+            if p.dtype != torch.float32 and p.grad.dtype != p.dtype:
+                raise TypeError("a 16-bit parameter's gradient has its dtype")
         coef = None
         if self.max_norm is not None or self.amp is not None:
             dev = all_params[0].device
             if self.last_norm is None or self.last_norm.device != dev:
                 self.last_norm = torch.zeros(1, device=dev)
                 self.last_coef = torch.zeros(1, device=dev)
-            NL = self._joint_norm_list(all_params)
             cap = float("inf") if self.max_norm is None else \
                 float(self.max_norm)
-            if self.amp is not None:
-                NL.amp_clip_norm(cap, self.amp, self.last_norm,
-                                 self.last_coef)
-            else:
-                NL.clip_norm(cap, self.last_norm, self.last_coef)
+            clip_norm_joint(self._norm_lists(all_params), cap,
+                            self.last_norm, self.last_coef, amp=self.amp)
             coef = self.last_coef
-        for k, (group, ps) in enumerate(zip(self.param_groups, groups)):
-            if not ps:
-                continue
-            L = self._group_list(k, ps)
+        for k, (group, ps_all) in enumerate(zip(self.param_groups, groups)):
             b1, b2 = group["betas"]
             rule = dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
                         eps=group["eps"], weight_decay=group["weight_decay"],
                         momentum=group["momentum"],
                         zero_grad=self.zero_grad_in_step)
-            if self.amp is not None:
-                L.amp_step(rule, self.amp, coef)
-                continue
-            steps = {int(self.state[p]["step"]) for p in ps}
-            if len(steps) != 1:
-                raise RuntimeError(
-                    "the parameters of one group have taken different "
-                    "numbers of steps; one launch applies one t to a group")
-            t = steps.pop() + 1
-            for p in ps:
-                self.state[p]["step"] = t
-            L.step(rule, t, coef)
+            for dt in _GTYPE:   # one launch per gradient dtype in the group
+                ps = [p for p in ps_all if p.grad.dtype == dt]
+                if ps:
+                    self._update(self._group_list((k, dt), ps), ps, rule,
+                                 coef)
         if self.amp is not None:
             self.amp.update(*self._amp_rule)
         return loss
+
+    def _update(self, L, ps, rule, coef):
+        if self.amp is not None:
+            L.amp_step(rule, self.amp, coef)
+            return
+        steps = {int(self.state[p]["step"]) for p in ps}
+        if len(steps) != 1:
+            raise RuntimeError(
+                "the parameters of one group have taken different numbers "
+                "of steps; one launch applies one t to a group")
+        t = steps.pop() + 1
+        for p in ps:
+            self.state[p]["step"] = t
+        L.step(rule, t, coef)
 
     # -- checkpoints ------------------------------------------------------
     def load_state_dict(self, state_dict):

@@ -184,6 +184,23 @@ class MtaList:
             pass
 
 
+def clip_norm_joint(lists, max_norm, norm_out, coef_out, amp=None):
+    """One clip over the joint norm of several MtaLists (each with its own
+    gradient type): mta_clip_norm_joint, or mta_amp_clip_norm_joint with
+    a loss-scale state."""
+    for t in (norm_out, coef_out):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda):
+            raise TypeError("norm/coef outputs are float32 GPU tensors")
+    handles = [L.handle for L in lists]
+    nptr = None if norm_out is None else norm_out.data_ptr()
+    if amp is None:
+        B.mta_clip_norm_joint(handles, max_norm, nptr, coef_out.data_ptr(),
+                              current_stream())
+    else:
+        B.mta_amp_clip_norm_joint(handles, max_norm, amp.ptr, nptr,
+                                  coef_out.data_ptr(), current_stream())
+
+
 class AmpState:
     """The 24-byte device loss-scale state of include/mta.h (mta_amp_state):
     scale, found_inf, growth_tracker, step.  Lives in device memory; reading

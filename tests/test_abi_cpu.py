@@ -198,3 +198,17 @@ def test_success_clears_the_last_error():
     assert M.mta_last_error() != ""
     M.mta_adamw_scalars((1e-3, 0.9, 0.999, 1e-8, 0.0), 1)
     assert M.mta_last_error() == ""
+
+
+def test_joint_norm_validation_before_any_device_work():
+    assert _err(M.mta_clip_norm_joint, [], 1.0, None, 0x1000) == -1
+    assert _err(M.mta_clip_norm_joint, [None], 1.0, None, 0x1000) == -1
+    assert _err(M.mta_clip_norm_joint, [None, None], 1.0, None,
+                0x1000) == -1
+    assert _err(M.mta_clip_norm_joint, [None], 0.0, None, 0x1000) == -1
+    assert _err(M.mta_clip_norm_joint, [None], 1.0, None, None) == -1
+    assert _err(M.mta_clip_norm_joint, [None], 1.0, None, 0x1002) == -2
+    assert _err(M.mta_amp_clip_norm_joint, [None], 1.0, None, None,
+                0x1000) == -1
+    assert _err(M.mta_amp_clip_norm_joint, [None], 1.0, 0x1004, None,
+                0x1000) == -2

@@ -1,0 +1,143 @@
+"""One clip over several lists (mta_clip_norm_joint,
+mta_amp_clip_norm_joint): lists with float32, bfloat16 and float16
+gradients and their own deferred factors, against the oracle's joint norm
+(1e-6 relative, the coefficient exact on the device norm), then every
+list's update against the oracle bit for bit with the joint coefficient."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_optimizer_mta_amd import (AmpState, MtaError,
+                                               clip_norm_joint)
+from mixed_precision_optimizer_mta_amd import workloads as WL
+
+from parity_util import (check_norm, compare, make_list, oracle_grads,
+                         oracle_state)
+
+pytestmark = pytest.mark.gpu
+
+
+def lists_of(specs):
+    """specs: [(sizes, gtype, mkind, vkind, scale, ident)] -> arenas."""
+    out = []
+    for sizes, g, m, v, scale, ident in specs:
+        wl = WL.Workload(f"joint{ident}", sizes, g, m, v, steps=2,
+                         g_sigma=0.05, scale=scale, ident=ident)
+        a = WL.Arena(wl, "cuda")
+        a.fill_weights()
+        out.append(a)
+    return out
+
+
+SPECS = [([4096 * 3 + 5, 700], WL.F32, 0, 0, 1.0, 61),
+         ([9000, 17, 4096], WL.BF16, 1, 0, 2.0 ** -8, 62),
+         ([5000], WL.F16, 0, 1, 0.5, 63)]
+
+
+@pytest.mark.parametrize("order", [(0, 1, 2), (2, 0, 1), (1,)])
+def test_joint_clip_over_mixed_gradient_types(order):
+    arenas = lists_of([SPECS[i] for i in order])
+    lists = [make_list(a) for a in arenas]
+    ost = [oracle_state(a) for a in arenas]
+    nd = torch.zeros(1, device="cuda")
+    cd = torch.zeros(1, device="cuda")
+    max_norm = 0.5
+    for t in (1, 2):
+        parts = []
+        for a, L, o in zip(arenas, lists, ost):
+            a.fill_grads(t)
+            for x, g in zip(o, oracle_grads(a)):
+                x.g = g
+            if a.wl.scale != 1.0:
+                L.scale(a.wl.scale, defer=True)
+            parts.append(([x.g for x in o], a.wl.gtype, a.wl.scale))
+        clip_norm_joint(lists, max_norm, nd, cd)
+        for a, L in zip(arenas, lists):
+            L.adamw_step(a.wl.hparams, t, cd)
+        torch.cuda.synchronize()
+        coef = np.float32(cd.item())
+        check_norm(np.float32(nd.item()), coef, O.joint_norm(parts),
+                   max_norm, f"joint {order} t={t}")
+        for a, o in zip(arenas, ost):
+            O.step_(o, a.wl.gtype, a.wl.mkind, a.wl.vkind, a.wl.lr,
+                    a.wl.beta1, a.wl.beta2, a.wl.eps, a.wl.weight_decay, t,
+                    s=a.wl.scale, coef=coef)
+            assert compare(a, o) == {"w": 0, "m": 0, "v": 0}
+    for L in lists:
+        L.close()
+
+
+def test_one_list_joint_is_the_plain_clip_and_repeats_bitwise():
+    (a,) = lists_of([SPECS[1]])
+    L = make_list(a)
+    a.fill_grads(1)
+    got = []
+    for joint in (False, True, True):
+        nd = torch.zeros(1, device="cuda")
+        cd = torch.zeros(1, device="cuda")
+        if joint:
+            clip_norm_joint([L], 0.5, nd, cd)
+        else:
+            L.clip_norm(0.5, nd, cd)
+        torch.cuda.synchronize()
+        got.append((nd.view(torch.int32).item(), cd.view(torch.int32).item()))
+    assert got[0] == got[1] == got[2]
+    # two lists twice: the same bits every time (fixed order of the sums)
+    b, c = lists_of([SPECS[0], SPECS[2]])
+    Lb, Lc = make_list(b), make_list(c)
+    b.fill_grads(1)
+    c.fill_grads(1)
+    bits = set()
+    for _ in range(4):
+        nd = torch.zeros(1, device="cuda")
+        cd = torch.zeros(1, device="cuda")
+        clip_norm_joint([L, Lb, Lc], 0.5, nd, cd)
+        torch.cuda.synchronize()
+        bits.add(nd.view(torch.int32).item())
+    assert len(bits) == 1
+    for x in (L, Lb, Lc):
+        x.close()
+
+
+def test_joint_rejects_a_repeated_list_and_pending_factor_under_amp():
+    a, b = lists_of([SPECS[0], SPECS[2]])
+    La, Lb = make_list(a), make_list(b)
+    nd = torch.zeros(1, device="cuda")
+    cd = torch.zeros(1, device="cuda")
+    with pytest.raises(MtaError) as e:
+        clip_norm_joint([La, Lb, La], 1.0, nd, cd)
+    assert e.value.code == -1
+    amp = AmpState(64.0)
+    Lb.scale(0.5, defer=True)
+    with pytest.raises(MtaError) as e:
+        clip_norm_joint([La, Lb], 1.0, nd, cd, amp=amp)
+    assert e.value.code == -6
+    La.close()
+    Lb.close()
+
+
+def test_loss_scaled_joint_clip_and_found_inf():
+    specs = [([4096 * 2 + 3], WL.F32, 0, 0, 1.0, 64),
+             ([7000, 11], WL.F16, 0, 0, 1.0, 65)]
+    arenas = lists_of(specs)
+    lists = [make_list(a) for a in arenas]
+    amp = AmpState(1024.0)
+    nd = torch.zeros(1, device="cuda")
+    cd = torch.zeros(1, device="cuda")
+    for t, bad in ((1, False), (2, True)):
+        for a in arenas:
+            a.fill_grads(t)
+        if bad:                        # an overflow in the float16 list
+            arenas[1].view("g", 1)[3] = float("inf")
+        parts = [(oracle_grads(a), a.wl.gtype, O.inv_scale(1024.0))
+                 for a in arenas]
+        clip_norm_joint(lists, 1.0, nd, cd, amp=amp)
+        torch.cuda.synchronize()
+        st = amp.read()
+        assert st["found_inf"] == (1.0 if bad else 0.0)
+        if not bad:
+            check_norm(np.float32(nd.item()), np.float32(cd.item()),
+                       O.joint_norm(parts), 1.0, f"amp joint t={t}")
+    for L in lists:
+        L.close()

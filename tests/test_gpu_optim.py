@@ -399,3 +399,81 @@ def test_master_weights_loss_scaled_step_replays_in_a_graph():
             assert not bool(pa.grad.any())
         assert opt_a.amp.read() == opt_b.amp.read()
     assert opt_a.amp.read()["step"] >= 6
+
+
+class _Mixed(torch.nn.Module):
+    """A bfloat16 model with one layer kept in float32 (a parameter whose
+    uses need full precision)."""
+
+    def __init__(self, seed):
+        super().__init__()
+        torch.manual_seed(seed)
+        self.a = torch.nn.Linear(300, 257).to(torch.bfloat16)
+        self.b = torch.nn.Linear(257, 10)          # float32
+
+    def forward(self, x):
+        h = torch.nn.functional.gelu(self.a(x))
+        return self.b(h.float())
+
+
+@pytest.mark.parametrize("kind", ["adamw", "adam", "sgd", "momentum"])
+def test_master_weights_with_a_float32_layer_match_the_oracle(kind):
+    # bfloat16 parameters: float32 masters and copies written back; the
+    # float32 layer is its own weight; one joint clip over both gradient
+    # types; every rule (momentum keeps a float32 buffer)
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _Mixed(23).cuda()
+    params = list(model.parameters())
+    adam = kind in ("adamw", "adam")
+    lr = 1e-3 if adam else 0.05
+    opt = MtaOptimizer(params, kind=kind, lr=lr, betas=(0.9, 0.99),
+                       weight_decay=0.05 if adam else 0.0, momentum=0.9,
+                       max_norm=0.5, master_weights=True)
+    rule = dict(kind=kind, lr=lr, beta1=0.9, beta2=0.99, eps=1e-8,
+                weight_decay=0.05 if adam else 0.0, momentum=0.9)
+    half = [p for p in params if p.dtype == torch.bfloat16]
+    full = [p for p in params if p.dtype == torch.float32]
+    assert half and full
+
+    def state(p):
+        n = p.numel()
+        m = np.zeros(n, np.float32) if kind != "sgd" else None
+        v = np.zeros(n, np.float32) if adam else None
+        if p.dtype == torch.float32:
+            return O.Tensor(_host(p).ravel(), None, m, v)
+        return O.Tensor(_host(p.float()).ravel(), None, m, v,
+                        np.zeros(n, np.uint16), O.BF16)
+
+    o_half = [state(p) for p in half]
+    o_full = [state(p) for p in full]
+    for t in range(1, 5):
+        torch.manual_seed(6000 + t)
+        x = torch.randn(32, 300, device="cuda", dtype=torch.bfloat16)
+        y = torch.randint(0, 10, (32,), device="cuda")
+        model.zero_grad(set_to_none=False)
+        torch.nn.functional.cross_entropy(model(x), y).backward()
+        for p, o in zip(half, o_half):
+            o.g = _bits16(p.grad)
+        for p, o in zip(full, o_full):
+            o.g = _host(p.grad).ravel()
+        opt.step()
+        torch.cuda.synchronize()
+        parts = [([o.g for o in o_full], O.F32, 1.0),
+                 ([o.g for o in o_half], O.BF16, 1.0)]
+        nrm = O.joint_norm(parts)
+        assert abs(float(opt.last_norm.item()) - nrm) <= 1e-6 * nrm
+        coef = np.float32(opt.last_coef.item())
+        assert coef == O.clip_coef(0.5, np.float32(opt.last_norm.item()))
+        O.opt_step_(o_full, rule, O.F32, 0, 0, t, coef=coef)
+        O.opt_step_(o_half, rule, O.BF16, 0, 0, t, coef=coef)
+        for p, o in zip(full, o_full):
+            assert np.array_equal(_host(p).ravel().view(np.uint32),
+                                  o.w.view(np.uint32)), (kind, t)
+        for p, o in zip(half, o_half):
+            w = opt.state[p]["master_weight"]
+            assert np.array_equal(_host(w).ravel().view(np.uint32),
+                                  o.w.view(np.uint32)), (kind, t)
+            assert np.array_equal(_bits16(p), o.w16), (kind, t)
+        if kind == "momentum":
+            for p in params:
+                assert opt.state[p]["momentum_buffer"].dtype == torch.float32

@@ -31,10 +31,10 @@ def test_step_without_gradients_is_a_no_op():
     assert torch.equal(ps[0].detach(), torch.zeros(10))
 
 
-def test_master_weights_refuse_float32_and_mixed_parameters():
+def test_master_weights_refuse_cpu_and_plain_mode_refuses_16_bit():
     ps = _params()
     ps[0].grad = torch.zeros(10)
-    with pytest.raises(TypeError):       # float32 parameters, CPU too
+    with pytest.raises(TypeError):       # parameters off the GPU
         MtaOptimizer(ps, master_weights=True).step()
     h = [torch.nn.Parameter(torch.zeros(10, dtype=torch.bfloat16))]
     h[0].grad = torch.zeros(10, dtype=torch.bfloat16)
