@@ -89,13 +89,15 @@ constexpr int kNormBlocksPerCu16 = 2;
 // Gradient bytes, at the end of the list, that the norm reads with
 // allocating loads so that the memory-side cache (256 MiB on MI355X) still
 // holds them when the update reads them again; the update's own accesses
-// stream past it.  Only for lists whose gradients total at most
-// kNormKeepListMiB: in a longer list the update moves many GB before it
-// reaches those tiles, they no longer hit, and the allocating loads only
-// slow the norm.  MTA_NORM_KEEP_MIB sets the budget for any list at list
-// creation (0: every norm load streams).
+// stream past it.  Only while the update moves at most kNormKeepReachMiB
+// before it reaches those tiles (its w, g, m, v traffic over the tiles
+// before them): the kept lines survive about 2 GB of it (124M float32
+// list, 1.6 GB: they hit; one eighth of the 1.56B list, 2.6 GB: they no
+// longer do, and the allocating loads only slow the norm).
+// MTA_NORM_KEEP_MIB sets the budget for any list at list creation (0:
+// every norm load streams).
 constexpr int kNormKeepMiB = 256;
-constexpr int64_t kNormKeepListMiB = 1024;
+constexpr int64_t kNormKeepReachMiB = 2048;
 
 int after_launch(hipError_t e, hipStream_t stream, const char *what) {
   if (e != hipSuccess)
@@ -587,20 +589,27 @@ int plan_list(const mta_tensor *tensors, int64_t count, int gtype, int mkind,
     for (const mta::StepTile &st : stiles)
       gtiles.push_back(mta::GradTile{st.g, st.lim, aligned(st.g, 16) ? 1u : 0u});
     // the last tiles, up to the keep budget
-    const int keep_default =
-        elements * static_cast<int64_t>(gsz) <= (kNormKeepListMiB << 20)
-            ? kNormKeepMiB
-            : 0;
-    uint64_t budget = static_cast<uint64_t>(env_int(
-                          "MTA_NORM_KEEP_MIB", keep_default, 0, 1 << 20))
-                      << 20;
+    const int keep_mib = env_int("MTA_NORM_KEEP_MIB", -1, 0, 1 << 20);
+    uint64_t budget =
+        static_cast<uint64_t>(keep_mib >= 0 ? keep_mib : kNormKeepMiB) << 20;
     keep_from = static_cast<uint32_t>(gtiles.size());
+    uint64_t kept_elems = 0;
     while (keep_from > 0) {
       const uint64_t bytes = uint64_t{gtiles[keep_from - 1].lim} * gsz;
       if (bytes > budget) break;
       budget -= bytes;
+      kept_elems += gtiles[keep_from - 1].lim;
       --keep_from;
     }
+    // the update's bytes per element: w read and written, g, and m and v
+    // read and written when the list has them
+    const uint64_t upd = 8 + gsz + (state < 0 || (state & 1) ? 2 * msz : 0) +
+                         (state < 0 || (state & 2) ? 2 * vsz : 0);
+    const uint64_t reach =
+        (static_cast<uint64_t>(elements) - kept_elems) * upd;
+    if (keep_mib < 0 &&
+        reach > static_cast<uint64_t>(kNormKeepReachMiB) << 20)
+      keep_from = static_cast<uint32_t>(gtiles.size());
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
   }

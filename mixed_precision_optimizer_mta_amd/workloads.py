@@ -29,7 +29,13 @@ Workloads (parameter counts are exact):
              of the 10,000 all-zero; packed bfloat16 m, f32 v; wd = 0.01.
 All use lr 3e-4, betas (0.9, 0.999), eps 1e-8, weight decay 0.1 (ragged:
 0.01), clip 1.0, and w ~ N(0, 0.02) unless stated.
+
+<name>_shard<r>of<N> is rank r's share of workload <name> when its flat
+element space is cut into N equal ranges (tensors split at the range
+edges): one GPU's list under sharded optimizer state, e.g.
+gpt2_xl_shard0of8 (194,681,800 params in 35 pieces).
 """
+import re
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -110,7 +116,33 @@ def ragged_sizes(count=10_000, seed=SEED):
         int(i) for i in zero)
 
 
+def shard_sizes(sizes, rank, world):
+    """The pieces of a tensor list that one of `world` equal ranges of its
+    flat element space holds (range `rank`): each tensor cut at the range
+    edges, empty pieces dropped, in list order.  This is one GPU's share of
+    a list whose optimizer state is sharded across `world` GPUs."""
+    total = sum(sizes)
+    lo, hi = total * rank // world, total * (rank + 1) // world
+    out, off = [], 0
+    for n in sizes:
+        a, b = max(lo, off), min(hi, off + n)
+        if b > a:
+            out.append(b - a)
+        off += n
+    return out
+
+
 def get(name):
+    m = re.fullmatch(r"(.+)_shard(\d+)of(\d+)", name)
+    if m:
+        base = get(m.group(1))
+        rank, world = int(m.group(2)), int(m.group(3))
+        if not 0 <= rank < world or base.zero_grad:
+            raise KeyError(name)
+        import dataclasses
+        return dataclasses.replace(
+            base, name=name, sizes=shard_sizes(base.sizes, rank, world),
+            ident=base.ident * 1000 + world * 10 + rank)
     if name == "tiny":
         return Workload("tiny", [384 * 384, 384 * 1536, 1536], F32, MOM_F32,
                         MOM_F32, steps=10, g_sigma=0.01, ident=1)

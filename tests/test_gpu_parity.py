@@ -461,3 +461,14 @@ def test_norm_keeps_the_last_256_mib_of_the_124m_list(monkeypatch):
     assert (256 << 20) - 4096 * 4 < kept * 4096 * 4 <= (256 << 20) + \
         64 * 4096 * 4
     L.close()
+
+
+def test_full_gpt2_xl_shard_in_a_flat_buffer_sampled():
+    # one GPU's eighth of the 1.56B list, its 35 pieces back to back as a
+    # sharded flat buffer holds them (pieces start at any element)
+    wl = WL.get("gpt2_xl_shard0of8")
+    offsets = [0]
+    for n in wl.sizes[:-1]:
+        offsets.append(offsets[-1] + n)
+    worst = lockstep(wl, wl.steps, offsets=offsets, nsample=1 << 20)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst

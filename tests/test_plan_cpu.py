@@ -77,25 +77,27 @@ def test_a_state_buffer_alone_can_block_the_vector_path():
     assert info["vector_tensors"] == 0   # m one element further than the rest
 
 
-def _kept(sizes, gtype):
-    """The norm's kept tiles of a padded list, from the tile lengths."""
+def _kept(sizes, gtype, mkind, vkind):
+    """The norm's kept tiles of a padded list, from the tile lengths: the
+    last tiles whose gradients fit 256 MiB, provided the update moves at
+    most 2 GiB (w, g, m, v, read and written) before it reaches them."""
     lims = []
     for n in sizes:
         lims += [4096] * (n // 4096) + ([n % 4096] if n % 4096 else [])
     gsz = 4 if gtype == 0 else 2
-    if sum(sizes) * gsz > 1 << 30:
-        return 0
-    budget, k = 256 << 20, 0
+    budget, k, elems = 256 << 20, 0, 0
     for lim in reversed(lims):
         if lim * gsz > budget:
             break
         budget -= lim * gsz
         k += 1
-    return k
+        elems += lim
+    upd = 8 + gsz + 2 * (2 if mkind else 4) + 2 * (2 if vkind else 4)
+    return 0 if (sum(sizes) - elems) * upd > 2 << 30 else k
 
 
 @pytest.mark.parametrize("name", ["gpt2_124m", "gpt2_124m_bf16g", "gpt2_xl",
-                                  "ragged", "tiny"])
+                                  "ragged", "tiny", "gpt2_xl_shard0of8"])
 def test_kept_tiles_follow_the_budget(name, monkeypatch):
     monkeypatch.delenv("MTA_NORM_KEEP_MIB", raising=False)
     wl = WL.get(name)
@@ -106,9 +108,12 @@ def test_kept_tiles_follow_the_budget(name, monkeypatch):
         o += -(-n // 128) * 128
     info = M.mta_list_plan(ents, wl.gtype, wl.mkind, wl.vkind)
     assert info["vector_tensors"] == sum(1 for n in wl.sizes if n)
-    assert info["norm_kept_tiles"] == _kept(wl.sizes, wl.gtype)
-    if name in ("gpt2_xl", "ragged"):
-        assert info["norm_kept_tiles"] == 0      # over 1 GiB of gradients
+    assert info["norm_kept_tiles"] == _kept(wl.sizes, wl.gtype, wl.mkind,
+                                            wl.vkind)
+    if name in ("gpt2_xl", "ragged", "gpt2_xl_shard0of8"):
+        assert info["norm_kept_tiles"] == 0      # reached too late
+    if name == "gpt2_124m":
+        assert 0 < info["norm_kept_tiles"] < info["tiles"]
     if name in ("gpt2_124m_bf16g", "tiny"):
         assert info["norm_kept_tiles"] == info["tiles"]   # all of it fits
     monkeypatch.setenv("MTA_NORM_KEEP_MIB", "0")

@@ -53,3 +53,25 @@ def test_float16_gradients_are_torch_conversions():
     a.fill_grads(2)
     assert a.g.dtype == torch.float16
     assert bool(torch.isfinite(a.g).all()) and float(a.g.abs().max()) > 100
+
+
+def test_shards_cover_the_list_exactly_once():
+    sizes = WL.get("gpt2_xl").sizes
+    world = 8
+    pieces = [WL.shard_sizes(sizes, r, world) for r in range(world)]
+    assert [sum(p) for p in pieces] == [sum(sizes) // world] * world
+    # walking the shards in order, every tensor is the sum of its pieces
+    flat = [n for p in pieces for n in p]
+    rebuilt, acc, i = [], 0, 0
+    for n in flat:
+        acc += n
+        if acc == sizes[i]:
+            rebuilt.append(acc)
+            acc, i = 0, i + 1
+    assert rebuilt == sizes and acc == 0
+    wl = WL.get("gpt2_xl_shard3of8")
+    assert wl.sizes == pieces[3] and wl.mkind == WL.MOM_BF16X2
+    # 8 elements in 3 ranges [0,2) [2,5) [5,8): a range inside one tensor,
+    # one ending on a tensor edge, one that is a whole tensor
+    assert [WL.shard_sizes([5, 3], r, 3) for r in range(3)] == \
+        [[2], [3], [3]]
