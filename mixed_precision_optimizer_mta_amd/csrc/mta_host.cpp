@@ -27,8 +27,8 @@ struct mta_list {
   uint32_t ntiles = 0;
   uint32_t keep_from = 0;  // first tile the norm reads with allocating loads
   int cus = 1;          // compute units of the device
-  int grid_update = 1;  // workgroups of an AdamW / scale launch
-  int grid_norm = 1;
+  int grid_update = 1;  // workgroups of an update launch
+  int grid_norm = 1;    // workgroups of a norm or in-place scale launch
   int state_buffers = 3;  // bit 0: tensors have m; bit 1: they have v
   int vector_tensors = 0;
   void *dev_block = nullptr;  // one allocation: tile tables, norm scratch
