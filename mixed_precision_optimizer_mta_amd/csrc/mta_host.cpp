@@ -684,7 +684,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   const size_t off_ticket =
       round_up(off_part + static_cast<size_t>(L->grid_norm) * sizeof(double),
                256);
-  const size_t total = off_ticket + 256;
+  const size_t total = off_ticket + mta::kTicketBytes;
 
   e = hipMalloc(&L->dev_block, total);
   if (e != hipSuccess) {
@@ -696,7 +696,7 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->d_stiles = reinterpret_cast<mta::StepTile *>(base + off_st);
   L->d_partials = reinterpret_cast<double *>(base + off_part);
   L->d_ticket = reinterpret_cast<unsigned int *>(base + off_ticket);
-  L->d_acc = reinterpret_cast<double *>(base + off_ticket + 8);
+  L->d_acc = reinterpret_cast<double *>(base + off_ticket + mta::kAccOffset);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   e = hipSuccess;
@@ -721,7 +721,8 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
     e = hipMemcpyAsync(L->d_partials, empty_slots.data(),
                        empty_slots.size() * sizeof(uint64_t),
                        hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipMemsetAsync(L->d_ticket, 0, 256, s);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(L->d_ticket, 0, mta::kTicketBytes, s);
   // the host vectors die with this call: wait for the copies
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {

@@ -81,9 +81,18 @@ struct Work {
 // creation) except between the storing workgroup and the finishing wave of
 // one launch, which re-arms it.
 constexpr uint64_t kNormSlotEmpty = 0xFFF0DEADBEEF0001ull;
+// The ticket region: kTicketGroups group counters and one top counter,
+// kTicketStride words (128 bytes) apart, then the float64 running total of
+// a norm over several lists.
+constexpr uint32_t kTicketGroups = 8;
+constexpr uint32_t kTicketStride = 32;
+constexpr size_t kTicketBytes = 2048;
+constexpr size_t kAccOffset = (kTicketGroups + 1) * kTicketStride * 4;
+static_assert(kAccOffset + 8 <= kTicketBytes, "ticket region layout");
+
 struct NormScratch {
   double *partials;
-  unsigned int *ticket;
+  unsigned int *ticket;  // the ticket region
   // A norm over several lists launches one norm per list: each adds the
   // float64 total the previous one left in *acc_in (null for the first)
   // and leaves its own in *acc_out (null when there is no later list).

@@ -632,9 +632,10 @@ k_momentum(const StepTile *__restrict__ tiles, uint32_t ntiles,
 //   accumulates with a float64 fma; the wave then reduces with DPP lane moves,
 //   the four waves combine through LDS, and the workgroup writes one float64
 //   partial.
-//   Stage 2 (the last workgroup to finish, chosen by an atomic ticket): one
-//   wave sums the partials in a fixed lane-strided order, takes the square
-//   root, forms the clip coefficient and writes both, then re-arms the ticket.
+//   Stage 2 (the last workgroup to finish, chosen by a two-level atomic
+//   ticket): one wave sums the partials in a fixed lane-strided order, takes
+//   the square root, forms the clip coefficient and writes both, then
+//   re-arms the ticket counters.
 // The grid and the tile order are fixed per list, so the result is the same
 // bits on every call.  The float64 sum of the squares of float32 values
 // cannot overflow, so the total is finite exactly when every x is.
@@ -829,9 +830,24 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles,
     __hip_atomic_store(slots + blockIdx.x,
                        static_cast<uint64_t>(__double_as_longlong(part)),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned int prev = __hip_atomic_fetch_add(
-        ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == gridDim.x - 1);
+    // two-level ticket: workgroup b counts in group b % kTicketGroups; the
+    // workgroup that completes its group counts at the top, and the one
+    // that completes the top finishes.  Eight counters on their own lines
+    // take the burst of atomics of workgroups that end together in
+    // parallel instead of one after another.
+    const uint32_t grp = blockIdx.x % kTicketGroups;
+    const uint32_t members =
+        (gridDim.x - grp + kTicketGroups - 1) / kTicketGroups;
+    bool last = false;
+    if (__hip_atomic_fetch_add(ticket + grp * kTicketStride, 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        members - 1) {
+      const uint32_t groups = min(gridDim.x, kTicketGroups);
+      last = __hip_atomic_fetch_add(ticket + kTicketGroups * kTicketStride,
+                                    1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    }
+    is_last = last;
   }
   __syncthreads();
   if (!is_last) return;
@@ -882,7 +898,10 @@ k_sumsq(const GradTile *__restrict__ tiles, uint32_t ntiles,
     if (d_norm) *d_norm = nrm;
     *d_coef = (c > 1.0f) ? 1.0f : c;
     if (amp) amp->found_inf = isfinite(total) ? 0.0f : 1.0f;
-    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every workgroup has counted by now: re-arm every counter
+    for (uint32_t k = 0; k <= kTicketGroups; ++k)
+      __hip_atomic_store(ticket + k * kTicketStride, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
