@@ -141,3 +141,56 @@ def test_loss_scaled_joint_clip_and_found_inf():
                        O.joint_norm(parts), 1.0, f"amp joint t={t}")
     for L in lists:
         L.close()
+
+
+def test_captured_joint_loss_scaled_step_replays_like_eager():
+    # the joint loss-scaled clip of a float32 and a float16 list, both
+    # lists' updates and the scale update, captured once and replayed;
+    # twin lists run the same calls eagerly
+    specs = [([4096 * 2 + 3, 100], WL.F32, 0, 0, 1.0, 66),
+             ([7000], WL.F16, 1, 1, 1.0, 67)]
+    a_cap, a_eag = lists_of(specs), lists_of(specs)
+    L_cap = [make_list(a) for a in a_cap]
+    L_eag = [make_list(a) for a in a_eag]
+    amp_c, amp_e = AmpState(256.0), AmpState(256.0)
+    outs = {k: (torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"))
+            for k in ("cap", "eag")}
+
+    def step(lists, arenas, amp, nd, cd):
+        clip_norm_joint(lists, 1.0, nd, cd, amp=amp)
+        for a, L in zip(arenas, lists):
+            L.amp_adamw_step(a.wl.hparams, amp, cd)
+        amp.update(2.0, 0.5, 2)
+
+    for a in a_cap + a_eag:
+        a.fill_grads(1)
+    step(L_cap, a_cap, amp_c, *outs["cap"])     # eager warm-up on both
+    step(L_eag, a_eag, amp_e, *outs["eag"])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        step(L_cap, a_cap, amp_c, *outs["cap"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for t in range(2, 7):
+        for a in a_cap + a_eag:
+            a.fill_grads(t)
+        if t == 4:                       # an overflow step, skipped by both
+            for a in (a_cap[1], a_eag[1]):
+                a.view("g", 0)[5] = float("inf")
+        torch.cuda.synchronize()
+        graph.replay()
+        step(L_eag, a_eag, amp_e, *outs["eag"])
+        torch.cuda.synchronize()
+        for x, y in zip(outs["cap"], outs["eag"]):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), t
+        assert amp_c.read() == amp_e.read(), t
+        for a, b in zip(a_cap, a_eag):
+            for buf in "wmv":
+                assert torch.equal(getattr(a, buf).view(torch.int16),
+                                   getattr(b, buf).view(torch.int16)), (t, buf)
+    assert amp_c.read()["step"] == 5          # six steps, one skipped
+    for L in L_cap + L_eag:
+        L.close()

@@ -75,6 +75,7 @@ def draw_case(seed):
 
 
 def run_case(c):
+    import mixed_precision_optimizer_mta_amd as M
     from mixed_precision_optimizer_mta_amd import AmpState, MtaList
     kind, gtype, mkind, vkind = c["kind"], c["gtype"], c["mkind"], c["vkind"]
     adam = kind in ("adamw", "adam")
@@ -103,6 +104,10 @@ def run_case(c):
     info = L.info()
     assert (info["tiles"], info["vector_tensors"]) == \
         expected_tiles(ents, gtype, mkind, vkind)
+    plan = M.mta_list_plan(ents, gtype, mkind, vkind)
+    for key in ("count", "elements", "tiles", "vector_tensors",
+                "state_buffers", "norm_kept_tiles"):
+        assert plan[key] == info[key], key
     copies = None
     picked = [p and c["copies"] for p in c["pick"]]
     if c["copies"]:
