@@ -49,6 +49,14 @@ are rebuilt whenever a parameter, gradient or state buffer moved
 ``load_state_dict`` keeps every state tensor in the dtype it was saved in
 (PyTorch's default would cast float32 masters and moments to a 16-bit
 parameter's dtype).
+
+Host cost: the checks, the device tables and the step counts form a plan
+that a step reuses while every parameter and gradient keeps its address and
+dtype, so a step costs two address reads per parameter on the host (0.04 ms
+for 110 tensors, 2.9 ms for 10,000) besides its launches.  Tensors are
+checked when the plan is built.  The per-parameter ``state[p]["step"]`` is
+brought up to date by ``state_dict()`` (and whenever the plan is rebuilt);
+in between, the count lives with the plan.
 """
 import torch
 
@@ -84,6 +92,7 @@ class MtaOptimizer(torch.optim.Optimizer):
         self.master_weights = bool(master_weights)
         self._lists = {}       # (group, grad dtype) -> (pointer key, MtaList)
         self._norm_cache = {}  # grad dtype -> (pointer key, MtaList)
+        self._plan = None      # see step()
         self.last_norm = None
         self.last_coef = None
         self.amp = None
@@ -221,62 +230,94 @@ class MtaOptimizer(torch.optim.Optimizer):
                 loss = closure()
         groups = [[p for p in g["params"] if p.grad is not None]
                   for g in self.param_groups]
-        all_params = [p for ps in groups for p in ps]
-        if not all_params:
+        # The plan (checked tensors, device tables, per-list step counts)
+        # is rebuilt only when a parameter or gradient moved or changed
+        # dtype: two addresses and a dtype per parameter per step, not the
+        # checks and the table keys.
+        sig = tuple((p.data_ptr(), p.grad.data_ptr(), p.grad.dtype)
+                    for ps in groups for p in ps)
+        if self._plan is None or sig != self._plan["sig"]:
+            self._sync_steps()
+            self._plan = self._build_plan(groups, sig)
+        plan = self._plan
+        if not plan["updates"]:
             return loss
+        coef = None
+        if self.max_norm is not None or self.amp is not None:
+            cap = float("inf") if self.max_norm is None else \
+                float(self.max_norm)
+            clip_norm_joint(plan["norm_lists"], cap, self.last_norm,
+                            self.last_coef, amp=self.amp)
+            coef = self.last_coef
+        for u in plan["updates"]:
+            group = self.param_groups[u["group"]]
+            b1, b2 = group["betas"]
+            rule = dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
+                        eps=group["eps"], weight_decay=group["weight_decay"],
+                        momentum=group["momentum"],
+                        zero_grad=self.zero_grad_in_step)
+            if self.amp is not None:
+                u["list"].amp_step(rule, self.amp, coef)
+            else:
+                u["t"] += 1
+                u["list"].step(rule, u["t"], coef)
+        if self.amp is not None:
+            self.amp.update(*self._amp_rule)
+        return loss
+
+    def _build_plan(self, groups, sig):
+        all_params = [p for ps in groups for p in ps]
         for p in all_params:
             self._check(p)
             if p.grad.dtype not in _GTYPE:
                 raise TypeError("gradients are float32, bfloat16 or float16")
             if p.dtype != torch.float32 and p.grad.dtype != p.dtype:
                 raise TypeError("a 16-bit parameter's gradient has its dtype")
-        coef = None
-        if self.max_norm is not None or self.amp is not None:
-            dev = all_params[0].device
-            if self.last_norm is None or self.last_norm.device != dev:
-                self.last_norm = torch.zeros(1, device=dev)
-                self.last_coef = torch.zeros(1, device=dev)
-            cap = float("inf") if self.max_norm is None else \
-                float(self.max_norm)
-            clip_norm_joint(self._norm_lists(all_params), cap,
-                            self.last_norm, self.last_coef, amp=self.amp)
-            coef = self.last_coef
-        for k, (group, ps_all) in enumerate(zip(self.param_groups, groups)):
-            b1, b2 = group["betas"]
-            rule = dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
-                        eps=group["eps"], weight_decay=group["weight_decay"],
-                        momentum=group["momentum"],
-                        zero_grad=self.zero_grad_in_step)
+        plan = dict(sig=sig, norm_lists=[], updates=[])
+        if not all_params:
+            return plan
+        dev = all_params[0].device
+        if self.last_norm is None or self.last_norm.device != dev:
+            self.last_norm = torch.zeros(1, device=dev)
+            self.last_coef = torch.zeros(1, device=dev)
+        plan["norm_lists"] = self._norm_lists(all_params)
+        for k, ps_all in enumerate(groups):
             for dt in _GTYPE:   # one launch per gradient dtype in the group
                 ps = [p for p in ps_all if p.grad.dtype == dt]
-                if ps:
-                    self._update(self._group_list((k, dt), ps), ps, rule,
-                                 coef)
-        if self.amp is not None:
-            self.amp.update(*self._amp_rule)
-        return loss
+                if not ps:
+                    continue
+                L = self._group_list((k, dt), ps)
+                steps = {int(self.state[p]["step"]) for p in ps}
+                if self.amp is None and len(steps) != 1:
+                    raise RuntimeError(
+                        "the parameters of one group have taken different "
+                        "numbers of steps; one launch applies one t to a "
+                        "group")
+                plan["updates"].append(dict(group=k, list=L, params=ps,
+                                            t=max(steps)))
+        return plan
 
-    def _update(self, L, ps, rule, coef):
-        if self.amp is not None:
-            L.amp_step(rule, self.amp, coef)
+    def _sync_steps(self):
+        """Write each list's step count into its parameters' state (the
+        step loop keeps one count per list, not per parameter)."""
+        if self._plan is None or self.amp is not None:
             return
-        steps = {int(self.state[p]["step"]) for p in ps}
-        if len(steps) != 1:
-            raise RuntimeError(
-                "the parameters of one group have taken different numbers "
-                "of steps; one launch applies one t to a group")
-        t = steps.pop() + 1
-        for p in ps:
-            self.state[p]["step"] = t
-        L.step(rule, t, coef)
+        for u in self._plan["updates"]:
+            for p in u["params"]:
+                self.state[p]["step"] = u["t"]
 
     # -- checkpoints ------------------------------------------------------
+    def state_dict(self):
+        self._sync_steps()
+        return super().state_dict()
+
     def load_state_dict(self, state_dict):
         """As torch.optim.Optimizer.load_state_dict, except that every state
         tensor comes back in the dtype it was saved in (masters and float32
         moments of a 16-bit parameter stay float32).  The state buffers are
         new allocations and the device tables are rebuilt on the next step:
         capture a graph of step() again after loading."""
+        self._plan = None          # its step counts belong to the old state
         super().load_state_dict(state_dict)
         ids = [i for g in state_dict["param_groups"] for i in g["params"]]
         params = [p for g in self.param_groups for p in g["params"]]
