@@ -477,3 +477,41 @@ def test_master_weights_with_a_float32_layer_match_the_oracle(kind):
         if kind == "momentum":
             for p in params:
                 assert opt.state[p]["momentum_buffer"].dtype == torch.float32
+
+
+def test_plan_follows_schedules_empty_params_and_missing_grads():
+    # a learning-rate schedule changes lr every step (no rebuild needed), a
+    # zero-element parameter and a group without gradients ride along, and
+    # a gradient that moves forces a rebuild; bitwise against the oracle
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model(29)
+    params = list(model.parameters())
+    empty = torch.nn.Parameter(torch.zeros(0, device="cuda"))
+    idle = torch.nn.Parameter(torch.ones(5, device="cuda"))   # never a grad
+    opt = MtaOptimizer([{"params": params + [empty]}, {"params": [idle]}],
+                       kind="adamw", lr=1e-3, betas=(0.9, 0.99),
+                       weight_decay=0.1, max_norm=0.7)
+    sched = torch.optim.lr_scheduler.LambdaLR(opt, lambda s: 1.0 / (1 + s))
+    ost = [O.Tensor(_host(p).ravel(), None, np.zeros(p.numel(), np.float32),
+                    np.zeros(p.numel(), np.float32)) for p in params]
+    for t in range(1, 6):
+        _grads(model, t)
+        empty.grad = torch.zeros(0, device="cuda")
+        if t == 4:                       # a gradient moves: rebuild
+            params[0].grad = params[0].grad.clone()
+        lr = opt.param_groups[0]["lr"]
+        for p, o in zip(params, ost):
+            o.g = _host(p.grad).ravel()
+        opt.step()
+        sched.step()
+        torch.cuda.synchronize()
+        coef = np.float32(opt.last_coef.item())
+        O.opt_step_(ost, dict(kind="adamw", lr=lr, beta1=0.9, beta2=0.99,
+                              eps=1e-8, weight_decay=0.1, momentum=0.0),
+                    O.F32, 0, 0, t, coef=coef)
+        for p, o in zip(params, ost):
+            assert np.array_equal(_host(p).ravel().view(np.uint32),
+                                  o.w.view(np.uint32)), t
+    assert torch.equal(idle.detach(), torch.ones(5, device="cuda"))
+    sd = opt.state_dict()
+    assert all(sd["state"][i]["step"] == 5 for i in range(len(params)))
