@@ -555,6 +555,18 @@ def main():
         "kernels_ms": {"k_sumsq": norm_ms, kernel: adamw_ms,
                        **({"k_scale": scale_ms} if inplace else {})},
         "norm_gbs": norm_bytes / (norm_ms * 1e-3) / 1e9,
+        # the second kernel of the step, measured the same way
+        "norm_roofline": {
+            "kernel": "k_sumsq", "bound": "hbm",
+            "achieved": norm_bytes / (norm_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": (None if args.layout != "padded" or inplace or
+                        len(norm_lists) > 1
+                        else measured_traffic(traffic_key(
+                            wl, args.opt, args.zero_grad), "k_sumsq")),
+            "bytes_per_launch": norm_bytes,
+        },
         **({"scale_gbs": scale_bytes / (scale_ms * 1e-3) / 1e9}
            if inplace else {}),
         "roofline": {
