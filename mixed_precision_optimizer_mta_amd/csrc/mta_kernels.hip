@@ -8,13 +8,15 @@
 //                 the norm and coefficient stay in device memory, section
 //                 "Values that stay on the card"); with a loss-scale state it
 //                 also reports whether any unscaled gradient is not finite.
+//                 Launches over several lists chain through a float64
+//                 running total (one cap over the joint length of all).
 //   k_adamw       AdamW over every (w, g, m, v) group (AdamWSteps, same
 //                 section), with the element arithmetic of "BendTorch
 //                 main.bend", section "Optimizers": adam_decay, adam_m, adam_v,
 //                 adam_w, and the packed bfloat16 moments of adamh_l /
 //                 adamhv_l (ph_of_bits, ph_to); when a tensor has one, it also
-//                 writes the bfloat16 copy of its new weights (Mica, section
-//                 "float16 and bfloat16, whole").  With a loss-scale state it
+//                 writes the bfloat16 or float16 copy of its new weights
+//                 (Mica, section "float16 and bfloat16, whole").  With a loss-scale state it
 //                 skips a step whose gradients were not finite and takes the
 //                 step number from device memory.  The same kernel runs Adam
 //                 with coupled decay (adam_grad with dec = false).
@@ -37,9 +39,10 @@
 // j*G + V*l + V-1, where V is 4 for k_adamw (a 16-byte access of a float32
 // buffer, 8 bytes of a 16-bit one, so all buffers share one element mapping)
 // and 16 bytes' worth for the single-buffer kernels.  The tail tile of a
-// tensor and the tiles of an unaligned tensor use the same mapping with
-// one-element accesses: loads clamped into the tile and issued before any
-// use, stores masked to the tile.  A lane owns whole elements, so a packed
+// tensor, the head tile peeled off a tensor whose buffers reach alignment
+// only after a few elements, and the tiles of a tensor that never does use
+// the same mapping with one-element accesses: loads clamped into the tile
+// and issued before any use, stores masked to the tile.  A lane owns whole elements, so a packed
 // bfloat16 moment is written with 8-byte or 16-bit stores and no 32-bit word
 // is ever shared between lanes (no read-modify-write of a neighbour's half).
 //
