@@ -90,7 +90,10 @@
 extern "C" {
 #endif
 
-#define MTA_ABI_VERSION 1
+/* 2: mta_list_info_t gained weight_copy_type and norm_kept_tiles (72 bytes;
+ *    a caller built against version 1 passes a 64-byte struct, so check
+ *    mta_abi_version() before calling mta_list_info or mta_list_plan). */
+#define MTA_ABI_VERSION 2
 
 typedef struct mta_list mta_list; /* opaque */
 

@@ -23,6 +23,9 @@ STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
                 -3: "MTA_EDTYPE", -4: "MTA_ENOMEM", -5: "MTA_EHIP",
                 -6: "MTA_ESTATE"}
 
+# MTA_ABI_VERSION of include/mta.h that these structs mirror
+ABI_VERSION = 2
+
 # every symbol include/mta.h declares
 EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_clip_norm", "mta_adamw_step", "mta_list_set_weight_copies",
@@ -130,6 +133,10 @@ def lib():
         for name in EXPORTS:
             if name != "mta_last_error":
                 getattr(L, name).restype = ctypes.c_int
+        if L.mta_abi_version() != ABI_VERSION:
+            raise RuntimeError(
+                f"{LIB_PATH} has ABI {L.mta_abi_version()}, this binding "
+                f"speaks {ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 

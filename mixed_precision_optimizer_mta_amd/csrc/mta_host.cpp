@@ -43,6 +43,11 @@ struct mta_list {
   float deferred_s = 1.0f;
 };
 
+// Layouts the ABI fixes (include/mta.h, MTA_ABI_VERSION 2).
+static_assert(sizeof(mta_tensor) == 40, "mta_tensor layout");
+static_assert(sizeof(mta_list_info_t) == 72, "mta_list_info_t layout");
+static_assert(sizeof(mta_opt) == 56, "mta_opt layout");
+
 namespace {
 
 thread_local char g_err[512] = "";
