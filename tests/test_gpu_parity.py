@@ -413,12 +413,15 @@ def test_independent_mode_report(name):
     assert worst["m"] <= 64 and worst["v"] <= 64, worst
 
 
-def test_norm_cache_policy_changes_no_bits(monkeypatch):
+@pytest.mark.parametrize("name", ["gpt2_124m", "gpt2_124m_bf16g",
+                                  "gpt2_124m_f16amp"])
+def test_norm_cache_policy_changes_no_bits(monkeypatch, name):
     # the norm's kept tiles (allocating loads) are a cache policy only:
     # every tile kept, none kept, or the default cut give the same norm,
-    # coefficient and update, bit for bit
-    wl = small("gpt2_124m")
+    # coefficient and update, bit for bit, for every gradient type
+    wl = small(name)
     wl = WL.scaled_down(wl, wl.sizes)
+    wl.amp = False
     results = []
     for keep in (None, "0", "100000"):
         if keep is None:
