@@ -45,6 +45,11 @@ def measured_traffic(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
+# --no-decay flags tensors below this many elements: in the GPT-2 layouts
+# exactly the biases and layer-norm gains (the largest, 6400, in gpt2_xl),
+# none of the weight matrices or embeddings (the smallest, 589,824)
+NO_DECAY_BELOW = 1 << 14
+
 KERNEL_OF = {"adamw": "k_adamw", "adam": "k_adamw", "sgd": "k_sgd",
              "momentum": "k_momentum"}
 
@@ -80,8 +85,13 @@ def update_bytes(wl, kind, zero, copy):
 def ceiling(wl, reps=10):
     """Best HBM rates of the ceiling probes (libmta_probe.so: no optimizer
     arithmetic) on buffers of the workload's size: a stream with the update's
-    exact bytes (read w, g, m, v; write w, m, v), a read-only stream and a
-    copy, each over grids of 1, 2, 4 and 8 workgroups per CU."""
+    exact bytes (read w, g, m, v; write w, m, v), a read-only stream, a
+    write-only stream and a copy, each over grids of 1, 2, 4 and 8
+    workgroups per CU (the write-only one also over half the CUs, where it
+    streams best).  serial_bound_gbs is the update's bytes with its reads at
+    the read-only rate and its writes at the write-only rate, one after the
+    other: what the update would reach if reads and writes never slowed each
+    other."""
     import ctypes
 
     import torch
@@ -93,6 +103,7 @@ def ceiling(wl, reps=10):
                                 c_int, vp]
     P.mta_probe_read.argtypes = [vp, i64, vp, c_int, vp]
     P.mta_probe_copy.argtypes = [vp, vp, i64, c_int, vp]
+    P.mta_probe_write.argtypes = [vp, i64, c_int, vp]
     n = -(-wl.n // 4096) * 4096
     gb = 4 if wl.gtype == 0 else 2
     mb = 2 if wl.mkind == 1 else 4
@@ -108,10 +119,10 @@ def ceiling(wl, reps=10):
     s = torch.cuda.current_stream()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
-    def best(launch, nbytes):
+    def best(launch, nbytes, per_cu=(1, 2, 4, 8)):
         out = (0.0, 0)
-        for bpc in (1, 2, 4, 8):
-            grid = cus * bpc
+        for bpc in per_cu:
+            grid = max(1, int(cus * bpc))
             for _ in range(2):
                 assert launch(grid) == 0
             a = torch.cuda.Event(enable_timing=True)
@@ -134,12 +145,20 @@ def ceiling(wl, reps=10):
                                           gr, sp), n * 4)
     cp = best(lambda gr: P.mta_probe_copy(w.data_ptr(), w2.data_ptr(), n, gr,
                                           sp), n * 8)
+    wr = best(lambda gr: P.mta_probe_write(w2.data_ptr(), n, gr, sp), n * 4,
+              per_cu=(0.5, 1, 2, 4))
+    rbytes, wbytes = 4 + gb + mb + vb, 4 + mb + vb
+    serial = (rbytes + wbytes) / (rbytes / rd[0] + wbytes / wr[0])
     return {"probe": "libmta_probe.so, trivial arithmetic, best of 1/2/4/8 "
                      "workgroups per CU",
             "update_mix_gbs": mix[0], "update_mix_frac": mix[0] / HBM_PEAK_GBS,
             "update_mix_blocks_per_cu": mix[1],
             "read_gbs": rd[0], "read_frac": rd[0] / HBM_PEAK_GBS,
-            "copy_gbs": cp[0], "copy_frac": cp[0] / HBM_PEAK_GBS}
+            "copy_gbs": cp[0], "copy_frac": cp[0] / HBM_PEAK_GBS,
+            "write_gbs": wr[0], "write_frac": wr[0] / HBM_PEAK_GBS,
+            "write_blocks_per_cu": wr[1],
+            "serial_bound_gbs": serial,
+            "serial_bound_frac": serial / HBM_PEAK_GBS}
 
 
 def cpu_model():
@@ -304,6 +323,11 @@ def main():
                          "cut into K runs of consecutive tensors, norms "
                          "chained by mta_clip_norm_joint) instead of one; "
                          "the update stays one list")
+    ap.add_argument("--no-decay", action="store_true",
+                    help="flag the tensors of under 2^14 elements (in the "
+                         "GPT-2 layouts: the biases and layer-norm gains) "
+                         "to take no weight decay, in the same update "
+                         "launch (mta_list_set_no_decay)")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -384,6 +408,10 @@ def main():
         copies = torch.empty(arena.total, dtype=cdt, device="cuda")
         L.set_weight_copies([copies[o:o + n] for o, n in
                              zip(arena.offsets, wl.sizes)])
+    no_decay = [n < NO_DECAY_BELOW for n in wl.sizes] if args.no_decay \
+        else None
+    if no_decay:
+        L.set_no_decay(no_decay)
     info = L.info()
     norm_lists = [L]
     if args.joint_norm > 1:
@@ -514,7 +542,7 @@ def main():
     value = wl.n * args.steps / (host_s)
     achieved = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     traffic = (None if args.weight_copy or args.layout != "padded" or inplace
-               else measured_traffic(traffic_key(wl, args.opt, args.zero_grad),
+               or args.no_decay else measured_traffic(traffic_key(wl, args.opt, args.zero_grad),
                                      kernel))
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) per "
@@ -546,6 +574,7 @@ def main():
             "optimizer": args.opt, "zero_grad": bool(args.zero_grad),
             "graph": bool(args.graph),
             "joint_norm_lists": len(norm_lists),
+            "no_decay_tensors": sum(no_decay) if no_decay else 0,
         },
         "step_gbs": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9,
         "step_hbm_frac": step_bytes / (dev_ms * 1e-3 / args.steps) / 1e9
@@ -583,6 +612,7 @@ def main():
             not args.zero_grad and not args.weight_copy:
         c = ceiling(wl)
         c["update_of_mix"] = achieved / c["update_mix_gbs"]
+        c["update_of_serial_bound"] = achieved / c["serial_bound_gbs"]
         out["ceiling"] = c
     if args.cpu_steps > 0:
         out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)

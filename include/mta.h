@@ -30,6 +30,8 @@
  *   mta_list_set_weight_copies  bfloat16 (or, by mta_list_set_weight_copies_as,
  *                   float16) copies of the new weights (Mica, section
  *                   "float16 and bfloat16, whole").
+ *   mta_list_set_no_decay  tensors that take no weight decay, in the same
+ *                   launch as those that do.
  *
  * Memory and ownership.  Every w, g, m, v pointer is device memory owned by
  * the caller (for example a PyTorch tensor's data pointer).  The library never
@@ -92,8 +94,9 @@ extern "C" {
 
 /* 2: mta_list_info_t gained weight_copy_type and norm_kept_tiles (72 bytes;
  *    a caller built against version 1 passes a 64-byte struct, so check
- *    mta_abi_version() before calling mta_list_info or mta_list_plan). */
-#define MTA_ABI_VERSION 2
+ *    mta_abi_version() before calling mta_list_info or mta_list_plan).
+ * 3: mta_list_set_no_decay. */
+#define MTA_ABI_VERSION 3
 
 typedef struct mta_list mta_list; /* opaque */
 
@@ -298,6 +301,24 @@ int mta_list_set_weight_copies(mta_list *list, void *const *w16,
  * MTA_EDTYPE for any other copy_type (nothing changes then). */
 int mta_list_set_weight_copies_as(mta_list *list, void *const *w16,
                                   int32_t copy_type, void *stream);
+
+/* Flag tensors that take no weight decay (biases and normalization gains,
+ * as a model usually keeps them), so that one list, and one launch per step,
+ * covers a decay group and a no-decay group whose other hyperparameters are
+ * equal.  Each flagged tensor is updated exactly as the same call with
+ * weight_decay = 0 would update it alone ("Mica 7.7", section "The whole model
+ * in one call": each group updated as a lone AdamWStep would update it):
+ * MTA_OPT_ADAMW takes dec = 1 (w' = w*1), MTA_OPT_ADAM takes
+ * ge' = ge + f32(w*0); SGD and momentum have no decay, so the flag changes
+ * nothing there.  Applies to mta_adamw_step, mta_step, mta_amp_adamw_step and
+ * mta_amp_step.  no_decay is a host array of `count` bytes in list order
+ * (nonzero = no decay); NULL clears every flag.  Rewrites the device tile
+ * table on `stream` and waits for that upload, like
+ * mta_list_set_weight_copies (the two settings are independent and both
+ * kept); must not overlap a running step of this list.  On failure the
+ * previous flags stay. */
+int mta_list_set_no_decay(mta_list *list, const uint8_t *no_decay,
+                          void *stream);
 
 /* Loss-scaled ClipGradNorms: as mta_clip_norm with the unscale factor
  * s = float32(1 / float64(d_amp->scale)) read on the device, and one more

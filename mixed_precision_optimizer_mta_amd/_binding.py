@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
                 -6: "MTA_ESTATE"}
 
 # MTA_ABI_VERSION of include/mta.h that these structs mirror
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every symbol include/mta.h declares
 EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
@@ -33,7 +33,8 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_abi_version", "mta_amp_clip_norm", "mta_amp_adamw_step",
            "mta_amp_update", "mta_step", "mta_amp_step",
            "mta_list_set_weight_copies_as", "mta_list_plan",
-           "mta_clip_norm_joint", "mta_amp_clip_norm_joint")
+           "mta_clip_norm_joint", "mta_amp_clip_norm_joint",
+           "mta_list_set_no_decay")
 
 
 class mta_tensor(ctypes.Structure):
@@ -113,6 +114,8 @@ def lib():
         L.mta_list_set_weight_copies.argtypes = [vp, ctypes.POINTER(vp), vp]
         L.mta_list_set_weight_copies_as.argtypes = [vp, ctypes.POINTER(vp),
                                                     ctypes.c_int32, vp]
+        L.mta_list_set_no_decay.argtypes = [vp, ctypes.POINTER(
+            ctypes.c_uint8), vp]
         L.mta_adamw_scalars.argtypes = [ctypes.POINTER(mta_adamw_hparams),
                                         i64, ctypes.POINTER(ctypes.c_float)]
         L.mta_list_info.argtypes = [vp, ctypes.POINTER(mta_list_info_t)]
@@ -229,6 +232,21 @@ def mta_list_set_weight_copies_as(handle, w16, copy_type, stream=0):
     _check(lib().mta_list_set_weight_copies_as(handle, _copy_array(w16),
                                                copy_type, stream),
            "mta_list_set_weight_copies_as")
+
+
+def mta_list_set_no_decay(handle, no_decay, stream=0):
+    """no_decay: one truth value per tensor of the list (True: the tensor
+    takes weight_decay = 0), or None to clear every flag."""
+    arr = None
+    if no_decay is not None:
+        count = mta_list_info(handle)["count"]
+        if len(no_decay) != count:
+            raise ValueError(f"no_decay has {len(no_decay)} entries, the "
+                             f"list {count} tensors")
+        arr = (ctypes.c_uint8 * max(1, count))(
+            *[1 if f else 0 for f in no_decay])
+    _check(lib().mta_list_set_no_decay(handle, arr, stream),
+           "mta_list_set_no_decay")
 
 
 def mta_adamw_scalars(hp, t):

@@ -20,6 +20,8 @@
 struct mta_list {
   std::vector<mta_tensor> tensors;  // the caller's table, kept for rebuilds
   std::vector<void *> w16;          // attached 16-bit weight copies (or null)
+  std::vector<uint8_t> no_decay;    // 1: the tensor takes weight_decay = 0
+                                    // (empty: none is flagged)
   int device = 0;
   int gtype = 0, mkind = 0, vkind = 0;
   int64_t count = 0;
@@ -38,6 +40,7 @@ struct mta_list {
   unsigned int *d_ticket = nullptr;
   double *d_acc = nullptr;  // running total of a norm over several lists
   int weight_copies = 0;  // tensors with an attached 16-bit copy
+  int no_decay_tensors = 0;  // tensors flagged by mta_list_set_no_decay
   int copy_type = MTA_BF16;  // format of the copies: MTA_BF16 or MTA_F16
   bool deferred = false;  // a MTA_SCALE_DEFER factor is pending
   float deferred_s = 1.0f;
@@ -267,13 +270,15 @@ uint64_t tiles_of(int64_t n, int64_t h) {
 }
 
 // One StepTile per tile of every non-empty tensor, in list order.  w16 may be
-// empty (no copies) or hold one pointer per tensor.  The tile cuts depend on
-// w, g, m, v only, so attaching copies never changes the tile count; a copy
-// that is not 16-byte aligned at the vector tiles' starts sends the tensor
-// down the element path.
+// empty (no copies) or hold one pointer per tensor; no_decay likewise (empty:
+// every tensor decays).  The tile cuts depend on w, g, m, v only, so
+// attaching copies or flags never changes the tile count; a copy that is not
+// 16-byte aligned at the vector tiles' starts sends the tensor down the
+// element path.
 void build_step_tiles(const std::vector<mta_tensor> &tensors,
-                      const std::vector<void *> &w16, int gtype, int mkind,
-                      int vkind, std::vector<mta::StepTile> *out) {
+                      const std::vector<void *> &w16,
+                      const std::vector<uint8_t> &no_decay, int gtype,
+                      int mkind, int vkind, std::vector<mta::StepTile> *out) {
   const uintptr_t gsz = elem_size(gtype != MTA_F32);
   const uintptr_t msz = elem_size(mkind == MTA_MOM_BF16X2);
   const uintptr_t vsz = elem_size(vkind == MTA_MOM_BF16X2);
@@ -282,6 +287,8 @@ void build_step_tiles(const std::vector<mta_tensor> &tensors,
     const mta_tensor &x = tensors[i];
     if (x.n == 0) continue;
     void *copy = w16.empty() ? nullptr : w16[i];
+    const uint32_t nd =
+        (!no_decay.empty() && no_decay[i]) ? mta::kTileNoDecay : 0u;
     const int64_t peel = vector_peel(x, gtype, mkind, vkind);
     const int64_t head = peel > 0 ? std::min(peel, x.n) : 0;
     const bool vec =
@@ -299,7 +306,7 @@ void build_step_tiles(const std::vector<mta_tensor> &tensors,
       st.m = at(x.m, msz);
       st.v = at(x.v, vsz);
       st.lim = static_cast<uint32_t>(lim);
-      st.vec = v ? 1u : 0u;
+      st.flags = (v ? mta::kTileVec : 0u) | nd;
       st.w16 = at(copy, 2);
       out->push_back(st);
     };
@@ -309,6 +316,35 @@ void build_step_tiles(const std::vector<mta_tensor> &tensors,
       push(base, left < mta::kTileElems ? left : mta::kTileElems, vec);
     }
   }
+}
+
+// Rebuild the list's step tile table with these weight copies and no-decay
+// flags and upload it on `stream`, waiting for the copy (the host table dies
+// with this call).  Nothing of the handle changes; the caller commits the
+// new copies and flags once this succeeds.
+int upload_step_tiles(mta_list *L, const std::vector<void *> &w16,
+                      const std::vector<uint8_t> &no_decay, void *stream) {
+  int rc = check_device(L);
+  if (rc) return rc;
+  std::vector<mta::StepTile> stiles;
+  try {
+    build_step_tiles(L->tensors, w16, no_decay, L->gtype, L->mkind, L->vkind,
+                     &stiles);
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  if (stiles.size() != L->ntiles)  // the cuts depend on w, g, m, v only
+    return fail(MTA_EINVAL, "internal: the tile count changed");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (!stiles.empty())
+    e = hipMemcpyAsync(L->d_stiles, stiles.data(),
+                       stiles.size() * sizeof(mta::StepTile),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "uploading the tile table: %s", hipGetErrorString(e));
+  return MTA_OK;
 }
 
 mta::Work work_of(const mta_list *L, int grid, void *stream) {
@@ -589,7 +625,7 @@ int plan_list(const mta_tensor *tensors, int64_t count, int gtype, int mkind,
     // one record per tile: buffer addresses offset to the tile's first
     // element, its length, and whether the vector path may be taken
     kept.assign(tensors, tensors + count);
-    build_step_tiles(kept, {}, gtype, mkind, vkind, &stiles);
+    build_step_tiles(kept, {}, {}, gtype, mkind, vkind, &stiles);
     gtiles.reserve(stiles.size());
     for (const mta::StepTile &st : stiles)
       gtiles.push_back(mta::GradTile{st.g, st.lim, aligned(st.g, 16) ? 1u : 0u});
@@ -786,29 +822,35 @@ int mta_list_set_weight_copies_as(mta_list *L, void *const *w16,
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");
   }
-  int rc = check_device(L);
+  const int rc = upload_step_tiles(L, copies, L->no_decay, stream);
   if (rc) return rc;
-  std::vector<mta::StepTile> stiles;
-  try {
-    build_step_tiles(L->tensors, copies, L->gtype, L->mkind, L->vkind,
-                     &stiles);
-  } catch (const std::bad_alloc &) {
-    return fail(MTA_ENOMEM, "host allocation failed");
-  }
-  if (stiles.size() != L->ntiles)  // the cuts depend on w, g, m, v only
-    return fail(MTA_EINVAL, "internal: the tile count changed");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (!stiles.empty())
-    e = hipMemcpyAsync(L->d_stiles, stiles.data(),
-                       stiles.size() * sizeof(mta::StepTile),
-                       hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess)
-    return fail(MTA_EHIP, "uploading the tile table: %s", hipGetErrorString(e));
   L->w16 = std::move(copies);
   L->weight_copies = attached;
   L->copy_type = copy_type;
+  return ok();
+}
+
+int mta_list_set_no_decay(mta_list *L, const uint8_t *no_decay,
+                          void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  std::vector<uint8_t> flags;
+  int flagged = 0;
+  try {
+    if (no_decay) {
+      flags.assign(L->tensors.size(), 0);
+      for (size_t i = 0; i < flags.size(); ++i) {
+        flags[i] = no_decay[i] ? 1 : 0;
+        flagged += flags[i];
+      }
+      if (flagged == 0) flags.clear();
+    }
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  const int rc = upload_step_tiles(L, L->w16, flags, stream);
+  if (rc) return rc;
+  L->no_decay = std::move(flags);
+  L->no_decay_tensors = flagged;
   return ok();
 }
 

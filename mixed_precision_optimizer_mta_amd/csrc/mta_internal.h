@@ -42,11 +42,17 @@ struct StepTile {
   const void *g;
   void *m;
   void *v;
-  uint32_t lim;  // elements in this tile, 1..kTileElems
-  uint32_t vec;  // 1: all buffers (w16 too, when present) 16-byte aligned
-  void *w16;     // 16-bit copy of w at this tile, or nullptr
+  uint32_t lim;    // elements in this tile, 1..kTileElems
+  uint32_t flags;  // kTileVec | kTileNoDecay
+  void *w16;       // 16-bit copy of w at this tile, or nullptr
 };
 static_assert(sizeof(StepTile) == 48, "step tile layout");
+
+// StepTile flags.
+constexpr uint32_t kTileVec = 1;      // all buffers (w16 too, when present)
+                                      // 16-byte aligned: the vector path
+constexpr uint32_t kTileNoDecay = 2;  // the tensor's step takes
+                                      // weight_decay = 0
 
 // Update rules, numbered as mta_opt_kind.
 constexpr int kRuleAdamW = MTA_OPT_ADAMW;

@@ -403,6 +403,7 @@ struct TileRef {
   MTA_GLOBAL uint16_t *pw16;  // 16-bit weight copy, or null
   uint32_t lim;
   bool full;
+  bool nodecay;  // the tensor's step takes weight_decay = 0
 };
 
 template <int G, bool MPacked, bool VPacked>
@@ -416,7 +417,8 @@ __device__ __forceinline__ TileRef<G, MPacked, VPacked> tile_ref(
   r.pv = gp<elem_t<Ref::V>>(st.v, 0);
   r.pw16 = gp<uint16_t>(st.w16, 0);
   r.lim = st.lim;
-  r.full = st.vec && st.lim == kTileElems;
+  r.full = (st.flags & kTileVec) && st.lim == kTileElems;
+  r.nodecay = (st.flags & kTileNoDecay) != 0;
   return r;
 }
 
@@ -527,7 +529,7 @@ __device__ void zero_grad_tiles(const StepTile *__restrict__ tiles,
   for (uint32_t t = stream_of_block(); t < ntiles; t += gridDim.x) {
     const StepTile st = tiles[t];
     MTA_GLOBAL elem_t<G> *pg = gp<elem_t<G>>(st.g, 0);
-    if (st.vec && st.lim == kTileElems) {
+    if ((st.flags & kTileVec) && st.lim == kTileElems) {
 #pragma unroll
       for (int j = 0; j < kAdamGroups; ++j) zero4<G>(pg, e0 + j * kAdamStride);
     } else {
@@ -592,10 +594,17 @@ __device__ __forceinline__ void update_tiles(
     // for `rec` placed before the vector loads would also wait for this one
     __builtin_amdgcn_sched_barrier(0);
     rec = tiles[min(tn + gridDim.x, last)];
+    // a tensor flagged no-decay takes the step's constants for
+    // weight_decay = 0: dec = f32(1 - lr*0) = 1 (AdamW), l2 = 0 (Adam)
+    StepScalars st = sc;
+    if (cur.nodecay) {
+      st.dec = 1.0f;
+      st.l2 = 0.0f;
+    }
     if (cur.full)
-      finish_tile(X, cur, e0, sc, coef);
+      finish_tile(X, cur, e0, st, coef);
     else
-      partial_tile<R>(cur, e0, sc, coef);
+      partial_tile<R>(cur, e0, st, coef);
     cur = nxt;
     t = tn;
     return more;

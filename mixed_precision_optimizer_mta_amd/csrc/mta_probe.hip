@@ -6,7 +6,8 @@
 // streams whole 4096-element tiles with the same contiguous lane mapping as
 // the update kernels (4 elements per lane per access: 16 bytes of a float32
 // buffer, 8 of a 16-bit one), nontemporal loads and stores, and a
-// grid-stride loop over tiles with two tiles of loads in flight.  n must be
+// grid-stride loop over tiles with two tiles of loads in flight (the
+// write-only probe has no loads).  n must be
 // a multiple of 4096 (the caller sizes the buffers); every index is below n.
 #include <hip/hip_runtime.h>
 
@@ -100,6 +101,17 @@ k_probe_read(const void *a, uint64_t ntiles, float *sink) {
   if (acc.x + acc.y + acc.z + acc.w == -1234.5f) sink[threadIdx.x] = acc.x;
 }
 
+// write only: 16 bytes per lane of a fixed value, one tile per trip
+__global__ void __launch_bounds__(kThreads)
+k_probe_write(void *b, uint64_t ntiles) {
+  const uint64_t l4 = threadIdx.x * 4;
+  const pf4 x = {1.0f, 1.0f, 1.0f, 1.0f};
+  for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x)
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j)
+      st<4>(b, t * kTile + j * (kThreads * 4) + l4, x);
+}
+
 // copy: 16 bytes per lane read and written
 __global__ void __launch_bounds__(kThreads)
 k_probe_copy(const void *a, void *b, uint64_t ntiles) {
@@ -161,6 +173,14 @@ int mta_probe_read(const void *a, int64_t n, float *sink, int grid,
   hipLaunchKernelGGL(k_probe_read, dim3(grid), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a,
                      static_cast<uint64_t>(n) / kTile, sink);
+  return hipGetLastError();
+}
+
+int mta_probe_write(void *b, int64_t n, int grid, void *stream) {
+  if (n <= 0 || n % kTile || grid < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_probe_write, dim3(grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), b,
+                     static_cast<uint64_t>(n) / kTile);
   return hipGetLastError();
 }
 

@@ -10,8 +10,15 @@ parameter group and gradient dtype.  A step is:
     every group (mta_clip_norm_joint over one norm list per gradient dtype,
     lists with no state buffers), the norm and coefficient left in device
     tensors (``last_norm``, ``last_coef``);
-  * one mta_step per parameter group and gradient dtype with that
-    coefficient.
+  * one mta_step per parameter set and gradient dtype with that
+    coefficient.  A set is one parameter group, or several groups with
+    equal lr, betas, eps and momentum and at most one nonzero weight decay
+    among them (the usual decay / no-decay split): they share one list and
+    one launch, the tensors of their zero-decay groups flagged to take no
+    decay (mta_list_set_no_decay), each updated exactly as its own group's
+    step would update it.  The sets are recomputed from the groups'
+    hyperparameters every step; a change of the sets (not of the values,
+    such as a new lr common to all) rebuilds the plan.
 
 With ``loss_scale`` (an initial scale) the step is loss-scaled on the
 device: ``opt.loss_scale`` is a one-element float32 device view of the
@@ -90,7 +97,7 @@ class MtaOptimizer(torch.optim.Optimizer):
         self.packed = bool(packed_moments)
         self.zero_grad_in_step = bool(zero_grad)
         self.master_weights = bool(master_weights)
-        self._lists = {}       # (group, grad dtype) -> (pointer key, MtaList)
+        self._lists = {}       # (groups, grad dtype) -> (key, MtaList)
         self._norm_cache = {}  # grad dtype -> (pointer key, MtaList)
         self._plan = None      # see step()
         self.last_norm = None
@@ -159,10 +166,11 @@ class MtaOptimizer(torch.optim.Optimizer):
             raise ValueError("every parameter needs a contiguous CUDA "
                              "gradient before step()")
 
-    def _group_list(self, k, params):
-        """The update list of parameter group k's params (all with one
-        gradient dtype; k is (group index, dtype))."""
-        groups, key = [], []
+    def _group_list(self, k, params, no_decay=None):
+        """The update list of these params (all with one gradient dtype;
+        k is (group indices, dtype)); no_decay: one flag per param, or
+        None."""
+        groups, key = [], [tuple(no_decay) if no_decay else None]
         for p in params:
             m, v = self._state_buffers(p)
             w = self.master(p)
@@ -188,8 +196,32 @@ class MtaOptimizer(torch.optim.Optimizer):
                 # one among them is its own weight and takes none)
                 L.set_weight_copies([None if p.dtype == torch.float32
                                      else p.detach() for p in params])
+            if no_decay and any(no_decay):
+                L.set_no_decay(no_decay)
             self._lists[k] = (key, L)
         return self._lists[k][1]
+
+    def _merge_sig(self):
+        """The parameter sets the current hyperparameters allow: for each
+        group, (index of the first group of its set, its weight decay is
+        0).  Groups with equal lr, betas, eps and momentum form one set when
+        at most one nonzero weight decay appears among them; otherwise each
+        of them is a set of its own."""
+        keys, nonzero = [], {}
+        for g in self.param_groups:
+            key = (float(g["lr"]), tuple(float(b) for b in g["betas"]),
+                   float(g["eps"]), float(g["momentum"]))
+            keys.append(key)
+            if float(g["weight_decay"]) != 0.0:
+                nonzero.setdefault(key, set()).add(float(g["weight_decay"]))
+        first, out = {}, []
+        for i, (g, key) in enumerate(zip(self.param_groups, keys)):
+            if len(nonzero.get(key, ())) > 1:
+                head = i
+            else:
+                head = first.setdefault(key, i)
+            out.append((head, float(g["weight_decay"]) == 0.0))
+        return tuple(out)
 
     def _norm_lists(self, all_params):
         """One norm list per gradient dtype (float32, bfloat16, float16
@@ -236,9 +268,11 @@ class MtaOptimizer(torch.optim.Optimizer):
         # checks and the table keys.
         sig = tuple((p.data_ptr(), p.grad.data_ptr(), p.grad.dtype)
                     for ps in groups for p in ps)
-        if self._plan is None or sig != self._plan["sig"]:
+        msig = self._merge_sig()
+        if self._plan is None or sig != self._plan["sig"] or \
+                msig != self._plan["merge_sig"]:
             self._sync_steps()
-            self._plan = self._build_plan(groups, sig)
+            self._plan = self._build_plan(groups, sig, msig)
         plan = self._plan
         if not plan["updates"]:
             return loss
@@ -250,10 +284,15 @@ class MtaOptimizer(torch.optim.Optimizer):
                             self.last_coef, amp=self.amp)
             coef = self.last_coef
         for u in plan["updates"]:
+            # the set's groups share every value but the weight decay; the
+            # flagged (zero-decay) tensors ignore the one given here
             group = self.param_groups[u["group"]]
             b1, b2 = group["betas"]
+            wd = next((w for w in (float(self.param_groups[i]
+                                         ["weight_decay"])
+                                   for i in u["groups"]) if w != 0.0), 0.0)
             rule = dict(kind=self.kind, lr=group["lr"], beta1=b1, beta2=b2,
-                        eps=group["eps"], weight_decay=group["weight_decay"],
+                        eps=group["eps"], weight_decay=wd,
                         momentum=group["momentum"],
                         zero_grad=self.zero_grad_in_step)
             if self.amp is not None:
@@ -265,7 +304,7 @@ class MtaOptimizer(torch.optim.Optimizer):
             self.amp.update(*self._amp_rule)
         return loss
 
-    def _build_plan(self, groups, sig):
+    def _build_plan(self, groups, sig, msig):
         all_params = [p for ps in groups for p in ps]
         for p in all_params:
             self._check(p)
@@ -273,7 +312,7 @@ class MtaOptimizer(torch.optim.Optimizer):
                 raise TypeError("gradients are float32, bfloat16 or float16")
             if p.dtype != torch.float32 and p.grad.dtype != p.dtype:
                 raise TypeError("a 16-bit parameter's gradient has its dtype")
-        plan = dict(sig=sig, norm_lists=[], updates=[])
+        plan = dict(sig=sig, merge_sig=msig, norm_lists=[], updates=[])
         if not all_params:
             return plan
         dev = all_params[0].device
@@ -281,20 +320,44 @@ class MtaOptimizer(torch.optim.Optimizer):
             self.last_norm = torch.zeros(1, device=dev)
             self.last_coef = torch.zeros(1, device=dev)
         plan["norm_lists"] = self._norm_lists(all_params)
-        for k, ps_all in enumerate(groups):
-            for dt in _GTYPE:   # one launch per gradient dtype in the group
-                ps = [p for p in ps_all if p.grad.dtype == dt]
+        for p in all_params:
+            self._state_buffers(p)
+        steps = []
+        for k, ps in enumerate(groups):
+            st = {int(self.state[p]["step"]) for p in ps}
+            if self.amp is None and len(st) > 1:
+                raise RuntimeError(
+                    "the parameters of one group have taken different "
+                    "numbers of steps; one launch applies one t to a group")
+            steps.append(max(st) if st else 0)
+        # the sets: groups of one merge head, and (the step count is one t
+        # per launch) of one step count unless the device counts steps
+        sets = {}
+        for k, (head, _) in enumerate(msig):
+            if groups[k]:
+                t = 0 if self.amp is not None else steps[k]
+                sets.setdefault((head, t), []).append(k)
+        used = set()
+        for (head, _), ks in sorted(sets.items(), key=lambda x: x[1][0]):
+            flagged = any(not msig[k][1] for k in ks) and \
+                any(msig[k][1] for k in ks)
+            for dt in _GTYPE:   # one launch per gradient dtype in the set
+                ps, nd = [], []
+                for k in ks:
+                    for p in groups[k]:
+                        if p.grad.dtype == dt:
+                            ps.append(p)
+                            nd.append(flagged and msig[k][1])
                 if not ps:
                     continue
-                L = self._group_list((k, dt), ps)
-                steps = {int(self.state[p]["step"]) for p in ps}
-                if self.amp is None and len(steps) != 1:
-                    raise RuntimeError(
-                        "the parameters of one group have taken different "
-                        "numbers of steps; one launch applies one t to a "
-                        "group")
-                plan["updates"].append(dict(group=k, list=L, params=ps,
-                                            t=max(steps)))
+                lk = (tuple(ks), dt)
+                used.add(lk)
+                L = self._group_list(lk, ps, nd if flagged else None)
+                plan["updates"].append(dict(
+                    group=ks[0], groups=tuple(ks), list=L, params=ps,
+                    t=max(steps[k] for k in ks)))
+        for lk in [x for x in self._lists if x not in used]:
+            self._lists.pop(lk)[1].close()
         return plan
 
     def _sync_steps(self):

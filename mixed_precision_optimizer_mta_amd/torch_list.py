@@ -120,6 +120,15 @@ class MtaList:
         # the list holds raw addresses: keep the tensors alive with it
         self._copies = None if copies is None else list(copies)
 
+    def set_no_decay(self, flags):
+        """flags: one truth value per group (True: that tensor's step
+        takes weight_decay = 0, in the same launch as the others), or None
+        to clear them."""
+        if flags is not None and len(flags) != len(self.sizes):
+            raise ValueError("one flag per tensor of the list")
+        B.mta_list_set_no_decay(self.handle, flags, current_stream())
+        self.no_decay = None if flags is None else [bool(f) for f in flags]
+
     def adamw_step(self, hparams, t, coef=None):
         if coef is not None and (coef.dtype != torch.float32 or
                                  not coef.is_cuda):

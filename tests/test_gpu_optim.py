@@ -515,3 +515,53 @@ def test_plan_follows_schedules_empty_params_and_missing_grads():
     assert torch.equal(idle.detach(), torch.ones(5, device="cuda"))
     sd = opt.state_dict()
     assert all(sd["state"][i]["step"] == 5 for i in range(len(params)))
+
+
+def test_decay_and_no_decay_groups_share_one_launch():
+    # the usual split (matrices decay, biases do not) is one list with the
+    # biases flagged; a second nonzero decay or a different lr separates
+    # the groups again, and equal values join them; every step bitwise
+    # against the oracle run group by group with each group's own decay
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model(37)
+    params = list(model.parameters())
+    mats = [p for p in params if p.dim() == 2]
+    vecs = [p for p in params if p.dim() == 1]
+    groups = [{"params": mats, "weight_decay": 0.1},
+              {"params": vecs, "weight_decay": 0.0}]
+    opt = MtaOptimizer(groups, kind="adamw", lr=1e-3, betas=(0.9, 0.99),
+                       max_norm=0.7)
+    ost = [[O.Tensor(_host(p).ravel(), None, np.zeros(p.numel(), np.float32),
+                     np.zeros(p.numel(), np.float32)) for p in g["params"]]
+           for g in groups]
+    launches = []
+    for t in range(1, 8):
+        if t == 3:                                  # two nonzero decays
+            opt.param_groups[1]["weight_decay"] = 0.05
+        if t == 4:                                  # equal again: one set
+            opt.param_groups[1]["weight_decay"] = 0.1
+        if t == 5:                                  # back to the split
+            opt.param_groups[1]["weight_decay"] = 0.0
+        if t == 6:                                  # different lr
+            opt.param_groups[1]["lr"] = 5e-4
+        if t == 7:
+            opt.param_groups[1]["lr"] = 1e-3
+        _grads(model, t)
+        for g, og in zip(groups, ost):
+            for p, o in zip(g["params"], og):
+                o.g = _host(p.grad).ravel()
+        opt.step()
+        launches.append(len(opt._plan["updates"]))
+        torch.cuda.synchronize()
+        coef = np.float32(opt.last_coef.item())
+        for g, og in zip(opt.param_groups, ost):
+            O.opt_step_(og, dict(kind="adamw", lr=g["lr"], beta1=0.9,
+                                 beta2=0.99, eps=1e-8,
+                                 weight_decay=g["weight_decay"],
+                                 momentum=0.0), O.F32, 0, 0, t, coef=coef)
+            for p, o in zip(g["params"], og):
+                assert np.array_equal(_host(p).ravel().view(np.uint32),
+                                      o.w.view(np.uint32)), t
+    assert launches == [1, 1, 2, 1, 1, 2, 1]
+    sd = opt.state_dict()
+    assert all(s["step"] == 7 for s in sd["state"].values())

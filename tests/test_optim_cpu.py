@@ -40,3 +40,35 @@ def test_master_weights_refuse_cpu_and_plain_mode_refuses_16_bit():
     h[0].grad = torch.zeros(10, dtype=torch.bfloat16)
     with pytest.raises(TypeError):       # 16-bit without master weights
         MtaOptimizer(h).step()
+
+
+def test_parameter_sets_follow_the_hyperparameters():
+    # groups with equal lr, betas, eps and momentum share a launch when at
+    # most one nonzero weight decay appears among them; the zero-decay
+    # groups' tensors are the flagged ones
+    def groups(*specs):
+        return [dict(params=_params(), **s) for s in specs]
+
+    def sets(opt):
+        return opt._merge_sig()
+
+    opt = MtaOptimizer(groups({"weight_decay": 0.1}, {"weight_decay": 0.0}),
+                       kind="adamw", lr=1e-3)
+    assert sets(opt) == ((0, False), (0, True))
+    # another nonzero decay: each group alone
+    opt.param_groups[1]["weight_decay"] = 0.05
+    assert sets(opt) == ((0, False), (1, False))
+    # equal decays share again; so do groups whose decays are all 0
+    opt.param_groups[1]["weight_decay"] = 0.1
+    assert sets(opt) == ((0, False), (0, False))
+    # a different lr (or betas, eps, momentum) separates
+    opt.param_groups[1]["lr"] = 2e-3
+    assert sets(opt) == ((0, False), (1, False))
+    opt = MtaOptimizer(groups({"weight_decay": 0.0}, {"weight_decay": 0.1},
+                              {"weight_decay": 0.0, "betas": (0.8, 0.9)},
+                              {"weight_decay": 0.0}),
+                       kind="adamw", lr=1e-3)
+    assert sets(opt) == ((0, True), (0, False), (2, True), (0, True))
+    # two nonzero decays in one bucket: none of that bucket's groups merge
+    opt.param_groups[3]["weight_decay"] = 0.2
+    assert sets(opt) == ((0, True), (1, False), (2, True), (3, False))
