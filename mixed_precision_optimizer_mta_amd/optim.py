@@ -26,7 +26,9 @@ current scale (multiply the loss by it before backward), the joint norm
 unscales by 1/scale and sets the found-inf flag, every group's update is
 skipped on overflow, and the scale then grows or backs off (PyTorch's
 GradScaler rule) -- no host synchronization anywhere.  The step counter
-lives in ``opt.amp`` (an AmpState), not in ``self.state``.
+lives in ``opt.amp`` (an AmpState), not in ``self.state``; ``state_dict()``
+saves that state under "mta_amp" (and each parameter's up-to-date "step"),
+and ``load_state_dict()`` restores it.
 
 ``capturable=True`` keeps the step counter on the device without loss
 scaling (a state whose scale is 1 and never grows: the unscale multiplies by
@@ -371,17 +373,49 @@ class MtaOptimizer(torch.optim.Optimizer):
 
     # -- checkpoints ------------------------------------------------------
     def state_dict(self):
+        """As torch.optim.Optimizer.state_dict, with every parameter's
+        "step" brought up to date.  With a loss-scale state (loss_scale= or
+        capturable=True) the count comes from the device counter, and the
+        state itself (scale, found_inf, growth_tracker, step) is saved under
+        "mta_amp"; reading it synchronizes the stream."""
         self._sync_steps()
-        return super().state_dict()
+        sd = super().state_dict()
+        if self.amp is not None:
+            amp = self.amp.read()
+            sd["mta_amp"] = amp
+            sd["state"] = {k: dict(v, step=amp["step"]) if "step" in v
+                           else v for k, v in sd["state"].items()}
+        return sd
 
     def load_state_dict(self, state_dict):
         """As torch.optim.Optimizer.load_state_dict, except that every state
         tensor comes back in the dtype it was saved in (masters and float32
         moments of a 16-bit parameter stay float32).  The state buffers are
         new allocations and the device tables are rebuilt on the next step:
-        capture a graph of step() again after loading."""
+        capture a graph of step() again after loading.
+
+        With a loss-scale state, the saved one ("mta_amp") is written back
+        to the device; a checkpoint without one (saved by a plain
+        optimizer) sets the device step counter from the parameters'
+        common "step" and keeps the current scale.  A plain optimizer
+        takes the saved per-parameter counts either way."""
         self._plan = None          # its step counts belong to the old state
+        if self.amp is not None:
+            amp = state_dict.get("mta_amp")
+            if amp is None:
+                steps = {int(v["step"]) for v in
+                         state_dict["state"].values() if "step" in v}
+                if len(steps) > 1:
+                    raise ValueError(
+                        "a loss-scaled optimizer keeps one step count; the "
+                        f"checkpoint's parameters have taken {sorted(steps)}")
+                cur = self.amp.read()
+                amp = dict(cur, step=steps.pop() if steps else cur["step"],
+                           found_inf=0.0)
         super().load_state_dict(state_dict)
+        if self.amp is not None:
+            self.amp.write(amp["scale"], amp["step"], amp["growth_tracker"],
+                           amp["found_inf"])
         ids = [i for g in state_dict["param_groups"] for i in g["params"]]
         params = [p for g in self.param_groups for p in g["params"]]
         saved = state_dict["state"]

@@ -565,3 +565,66 @@ def test_decay_and_no_decay_groups_share_one_launch():
     assert launches == [1, 1, 2, 1, 1, 2, 1]
     sd = opt.state_dict()
     assert all(s["step"] == 7 for s in sd["state"].values())
+
+
+def _scaled_grads(model, opt, t, inf_at=None):
+    torch.manual_seed(3000 + t)
+    x = torch.randn(32, 300, device="cuda")
+    y = torch.randint(0, 10, (32,), device="cuda")
+    model.zero_grad(set_to_none=False)
+    loss = torch.nn.functional.cross_entropy(model(x), y)
+    (loss * opt.loss_scale).backward()
+    if t == inf_at:
+        next(model.parameters()).grad[0, 0] = float("inf")
+
+
+def test_loss_scaled_state_dict_resumes_exactly():
+    # a loss-scaled run checkpointed after an overflow step: the scale, the
+    # growth tracker and the device step counter come back with the
+    # moments, so the resumed run continues bit for bit (an optimizer made
+    # with another initial scale takes the saved one); a plain optimizer
+    # loading the same checkpoint takes the step count per parameter, and a
+    # loss-scaled one loading a plain checkpoint takes its count
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    kw = dict(kind="adamw", lr=1e-3, weight_decay=0.1, max_norm=1.0,
+              growth_interval=2)
+    model_a = _model(13)
+    opt_a = MtaOptimizer(model_a.parameters(), loss_scale=256.0, **kw)
+    for t in range(1, 5):
+        _scaled_grads(model_a, opt_a, t, inf_at=2)
+        opt_a.step()
+    sd = copy.deepcopy(opt_a.state_dict())
+    amp_a = opt_a.amp.read()
+    assert sd["mta_amp"] == amp_a and amp_a["step"] == 3
+    assert all(s["step"] == 3 for s in sd["state"].values())
+    model_b = _model(99)
+    with torch.no_grad():
+        for pb, pa in zip(model_b.parameters(), model_a.parameters()):
+            pb.copy_(pa)
+    opt_b = MtaOptimizer(model_b.parameters(), loss_scale=65536.0, **kw)
+    opt_b.load_state_dict(sd)
+    assert opt_b.amp.read() == amp_a
+    for t in range(5, 9):
+        for m, o in ((model_a, opt_a), (model_b, opt_b)):
+            _scaled_grads(m, o, t, inf_at=7)
+            o.step()
+        torch.cuda.synchronize()
+        assert opt_a.amp.read() == opt_b.amp.read(), t
+        for pa, pb in zip(model_a.parameters(), model_b.parameters()):
+            assert torch.equal(pa.detach().view(torch.int32),
+                               pb.detach().view(torch.int32)), t
+    plain = MtaOptimizer(_model(5).parameters(), **{k: v for k, v in
+                                                     kw.items()
+                                                     if k != "growth_interval"})
+    plain.load_state_dict(sd)
+    assert all(s["step"] == 3 for s in plain.state_dict()["state"].values())
+    model_c = _model(17)
+    opt_c = MtaOptimizer(model_c.parameters(), kind="adamw", lr=1e-3,
+                         weight_decay=0.1, max_norm=1.0)
+    for t in range(1, 3):
+        _grads(model_c, t)
+        opt_c.step()
+    scaled = MtaOptimizer(_model(17).parameters(), loss_scale=512.0, **kw)
+    scaled.load_state_dict(opt_c.state_dict())
+    st = scaled.amp.read()
+    assert (st["step"], st["scale"], st["found_inf"]) == (2, 512.0, 0.0)
