@@ -4,7 +4,7 @@ Marshalling only, like MtaList: it allocates the state buffers a rule needs
 (float32, or bfloat16 for packed Adam-family moments), keeps them in
 ``self.state`` under PyTorch's names (exp_avg, exp_avg_sq, momentum_buffer)
 so ``state_dict()`` / ``load_state_dict()`` work, and drives one list per
-parameter group and gradient dtype.  A step is:
+parameter set (below) and gradient dtype.  A step is:
 
   * with ``max_norm``: one clip over the joint norm of every gradient of
     every group (mta_clip_norm_joint over one norm list per gradient dtype,

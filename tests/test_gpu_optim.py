@@ -1,6 +1,7 @@
 """MtaOptimizer, the torch.optim-style front end: a real torch model's
 parameters and autograd gradients, one joint clip over every parameter
-group, one launch per group.  Checked bit for bit against the oracle
+group, one launch per parameter set (groups that differ only by a zero
+weight decay share one).  Checked bit for bit against the oracle
 (lockstep on the device coefficient) and within rounding against
 torch.optim.AdamW + clip_grad_norm_; state_dict round trips continue
 exactly; reallocated gradients rebuild the tables."""
