@@ -5,8 +5,9 @@ several tiles; aligned, shifted off 16-byte alignment, or back to back in
 flat buffers; sometimes the gradient shifted against the other buffers), a
 gradient type, moment kinds, an update rule, gradient zeroing, a deferred
 unscale or a device loss scale, bfloat16 or float16 weight copies on a
-random subset of tensors, a clip threshold (from always clipping to never)
-and occasionally a non-finite gradient, then runs two lockstep steps
+random subset of tensors, no-decay flags on another random subset, a clip
+threshold (from always clipping to never) and occasionally a non-finite
+gradient, then runs two lockstep steps
 through the C ABI against the oracle
 and compares every buffer bit for bit (w, g, the rule's state buffers, the
 copies), the norm (1e-6 relative), the clip coefficient (exact) and, under
@@ -71,6 +72,9 @@ def draw_case(seed):
         flat=bool(rng.random() < 0.5),
         g_shift=int(rng.choice([0, 0, 0, 0, 0, 1, 2, 5])),
     )
+    # drawn last, so the cases of the earlier draws stay as they were
+    c["nodecay"] = bool(rng.random() < 0.35)
+    c["nd_pick"] = [bool(x) for x in rng.random(count) < 0.5]
     return c
 
 
@@ -115,9 +119,14 @@ def run_case(c):
                              c["copy_f16"] else torch.bfloat16, device="cuda")
         L.set_weight_copies([copies[o:o + n] if p else None for o, n, p in
                              zip(arena.offsets, wl.sizes, picked)])
+    flags = [f and c["nodecay"] for f in c["nd_pick"]]
+    if c["nodecay"]:
+        L.set_no_decay(flags)
     opt = dict(kind=kind, lr=1e-3 if adam else 0.05, beta1=0.9, beta2=0.99,
                eps=1e-8, weight_decay=0.05 if adam else 0.0, momentum=0.8,
                zero_grad=c["zero"])
+    # the flagged tensors' own rule: the same step with weight_decay = 0
+    opt_nd = dict(opt, weight_decay=0.0)
     ost = []
     for i, n in enumerate(wl.sizes):
         views = [arena.view(b, i) for b in "wgmv"]
@@ -154,14 +163,29 @@ def run_case(c):
         what = f"case {c} t={t}"
         check_norm(np.float32(nd.item()), coef,
                    O.norm([o.g for o in ost], gtype, s), wl.max_norm, what)
+        subs = [([o for o, f in zip(ost, flags) if not f], opt),
+                ([o for o, f in zip(ost, flags) if f], opt_nd)]
         if c["amp"]:
-            O.amp_opt_step_(ost, opt, gtype, mkind, vkind, amp_o,
-                            wl.max_norm, coef=coef, zero=c["zero"])
+            found = not np.isfinite(O.norm([o.g for o in ost], gtype, s))
+            if found:                  # the whole step is skipped
+                O.amp_opt_step_(ost, opt, gtype, mkind, vkind, amp_o,
+                                wl.max_norm, coef=coef, zero=c["zero"])
+            else:
+                for sub, rule in subs:
+                    if sub:
+                        one = O.AmpState(amp_o.scale, amp_o.step,
+                                         amp_o.tracker)
+                        O.amp_opt_step_(sub, rule, gtype, mkind, vkind, one,
+                                        wl.max_norm, coef=coef,
+                                        zero=c["zero"])
+                amp_o.found_inf = np.float32(0.0)
             amp_o.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
             check_amp_state(amp_d.read(), amp_o, what)
         else:
-            O.opt_step_(ost, opt, gtype, mkind, vkind, t, s=s, coef=coef,
-                        zero=c["zero"])
+            for sub, rule in subs:
+                if sub:
+                    O.opt_step_(sub, rule, gtype, mkind, vkind, t, s=s,
+                                coef=coef, zero=c["zero"])
         for i, (o, n) in enumerate(zip(ost, wl.sizes)):
             if n == 0:
                 continue
