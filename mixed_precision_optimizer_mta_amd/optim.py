@@ -36,7 +36,10 @@ exactly 1), so ``step()`` can be captured in a HIP graph and replayed; the
 one difference from the plain step is that a non-finite gradient skips the
 update instead of spreading NaN.  Run one eager step first (it builds the
 device tables, which allocates), and keep the gradients' storage across
-replays (``zero_grad=True`` zeroes them inside the update launch).
+replays (``zero_grad=True`` zeroes them inside the update launch).  A
+replay reuses the captured tables and hyperparameters: after a change that
+rebuilds the plan (a moved gradient, a change of the parameter sets) or of
+a hyperparameter, run an eager step and capture again.
 
 ``master_weights=True`` is for a model kept in bfloat16 or float16: the
 optimizer holds a float32 master copy of every 16-bit parameter (``state[p]
