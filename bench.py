@@ -347,9 +347,9 @@ def main():
                          "counters of a profile")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU "
-              "path (the sharded design is described, not built)",
-              file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU "
+              "path (the step measured here is one GPU's; how it would shard "
+              "is described, not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
