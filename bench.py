@@ -605,6 +605,11 @@ def main():
             "bytes_per_launch": adamw_bytes,
         },
     }
+    # the counters' HBM bytes per launch at the same live launch time
+    for key, ms in (("norm_roofline", norm_ms), ("roofline", adamw_ms)):
+        r = out[key]
+        r["traffic_gbs"] = (None if r["traffic"] is None
+                            else r["traffic"] / (ms * 1e-3) / 1e9)
     L.close()
     for x in norm_lists[1:] if len(norm_lists) > 1 else []:
         x.close()
