@@ -629,3 +629,62 @@ def test_loss_scaled_state_dict_resumes_exactly():
     scaled.load_state_dict(opt_c.state_dict())
     st = scaled.amp.read()
     assert (st["step"], st["scale"], st["found_inf"]) == (2, 512.0, 0.0)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_master_weights_with_a_no_decay_group_share_one_launch(dt):
+    # a 16-bit model in the usual two groups: one list whose tensors carry
+    # both their 16-bit parameter (the weight copy) and, for the biases, the
+    # no-decay flag; masters and parameters bitwise against the oracle run
+    # group by group (float16 loss-scaled, as a float16 run is)
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model(41).to(dt)
+    params = list(model.parameters())
+    mats = [p for p in params if p.dim() == 2]
+    vecs = [p for p in params if p.dim() == 1]
+    groups = [{"params": mats, "weight_decay": 0.1},
+              {"params": vecs, "weight_decay": 0.0}]
+    gt = O.BF16 if dt == torch.bfloat16 else O.F16
+    scaled = dt == torch.float16
+    opt = MtaOptimizer(groups, kind="adamw", lr=1e-3, max_norm=1.0,
+                       master_weights=True,
+                       loss_scale=1024.0 if scaled else None)
+    ost = [[O.Tensor(_host(p.float()).ravel(), None,
+                     np.zeros(p.numel(), np.float32),
+                     np.zeros(p.numel(), np.float32),
+                     np.zeros(p.numel(), np.uint16), gt)
+            for p in g["params"]] for g in groups]
+    amp_o = O.AmpState(1024.0) if scaled else None
+    for t in range(1, 4):
+        torch.manual_seed(5000 + t)
+        x = torch.randn(32, 300, device="cuda", dtype=dt)
+        y = torch.randint(0, 10, (32,), device="cuda")
+        model.zero_grad(set_to_none=False)
+        loss = torch.nn.functional.cross_entropy(model(x).float(), y)
+        (loss * opt.loss_scale if scaled else loss).backward()
+        for g, og in zip(groups, ost):
+            for p, o in zip(g["params"], og):
+                o.g = _bits16(p.grad)
+        opt.step()
+        torch.cuda.synchronize()
+        assert len(opt._plan["updates"]) == 1
+        coef = np.float32(opt.last_coef.item())
+        for g, og in zip(groups, ost):
+            rule = dict(kind="adamw", lr=1e-3, beta1=0.9, beta2=0.999,
+                        eps=1e-8, weight_decay=g["weight_decay"],
+                        momentum=0.0)
+            if scaled:
+                one = O.AmpState(amp_o.scale, amp_o.step, amp_o.tracker)
+                _, _, found = O.amp_opt_step_(og, rule, gt, 0, 0, one, 1.0,
+                                              coef=coef)
+                assert not found
+            else:
+                O.opt_step_(og, rule, gt, 0, 0, t, coef=coef)
+        if scaled:
+            amp_o.update(2.0, 0.5, 2000)
+        for g, og in zip(groups, ost):
+            for p, o in zip(g["params"], og):
+                w = opt.state[p]["master_weight"]
+                assert np.array_equal(_host(w).ravel().view(np.uint32),
+                                      o.w.view(np.uint32)), (t, "master")
+                assert np.array_equal(_bits16(p), o.w16), (t, "parameter")
