@@ -195,16 +195,29 @@ def test_loss_scaled_front_end_matches_the_oracle_and_skips_overflow():
     assert opt.amp.read()["step"] == 5
 
 
-def test_capturable_step_replays_like_eager_steps():
+def _split_groups(model):
+    """The usual two groups: matrices decay, biases do not."""
+    ps = list(model.parameters())
+    return [{"params": [p for p in ps if p.dim() == 2]},
+            {"params": [p for p in ps if p.dim() == 1], "weight_decay": 0.0}]
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_capturable_step_replays_like_eager_steps(split):
     # the optimizer step captured once in a HIP graph; gradients are made
-    # eagerly into the same storage before every replay
+    # eagerly into the same storage before every replay; split: a decay and
+    # a no-decay group in one launch (the flags live in the captured tables)
     from mixed_precision_optimizer_mta_amd import MtaOptimizer
     a = _model(13)
     b = copy.deepcopy(a)
     kw = dict(kind="adamw", lr=1e-3, weight_decay=0.1, max_norm=1.0,
               capturable=True, zero_grad=True)
-    opt_a, opt_b = MtaOptimizer(a.parameters(), **kw), \
-        MtaOptimizer(b.parameters(), **kw)
+
+    def params(m):
+        return _split_groups(m) if split else m.parameters()
+
+    opt_a, opt_b = MtaOptimizer(params(a), **kw), \
+        MtaOptimizer(params(b), **kw)
     _grads(a, 1)
     _grads(b, 1)
     opt_a.step()                   # eager: builds the tables
@@ -229,6 +242,7 @@ def test_capturable_step_replays_like_eager_steps():
         assert opt_a.amp.read() == opt_b.amp.read()
     assert opt_a.amp.read()["step"] == 7
     assert opt_a.loss_scale.item() == 1.0
+    assert len(opt_a._plan["updates"]) == 1
 
 
 def test_capturable_matches_the_plain_step_on_finite_gradients():
