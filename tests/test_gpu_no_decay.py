@@ -101,24 +101,6 @@ def nodecay_lockstep(wl, opt, flags, steps, offsets=None, copies=None,
           f"{wl.count} tensors undecayed, bitwise", flush=True)
 
 
-def test_flags_take_effect_in_the_oracle():
-    # the comparison below would be empty if a flag changed nothing: one
-    # AdamW and one Adam step of the same tensor with and without decay
-    # must differ in w
-    rng = np.random.default_rng(7)
-    w = (rng.standard_normal(64) * 0.02).astype(np.float32)
-    g = (rng.standard_normal(64) * 0.01).astype(np.float32)
-    for kind in ("adamw", "adam"):
-        out = []
-        for f in (False, True):
-            x = O.Tensor(w.copy(), g.copy(), np.zeros(64, np.float32),
-                         np.zeros(64, np.float32))
-            O.opt_step_([x], own_opt(opt_for(kind), f), WL.F32, WL.MOM_F32,
-                        WL.MOM_F32, 1)
-            out.append(x.w)
-        assert not np.array_equal(out[0], out[1]), kind
-
-
 @pytest.mark.parametrize("pattern", ["odd", "ends", "all", "none"])
 @pytest.mark.parametrize("kind", ["adamw", "adam"])
 def test_no_decay_patterns(kind, pattern):

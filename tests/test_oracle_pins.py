@@ -977,3 +977,32 @@ def test_joint_norm_over_mixed_gradient_types_is_the_exact_norm():
         O.sumsq(a, O.F32)
     # a missing part changes the result: every part is counted
     assert O.joint_sumsq(parts[:2]) < got
+
+
+@pytest.mark.parametrize("kind", ["adamw", "adam"])
+def test_zero_decay_keeps_a_zero_gradient_tensor_exactly(kind):
+    # The reading behind per-tensor no-decay flags: a flagged tensor takes
+    # the step with weight_decay = 0.  Closed form from zero gradient and
+    # zero moments: m1 = v1 = 0, so the Adam term is (-step * 0) / eps = -0
+    # and w_new = w' exactly.  With weight_decay = 0, AdamW's factor is
+    # f32(1 - lr*0) = 1 and Adam's coupled term is w*0 = +-0, so w keeps
+    # every bit; with weight_decay > 0, AdamW gives w * f32(1 - lr*wd)
+    # exactly and Adam's coupled term moves w.
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal(257) * 0.02).astype(np.float32)
+    lr, wd = 3e-4, 0.1
+    out = {}
+    for decay in (0.0, wd):
+        x = O.Tensor(w.copy(), np.zeros(257, np.float32),
+                     np.zeros(257, np.float32), np.zeros(257, np.float32))
+        O.opt_step_([x], dict(kind=kind, lr=lr, beta1=0.9, beta2=0.999,
+                              eps=1e-8, weight_decay=decay, momentum=0.0),
+                    O.F32, O.MOM_F32, O.MOM_F32, 1)
+        out[decay] = x.w
+    assert np.array_equal(out[0.0].view(np.uint32), w.view(np.uint32))
+    if kind == "adamw":
+        dec = np.float32(1.0 - lr * wd)
+        assert np.array_equal(out[wd].view(np.uint32),
+                              (w * dec).view(np.uint32))
+    else:
+        assert not np.array_equal(out[wd], w)
