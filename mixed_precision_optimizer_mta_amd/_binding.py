@@ -238,7 +238,7 @@ def mta_list_set_no_decay(handle, no_decay, stream=0):
     """no_decay: one truth value per tensor of the list (True: the tensor
     takes weight_decay = 0), or None to clear every flag."""
     arr = None
-    if no_decay is not None:
+    if no_decay is not None and handle:
         count = mta_list_info(handle)["count"]
         if len(no_decay) != count:
             raise ValueError(f"no_decay has {len(no_decay)} entries, the "

@@ -89,6 +89,9 @@ def test_calls_on_a_null_handle_fail_cleanly():
     assert _err(M.mta_amp_clip_norm, None, 1.0, 0x1000, None, 0x2000) == -1
     assert _err(M.mta_amp_adamw_step, None, (1e-3, .9, .999, 1e-8, 0.),
                 0x1000, None) == -1
+    assert _err(M.mta_list_set_no_decay, None, [True, False]) == -1
+    assert _err(M.mta_list_set_no_decay, None, None) == -1
+    assert _err(M.mta_list_set_weight_copies, None, None) == -1
     M.mta_list_destroy(None)
 
 
