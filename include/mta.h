@@ -8,6 +8,10 @@
  *                   every float type", section "The whole model in one call":
  *                   every cell of several tensors times one factor, the
  *                   unscaling a float16 step needs before its clip.
+ *   mta_scale_device  ScaleTensors by a factor held in device memory: with
+ *                   the coefficient mta_clip_norm left there, the clipped
+ *                   gradients themselves ("measured, decided and scaled" on
+ *                   the card, section "Values that stay on the card").
  *   mta_clip_norm   ClipGradNorms -- same page and section: one cap over the
  *                   joint L2 norm of every gradient; section "Values that stay
  *                   on the card": the norm is measured and the factor decided
@@ -42,7 +46,8 @@
  * addresses for the handle's life.
  *
  * Layouts.
- *   w            float32, n elements.
+ *   w            float32, n elements; NULL for every tensor of a
+ *                gradient-only list (norm and scale calls only).
  *   g            float32, bfloat16 or IEEE float16 (MTA_F32 / MTA_BF16 /
  *                MTA_F16, whole list), n elements.
  *   m, v         the optimizer state.  Either may be NULL for every tensor of
@@ -95,8 +100,9 @@ extern "C" {
 /* 2: mta_list_info_t gained weight_copy_type and norm_kept_tiles (72 bytes;
  *    a caller built against version 1 passes a 64-byte struct, so check
  *    mta_abi_version() before calling mta_list_info or mta_list_plan).
- * 3: mta_list_set_no_decay. */
-#define MTA_ABI_VERSION 3
+ * 3: mta_list_set_no_decay.
+ * 4: mta_scale_device. */
+#define MTA_ABI_VERSION 4
 
 typedef struct mta_list mta_list; /* opaque */
 
@@ -113,7 +119,10 @@ typedef enum {
   MTA_ESTATE = -6  /* call not allowed in the handle's current state */
 } mta_status;
 
-/* One parameter group: the caller's device buffers and the element count. */
+/* One parameter group: the caller's device buffers and the element count.
+ * A gradient-only list gives g alone (w, m and v NULL for every tensor): it
+ * serves mta_clip_norm, mta_clip_norm_joint, mta_scale and mta_scale_device,
+ * and refuses every update and weight copies with MTA_ESTATE. */
 typedef struct {
   float *w;  /* master weights, float32 [n]               (read, written) */
   void *g;   /* gradient, list's gradient type [n]        (read; written only by MTA_SCALE_INPLACE) */
@@ -221,6 +230,19 @@ int mta_list_destroy(mta_list *list);
  * mta_adamw_step, which clears it.  A second MTA_SCALE_DEFER before that step
  * returns MTA_ESTATE.  factor must be finite. */
 int mta_scale(mta_list *list, float factor, int flags, void *stream);
+
+/* ScaleTensors in place by a factor in DEVICE memory: one launch, the
+ * kernel reads *d_factor (4-byte aligned float32) and writes
+ * g = f32(g * factor), a 16-bit gradient rounded back to its type
+ * (nearest-even, NaN -> 0xFFFF) -- MTA_SCALE_INPLACE with a factor the host
+ * never sees, so no synchronization.  With the d_coef of mta_clip_norm this
+ * clips the gradients themselves, as PyTorch's clip_grad_norm_ does (for a
+ * caller that reads them or updates with another optimizer; the fused step
+ * applies the coefficient in mta_adamw_step instead and needs no such pass).
+ * Whatever the device holds is applied: a NaN factor makes every gradient
+ * NaN.  A pending MTA_SCALE_DEFER factor is untouched and still applies to
+ * the next reads.  d_factor NULL: MTA_EINVAL. */
+int mta_scale_device(mta_list *list, const float *d_factor, void *stream);
 
 /* ClipGradNorms: one launch.  Computes the joint L2 norm of f32(g*s) over
  * every gradient of the list (s = the deferred scale factor, else 1), and

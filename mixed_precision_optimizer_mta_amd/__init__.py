@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     mta_clip_norm, mta_clip_norm_joint,
     mta_last_error, mta_list_create, mta_list_destroy, mta_list_info,
     mta_list_plan, mta_list_set_no_decay, mta_list_set_weight_copies,
-    mta_list_set_weight_copies_as, mta_scale, mta_step)
-from .torch_list import AmpState, MtaList, clip_norm_joint  # noqa: F401
+    mta_list_set_weight_copies_as, mta_scale, mta_scale_device, mta_step)
+from .torch_list import (AmpState, GradClipper, MtaList,  # noqa: F401
+                         clip_norm_joint)
 from .optim import MtaOptimizer  # noqa: F401

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
                 -6: "MTA_ESTATE"}
 
 # MTA_ABI_VERSION of include/mta.h that these structs mirror
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # every symbol include/mta.h declares
 EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
@@ -34,7 +34,7 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_amp_update", "mta_step", "mta_amp_step",
            "mta_list_set_weight_copies_as", "mta_list_plan",
            "mta_clip_norm_joint", "mta_amp_clip_norm_joint",
-           "mta_list_set_no_decay")
+           "mta_list_set_no_decay", "mta_scale_device")
 
 
 class mta_tensor(ctypes.Structure):
@@ -104,6 +104,7 @@ def lib():
                                       ctypes.POINTER(vp)]
         L.mta_list_destroy.argtypes = [vp]
         L.mta_scale.argtypes = [vp, f32, c_int, vp]
+        L.mta_scale_device.argtypes = [vp, vp, vp]
         L.mta_clip_norm.argtypes = [vp, f32, vp, vp, vp]
         L.mta_clip_norm_joint.argtypes = [ctypes.POINTER(vp), i64, f32, vp,
                                           vp, vp]
@@ -190,6 +191,12 @@ def mta_list_destroy(handle):
 
 def mta_scale(handle, factor, flags, stream=0):
     _check(lib().mta_scale(handle, factor, flags, stream), "mta_scale")
+
+
+def mta_scale_device(handle, d_factor, stream=0):
+    """g = g * (*d_factor) in place; d_factor a device pointer."""
+    _check(lib().mta_scale_device(handle, d_factor, stream),
+           "mta_scale_device")
 
 
 def mta_clip_norm(handle, max_norm, d_norm, d_coef, stream=0):

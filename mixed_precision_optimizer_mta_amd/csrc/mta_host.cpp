@@ -32,6 +32,7 @@ struct mta_list {
   int grid_update = 1;  // workgroups of an update launch
   int grid_norm = 1;    // workgroups of a norm or in-place scale launch
   int state_buffers = 3;  // bit 0: tensors have m; bit 1: they have v
+  bool has_w = true;      // false: a gradient-only list (no w, m, v)
   int vector_tensors = 0;
   void *dev_block = nullptr;  // one allocation: tile tables, norm scratch
   mta::GradTile *d_gtiles = nullptr;
@@ -478,6 +479,10 @@ int step_common(mta_list *L, const mta_opt *o, int64_t t, const float *d_coef,
   int rc = check_opt(o, t);
   if (rc) return rc;
   if (!L) return fail(MTA_EINVAL, "list is NULL");
+  if (!L->has_w)
+    return fail(MTA_ESTATE,
+                "a gradient-only list (no w) serves the norm and the scale "
+                "calls, not an update");
   const bool needs_m = o->kind != MTA_OPT_SGD;
   const bool needs_v = adam_family(o->kind);
   if ((needs_m && !(L->state_buffers & 1)) ||
@@ -585,18 +590,24 @@ int plan_list(const mta_tensor *tensors, int64_t count, int gtype, int mkind,
         return fail(MTA_EINVAL, "tensor %lld: n too large",
                     static_cast<long long>(i));
       if (x.n == 0) continue;
-      if (!x.w || !x.g)
-        return fail(MTA_EINVAL, "tensor %lld: w or g is NULL",
+      if (!x.g)
+        return fail(MTA_EINVAL, "tensor %lld: g is NULL",
                     static_cast<long long>(i));
-      const int st = (x.m ? 1 : 0) | (x.v ? 2 : 0);
+      if (!x.w && (x.m || x.v))
+        return fail(MTA_EINVAL,
+                    "tensor %lld: m or v without w (only a gradient-only "
+                    "list, w, m and v all NULL, may leave w out)",
+                    static_cast<long long>(i));
+      // bit 0: m, bit 1: v, bit 2: w
+      const int st = (x.m ? 1 : 0) | (x.v ? 2 : 0) | (x.w ? 4 : 0);
       if (state < 0) {
         state = st;
         state_from = i;
       } else if (st != state) {
         return fail(MTA_EINVAL,
-                    "tensor %lld: its m / v buffers are not given the way "
-                    "tensor %lld's are (a list has the same state buffers "
-                    "on every tensor)",
+                    "tensor %lld: its w / m / v buffers are not given the "
+                    "way tensor %lld's are (a list has the same buffers on "
+                    "every tensor)",
                     static_cast<long long>(i),
                     static_cast<long long>(state_from));
       }
@@ -706,7 +717,9 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->keep_from = plan.keep_from;
   L->vector_tensors = plan.vec_tensors;
   L->cus = cus;
-  L->state_buffers = plan.state < 0 ? 3 : plan.state;  // no element: any rule
+  // no element: any rule
+  L->state_buffers = plan.state < 0 ? 3 : (plan.state & 3);
+  L->has_w = plan.state < 0 || (plan.state & 4);
   const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
   const int bpc_n = env_int(
       "MTA_NORM_BLOCKS_PER_CU",
@@ -794,6 +807,8 @@ int mta_list_set_weight_copies_as(mta_list *L, void *const *w16,
   if (copy_type != MTA_BF16 && copy_type != MTA_F16)
     return fail(MTA_EDTYPE, "a weight copy is bfloat16 or float16, not %d",
                 static_cast<int>(copy_type));
+  if (w16 && !L->has_w)
+    return fail(MTA_ESTATE, "a gradient-only list has no weights to copy");
   std::vector<void *> copies;
   int attached = 0;
   try {
@@ -874,7 +889,7 @@ int mta_list_plan(const mta_tensor *tensors, int64_t count, int gtype,
   out->gtype = gtype;
   out->mkind = mkind;
   out->vkind = vkind;
-  out->state_buffers = plan.state < 0 ? 3 : plan.state;
+  out->state_buffers = plan.state < 0 ? 3 : (plan.state & 3);
   out->weight_copy_type = MTA_BF16;
   out->norm_kept_tiles =
       static_cast<int32_t>(plan.stiles.size() - plan.keep_from);
@@ -921,8 +936,21 @@ int mta_scale(mta_list *L, float factor, int flags, void *stream) {
   if (L->ntiles == 0) return ok();
   // the norm's grid: the same two-tile walk over the gradient alone
   const mta::Work wk = work_of(L, L->grid_norm, stream);
-  return after_launch(mta::launch_scale(L->gtype, wk, factor), wk.stream,
-                      "mta_scale");
+  return after_launch(mta::launch_scale(L->gtype, wk, factor, nullptr),
+                      wk.stream, "mta_scale");
+}
+
+int mta_scale_device(mta_list *L, const float *d_factor, void *stream) {
+  if (!L) return fail(MTA_EINVAL, "list is NULL");
+  if (!d_factor) return fail(MTA_EINVAL, "d_factor is NULL");
+  if (!aligned(d_factor, 4))
+    return fail(MTA_EALIGN, "d_factor must be 4-byte aligned");
+  int rc = check_device(L);
+  if (rc) return rc;
+  if (L->ntiles == 0) return ok();
+  const mta::Work wk = work_of(L, L->grid_norm, stream);
+  return after_launch(mta::launch_scale(L->gtype, wk, 1.0f, d_factor),
+                      wk.stream, "mta_scale_device");
 }
 
 int mta_clip_norm(mta_list *L, float max_norm, float *d_norm, float *d_coef,

@@ -124,7 +124,9 @@ hipError_t launch_update(int rule, int gtype, int mkind, int vkind,
 hipError_t launch_sumsq(int gtype, const Work &work, float s, float max_norm,
                         NormScratch scratch, float *d_norm, float *d_coef,
                         mta_amp_state *amp);
-hipError_t launch_scale(int gtype, const Work &work, float s);
+// d_s: null, or a device float that replaces s (read by the kernel).
+hipError_t launch_scale(int gtype, const Work &work, float s,
+                        const float *d_s);
 hipError_t launch_amp_update(mta_amp_state *state, double growth,
                              double backoff, int32_t interval,
                              hipStream_t stream);

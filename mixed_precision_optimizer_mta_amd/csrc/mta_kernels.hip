@@ -23,7 +23,10 @@
 //   k_sgd, k_momentum  the SGD and momentum-SGD rules (sgd_l, mom_l), on the
 //                 same tile walk.  Every update kernel can also zero the
 //                 gradient after reading it, as every step loop there does.
-//   k_scale       ScaleTensors in place (same Mica section).
+//   k_scale       ScaleTensors in place (same Mica section), by a factor
+//                 given by the host or read from device memory (the clip
+//                 coefficient a norm left there: the gradients scaled on
+//                 the card, section "Values that stay on the card").
 //   k_amp_update  the loss-scale update after a step (one thread).
 // Each of the first three is one launch over the whole tensor list.
 //
@@ -994,7 +997,9 @@ __device__ __forceinline__ void scale_any_tile(const GradTile &tl, uint32_t e0,
 // k_sumsq's walk, so that enough bytes are in flight to cover HBM latency.
 template <int D>
 __global__ void __launch_bounds__(kBlock)
-k_scale(const GradTile *__restrict__ tiles, uint32_t ntiles, float s) {
+k_scale(const GradTile *__restrict__ tiles, uint32_t ntiles, float s,
+        const float *__restrict__ d_s) {
+  if (d_s) s = *d_s;  // a factor in device memory, read once per workgroup
   constexpr int V = kWide<D>;
   constexpr int G = kTileElems / (kBlock * V);
   constexpr int U = 2;
@@ -1132,9 +1137,9 @@ hipError_t launch_sumsq_t(const Work &wk, float s, float max_norm,
 }
 
 template <int D>
-hipError_t launch_scale_t(const Work &wk, float s) {
+hipError_t launch_scale_t(const Work &wk, float s, const float *d_s) {
   hipLaunchKernelGGL((k_scale<D>), dim3(wk.grid), dim3(kBlock), 0, wk.stream,
-                     wk.gtiles, wk.ntiles, s);
+                     wk.gtiles, wk.ntiles, s, d_s);
   return hipGetLastError();
 }
 
@@ -1166,11 +1171,12 @@ hipError_t launch_sumsq(int gtype, const Work &wk, float s, float max_norm,
   }
 }
 
-hipError_t launch_scale(int gtype, const Work &wk, float s) {
+hipError_t launch_scale(int gtype, const Work &wk, float s,
+                        const float *d_s) {
   switch (gtype) {
-    case kF32: return launch_scale_t<kF32>(wk, s);
-    case kBF16: return launch_scale_t<kBF16>(wk, s);
-    case kF16: return launch_scale_t<kF16>(wk, s);
+    case kF32: return launch_scale_t<kF32>(wk, s, d_s);
+    case kBF16: return launch_scale_t<kBF16>(wk, s, d_s);
+    case kF16: return launch_scale_t<kF16>(wk, s, d_s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -80,6 +80,13 @@ class MtaList:
                     B.MTA_SCALE_DEFER if defer else B.MTA_SCALE_INPLACE,
                     current_stream())
 
+    def scale_device(self, factor):
+        """g = g * factor in place, factor a one-element float32 GPU tensor
+        (for instance the coef a clip_norm left)."""
+        if factor.dtype != torch.float32 or not factor.is_cuda:
+            raise TypeError("the factor is a float32 GPU tensor")
+        B.mta_scale_device(self.handle, factor.data_ptr(), current_stream())
+
     def clip_norm(self, max_norm, norm_out, coef_out):
         """norm_out (may be None) and coef_out: float32 device tensors."""
         for t in (norm_out, coef_out):
@@ -208,6 +215,66 @@ def clip_norm_joint(lists, max_norm, norm_out, coef_out, amp=None):
     else:
         B.mta_amp_clip_norm_joint(handles, max_norm, amp.ptr, nptr,
                                   coef_out.data_ptr(), current_stream())
+
+
+class GradClipper:
+    """PyTorch's clip_grad_norm_ on the device, for gradients an optimizer
+    of another kind will read: the joint L2 norm of every gradient, the
+    coefficient min(1, max_norm / (norm + 1e-6)) and every gradient scaled by
+    it in place (ClipGradNorms measured, decided and scaled on the card).
+    One gradient-only list per gradient dtype (built once, on the first call
+    and again whenever a gradient moves); a call launches one norm per list
+    (chained to a joint norm) and one in-place scale per list, and reads
+    nothing back: the norm and the coefficient stay in device tensors."""
+
+    def __init__(self, params):
+        self.params = [p for p in params]
+        self._lists, self._key = [], None
+        self.norm = self.coef = None
+
+    def _build(self, ps):
+        for L in self._lists:
+            L.close()
+        self._lists = []
+        for dt in _G:
+            gs = [p.grad for p in ps if p.grad.dtype == dt]
+            if gs:
+                L = MtaList([], entries=[(None, g.data_ptr(), None, None,
+                                          g.numel()) for g in gs],
+                            gtype=_G[dt], mkind=B.MTA_MOM_F32,
+                            vkind=B.MTA_MOM_F32)
+                L._keep = gs
+                self._lists.append(L)
+
+    def __call__(self, max_norm):
+        """Clip every gradient in place; returns the pre-clip joint norm as
+        a one-element float32 device tensor (coef in ``self.coef``)."""
+        ps = [p for p in self.params if p.grad is not None]
+        for p in ps:
+            g = p.grad
+            if g.dtype not in _G or not g.is_cuda or not g.is_contiguous():
+                raise TypeError("gradients are contiguous float32, bfloat16 "
+                                "or float16 GPU tensors")
+        key = tuple((p.grad.data_ptr(), p.grad.dtype, p.grad.numel())
+                    for p in ps)
+        if key != self._key:
+            self._build(ps)
+            self._key = key
+        if not self._lists:
+            return None
+        dev = ps[0].grad.device
+        if self.norm is None or self.norm.device != dev:
+            self.norm = torch.zeros(1, device=dev)
+            self.coef = torch.zeros(1, device=dev)
+        clip_norm_joint(self._lists, float(max_norm), self.norm, self.coef)
+        for L in self._lists:
+            L.scale_device(self.coef)
+        return self.norm
+
+    def close(self):
+        for L in self._lists:
+            L.close()
+        self._lists, self._key = [], None
 
 
 class AmpState:

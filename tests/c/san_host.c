@@ -101,6 +101,16 @@ int main(void) {
     CHECK(mta_list_plan(NULL, 0, MTA_F32, 0, 0, NULL) == MTA_EINVAL,
           "plan NULL out");
     CHECK(mta_list_plan(NULL, 0, 7, 0, 0, &info) == MTA_EDTYPE, "gtype");
+    CHECK(mta_scale_device(NULL, fake, NULL) == MTA_EINVAL, "scale dev");
+    /* a gradient-only table is a list; m without w is not */
+    mta_tensor go[2] = {{NULL, addr(0x7f2000000000ull, 0), NULL, NULL, 100},
+                        {NULL, addr(0x7f2000000000ull, 512), NULL, NULL, 9}};
+    CHECK(mta_list_plan(go, 2, MTA_F32, 0, 0, &info) == MTA_OK &&
+              info.state_buffers == 0 && info.elements == 109,
+          "gradient-only plan");
+    go[1].m = addr(0x7f3000000000ull, 0);
+    CHECK(mta_list_plan(go, 2, MTA_F32, 0, 0, &info) == MTA_EINVAL,
+          "m without w");
   }
 
   /* random tables through the planner: sizes 0..2^20 with a few huge ones,

@@ -22,7 +22,9 @@ hipError_t launch_sumsq(int, const Work &, float, float, NormScratch, float *,
                         float *, mta_amp_state *) {
   reached("launch_sumsq");
 }
-hipError_t launch_scale(int, const Work &, float) { reached("launch_scale"); }
+hipError_t launch_scale(int, const Work &, float, const float *) {
+  reached("launch_scale");
+}
 hipError_t launch_amp_update(mta_amp_state *, double, double, int32_t,
                              hipStream_t) {
   reached("launch_amp_update");

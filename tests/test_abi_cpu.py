@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert M.mta_abi_version() == 3 == B.ABI_VERSION
+    assert M.mta_abi_version() == 4 == B.ABI_VERSION
     # the binding's mirror of mta_list_info_t has the header's size
     assert ctypes.sizeof(B.mta_list_info_t) == 72
 
@@ -91,6 +91,7 @@ def test_calls_on_a_null_handle_fail_cleanly():
                 0x1000, None) == -1
     assert _err(M.mta_list_set_no_decay, None, [True, False]) == -1
     assert _err(M.mta_list_set_no_decay, None, None) == -1
+    assert _err(M.mta_scale_device, None, 0x1000) == -1
     assert _err(M.mta_list_set_weight_copies, None, None) == -1
     M.mta_list_destroy(None)
 

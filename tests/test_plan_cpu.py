@@ -133,3 +133,24 @@ def test_plan_reports_the_errors_create_reports():
             with pytest.raises(M.MtaError) as e:
                 fn(ents, g, m, v)
             assert e.value.code == code, (fn.__name__, ents)
+
+
+def test_gradient_only_tables():
+    # g alone (w, m, v NULL on every tensor) is a valid list with no state
+    # buffers and the same tile cuts as a full list over the same gradients;
+    # m or v without w, or w on some tensors only, is refused
+    sizes = [5, 4096, 9000, 0, 77]
+    full, gonly, pos = [], [], 0
+    for n in sizes:
+        full.append((BASE[0] + 4 * pos, BASE[1] + 4 * pos, None, None, n))
+        gonly.append((None, BASE[1] + 4 * pos, None, None, n))
+        pos += -(-n // 64) * 64
+    a = M.mta_list_plan(full, 0, 0, 0)
+    b = M.mta_list_plan(gonly, 0, 0, 0)
+    assert b["state_buffers"] == 0
+    for k in ("count", "elements", "tiles", "vector_tensors"):
+        assert a[k] == b[k], k
+    with pytest.raises(M.MtaError):              # m without w
+        M.mta_list_plan([(None, BASE[1], BASE[2], None, 8)], 0, 0, 0)
+    with pytest.raises(M.MtaError):              # w on one tensor only
+        M.mta_list_plan([gonly[0], full[1]], 0, 0, 0)
