@@ -235,6 +235,45 @@ def cpu_baseline_parallel(arena, wl, steps, threads):
                       f"threads, {dt:.2f} s"}
 
 
+def torch_reference(arena, wl, steps=100, warmup=10):
+    """PyTorch's own step on the same tensors, for context: every tensor a
+    torch Parameter over its slice of the arena (its gradient the slice of
+    g), then torch.nn.utils.clip_grad_norm_ + torch.optim.AdamW(fused=True)
+    with the workload's hyperparameters (PyTorch keeps float32 moments of
+    its own).  Device time per step from HIP events over `steps` steps.
+    Float32 gradients only (PyTorch needs the parameter's dtype)."""
+    import torch
+    ps = []
+    for i, n in enumerate(wl.sizes):
+        if n:
+            p = torch.nn.Parameter(arena.view("w", i))
+            p.grad = arena.view("g", i)
+            ps.append(p)
+    opt = torch.optim.AdamW(ps, lr=wl.lr, betas=(wl.beta1, wl.beta2),
+                            eps=wl.eps, weight_decay=wl.weight_decay,
+                            fused=True)
+
+    def step():
+        torch.nn.utils.clip_grad_norm_(ps, wl.max_norm)
+        opt.step()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"kind": "torch.nn.utils.clip_grad_norm_ + "
+                    "torch.optim.AdamW(fused=True), float32 moments",
+            "torch": torch.__version__, "steps": steps, "ms_per_step": ms,
+            "params_per_s": wl.n / (ms * 1e-3)}
+
+
 def cpu_baseline(arena, wl, steps, opt=None):
     """The oracle as it stands (single thread) on host copies of the same
     list: `steps` whole steps (norm + update)."""
@@ -328,6 +367,11 @@ def main():
                          "GPT-2 layouts: the biases and layer-norm gains) "
                          "to take no weight decay, in the same update "
                          "launch (mta_list_set_no_decay)")
+    ap.add_argument("--torch-reference", action="store_true",
+                    help="after the timed steps, also time PyTorch's own "
+                         "clip_grad_norm_ + AdamW(fused=True) on the same "
+                         "tensors (float32-gradient workloads), reported as "
+                         "torch_reference")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -625,6 +669,12 @@ def main():
             threads = max(1, min(16, os.cpu_count() or 1))
             out["cpu_baseline_parallel"] = cpu_baseline_parallel(
                 arena, wl, args.cpu_steps, threads)
+    if args.torch_reference:
+        if wl.gtype != WL.F32 or wl.amp:
+            print("--torch-reference needs float32 gradients without loss "
+                  "scaling", file=sys.stderr)
+            sys.exit(2)
+        out["torch_reference"] = torch_reference(arena, wl)
     print(json.dumps(out), flush=True)
 
 
