@@ -426,6 +426,11 @@ def main():
               "(not loss-scaled): e.g. --workload gpt2_124m_bf16g",
               file=sys.stderr)
         sys.exit(2)
+    if args.torch_reference and (wl.gtype != WL.F32 or wl.amp):
+        print("--torch-reference needs float32 gradients without loss "
+              "scaling (PyTorch's optimizers take the parameter's dtype)",
+              file=sys.stderr)
+        sys.exit(2)
     if args.graph and not wl.amp:
         print("--graph needs a loss-scaled workload (its step counter and "
               "scale live on the device, so a captured step can be "
@@ -670,10 +675,6 @@ def main():
             out["cpu_baseline_parallel"] = cpu_baseline_parallel(
                 arena, wl, args.cpu_steps, threads)
     if args.torch_reference:
-        if wl.gtype != WL.F32 or wl.amp:
-            print("--torch-reference needs float32 gradients without loss "
-                  "scaling", file=sys.stderr)
-            sys.exit(2)
         out["torch_reference"] = torch_reference(arena, wl)
     print(json.dumps(out), flush=True)
 
