@@ -368,10 +368,14 @@ def main():
                          "to take no weight decay, in the same update "
                          "launch (mta_list_set_no_decay)")
     ap.add_argument("--torch-reference", action="store_true",
-                    help="after the timed steps, also time PyTorch's own "
-                         "clip_grad_norm_ + AdamW(fused=True) on the same "
-                         "tensors (float32-gradient workloads), reported as "
-                         "torch_reference")
+                    help="insist on the PyTorch comparison (an error on a "
+                         "workload it cannot run); by default it runs on "
+                         "every float32-gradient AdamW workload: after the "
+                         "timed steps, PyTorch's own clip_grad_norm_ + "
+                         "AdamW(fused=True) on the same tensors, reported "
+                         "as torch_reference")
+    ap.add_argument("--no-torch-reference", action="store_true",
+                    help="skip the PyTorch comparison")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -426,11 +430,16 @@ def main():
               "(not loss-scaled): e.g. --workload gpt2_124m_bf16g",
               file=sys.stderr)
         sys.exit(2)
-    if args.torch_reference and (wl.gtype != WL.F32 or wl.amp):
-        print("--torch-reference needs float32 gradients without loss "
-              "scaling (PyTorch's optimizers take the parameter's dtype)",
-              file=sys.stderr)
+    # PyTorch's step on the same tensors needs float32 gradients (its
+    # optimizers take the parameter's dtype) and is the AdamW step itself
+    ref_ok = wl.gtype == WL.F32 and not wl.amp and args.opt == "adamw" \
+        and not args.zero_grad and not args.weight_copy and \
+        not args.scale_inplace
+    if args.torch_reference and not ref_ok:
+        print("--torch-reference needs a plain AdamW step on float32 "
+              "gradients", file=sys.stderr)
         sys.exit(2)
+    torch_ref = ref_ok and not args.no_torch_reference
     if args.graph and not wl.amp:
         print("--graph needs a loss-scaled workload (its step counter and "
               "scale live on the device, so a captured step can be "
@@ -674,7 +683,7 @@ def main():
             threads = max(1, min(16, os.cpu_count() or 1))
             out["cpu_baseline_parallel"] = cpu_baseline_parallel(
                 arena, wl, args.cpu_steps, threads)
-    if args.torch_reference:
+    if torch_ref:
         out["torch_reference"] = torch_reference(arena, wl)
     print(json.dumps(out), flush=True)
 
