@@ -702,3 +702,39 @@ def test_master_weights_with_a_no_decay_group_share_one_launch(dt):
                 assert np.array_equal(_host(w).ravel().view(np.uint32),
                                       o.w.view(np.uint32)), (t, "master")
                 assert np.array_equal(_bits16(p), o.w16), (t, "parameter")
+
+
+def test_works_under_torch_grad_scaler():
+    # PyTorch's own loss-scaling loop drives MtaOptimizer like any
+    # optimizer: GradScaler unscales the gradients in place, skips the step
+    # on an overflow and adjusts its scale; the parameters follow
+    # torch.optim.AdamW under the same scaler within rounding (PyTorch's
+    # lerp uses an fma), and the overflow step leaves them untouched
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    a = _model(23)
+    b = copy.deepcopy(a)
+    opt_a = MtaOptimizer(a.parameters(), kind="adamw", lr=1e-3,
+                         weight_decay=0.1)
+    opt_b = torch.optim.AdamW(b.parameters(), lr=1e-3, weight_decay=0.1,
+                              foreach=False)
+    sc_a = torch.amp.GradScaler("cuda", init_scale=1024.0, growth_interval=2)
+    sc_b = torch.amp.GradScaler("cuda", init_scale=1024.0, growth_interval=2)
+    for t in range(1, 7):
+        before = [p.detach().clone() for p in a.parameters()]
+        for m, opt, sc in ((a, opt_a, sc_a), (b, opt_b, sc_b)):
+            torch.manual_seed(4000 + t)
+            x = torch.randn(32, 300, device="cuda")
+            y = torch.randint(0, 10, (32,), device="cuda")
+            m.zero_grad(set_to_none=False)
+            loss = torch.nn.functional.cross_entropy(m(x), y)
+            sc.scale(loss).backward()
+            if t == 3:
+                next(m.parameters()).grad[0, 0] = float("inf")
+            sc.step(opt)
+            sc.update()
+        torch.cuda.synchronize()
+        assert sc_a.get_scale() == sc_b.get_scale(), t
+        for pa, pb, p0 in zip(a.parameters(), b.parameters(), before):
+            if t == 3:
+                assert torch.equal(pa.detach(), p0), "overflow step taken"
+            torch.testing.assert_close(pa, pb, rtol=1e-5, atol=1e-7)
