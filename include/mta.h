@@ -6,19 +6,21 @@
  *
  *   mta_scale       ScaleTensors -- "Mica 7.7: a training step on the card, in
  *                   every float type", section "The whole model in one call":
- *                   every cell of several tensors times one factor, the
- *                   unscaling a float16 step needs before its clip.
+ *                   one factor applied to every element of many tensors;
+ *                   there it is how a float16 step removes its loss scale
+ *                   ahead of the clip.
  *   mta_scale_device  ScaleTensors by a factor held in device memory: with
  *                   the coefficient mta_clip_norm left there, the clipped
- *                   gradients themselves ("measured, decided and scaled" on
- *                   the card, section "Values that stay on the card").
- *   mta_clip_norm   ClipGradNorms -- same page and section: one cap over the
- *                   joint L2 norm of every gradient; section "Values that stay
- *                   on the card": the norm is measured and the factor decided
- *                   on the device, and both stay there until the host asks.
- *   mta_adamw_step  AdamWSteps -- same page and section: one launch however
- *                   many tensors, each group updated exactly as a lone
- *                   AdamWStep would update it.  The element arithmetic is that
+ *                   gradients themselves, the scaling done on the device
+ *                   as well (section "Values that stay on the card").
+ *   mta_clip_norm   ClipGradNorms -- same page and section: a single clip
+ *                   threshold over the L2 norm of all gradients taken
+ *                   together; section "Values that stay on the card": the
+ *                   norm and the factor are both formed on the device and
+ *                   stay there until the host reads them.
+ *   mta_adamw_step  AdamWSteps -- same page and section: a single launch
+ *                   whatever the number of tensors, leaving every group as
+ *                   the single-group AdamWStep would.  The element arithmetic is that
  *                   of "BendTorch main.bend", section "Optimizers" (adam_decay,
  *                   adam_m, adam_v, adam_w in PyTorch's order; packed
  *                   bfloat16 moments as in adamh_l / adamhv_l; bias
@@ -29,13 +31,20 @@
  *                   (sgd_l), momentum SGD (mom_l); optionally zeroing the
  *                   gradient as every step loop there does.
  *   mta_amp_*       the same steps under a dynamic loss scale kept in device
- *                   memory (Mica: the unscaling a float16 step needs), with
- *                   PyTorch's GradScaler rule for skipping and rescaling.
+ *                   memory (Mica, same section: a float16 step divides its
+ *                   loss scale out before the clip; section "Values that
+ *                   stay on the card": the loss is scaled on the device),
+ *                   with PyTorch's GradScaler rule for skipping and
+ *                   rescaling.
  *   mta_list_set_weight_copies  bfloat16 (or, by mta_list_set_weight_copies_as,
  *                   float16) copies of the new weights (Mica, section
  *                   "float16 and bfloat16, whole").
  *   mta_list_set_no_decay  tensors that take no weight decay, in the same
  *                   launch as those that do.
+ *   mta_list_create, mta_list_destroy  the list handle: the tensors of a
+ *                   step described once, on the device, so that each call
+ *                   above is a single launch over all of them (same page,
+ *                   section "The whole model in one call").
  *
  * Memory and ownership.  Every w, g, m, v pointer is device memory owned by
  * the caller (for example a PyTorch tensor's data pointer).  The library never
@@ -83,10 +92,18 @@
  *
  * Errors.  Functions return MTA_OK (0) or a negative mta_status.  On failure
  * nothing has been enqueued and mta_last_error() (per host thread) says why.
- * Arguments are checked before any device work.  A fault inside a kernel is
- * asynchronous: it is reported by the caller's next synchronizing act (or, with
- * the environment variable MTA_DEBUG_SYNC=1, by the call that launched it,
- * which then waits for its own work and returns MTA_EHIP).
+ * Arguments are checked before any device work, so a request the library
+ * cannot serve is turned away before anything runs (the reading taken of
+ * "Mica 7.7", section "The card a program uses", where an invalid card
+ * number stops the program at its start).  A fault inside a kernel is
+ * asynchronous: work is queued on the caller's stream, and a failure of a
+ * queued kernel is reported by the caller's next act that waits on it
+ * (section "Upgrading": a queued kernel's failure surfaces at the next
+ * waiting act).  With the environment variable MTA_DEBUG_SYNC=1 every call
+ * that launches work waits for it before returning, so a kernel failure is
+ * reported, as MTA_EHIP, by the call that launched it (section "Kernels
+ * ready at the start": the debug tier waits for each kernel so the failure
+ * is named where it happened).  MTA_DEBUG_SYNC is read once per process.
  */
 #ifndef MTA_H
 #define MTA_H
@@ -142,10 +159,10 @@ typedef struct {
 /* Loss-scale state for float16 (or bfloat16) training with dynamic loss
  * scaling, kept by the caller in DEVICE memory (24 bytes, 8-byte aligned) and
  * read and written only by the device, so no step needs a host sync.  The
- * gradients hold scale * (true gradient).  Reading of the pages' "the
- * unscaling a float16 step needs before its clip" ("Mica 7.7", section "The
- * whole model in one call"): PyTorch's GradScaler, whose numerics the pages
- * promise.  Initialise scale (e.g. 65536), the other fields to 0. */
+ * gradients hold scale * (true gradient).  "Mica 7.7", section "The whole
+ * model in one call", has a float16 step divide its loss scale out of the
+ * gradients before the clip; the reading taken for how the scale itself
+ * moves is PyTorch's GradScaler, whose numerics the pages promise.  Initialise scale (e.g. 65536), the other fields to 0. */
 typedef struct {
   float scale;            /* loss scale */
   float found_inf;        /* 1 when the last norm saw a non-finite unscaled
@@ -212,15 +229,25 @@ typedef struct {
                                mta_adamw_step read f32(g * factor) in registers */
 
 /* Create a list handle over `count` (>= 0) tensors described by the host array
- * `tensors`.  Validates every entry, builds the tile tables and copies them
- * to the current device on `stream`, then waits for that copy.
- * Allocates device memory (the only call that does).  On success *out owns the
- * handle; release it with mta_list_destroy. */
+ * `tensors` ("Mica 7.7", section "The whole model in one call": the calls
+ * take every tensor of the model at once, one launch each; the handle is
+ * that set of tensors, described once, so that no call re-describes it).
+ * Validates every entry (null or misaligned buffers, negative sizes,
+ * overlapping buffers, unknown types: MTA_EINVAL, MTA_EALIGN, MTA_EDTYPE,
+ * before any device work), builds the tile tables and copies them to the
+ * current device on `stream`, then waits for that copy.  Allocates device
+ * memory (MTA_ENOMEM when that fails).  On success *out owns the handle;
+ * release it with mta_list_destroy.  On failure *out is NULL and nothing
+ * is allocated. */
 int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
                     int mkind, int vkind, void *stream, mta_list **out);
 
-/* Free a handle.  The caller must have synchronized every stream that used it.
- * NULL is accepted and ignored. */
+/* Free a handle: its device tables and norm scratch (the counterpart of
+ * mta_list_create, same passage).  The caller must have synchronized every
+ * stream that used it: a kernel still running on the handle's tables would
+ * read freed memory.  NULL is accepted and ignored.  MTA_EHIP when the HIP
+ * runtime refuses the free (the handle is released on the host either
+ * way). */
 int mta_list_destroy(mta_list *list);
 
 /* ScaleTensors over the list's gradients.  MTA_SCALE_INPLACE launches one
@@ -254,9 +281,9 @@ int mta_scale_device(mta_list *list, const float *d_factor, void *stream);
 int mta_clip_norm(mta_list *list, float max_norm, float *d_norm, float *d_coef,
                   void *stream);
 
-/* ClipGradNorms over several lists: one cap over the joint length of every
- * gradient of every list ("Mica 7.7", section "The whole model in one
- * call"), each list keeping its own gradient type and its own pending
+/* ClipGradNorms over several lists: a single clip threshold applied to the
+ * L2 norm taken jointly over every gradient of every list ("Mica 7.7",
+ * section "The whole model in one call"), each list keeping its own gradient type and its own pending
  * deferred factor (a bfloat16 program whose high-numerics parameters keep
  * float32 gradients: "Precision and numerics", Parameters).  One launch per
  * list, in order on `stream`; each adds its float64 sum of squares to the
@@ -329,7 +356,8 @@ int mta_list_set_weight_copies_as(mta_list *list, void *const *w16,
  * covers a decay group and a no-decay group whose other hyperparameters are
  * equal.  Each flagged tensor is updated exactly as the same call with
  * weight_decay = 0 would update it alone ("Mica 7.7", section "The whole model
- * in one call": each group updated as a lone AdamWStep would update it):
+ * in one call": a multi-tensor step leaves each group as the single-group
+ * step would):
  * MTA_OPT_ADAMW takes dec = 1 (w' = w*1), MTA_OPT_ADAM takes
  * ge' = ge + f32(w*0); SGD and momentum have no decay, so the flag changes
  * nothing there.  Applies to mta_adamw_step, mta_step, mta_amp_adamw_step and
@@ -394,10 +422,15 @@ int mta_amp_update(mta_amp_state *d_amp, double growth_factor,
                    void *stream);
 
 /* Host only, no device work: the seven float32 constants the AdamW kernel
- * receives for step t, in the order {step, bc2, c1, c2, b2, eps, dec}. */
+ * receives for step t, in the order {step, bc2, c1, c2, b2, eps, dec}
+ * ("BendTorch main.bend", section "Optimizers": the Opt type's comment and
+ * Opt.at for step and bc2, the adam_m comment for 1 - beta formed in
+ * float64; section "Training": 1 - b^t with t = 1 first). */
 int mta_adamw_scalars(const mta_adamw_hparams *hp, int64_t t, float out[7]);
 
-/* Host only: describe a handle. */
+/* Host only: describe a handle -- its tensors, tiles and launch grids (the
+ * list of "Mica 7.7", section "The whole model in one call", as the device
+ * sees it; section "The card a program uses": the device it lives on). */
 int mta_list_info(const mta_list *list, mta_list_info_t *out);
 
 /* Host only: the shape mta_list_create would give a list of these tensors,
@@ -413,10 +446,17 @@ int mta_list_info(const mta_list *list, mta_list_info_t *out);
 int mta_list_plan(const mta_tensor *tensors, int64_t count, int gtype,
                   int mkind, int vkind, mta_list_info_t *out);
 
-/* Message for the last failure on the calling host thread ("" if none). */
+/* Message for the last failure on the calling host thread ("" if none),
+ * naming the call and the argument or HIP error: a failure named where it
+ * happened ("Mica 7.7", sections "Kernels ready at the start" and
+ * "Upgrading").  The pointer stays valid until the thread's next call
+ * into the library; a successful call clears it. */
 const char *mta_last_error(void);
 
-/* MTA_ABI_VERSION of the built library. */
+/* MTA_ABI_VERSION of the built library.  A binding compares it with the
+ * version it was written for when it loads the library and refuses a
+ * mismatch before any work ("Mica 7.7", section "The card a program uses":
+ * a request that cannot be met is refused at the start). */
 int mta_abi_version(void);
 
 #ifdef __cplusplus
