@@ -83,15 +83,13 @@ bool debug_sync() {
   return on;
 }
 
-// Workgroups per compute unit of the persistent launches.  A workgroup is
-// four wave64s; the grid walks the tile table with a grid stride.  Measured
-// on gfx950 (MI355X): every update rule streams best with one long-lived
-// workgroup per CU that keeps two tiles of loads in flight (fewer concurrent
-// streams, better HBM page locality; two, three or four per CU measured
-// 3-9% slower).  The norm keeps two tiles of loads in flight per workgroup:
-// one workgroup per CU for float32 gradients, two for 16-bit ones (half the
-// bytes per tile, so twice the workgroups for the same bytes in flight).
-constexpr int kUpdateBlocksPerCu = 1;
+// Launch shapes.  A workgroup is four wave64s.  The update kernels launch
+// one workgroup per tile (the hardware hands tiles out in order; see the
+// kernels).  The norm and the in-place scale are persistent grids that walk
+// the tile table with a grid stride, two tiles of loads in flight per
+// workgroup: one workgroup per CU for float32 gradients, two for 16-bit
+// ones (half the bytes per tile, so twice the workgroups for the same bytes
+// in flight).  Measured on gfx950 (MI355X).
 constexpr int kNormBlocksPerCuF32 = 1;
 constexpr int kNormBlocksPerCu16 = 2;
 
@@ -720,13 +718,11 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   // no element: any rule
   L->state_buffers = plan.state < 0 ? 3 : (plan.state & 3);
   L->has_w = plan.state < 0 || (plan.state & 4);
-  const int bpc_u = env_int("MTA_BLOCKS_PER_CU", kUpdateBlocksPerCu, 1, 64);
   const int bpc_n = env_int(
       "MTA_NORM_BLOCKS_PER_CU",
       gtype == MTA_F32 ? kNormBlocksPerCuF32 : kNormBlocksPerCu16, 1, 64);
   const int64_t tiles_or_one = std::max<int64_t>(1, L->ntiles);
-  L->grid_update = static_cast<int>(
-      std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_u));
+  L->grid_update = static_cast<int>(tiles_or_one);  // one per tile
   L->grid_norm = static_cast<int>(
       std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_n));
 

@@ -36,7 +36,9 @@
 // Work is cut into tiles of kTileElems elements of one tensor.  The tile
 // tables are built once per list on the host: each record holds the tile's
 // own buffer addresses, length and alignment, so one scalar load describes a
-// tile.  A persistent grid walks the tiles with a grid stride.  Inside a full
+// tile.  The update kernels run one workgroup per tile; the norm and the
+// in-place scale are persistent grids that walk the tiles with a grid
+// stride.  Inside a full
 // tile of a 16-byte-aligned tensor every wave instruction reads or writes one
 // contiguous run of memory: lane l of group j owns elements j*G + V*l ..
 // j*G + V*l + V-1, where V is 4 for k_adamw (a 16-byte access of a float32
@@ -251,6 +253,27 @@ __device__ __forceinline__ uint32_t stream_of_block() {
              : (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
 }
 
+// The update kernels are not persistent: workgroup b updates one tile, and
+// the grid has one workgroup per tile.  The hardware dispatches workgroups
+// in order as earlier ones retire, so the tiles in flight always form one
+// narrow window that moves through the list front to back.  (A persistent
+// grid-stride walk lets its workgroups drift apart over thousands of
+// iterations; the window of open rows widens and the update measured 6-12%
+// slower on the 1.56B-parameter lists.)  Within each run of 8 * kXcdRun
+// workgroups, XCD x (workgroup b goes to XCD b % 8) takes kXcdRun
+// consecutive tiles, so every XCD streams contiguous runs of each buffer:
+// measured against plain b -> b, +1% to +5% depending on the list, best at
+// runs of 16-32 tiles.  The last partial run keeps b -> b.
+constexpr uint32_t kXcdRun = 32;
+
+__device__ __forceinline__ uint32_t tile_of_block() {
+  const uint32_t b = blockIdx.x;
+  const uint32_t full = gridDim.x / (kXcds * kXcdRun) * (kXcds * kXcdRun);
+  if (b >= full) return b;
+  const uint32_t x = b % kXcds, k = b / kXcds;
+  return (k / kXcdRun) * (kXcds * kXcdRun) + x * kXcdRun + k % kXcdRun;
+}
+
 // ---------------------------------------------------------------------------
 // b^t rounded to the nearest float64, for step counts that live in device
 // memory: square-and-multiply in double-double (a float64 pair whose sum
@@ -338,14 +361,12 @@ constexpr int kAdamVec = 4;                                   // per access
 constexpr int kAdamGroups = kTileElems / (kBlock * kAdamVec); // 4
 constexpr uint32_t kAdamStride = kBlock * kAdamVec;           // 1024
 
-// The update kernels keep two tiles in flight per lane: while one computes
-// tile t from one register set it has already issued every load of tile
-// t + gridDim.x into the other.  With one workgroup per CU (one wave per
-// SIMD) this keeps HBM busy through the ~1000 VALU instructions a lane spends
-// on an AdamW tile; it measured 3-5% above the single-buffered loop at any
-// grid size on gfx950.  The register sets hold the raw loaded vectors;
-// unpacking happens when a tile is computed, so no wait is needed between a
-// tile's loads.
+// A workgroup issues every load of its tile as raw vectors first, then
+// unpacks and computes: no wait falls between a tile's loads.  The
+// compiler keeps the update at about 170-230 VGPRs, two workgroups per CU,
+// so each CU has two tiles' loads in flight while it computes (a variant
+// that kept it under 96 VGPRs, at up to five workgroups per CU, measured
+// slower).
 
 // raw vectors of one lane's share of a full tile (4 accesses per buffer)
 template <int D>
@@ -523,97 +544,70 @@ __device__ __forceinline__ void partial_tile(
     }
 }
 
-// +0 into every gradient element of the list: the whole work of a skipped
+// +0 into every gradient element of one tile: the whole work of a skipped
 // loss-scaled step that was asked to zero the gradients.
 template <int G>
-__device__ void zero_grad_tiles(const StepTile *__restrict__ tiles,
-                                uint32_t ntiles) {
-  const uint32_t e0 = threadIdx.x * kAdamVec;
-  for (uint32_t t = stream_of_block(); t < ntiles; t += gridDim.x) {
-    const StepTile st = tiles[t];
-    MTA_GLOBAL elem_t<G> *pg = gp<elem_t<G>>(st.g, 0);
-    if ((st.flags & kTileVec) && st.lim == kTileElems) {
+__device__ __forceinline__ void zero_grad_tile(const StepTile &st,
+                                               uint32_t e0) {
+  MTA_GLOBAL elem_t<G> *pg = gp<elem_t<G>>(st.g, 0);
+  if ((st.flags & kTileVec) && st.lim == kTileElems) {
 #pragma unroll
-      for (int j = 0; j < kAdamGroups; ++j) zero4<G>(pg, e0 + j * kAdamStride);
-    } else {
+    for (int j = 0; j < kAdamGroups; ++j) zero4<G>(pg, e0 + j * kAdamStride);
+  } else {
 #pragma unroll
-      for (int j = 0; j < kAdamGroups; ++j)
+    for (int j = 0; j < kAdamGroups; ++j)
 #pragma unroll
-        for (int k = 0; k < kAdamVec; ++k) {
-          const uint32_t e = e0 + j * kAdamStride + k;
-          if (e < st.lim) zero1<G>(pg, e);
-        }
-    }
+      for (int k = 0; k < kAdamVec; ++k) {
+        const uint32_t e = e0 + j * kAdamStride + k;
+        if (e < st.lim) zero1<G>(pg, e);
+      }
   }
 }
 
-// The body of every update kernel: a persistent grid-stride walk of the
-// tile table with register double buffering.
+// The body of every update kernel: the one tile of this workgroup.
 template <int R, int G, bool MPacked, bool VPacked>
-__device__ __forceinline__ void update_tiles(
+__device__ __forceinline__ void update_tile(
     const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
     const float *__restrict__ d_coef, const AmpStep &amp) {
-  using Regs = TileRegs<R, G, MPacked, VPacked>;
   using Ref = TileRef<G, MPacked, VPacked>;
+  const uint32_t t = tile_of_block();
+  if (t >= ntiles) return;  // never, with one workgroup per tile
+  const uint32_t e0 = threadIdx.x * kAdamVec;
+  const StepTile rec = tiles[t];
+  // loss-scaled step: skipped when an unscaled gradient was not finite
+  // (zeroing the gradients still happens when asked)
+  if (amp.state && amp.state->found_inf != 0.0f) {
+    if (sc.zero) zero_grad_tile<G>(rec, e0);
+    return;
+  }
+  const float coef = d_coef ? *d_coef : 1.0f;
+  const Ref cur = tile_ref<G, MPacked, VPacked>(rec);
+  TileRegs<R, G, MPacked, VPacked> X;
+  if (cur.full) issue_tile(X, cur, e0);
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight first
   if (amp.state) {
-    // loss-scaled step: skipped when an unscaled gradient was not finite
-    // (zeroing the gradients still happens when asked); otherwise the
-    // unscale factor, and for the Adam family t and the two t-dependent
-    // constants, come from the device state, formed in float64 as the host
-    // forms them
-    if (amp.state->found_inf != 0.0f) {
-      if (sc.zero) zero_grad_tiles<G>(tiles, ntiles);
-      return;
-    }
+    // while the loads are in flight: the unscale factor, and for the Adam
+    // family t and the two t-dependent constants, from the device state,
+    // formed in float64 as the host forms them
     if constexpr (kUsesV<R>) {
-      const int64_t t = amp.state->step + 1;
-      const double q1 = 1.0 - pow_rn(amp.beta1, t);
-      const double q2 = 1.0 - pow_rn(amp.beta2, t);
+      const int64_t step = amp.state->step + 1;
+      const double q1 = 1.0 - pow_rn(amp.beta1, step);
+      const double q2 = 1.0 - pow_rn(amp.beta2, step);
       sc.nstep = -static_cast<float>(amp.lr / q1);
       sc.bc2 = static_cast<float>(sqrt(q2));
     }
     sc.s = inv_scale(amp.state->scale);
   }
-  const float coef = d_coef ? *d_coef : 1.0f;
-  const uint32_t e0 = threadIdx.x * kAdamVec;
-  uint32_t t = stream_of_block();
-  if (t >= ntiles) return;
-  const uint32_t last = ntiles - 1;
-  Regs A, B;
-  Ref cur = tile_ref<G, MPacked, VPacked>(tiles[t]);
-  // the record of the next tile, read one iteration ahead (clamped to the
-  // last tile, so the scalar load is always in bounds)
-  StepTile rec = tiles[min(t + gridDim.x, last)];
-  if (cur.full) issue_tile(A, cur, e0);
-  // one iteration: issue every load of tile t + gridDim.x into Y, then the
-  // scalar load of the record after it, then compute and store tile t from
-  // X; two iterations per loop trip so X and Y alternate by name
-  auto step = [&](Regs &X, Regs &Y) -> bool {
-    const uint32_t tn = t + gridDim.x;
-    const bool more = tn < ntiles;
-    const Ref nxt = tile_ref<G, MPacked, VPacked>(rec);
-    if (more && nxt.full) issue_tile(Y, nxt, e0);
-    // only now the next record: scalar loads return out of order, so a wait
-    // for `rec` placed before the vector loads would also wait for this one
-    __builtin_amdgcn_sched_barrier(0);
-    rec = tiles[min(tn + gridDim.x, last)];
-    // a tensor flagged no-decay takes the step's constants for
-    // weight_decay = 0: dec = f32(1 - lr*0) = 1 (AdamW), l2 = 0 (Adam)
-    StepScalars st = sc;
-    if (cur.nodecay) {
-      st.dec = 1.0f;
-      st.l2 = 0.0f;
-    }
-    if (cur.full)
-      finish_tile(X, cur, e0, st, coef);
-    else
-      partial_tile<R>(cur, e0, st, coef);
-    cur = nxt;
-    t = tn;
-    return more;
-  };
-  while (step(A, B) && step(B, A)) {
+  // a tensor flagged no-decay takes the step's constants for
+  // weight_decay = 0: dec = f32(1 - lr*0) = 1 (AdamW), l2 = 0 (Adam)
+  if (cur.nodecay) {
+    sc.dec = 1.0f;
+    sc.l2 = 0.0f;
   }
+  if (cur.full)
+    finish_tile(X, cur, e0, sc, coef);
+  else
+    partial_tile<R>(cur, e0, sc, coef);
 }
 
 // AdamW (L2 = false) and Adam with coupled decay (L2 = true).
@@ -621,7 +615,7 @@ template <int G, bool MPacked, bool VPacked, bool L2>
 __global__ void __launch_bounds__(kBlock)
 k_adamw(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
         const float *__restrict__ d_coef, AmpStep amp) {
-  update_tiles<L2 ? kRuleAdam : kRuleAdamW, G, MPacked, VPacked>(
+  update_tile<L2 ? kRuleAdam : kRuleAdamW, G, MPacked, VPacked>(
       tiles, ntiles, sc, d_coef, amp);
 }
 
@@ -629,15 +623,15 @@ template <int G>
 __global__ void __launch_bounds__(kBlock)
 k_sgd(const StepTile *__restrict__ tiles, uint32_t ntiles, StepScalars sc,
       const float *__restrict__ d_coef, AmpStep amp) {
-  update_tiles<kRuleSgd, G, false, false>(tiles, ntiles, sc, d_coef, amp);
+  update_tile<kRuleSgd, G, false, false>(tiles, ntiles, sc, d_coef, amp);
 }
 
 template <int G>
 __global__ void __launch_bounds__(kBlock)
 k_momentum(const StepTile *__restrict__ tiles, uint32_t ntiles,
            StepScalars sc, const float *__restrict__ d_coef, AmpStep amp) {
-  update_tiles<kRuleMomentum, G, false, false>(tiles, ntiles, sc, d_coef,
-                                               amp);
+  update_tile<kRuleMomentum, G, false, false>(tiles, ntiles, sc, d_coef,
+                                              amp);
 }
 
 // ---------------------------------------------------------------------------
