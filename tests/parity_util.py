@@ -8,6 +8,9 @@ the device norm; then the oracle runs its step with that coefficient and
 w, m, v are compared element by element (float32: 2 ulp, packed bfloat16:
 1 bf16 ulp).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -18,6 +21,46 @@ from mixed_precision_optimizer_mta_amd import workloads as WL
 NORM_RTOL = 1e-6
 F32_ULP = 2
 BF16_ULP = 1
+
+# host threads for the oracle's per-tensor work on large lists (the GPU
+# boxes give one GPU's job 16 cores); the oracle is called through ctypes,
+# which releases the GIL, so its calls on disjoint tensors run in parallel
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def in_groups(items, fn, threads=THREADS):
+    """fn(group) for `threads` disjoint groups of items (round robin by
+    size, largest first), in parallel; returns the results in group
+    order.  Each item is touched by exactly one call."""
+    if threads <= 1 or len(items) <= 1:
+        return [fn(list(items))]
+    order = sorted(range(len(items)), key=lambda i: -_size(items[i]))
+    groups = [[] for _ in range(min(threads, len(items)))]
+    load = [0] * len(groups)
+    for i in order:
+        k = load.index(min(load))
+        groups[k].append(items[i])
+        load[k] += _size(items[i])
+    with ThreadPoolExecutor(len(groups)) as ex:
+        return list(ex.map(fn, groups))
+
+
+def _size(x):
+    return x.w.size if getattr(x, "w", None) is not None else x.g.size
+
+
+def host_arena(arena, bufs="wgmv"):
+    """Whole arena buffers on the host, one device-to-host copy each:
+    float32 buffers as float32 arrays, 16-bit ones as uint16 bit
+    patterns."""
+    out = {}
+    for b in bufs:
+        t = getattr(arena, b).detach()
+        if t.dtype == torch.float32:
+            out[b] = t.cpu().numpy()
+        else:
+            out[b] = t.cpu().view(torch.int16).numpy().view(np.uint16)
+    return out
 
 
 def f32_ulp(a, b):
@@ -81,12 +124,16 @@ def oracle_state(arena, idx=None):
                          grad_np(arena.g[sel], wl.gtype),
                          mom_np(arena.m[sel], wl.mkind),
                          mom_np(arena.v[sel], wl.vkind))]
+    h = host_arena(arena)
     out = []
-    for i in range(wl.count):
-        out.append(O.Tensor(dev_f32(arena.view("w", i)),
-                            grad_np(arena.view("g", i), wl.gtype),
-                            mom_np(arena.view("m", i), wl.mkind),
-                            mom_np(arena.view("v", i), wl.vkind)))
+    for i, n in enumerate(wl.sizes):
+        o = arena.offsets[i]
+        og = o + arena.g_shift
+        m, v = h["m"][o:o + n], h["v"][o:o + n]
+        out.append(O.Tensor(
+            h["w"][o:o + n].copy(), h["g"][og:og + n].copy(),
+            O.pack_halves(m) if wl.mkind == WL.MOM_BF16X2 else m.copy(),
+            O.pack_halves(v) if wl.vkind == WL.MOM_BF16X2 else v.copy()))
     return out
 
 
@@ -95,7 +142,10 @@ def oracle_grads(arena, idx=None):
     if idx is not None:
         sel = torch.as_tensor(idx, device=arena.device)
         return [grad_np(arena.g[sel], wl.gtype)]
-    return [grad_np(arena.view("g", i), wl.gtype) for i in range(wl.count)]
+    g = host_arena(arena, "g")["g"]
+    sh = arena.g_shift
+    return [g[o + sh:o + sh + n].copy()
+            for o, n in zip(arena.offsets, wl.sizes)]
 
 
 def compare(arena, ostate, idx=None, what=""):
@@ -104,28 +154,46 @@ def compare(arena, ostate, idx=None, what=""):
     wl = arena.wl
     if idx is not None:
         sel = torch.as_tensor(idx, device=arena.device)
-        pairs = [(arena.w[sel], arena.m[sel], arena.v[sel], ostate[0], len(idx))]
+        pairs = [(dev_f32(arena.w[sel]), _host_mom(arena.m[sel], wl.mkind),
+                  _host_mom(arena.v[sel], wl.vkind), ostate[0], len(idx))]
     else:
-        pairs = [(arena.view("w", i), arena.view("m", i), arena.view("v", i),
-                  ostate[i], wl.sizes[i]) for i in range(wl.count)]
+        h = host_arena(arena, "wmv")
+        pairs = [(h["w"][o:o + n], h["m"][o:o + n], h["v"][o:o + n],
+                  ostate[i], n)
+                 for i, (o, n) in enumerate(zip(arena.offsets, wl.sizes))]
     worst = {"w": 0, "m": 0, "v": 0}
     for w, m, v, o, n in pairs:
         if n == 0:
             continue
-        dw = f32_ulp(dev_f32(w), o.w)
-        worst["w"] = max(worst["w"], int(dw.max()))
+        worst["w"] = max(worst["w"], ulp_max(w, o.w, False))
         for name, t, kind, ob in (("m", m, wl.mkind, o.m),
                                   ("v", v, wl.vkind, o.v)):
-            if kind == WL.MOM_BF16X2:
-                d = bf16_ulp(dev_bf16_bits(t), O.unpack_words(ob, n))
-            else:
-                d = f32_ulp(dev_f32(t), ob)
-            worst[name] = max(worst[name], int(d.max()))
+            packed = kind == WL.MOM_BF16X2
+            want = O.unpack_words(ob, n) if packed else ob
+            worst[name] = max(worst[name], ulp_max(t, want, packed))
     assert worst["w"] <= F32_ULP, (what, worst)
     for name, kind in (("m", wl.mkind), ("v", wl.vkind)):
         tol = BF16_ULP if kind == WL.MOM_BF16X2 else F32_ULP
         assert worst[name] <= tol, (what, worst)
     return worst
+
+
+def _host_mom(t, kind):
+    return dev_bf16_bits(t) if kind == WL.MOM_BF16X2 else dev_f32(t)
+
+
+def ulp_max(got, want, bf16):
+    """Largest ulp distance between two arrays of one buffer (float32
+    values, or bfloat16 bit patterns when bf16); 0 at once when they are
+    the same bits."""
+    it = np.uint16 if bf16 else np.uint32
+    a = np.ascontiguousarray(got).view(it)
+    b = np.ascontiguousarray(want).view(it)
+    if a.shape == b.shape and np.array_equal(a, b):
+        return 0
+    d = bf16_ulp(a, b) if bf16 else f32_ulp(a.view(np.float32),
+                                            b.view(np.float32))
+    return int(d.max())
 
 
 def check_norm(norm_gpu, coef_gpu, norm_oracle, max_norm, what=""):
@@ -211,9 +279,14 @@ def check_amp_state(dev, ora, what=""):
 
 
 def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
-             check_guards=False, clip=True, inject=None, g_shift=0):
+             check_guards=False, clip=True, inject=None, g_shift=0,
+             compare_steps=None):
     """Run `steps` device steps in lockstep with the oracle; returns the
-    worst ulp distances seen.
+    worst ulp distances seen.  Every element (or every sampled position
+    when nsample is set) is compared after the steps in compare_steps
+    (None: after every step) and always after the last; the norm is
+    checked at norm_steps (None: every step).  The oracle's state stays in
+    lockstep at every step either way.
 
     A loss-scaled workload (wl.amp) runs mta_amp_clip_norm,
     mta_amp_adamw_step and mta_amp_update against oracle.amp_step_ and
@@ -284,10 +357,15 @@ def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
             amp_o.update(wl.amp_growth, wl.amp_backoff, wl.amp_interval)
             check_amp_state(amp_d.read(), amp_o, f"{wl.name} t={t}")
         else:
-            O.step_(ostate, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
-                    wl.beta2, wl.eps, wl.weight_decay, t, s=s, coef=coef)
-        got = compare(arena, ostate, idx, f"{wl.name} t={t}")
-        worst = {k: max(worst[k], got[k]) for k in worst}
+            # the oracle's own step over disjoint groups of tensors: with
+            # the coefficient given, each tensor's update depends on that
+            # tensor alone
+            in_groups(ostate, lambda grp: O.step_(
+                grp, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
+                wl.beta2, wl.eps, wl.weight_decay, t, s=s, coef=coef))
+        if compare_steps is None or t in compare_steps or t == steps:
+            got = compare(arena, ostate, idx, f"{wl.name} t={t}")
+            worst = {k: max(worst[k], got[k]) for k in worst}
     if check_guards:
         torch.cuda.synchronize()
         inside = torch.zeros(arena.total, dtype=torch.bool, device="cuda")
@@ -302,3 +380,145 @@ def lockstep(wl, steps, offsets=None, nsample=None, norm_steps=None,
     extra = f" amp: {skipped} skipped, state {amp_d.read()}" if wl.amp else ""
     print(f"{wl.name}: steps={steps} worst ulp {worst}{extra}", flush=True)
     return worst
+
+
+# ------------------------------------------------------------ other rules
+
+def opt_for(kind, zero=False, lr=None):
+    adam = kind in ("adamw", "adam")
+    return dict(kind=kind, lr=lr if lr is not None else (3e-4 if adam
+                                                          else 0.05),
+                beta1=0.9, beta2=0.999, eps=1e-8,
+                weight_decay=0.1 if adam else 0.0, momentum=0.9,
+                zero_grad=zero)
+
+
+def uses(kind):
+    """(has m, has v) of a rule's list."""
+    return kind != "sgd", kind in ("adamw", "adam")
+
+
+def make_rule_list(arena, kind):
+    from mixed_precision_optimizer_mta_amd import MtaList
+    wl = arena.wl
+    has_m, has_v = uses(kind)
+    ents = [(w, g, m if has_m else None, v if has_v else None, n)
+            for (w, g, m, v, n) in arena.entries()]
+    return MtaList([], entries=ents, gtype=wl.gtype, mkind=wl.mkind,
+                   vkind=wl.vkind)
+
+
+def oracle_rule_state(arena, kind, idx=None):
+    wl = arena.wl
+    has_m, has_v = uses(kind)
+    if idx is None:
+        out = oracle_state(arena)
+        for o in out:
+            o.m = o.m if has_m else None
+            o.v = o.v if has_v else None
+        return out
+    sel = torch.as_tensor(idx, device=arena.device)
+    return [O.Tensor(dev_f32(arena.w[sel]), grad_np(arena.g[sel], wl.gtype),
+                     mom_np(arena.m[sel], wl.mkind) if has_m else None,
+                     mom_np(arena.v[sel], wl.vkind) if has_v else None)]
+
+
+def compare_rule(arena, ost, kind, idx=None, what=""):
+    """Bitwise comparison of w, g and the rule's state buffers."""
+    wl = arena.wl
+    has_m, has_v = uses(kind)
+    if idx is not None:
+        sel = torch.as_tensor(idx, device=arena.device)
+        views = [(dev_f32(arena.w[sel]), grad_np(arena.g[sel], wl.gtype),
+                  _host_mom(arena.m[sel], wl.mkind),
+                  _host_mom(arena.v[sel], wl.vkind), len(idx))]
+    else:
+        h = host_arena(arena)
+        sh = arena.g_shift
+        views = [(h["w"][o:o + n], h["g"][o + sh:o + sh + n],
+                  h["m"][o:o + n], h["v"][o:o + n], n)
+                 for o, n in zip(arena.offsets, wl.sizes)]
+    gbits = wl.gtype != WL.F32
+    for (w, g, m, v, n), o in zip(views, ost):
+        if n == 0:
+            continue
+        assert ulp_max(w, o.w, False) == 0, (what, "w")
+        gi = np.uint16 if gbits else np.uint32
+        assert np.array_equal(np.ascontiguousarray(g).view(gi),
+                              np.ascontiguousarray(o.g).view(gi)), \
+            (what, "g")
+        for has, t, kind_, ob, name in ((has_m, m, wl.mkind, o.m, "m"),
+                                        (has_v, v, wl.vkind, o.v, "v")):
+            if not has:
+                continue
+            packed = kind_ == WL.MOM_BF16X2
+            want = O.unpack_words(ob, n) if packed else ob
+            d = ulp_max(t, want, packed)
+            assert d == 0, (what, name, d)
+
+
+def rule_lockstep(wl, opt, steps, offsets=None, nsample=None,
+                  norm_steps=None, check_guards=False, g_shift=0,
+                  compare_steps=None):
+    """lockstep for any rule through mta_step: norm checked at norm_steps
+    (None: every step), w, g and the rule's state compared bit for bit
+    after compare_steps (None: every step) and after the last."""
+    assert not (g_shift and nsample is not None)
+    arena = WL.Arena(wl, "cuda", offsets, g_shift=g_shift)
+    arena.fill_weights()
+    kind, zero = opt["kind"], bool(opt.get("zero_grad"))
+    L = make_rule_list(arena, kind)
+    idx = None if nsample is None else sample_positions(wl, arena.offsets,
+                                                        nsample)
+    ost = oracle_rule_state(arena, kind, idx)
+    before = None
+    if check_guards:
+        before = {b: getattr(arena, b).clone() for b in "wgmv"}
+    nd = torch.full((1,), -1.0, device="cuda")
+    cd = torch.full((1,), -1.0, device="cuda")
+    for t in range(1, steps + 1):
+        arena.fill_grads(t)
+        if check_guards:
+            before["g"] = arena.g.clone()
+        for o, g in zip(ost, oracle_grads(arena, idx)):
+            o.g = g
+        full_g = None
+        if idx is not None and (norm_steps is None or t in norm_steps):
+            full_g = oracle_grads(arena)     # before a zeroing step runs
+        if wl.scale != 1.0:
+            L.scale(wl.scale, defer=True)
+        L.clip_norm(wl.max_norm, nd, cd)
+        L.step(opt, t, cd)
+        torch.cuda.synchronize()
+        ng, coef = np.float32(nd.item()), np.float32(cd.item())
+        if norm_steps is None or t in norm_steps:
+            # the oracle's step below may zero its copies: read them first
+            gs = [o.g for o in ost] if idx is None else full_g
+            check_norm(ng, coef, O.norm(gs, wl.gtype, wl.scale), wl.max_norm,
+                       f"{wl.name} {kind} t={t}")
+        else:
+            want = O.clip_coef(wl.max_norm, ng)
+            assert coef.view(np.uint32) == want.view(np.uint32)
+        in_groups(ost, lambda grp: O.opt_step_(
+            grp, opt, wl.gtype, wl.mkind, wl.vkind, t, s=wl.scale,
+            coef=coef, zero=zero))
+        if compare_steps is None or t in compare_steps or t == steps:
+            compare_rule(arena, ost, kind, idx, f"{wl.name} {kind} t={t}")
+        if check_guards:
+            has_m, has_v = uses(kind)
+            for b in "wgmv":
+                sh = arena.g_shift if b == "g" else 0
+                inside = torch.zeros(arena.total, dtype=torch.bool,
+                                     device="cuda")
+                for o, n in zip(arena.offsets, wl.sizes):
+                    inside[o + sh:o + sh + n] = True
+                now = getattr(arena, b)
+                ity = torch.int32 if now.dtype == torch.float32 else \
+                    torch.int16
+                diff = now.view(ity) != before[b].view(ity)
+                if b in "wg" or (b == "m" and has_m) or (b == "v" and has_v):
+                    diff = diff & ~inside    # only inside its tensors
+                assert not bool(diff.any()), f"{kind}: {b} written outside"
+    L.close()
+    print(f"{wl.name} {kind} zero={zero}: {steps} steps bitwise",
+          flush=True)

@@ -15,9 +15,9 @@ from mixed_precision_optimizer_mta_amd import workloads as WL
 
 pytestmark = pytest.mark.gpu
 
-from parity_util import (bf16_ulp, check_amp_state, check_norm,  # noqa: E402
-                         dev_bf16_bits, dev_f32, f32_ulp, grad_np, mom_np,
-                         oracle_grads, sample_positions)
+from parity_util import (check_amp_state, compare_rule,  # noqa: E402
+                         dev_bf16_bits, dev_f32, make_rule_list, opt_for,
+                         oracle_grads, oracle_rule_state, rule_lockstep)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,131 +31,6 @@ def _device():
 
 EDGE = [0, 1, 2, 3, 7, 8, 9, 15, 17, 4095, 4096, 4097, 8191, 8193,
         3 * 4096 + 5]
-
-
-def opt_for(kind, zero=False, lr=None):
-    adam = kind in ("adamw", "adam")
-    return dict(kind=kind, lr=lr if lr is not None else (3e-4 if adam
-                                                          else 0.05),
-                beta1=0.9, beta2=0.999, eps=1e-8,
-                weight_decay=0.1 if adam else 0.0, momentum=0.9,
-                zero_grad=zero)
-
-
-def uses(kind):
-    return kind != "sgd", kind in ("adamw", "adam")
-
-
-def make_rule_list(arena, kind):
-    from mixed_precision_optimizer_mta_amd import MtaList
-    wl = arena.wl
-    has_m, has_v = uses(kind)
-    ents = [(w, g, m if has_m else None, v if has_v else None, n)
-            for (w, g, m, v, n) in arena.entries()]
-    return MtaList([], entries=ents, gtype=wl.gtype, mkind=wl.mkind,
-                   vkind=wl.vkind)
-
-
-def oracle_rule_state(arena, kind, idx=None):
-    wl = arena.wl
-    has_m, has_v = uses(kind)
-    if idx is not None:
-        sel = torch.as_tensor(idx, device=arena.device)
-        views = [(arena.w[sel], arena.g[sel], arena.m[sel], arena.v[sel])]
-    else:
-        views = [tuple(arena.view(b, i) for b in "wgmv")
-                 for i in range(wl.count)]
-    out = []
-    for w, g, m, v in views:
-        out.append(O.Tensor(dev_f32(w), grad_np(g, wl.gtype),
-                            mom_np(m, wl.mkind) if has_m else None,
-                            mom_np(v, wl.vkind) if has_v else None))
-    return out
-
-
-def compare_rule(arena, ost, kind, idx=None, what=""):
-    """Bitwise comparison of w, g and the rule's state buffers."""
-    wl = arena.wl
-    has_m, has_v = uses(kind)
-    if idx is not None:
-        sel = torch.as_tensor(idx, device=arena.device)
-        views = [(arena.w[sel], arena.g[sel], arena.m[sel], arena.v[sel],
-                  len(idx))]
-    else:
-        views = [tuple(arena.view(b, i) for b in "wgmv") + (wl.sizes[i],)
-                 for i in range(wl.count)]
-    for (w, g, m, v, n), o in zip(views, ost):
-        if n == 0:
-            continue
-        assert f32_ulp(dev_f32(w), o.w).max() == 0, (what, "w")
-        assert np.array_equal(grad_np(g, wl.gtype), o.g), (what, "g")
-        for has, t, kind_, ob, name in ((has_m, m, wl.mkind, o.m, "m"),
-                                        (has_v, v, wl.vkind, o.v, "v")):
-            if not has:
-                continue
-            if kind_ == WL.MOM_BF16X2:
-                d = bf16_ulp(dev_bf16_bits(t), O.unpack_words(ob, n))
-            else:
-                d = f32_ulp(dev_f32(t), ob)
-            assert d.max() == 0, (what, name, int(d.max()))
-
-
-def rule_lockstep(wl, opt, steps, offsets=None, nsample=None,
-                  norm_steps=None, check_guards=False, g_shift=0):
-    assert not (g_shift and nsample is not None)
-    arena = WL.Arena(wl, "cuda", offsets, g_shift=g_shift)
-    arena.fill_weights()
-    kind, zero = opt["kind"], bool(opt.get("zero_grad"))
-    L = make_rule_list(arena, kind)
-    idx = None if nsample is None else sample_positions(wl, arena.offsets,
-                                                        nsample)
-    ost = oracle_rule_state(arena, kind, idx)
-    before = None
-    if check_guards:
-        before = {b: getattr(arena, b).clone() for b in "wgmv"}
-    nd = torch.full((1,), -1.0, device="cuda")
-    cd = torch.full((1,), -1.0, device="cuda")
-    for t in range(1, steps + 1):
-        arena.fill_grads(t)
-        if check_guards:
-            before["g"] = arena.g.clone()
-        for o, g in zip(ost, oracle_grads(arena, idx)):
-            o.g = g
-        full_g = None
-        if idx is not None and (norm_steps is None or t in norm_steps):
-            full_g = oracle_grads(arena)     # before a zeroing step runs
-        if wl.scale != 1.0:
-            L.scale(wl.scale, defer=True)
-        L.clip_norm(wl.max_norm, nd, cd)
-        L.step(opt, t, cd)
-        torch.cuda.synchronize()
-        ng, coef = np.float32(nd.item()), np.float32(cd.item())
-        if norm_steps is None or t in norm_steps:
-            # the oracle's step below may zero its copies: read them first
-            gs = [o.g for o in ost] if idx is None else full_g
-            check_norm(ng, coef, O.norm(gs, wl.gtype, wl.scale), wl.max_norm,
-                       f"{wl.name} {kind} t={t}")
-        O.opt_step_(ost, opt, wl.gtype, wl.mkind, wl.vkind, t, s=wl.scale,
-                    coef=coef, zero=zero)
-        compare_rule(arena, ost, kind, idx, f"{wl.name} {kind} t={t}")
-        if check_guards:
-            has_m, has_v = uses(kind)
-            for b in "wgmv":
-                sh = arena.g_shift if b == "g" else 0
-                inside = torch.zeros(arena.total, dtype=torch.bool,
-                                     device="cuda")
-                for o, n in zip(arena.offsets, wl.sizes):
-                    inside[o + sh:o + sh + n] = True
-                now = getattr(arena, b)
-                ity = torch.int32 if now.dtype == torch.float32 else \
-                    torch.int16
-                diff = now.view(ity) != before[b].view(ity)
-                if b in "wg" or (b == "m" and has_m) or (b == "v" and has_v):
-                    diff = diff & ~inside    # only inside its tensors
-                assert not bool(diff.any()), f"{kind}: {b} written outside"
-    L.close()
-    print(f"{wl.name} {kind} zero={zero}: {steps} steps bitwise",
-          flush=True)
 
 
 RULE_CASES = [(k, g) for k in ("adam", "sgd", "momentum") for g in (0, 1, 2)]
@@ -285,10 +160,10 @@ def test_state_buffer_checks():
     assert e.value.code == -1
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("kind", ["adam", "sgd", "momentum"])
-def test_full_gpt2_124m_rules_sampled(kind):
+def test_full_gpt2_124m_rules_every_element(kind):
     wl = WL.get("gpt2_124m")
     if kind != "adam":
         wl.weight_decay = 0.0
-    rule_lockstep(wl, opt_for(kind, zero=(kind == "momentum")), 3,
-                  nsample=1 << 18, norm_steps={1, 3})
+    rule_lockstep(wl, opt_for(kind, zero=(kind == "momentum")), 3)

@@ -2,8 +2,8 @@
 
 Every test here runs the hot path on the device -- mta_scale (deferred or
 in place), mta_clip_norm, mta_adamw_step -- and compares with the oracle
-element by element (lockstep protocol, see parity_util).  Small lists are
-compared in full; full-size lists at sampled positions plus the full norm.
+element by element (lockstep protocol, see parity_util).  Every list, the
+full-size workloads included, is compared on every element.
 """
 
 import numpy as np
@@ -344,22 +344,28 @@ def test_full_gpt2_124m_every_element():
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
-def test_full_gpt2_124m_bf16_grads_100_steps_sampled():
+@pytest.mark.timeout(600)
+def test_full_gpt2_124m_bf16_grads_100_steps_every_element():
+    # the oracle keeps the whole list in lockstep for all 100 steps; the
+    # norm is checked at every step and every element of w, m, v after
+    # steps 1, 2, 10, 20, ..., 100
     wl = WL.get("gpt2_124m_bf16g")
-    worst = lockstep(wl, wl.steps, nsample=1 << 18,
-                     norm_steps={1, 2, 3, 10, 50, 99, 100})
+    worst = lockstep(wl, wl.steps,
+                     compare_steps={1, 2} | set(range(10, 101, 10)))
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
-def test_full_gpt2_xl_packed_sampled():
+@pytest.mark.timeout(600)
+def test_full_gpt2_xl_packed_every_element():
     wl = WL.get("gpt2_xl")
-    worst = lockstep(wl, wl.steps, nsample=1 << 20)
+    worst = lockstep(wl, wl.steps)
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
-def test_full_ragged_sampled():
+@pytest.mark.timeout(600)
+def test_full_ragged_every_element():
     wl = WL.get("ragged")
-    worst = lockstep(wl, wl.steps, nsample=1 << 20)
+    worst = lockstep(wl, wl.steps)
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
@@ -466,12 +472,13 @@ def test_norm_keeps_the_last_256_mib_of_the_124m_list(monkeypatch):
     L.close()
 
 
-def test_full_gpt2_xl_shard_in_a_flat_buffer_sampled():
+@pytest.mark.timeout(300)
+def test_full_gpt2_xl_shard_in_a_flat_buffer_every_element():
     # one GPU's eighth of the 1.56B list, its 35 pieces back to back as a
     # sharded flat buffer holds them (pieces start at any element)
     wl = WL.get("gpt2_xl_shard0of8")
     offsets = [0]
     for n in wl.sizes[:-1]:
         offsets.append(offsets[-1] + n)
-    worst = lockstep(wl, wl.steps, offsets=offsets, nsample=1 << 20)
+    worst = lockstep(wl, wl.steps, offsets=offsets)
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
