@@ -7,6 +7,9 @@ A loss-scaled workload runs mta_amp_clip_norm, mta_amp_adamw_step and
 mta_amp_update (a one-thread launch) instead.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The default workload is gpt2_xl, the 1.56B-parameter list with packed
+bfloat16 moments: the largest of the workloads, and one that fits one GPU.
 """
 import argparse
 import hashlib
@@ -82,22 +85,70 @@ def update_bytes(wl, kind, zero, copy):
     return b + (gb if zero else 0) + (2 if copy else 0)
 
 
-def ceiling(wl, reps=10):
-    """Best HBM rates of the ceiling probes (libmta_probe.so: no optimizer
-    arithmetic) on buffers of the workload's size: a stream with the update's
-    exact bytes (read w, g, m, v; write w, m, v), a read-only stream, a
-    write-only stream and a copy, each over grids of 1, 2, 4 and 8
-    workgroups per CU (the write-only one also over half the CUs, where it
-    streams best).  serial_bound_gbs is the update's bytes with its reads at
-    the read-only rate and its writes at the write-only rate, one after the
-    other: what the update would reach if reads and writes never slowed each
-    other."""
+PROBE_LIB = os.path.join(ROOT, "bench_probes", "libmta_probe.so")
+
+
+def independent_ceiling(wl, reps=5):
+    """HBM rates of AMD- and PyTorch-owned kernels (none of this library's
+    code) on float32 buffers of the workload's parameter count, on the same
+    GPU: torch's fill_ (write only), Tensor.copy_ (a hipMemcpy device to
+    device), torch.add(a, b, out=c) (2 reads : 1 write) and
+    torch.addcmul(a, b, c, out=d) (3 : 1).  Best of `reps` launches after
+    two warm-ups, algorithmic bytes / event time."""
+    import torch
+    n = wl.n
+    bufs = [torch.ones(n, device="cuda") for _ in range(4)]
+    a, b, c, d = bufs
+    s = torch.cuda.current_stream()
+
+    def best(fn, nbytes):
+        for _ in range(2):
+            fn()
+        out = 0.0
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            out = max(out, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        return out
+
+    res = {
+        "fill_gbs": best(lambda: d.fill_(0.5), 4 * n),
+        "copy_gbs": best(lambda: d.copy_(a), 8 * n),
+        "add_gbs": best(lambda: torch.add(a, b, out=d), 12 * n),
+        "addcmul_gbs": best(lambda: torch.addcmul(a, b, c, out=d), 16 * n),
+    }
+    del bufs, a, b, c, d
+    torch.cuda.empty_cache()
+    out = {"kernels": "torch " + torch.__version__ + ": fill_, copy_ "
+                      "(hipMemcpy device to device), add(out=), "
+                      "addcmul(out=); float32 buffers of the workload's "
+                      "parameter count; best of %d launches" % reps}
+    for k, v in res.items():
+        out[k] = v
+        out[k.replace("_gbs", "_frac")] = v / HBM_PEAK_GBS
+    return out
+
+
+def probe_ceiling(wl, reps=10):
+    """Best HBM rates of this project's ceiling probes
+    (bench_probes/libmta_probe.so: no optimizer arithmetic) on buffers of
+    the workload's size: a stream with the update's exact bytes (read w, g,
+    m, v; write w, m, v), a read-only stream, a write-only stream and a
+    copy, each over grids of 1, 2, 4 and 8 workgroups per CU (the
+    write-only one also over half the CUs).  These share the update's lane
+    mapping, so they bound that design, not the device."""
     import ctypes
 
     import torch
 
-    from mixed_precision_optimizer_mta_amd import build as MB
-    P = ctypes.CDLL(MB.PROBE_LIB)
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is not built: python "
+                         "bench_probes/build.py")
+    P = ctypes.CDLL(PROBE_LIB)
     vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     P.mta_probe_mix.argtypes = [vp, vp, vp, vp, i64, c_int, c_int, c_int,
                                 c_int, vp]
@@ -149,8 +200,8 @@ def ceiling(wl, reps=10):
               per_cu=(0.5, 1, 2, 4))
     rbytes, wbytes = 4 + gb + mb + vb, 4 + mb + vb
     serial = (rbytes + wbytes) / (rbytes / rd[0] + wbytes / wr[0])
-    return {"probe": "libmta_probe.so, trivial arithmetic, best of 1/2/4/8 "
-                     "workgroups per CU",
+    return {"probe": "bench_probes/libmta_probe.so, trivial arithmetic, "
+                     "best of 1/2/4/8 workgroups per CU",
             "update_mix_gbs": mix[0], "update_mix_frac": mix[0] / HBM_PEAK_GBS,
             "update_mix_blocks_per_cu": mix[1],
             "read_gbs": rd[0], "read_frac": rd[0] / HBM_PEAK_GBS,
@@ -162,14 +213,28 @@ def ceiling(wl, reps=10):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family, model
+    and stepping (the latter three identify the generation when a virtual
+    machine shortens the name), and the logical CPUs this process may use
+    against those the machine shows."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                  # the first processor is enough
+                k, _, v = line.partition(":")
+                info[k.strip()] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return (f"{info.get('model name', 'unknown')} (family "
+            f"{info.get('cpu family', '?')}, model {info.get('model', '?')}, "
+            f"stepping {info.get('stepping', '?')}); {usable} of "
+            f"{os.cpu_count()} logical CPUs usable")
 
 
 def cpu_baseline_parallel(arena, wl, steps, threads):
@@ -329,21 +394,30 @@ def cpu_baseline(arena, wl, steps, opt=None):
                       f"{dt:.2f} s"}
 
 
-def main():
+def auto_cpu_steps(n):
+    """Whole oracle steps of the CPU baseline by default: about 20 s of one
+    host core at the oracle's ~3.4e8 params/s, at least 1, at most 60."""
+    return max(1, min(60, round(20 * 3.4e8 / n)))
+
+
+def make_parser():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--workload", default="gpt2_xl",
+                    help="default gpt2_xl: the 1.56B-parameter list, the "
+                         "largest workload that fits one GPU")
     ap.add_argument("--layout", default="padded", choices=["padded", "flat"],
                     help="padded: every tensor starts 16-byte aligned in "
                          "each buffer; flat: tensors back to back in one "
                          "buffer per kind, as a flat parameter / gradient "
                          "buffer holds them (a tensor may start anywhere)")
-    ap.add_argument("--cpu-steps", type=int, default=30,
-                    help="oracle steps of the CPU baseline (0 = skip); the "
-                         "default is about 11 s of one host core on the "
-                         "124M list")
+    ap.add_argument("--cpu-steps", type=int, default=None,
+                    help="oracle steps of the CPU baseline (0 = skip); by "
+                         "default as many whole steps as take about 20 s "
+                         "of one host core (4 on the 1.56B list, 55 on "
+                         "the 124M one), at least 1")
     ap.add_argument("--weight-copy", nargs="?", const="bf16", default=None,
                     choices=["bf16", "f16"],
                     help="also write a 16-bit copy (bfloat16 by default, or "
@@ -368,14 +442,10 @@ def main():
                          "to take no weight decay, in the same update "
                          "launch (mta_list_set_no_decay)")
     ap.add_argument("--torch-reference", action="store_true",
-                    help="insist on the PyTorch comparison (an error on a "
-                         "workload it cannot run); by default it runs on "
-                         "every float32-gradient AdamW workload: after the "
-                         "timed steps, PyTorch's own clip_grad_norm_ + "
-                         "AdamW(fused=True) on the same tensors, reported "
-                         "as torch_reference")
-    ap.add_argument("--no-torch-reference", action="store_true",
-                    help="skip the PyTorch comparison")
+                    help="after the timed steps, also time PyTorch's own "
+                         "clip_grad_norm_ + AdamW(fused=True) on the same "
+                         "tensors (float32-gradient AdamW workloads only), "
+                         "reported as torch_reference")
     ap.add_argument("--opt", default="adamw",
                     choices=["adamw", "adam", "sgd", "momentum"],
                     help="update rule (mta_step); adamw runs mta_adamw_step")
@@ -387,13 +457,22 @@ def main():
                          "replays (value and ms_per_step then come from the "
                          "replays; per-kernel times from the eager pass)")
     ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the HBM ceiling probes (the update's byte "
-                         "mix with trivial arithmetic, read-only, copy)")
+                    help="skip the independent ceiling (AMD- and "
+                         "PyTorch-owned kernels on buffers of the "
+                         "workload's size)")
+    ap.add_argument("--probes", action="store_true",
+                    help="also time this project's ceiling probes "
+                         "(bench_probes/libmta_probe.so, built by "
+                         "python bench_probes/build.py)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB, 5 times: "
                          "the known-size kernel that scales the HBM byte "
                          "counters of a profile")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = make_parser().parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU "
               "path (the step measured here is one GPU's; how it would shard "
@@ -439,7 +518,7 @@ def main():
         print("--torch-reference needs a plain AdamW step on float32 "
               "gradients", file=sys.stderr)
         sys.exit(2)
-    torch_ref = ref_ok and not args.no_torch_reference
+    torch_ref = args.torch_reference
     if args.graph and not wl.amp:
         print("--graph needs a loss-scaled workload (its step counter and "
               "scale live on the device, so a captured step can be "
@@ -671,18 +750,31 @@ def main():
     L.close()
     for x in norm_lists[1:] if len(norm_lists) > 1 else []:
         x.close()
-    if not args.no_ceiling and args.opt in ("adamw", "adam") and \
+    if not args.no_ceiling:
+        c = independent_ceiling(wl)
+        c["update_of_add"] = achieved / c["add_gbs"]
+        c["update_of_addcmul"] = achieved / c["addcmul_gbs"]
+        out["ceiling"] = c
+    if args.probes and args.opt in ("adamw", "adam") and \
             not args.zero_grad and not args.weight_copy:
-        c = ceiling(wl)
+        c = probe_ceiling(wl)
         c["update_of_mix"] = achieved / c["update_mix_gbs"]
         c["update_of_serial_bound"] = achieved / c["serial_bound_gbs"]
-        out["ceiling"] = c
-    if args.cpu_steps > 0:
-        out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)
+        out["probe_ceiling"] = c
+    cpu_steps = auto_cpu_steps(wl.n) if args.cpu_steps is None \
+        else args.cpu_steps
+    if cpu_steps > 0:
+        out["cpu_baseline"] = cpu_baseline(arena, wl, cpu_steps, opt)
         if not general and not wl.amp and not args.weight_copy:
-            threads = max(1, min(16, os.cpu_count() or 1))
+            # the GPU machines give one GPU's job 16 cores: the pool takes at
+            # most that many, and no more than this process may use
+            try:
+                usable = len(os.sched_getaffinity(0))
+            except (AttributeError, OSError):
+                usable = os.cpu_count() or 1
+            threads = max(1, min(16, usable))
             out["cpu_baseline_parallel"] = cpu_baseline_parallel(
-                arena, wl, args.cpu_steps, threads)
+                arena, wl, cpu_steps, threads)
     if torch_ref:
         out["torch_reference"] = torch_reference(arena, wl)
     print(json.dumps(out), flush=True)

@@ -1,6 +1,6 @@
 // mta_probe.hip -- HBM ceiling probes for the update's traffic mix.
 //
-// Measurement instruments, not part of the optimizer: bench.py --ceiling
+// Measurement instruments, not part of the optimizer: bench.py --probes
 // times them to show what a kernel with the same bytes as an update launch
 // can reach on this device when it does (almost) no arithmetic.  Each probe
 // streams whole 4096-element tiles with the same contiguous lane mapping as

@@ -18,9 +18,6 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmta.so")
 SOURCES = [os.path.join(CSRC, "mta_kernels.hip"),
            os.path.join(CSRC, "mta_host.cpp")]
-# HBM ceiling probes (measurement only; bench.py --ceiling loads them)
-PROBE_LIB = os.path.join(HERE, "libmta_probe.so")
-PROBE_SOURCES = [os.path.join(CSRC, "mta_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -33,9 +30,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
 
 
 def build(verbose=False):
-    """Compile libmta.so and the probe library; always recompiles.  Returns
-    libmta.so's path."""
-    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    """Compile libmta.so; always recompiles.  Returns its path."""
     return _compile(LIB, SOURCES, verbose)
 
 

@@ -80,3 +80,15 @@ def test_traffic_keys():
     assert bench.traffic_key(wl, "adamw", False) == "gpt2_124m"
     assert bench.traffic_key(wl, "adam", False) == "gpt2_124m+adam"
     assert bench.traffic_key(wl, "sgd", True) == "gpt2_124m+sgd+zero"
+
+
+def test_defaults_run_the_largest_single_gpu_workload():
+    args = bench.make_parser().parse_args([])
+    assert args.workload == "gpt2_xl"
+    assert (args.gpus, args.torch_reference, args.probes) == (1, False,
+                                                              False)
+    # about 20 s of one host core: 4 whole oracle steps of the 1.56B list,
+    # 55 of the 124M one
+    assert bench.auto_cpu_steps(WL.get("gpt2_xl").n) == 4
+    assert bench.auto_cpu_steps(WL.get("gpt2_124m").n) == 55
+    assert bench.auto_cpu_steps(WL.get("tiny").n) == 60
