@@ -362,11 +362,16 @@ constexpr int kAdamGroups = kTileElems / (kBlock * kAdamVec); // 4
 constexpr uint32_t kAdamStride = kBlock * kAdamVec;           // 1024
 
 // A workgroup issues every load of its tile as raw vectors first, then
-// unpacks and computes: no wait falls between a tile's loads.  The
-// compiler keeps the update at about 170-230 VGPRs, two workgroups per CU,
-// so each CU has two tiles' loads in flight while it computes (a variant
-// that kept it under 96 VGPRs, at up to five workgroups per CU, measured
-// slower).
+// unpacks and computes: no wait falls between a tile's loads.  At most two
+// workgroups run on a CU at a time, so each CU has about two tiles' loads
+// in flight while it computes.  The register count alone would let three
+// to six fit (130-150 VGPRs for the Adam family, fewer for SGD and
+// momentum); the launch reserves kUpdateLdsBytes of LDS per workgroup,
+// which no kernel touches, so that only two fit in a CU's 160 KiB.  Three
+// or four per CU measured 5-7% slower on the 1.56B-parameter and ragged
+// lists and 2-3% slower on the 124M ones; two is as fast or faster for
+// every rule.
+constexpr unsigned kUpdateLdsBytes = 64u << 10;
 
 // raw vectors of one lane's share of a full tile (4 accesses per buffer)
 template <int D>
@@ -1078,8 +1083,9 @@ __global__ void k_amp_update(mta_amp_state *__restrict__ st, double growth,
 template <int G, bool M, bool V, bool L2>
 hipError_t launch_adamw_t(const Work &wk, const StepScalars &sc,
                           const float *d_coef, const AmpStep &amp) {
-  hipLaunchKernelGGL((k_adamw<G, M, V, L2>), dim3(wk.grid), dim3(kBlock), 0,
-                     wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
+  hipLaunchKernelGGL((k_adamw<G, M, V, L2>), dim3(wk.grid), dim3(kBlock),
+                     kUpdateLdsBytes, wk.stream, wk.stiles, wk.ntiles, sc,
+                     d_coef, amp);
   return hipGetLastError();
 }
 
@@ -1106,13 +1112,15 @@ hipError_t launch_update_g(int rule, int mkind, int vkind, const Work &wk,
     case kRuleAdam:
       return launch_adamw_g<G, true>(mkind, vkind, wk, sc, d_coef, amp);
     case kRuleSgd:
-      hipLaunchKernelGGL((k_sgd<G>), dim3(wk.grid), dim3(kBlock), 0,
-                         wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
+      hipLaunchKernelGGL((k_sgd<G>), dim3(wk.grid), dim3(kBlock),
+                         kUpdateLdsBytes, wk.stream, wk.stiles, wk.ntiles, sc,
+                         d_coef, amp);
       return hipGetLastError();
     case kRuleMomentum:
       if (mkind != 0) return hipErrorInvalidValue;  // float32 buffer only
-      hipLaunchKernelGGL((k_momentum<G>), dim3(wk.grid), dim3(kBlock), 0,
-                         wk.stream, wk.stiles, wk.ntiles, sc, d_coef, amp);
+      hipLaunchKernelGGL((k_momentum<G>), dim3(wk.grid), dim3(kBlock),
+                         kUpdateLdsBytes, wk.stream, wk.stiles, wk.ntiles, sc,
+                         d_coef, amp);
       return hipGetLastError();
     default:
       return hipErrorInvalidValue;
