@@ -118,8 +118,9 @@ extern "C" {
  *    a caller built against version 1 passes a 64-byte struct, so check
  *    mta_abi_version() before calling mta_list_info or mta_list_plan).
  * 3: mta_list_set_no_decay.
- * 4: mta_scale_device. */
-#define MTA_ABI_VERSION 4
+ * 4: mta_scale_device.
+ * 5: mta_clip_norm_noalloc. */
+#define MTA_ABI_VERSION 5
 
 typedef struct mta_list mta_list; /* opaque */
 
@@ -280,6 +281,29 @@ int mta_scale_device(mta_list *list, const float *d_factor, void *stream);
  * mta_adamw_step.  max_norm must be > 0 (infinity allowed, NaN not). */
 int mta_clip_norm(mta_list *list, float max_norm, float *d_norm, float *d_coef,
                   void *stream);
+
+/* mta_clip_norm for callers that cannot allocate device memory (code that
+ * must not call hipMalloc: tight serving loops, harnesses that forbid it).
+ * No list handle: the gradients are described by the host array `tensors`
+ * (count >= 0 entries, checked as mta_list_create checks them; only g is
+ * read, and w, m, v may all be NULL), `scale` is the unscale factor s of
+ * mta_clip_norm (1 for none; finite), and the result is the norm and
+ * coefficient mta_clip_norm writes for the same gradients, bit for bit
+ * (same kernel, same launch shape).  The call allocates no device memory:
+ * its tile table and reduction scratch live in one device array of the
+ * library, 32 MiB, which each device the library runs on holds until the
+ * process ends; it holds the table of up to about 2.09 million tiles of
+ * 4096 elements (about 8.6e9 gradient elements in whole tiles), and a
+ * larger list returns MTA_EINVAL before any device work.  The call stages
+ * the table with copies on `stream`, launches the norm there and waits for
+ * all of it before returning (it is not for graph capture).  The array is
+ * shared by every call on a device and keeps the last call's contents:
+ * each call re-initializes what it reads, and the library serializes its
+ * calls within a process; calls from different processes use their own
+ * copies. */
+int mta_clip_norm_noalloc(const mta_tensor *tensors, int64_t count,
+                          int gtype, float scale, float max_norm,
+                          float *d_norm, float *d_coef, void *stream);
 
 /* ClipGradNorms over several lists: a single clip threshold applied to the
  * L2 norm taken jointly over every gradient of every list ("Mica 7.7",

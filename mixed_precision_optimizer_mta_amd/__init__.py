@@ -12,7 +12,7 @@ from ._binding import (  # noqa: F401
     MTA_SCALE_DEFER, MTA_SCALE_INPLACE, MTA_STEP_ZERO_GRAD, MtaError, lib,
     mta_abi_version, mta_adamw_scalars, mta_adamw_step, mta_amp_adamw_step,
     mta_amp_clip_norm, mta_amp_clip_norm_joint, mta_amp_step, mta_amp_update,
-    mta_clip_norm, mta_clip_norm_joint,
+    mta_clip_norm, mta_clip_norm_joint, mta_clip_norm_noalloc,
     mta_last_error, mta_list_create, mta_list_destroy, mta_list_info,
     mta_list_plan, mta_list_set_no_decay, mta_list_set_weight_copies,
     mta_list_set_weight_copies_as, mta_scale, mta_scale_device, mta_step)

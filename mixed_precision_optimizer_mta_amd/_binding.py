@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MTA_OK", -1: "MTA_EINVAL", -2: "MTA_EALIGN",
                 -6: "MTA_ESTATE"}
 
 # MTA_ABI_VERSION of include/mta.h that these structs mirror
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # every symbol include/mta.h declares
 EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
@@ -34,7 +34,8 @@ EXPORTS = ("mta_list_create", "mta_list_destroy", "mta_scale",
            "mta_amp_update", "mta_step", "mta_amp_step",
            "mta_list_set_weight_copies_as", "mta_list_plan",
            "mta_clip_norm_joint", "mta_amp_clip_norm_joint",
-           "mta_list_set_no_decay", "mta_scale_device")
+           "mta_list_set_no_decay", "mta_scale_device",
+           "mta_clip_norm_noalloc")
 
 
 class mta_tensor(ctypes.Structure):
@@ -123,6 +124,8 @@ def lib():
         L.mta_list_plan.argtypes = [ctypes.POINTER(mta_tensor), i64, c_int,
                                     c_int, c_int,
                                     ctypes.POINTER(mta_list_info_t)]
+        L.mta_clip_norm_noalloc.argtypes = [ctypes.POINTER(mta_tensor), i64,
+                                            c_int, f32, f32, vp, vp, vp]
         L.mta_amp_clip_norm.argtypes = [vp, f32, vp, vp, vp, vp]
         L.mta_amp_adamw_step.argtypes = [vp,
                                          ctypes.POINTER(mta_adamw_hparams),
@@ -202,6 +205,16 @@ def mta_scale_device(handle, d_factor, stream=0):
 def mta_clip_norm(handle, max_norm, d_norm, d_coef, stream=0):
     _check(lib().mta_clip_norm(handle, max_norm, d_norm, d_coef, stream),
            "mta_clip_norm")
+
+
+def mta_clip_norm_noalloc(tensors, gtype, scale, max_norm, d_norm, d_coef,
+                          stream=0):
+    """The allocation-free norm: tensors as for mta_list_create (only g is
+    read); d_norm (or None) and d_coef device pointers."""
+    arr = _tensor_table(tensors)
+    _check(lib().mta_clip_norm_noalloc(arr, len(tensors), gtype, scale,
+                                       max_norm, d_norm, d_coef, stream),
+           "mta_clip_norm_noalloc")
 
 
 def _handles(handles):

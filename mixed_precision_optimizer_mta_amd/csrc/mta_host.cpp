@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -973,6 +974,109 @@ int mta_adamw_step(mta_list *L, const mta_adamw_hparams *hp, int64_t t,
 int mta_step(mta_list *L, const mta_opt *opt, int64_t t, const float *d_coef,
              void *stream) {
   return step_common(L, opt, t, d_coef, nullptr, stream, "mta_step");
+}
+
+int mta_clip_norm_noalloc(const mta_tensor *tensors, int64_t count,
+                          int gtype, float scale, float max_norm,
+                          float *d_norm, float *d_coef, void *stream) {
+  // the checks of mta_clip_norm, on a tensor array instead of a list
+  if (!(max_norm > 0.0f))
+    return fail(MTA_EINVAL, "max_norm must be > 0 (got %g)",
+                static_cast<double>(max_norm));
+  if (!std::isfinite(scale))
+    return fail(MTA_EINVAL, "scale factor must be finite");
+  if (!d_coef) return fail(MTA_EINVAL, "d_coef is NULL");
+  if (!aligned(d_coef, 4) || (d_norm && !aligned(d_norm, 4)))
+    return fail(MTA_EALIGN, "d_norm / d_coef must be 4-byte aligned");
+  Plan plan;
+  try {
+    const int rc = plan_list(tensors, count, gtype, MTA_MOM_F32, MTA_MOM_F32,
+                             &plan);
+    if (rc) return rc;
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0)
+    return fail(MTA_EHIP, "cannot read the compute-unit count: %s",
+                hipGetErrorString(e));
+  // the launch shape of mta_clip_norm on the same tensors
+  const int64_t ntiles = static_cast<int64_t>(plan.gtiles.size());
+  const int bpc_n = env_int(
+      "MTA_NORM_BLOCKS_PER_CU",
+      gtype == MTA_F32 ? kNormBlocksPerCuF32 : kNormBlocksPerCu16, 1, 64);
+  const int grid = static_cast<int>(std::min<int64_t>(
+      std::max<int64_t>(1, ntiles), static_cast<int64_t>(cus) * bpc_n));
+  // scratch layout: ticket region, partial slots, gradient tile table
+  const size_t off_part = mta::kTicketBytes;
+  const size_t off_gt = round_up(off_part + sizeof(double) * grid, 256);
+  const size_t need = off_gt + sizeof(mta::GradTile) * plan.gtiles.size();
+  if (need > mta::kNoAllocScratchBytes)
+    return fail(MTA_EINVAL,
+                "the list needs %zu bytes of scratch; the allocation-free "
+                "norm has %zu (%lld tiles of %d elements here, at most %zu)",
+                need, mta::kNoAllocScratchBytes,
+                static_cast<long long>(ntiles), mta::kTileElems,
+                (mta::kNoAllocScratchBytes - off_gt) /
+                    sizeof(mta::GradTile));
+  void *base = nullptr;
+  e = mta::noalloc_scratch(dev, &base);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "the scratch's device address: %s",
+                hipGetErrorString(e));
+  std::vector<uint64_t> slots;
+  try {
+    slots.assign(static_cast<size_t>(grid), mta::kNormSlotEmpty);
+  } catch (const std::bad_alloc &) {
+    return fail(MTA_ENOMEM, "host allocation failed");
+  }
+  char *const b = static_cast<char *>(base);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // one call at a time per process: the scratch is shared by every call on
+  // a device, and each call waits for its own work before it returns
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lock(mu);
+  // the ticket counters and the running total start at zero, every partial
+  // slot empty (the array keeps whatever the last call left)
+  e = hipMemsetAsync(b, 0, mta::kTicketBytes, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(b + off_part, slots.data(),
+                       slots.size() * sizeof(uint64_t),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !plan.gtiles.empty())
+    e = hipMemcpyAsync(b + off_gt, plan.gtiles.data(),
+                       plan.gtiles.size() * sizeof(mta::GradTile),
+                       hipMemcpyHostToDevice, s);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "mta_clip_norm_noalloc: staging: %s",
+                hipGetErrorString(e));
+  mta::Work wk{};
+  wk.gtiles = reinterpret_cast<const mta::GradTile *>(b + off_gt);
+  wk.stiles = nullptr;
+  wk.ntiles = static_cast<uint32_t>(ntiles);
+  wk.keep_from = plan.keep_from;
+  wk.grid = grid;
+  wk.stream = s;
+  const mta::NormScratch scr{reinterpret_cast<double *>(b + off_part),
+                             reinterpret_cast<unsigned int *>(b), nullptr,
+                             nullptr};
+  e = mta::launch_sumsq(gtype, wk, scale, max_norm, scr, d_norm, d_coef,
+                        nullptr);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "mta_clip_norm_noalloc: launch failed: %s",
+                hipGetErrorString(e));
+  // the staging vectors die with this call, and the next call reuses the
+  // scratch: wait for this one's copies and kernel
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(MTA_EHIP, "mta_clip_norm_noalloc: kernel failed: %s",
+                hipGetErrorString(e));
+  return ok();
 }
 
 int mta_amp_clip_norm(mta_list *L, float max_norm, mta_amp_state *d_amp,

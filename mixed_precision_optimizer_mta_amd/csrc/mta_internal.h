@@ -131,4 +131,12 @@ hipError_t launch_amp_update(mta_amp_state *state, double growth,
                              double backoff, int32_t interval,
                              hipStream_t stream);
 
+// The allocation-free norm's scratch: a file-scope device array in
+// mta_kernels.hip of this many bytes (its ticket region, its partial
+// slots, then its gradient tile table).
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+// The device address of that array on the current device (taken with
+// hipGetSymbolAddress on the first call on each device, kept per device).
+hipError_t noalloc_scratch(int device, void **out);
+
 }  // namespace mta

@@ -57,6 +57,7 @@
 // are the explicit float64 fma of the norm's accumulation and of the
 // double-double power, which need to be accurate, not to follow a fixed
 // rounding sequence.
+#include <mutex>
 #include <type_traits>
 
 #include "mta_internal.h"
@@ -1181,6 +1182,34 @@ hipError_t launch_scale(int gtype, const Work &wk, float s,
     case kF16: return launch_scale_t<kF16>(wk, s, d_s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The scratch of mta_clip_norm_noalloc, for callers that cannot allocate
+// device memory: one copy per device, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only
+// the address hipGetSymbolAddress returns for the current device is ever
+// passed to a kernel or a copy.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(int device, void **out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void *ptr = nullptr;
+    const hipError_t e =
+        hipGetSymbolAddress(reinterpret_cast<void **>(&ptr),
+                            HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_amp_update(mta_amp_state *st, double growth, double backoff,

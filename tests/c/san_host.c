@@ -81,6 +81,23 @@ int main(void) {
           "clip");
     CHECK(mta_clip_norm_joint(NULL, 1, 1.0f, fake, fake + 1, NULL) ==
               MTA_EINVAL, "joint");
+    {
+      /* the allocation-free norm refuses before any HIP call */
+      mta_tensor bad = {NULL, addr(0x7f1000000000ull, 1), NULL, NULL, 64};
+      CHECK(mta_clip_norm_noalloc(&bad, 1, MTA_F32, 1.0f, 0.0f, fake,
+                                  fake + 1, NULL) == MTA_EINVAL,
+            "noalloc max_norm");
+      CHECK(mta_clip_norm_noalloc(&bad, 1, MTA_F32, 1.0f, 1.0f, fake, NULL,
+                                  NULL) == MTA_EINVAL, "noalloc coef");
+      CHECK(mta_clip_norm_noalloc(&bad, 1, MTA_F32, 1.0f, 1.0f, fake,
+                                  fake + 1, NULL) == MTA_EALIGN,
+            "noalloc g align");
+      CHECK(mta_clip_norm_noalloc(NULL, 1, MTA_F32, 1.0f, 1.0f, fake,
+                                  fake + 1, NULL) == MTA_EINVAL,
+            "noalloc NULL table");
+      CHECK(mta_clip_norm_noalloc(&bad, 1, 7, 1.0f, 1.0f, fake, fake + 1,
+                                  NULL) == MTA_EDTYPE, "noalloc gtype");
+    }
     CHECK(mta_adamw_step(NULL, &hp, 1, NULL, NULL) == MTA_EINVAL, "adamw");
     CHECK(mta_step(NULL, &o, 1, NULL, NULL) == MTA_EINVAL, "step");
     CHECK(mta_list_set_weight_copies(NULL, NULL, NULL) == MTA_EINVAL,

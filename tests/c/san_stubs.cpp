@@ -29,5 +29,6 @@ hipError_t launch_amp_update(mta_amp_state *, double, double, int32_t,
                              hipStream_t) {
   reached("launch_amp_update");
 }
+hipError_t noalloc_scratch(int, void **) { reached("noalloc_scratch"); }
 
 }  // namespace mta

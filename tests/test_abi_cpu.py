@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert M.mta_abi_version() == 4 == B.ABI_VERSION
+    assert M.mta_abi_version() == 5 == B.ABI_VERSION
     # the binding's mirror of mta_list_info_t has the header's size
     assert ctypes.sizeof(B.mta_list_info_t) == 72
 
