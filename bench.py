@@ -464,6 +464,11 @@ def make_parser():
                     help="also time this project's ceiling probes "
                          "(bench_probes/libmta_probe.so, built by "
                          "python bench_probes/build.py)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only time the independent ceiling (AMD- and "
+                         "PyTorch-owned kernels on buffers of the "
+                         "workload's size) and print it as one JSON line: "
+                         "a trace of this run holds those kernels alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB, 5 times: "
                          "the known-size kernel that scales the HBM byte "
@@ -498,8 +503,12 @@ def main():
                           "calibrate_copy_bytes_written": 4 * n,
                           "launches": 5}), flush=True)
         return
-    M.lib()
     wl = WL.get(args.workload)
+    if args.ceiling_only:
+        print(json.dumps({"workload": wl.name, "params": wl.n,
+                          "ceiling": independent_ceiling(wl)}), flush=True)
+        return
+    M.lib()
     if args.joint_norm > 1 and args.scale_inplace:
         print("--joint-norm with --scale-inplace is not measured",
               file=sys.stderr)
