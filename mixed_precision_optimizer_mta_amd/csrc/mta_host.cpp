@@ -41,6 +41,10 @@ struct mta_list {
   double *d_partials = nullptr;
   unsigned int *d_ticket = nullptr;
   double *d_acc = nullptr;  // running total of a norm over several lists
+  uint64_t *d_amp_cache = nullptr;  // loss-scaled step constants (kernels)
+  uint32_t amp_gen = 0;             // generation of amp_hp (1..255)
+  double amp_hp[3] = {0, 0, 0};     // lr, beta1, beta2 of the last
+                                    // loss-scaled step on this list
   int weight_copies = 0;  // tensors with an attached 16-bit copy
   int no_decay_tensors = 0;  // tensors flagged by mta_list_set_no_decay
   int copy_type = MTA_BF16;  // format of the copies: MTA_BF16 or MTA_F16
@@ -505,9 +509,20 @@ int step_common(mta_list *L, const mta_opt *o, int64_t t, const float *d_coef,
   mta::StepScalars sc = opt_scalars(*o, t);
   sc.s = (!d_amp && L->deferred) ? L->deferred_s : 1.0f;
   sc.copy_f16 = L->copy_type == MTA_F16 ? 1u : 0u;
-  const mta::AmpStep amp = d_amp
-      ? mta::AmpStep{d_amp, o->lr, o->beta1, o->beta2}
-      : mta::AmpStep{};
+  mta::AmpStep amp{};
+  if (d_amp) {
+    // a new generation whenever the constants' inputs change (the device
+    // cache is keyed by it and by t)
+    if (L->amp_gen == 0 || L->amp_hp[0] != o->lr ||
+        L->amp_hp[1] != o->beta1 || L->amp_hp[2] != o->beta2) {
+      L->amp_gen = L->amp_gen % 255 + 1;
+      L->amp_hp[0] = o->lr;
+      L->amp_hp[1] = o->beta1;
+      L->amp_hp[2] = o->beta2;
+    }
+    amp = mta::AmpStep{d_amp, o->lr, o->beta1, o->beta2, L->d_amp_cache,
+                       L->amp_gen};
+  }
   if (L->ntiles > 0) {
     const mta::Work wk = work_of(L, L->grid_update, stream);
     const hipError_t e = mta::launch_update(o->kind, L->gtype, L->mkind,
@@ -748,6 +763,8 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
   L->d_partials = reinterpret_cast<double *>(base + off_part);
   L->d_ticket = reinterpret_cast<unsigned int *>(base + off_ticket);
   L->d_acc = reinterpret_cast<double *>(base + off_ticket + mta::kAccOffset);
+  L->d_amp_cache =
+      reinterpret_cast<uint64_t *>(base + off_ticket + mta::kAmpCacheOffset);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   e = hipSuccess;

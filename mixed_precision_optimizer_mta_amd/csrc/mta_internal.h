@@ -116,7 +116,21 @@ static_assert(sizeof(mta_amp_state) == 24, "loss-scale state layout");
 struct AmpStep {
   const mta_amp_state *state;  // nullptr: constants come from the host
   double lr, beta1, beta2;
+  // The list's cache of the last step's t-dependent constants: two 64-bit
+  // words, each (tag << 32) | float32 bits, for nstep and bc2; the tag is
+  // (gen << 24) | (t mod 2^24).  gen (1..255, never 0) is the list's
+  // generation of (lr, beta1, beta2), bumped on the host whenever they
+  // change, so a tag names one set of constants and a word that starts
+  // zeroed never matches.
+  uint64_t *cache;
+  uint32_t gen;
 };
+
+// Where a list's amp constant cache sits in its ticket region.
+constexpr size_t kAmpCacheOffset = 1536;
+static_assert(kAmpCacheOffset >= kAccOffset + 8 &&
+                  kAmpCacheOffset + 16 <= kTicketBytes,
+              "amp cache inside the ticket region, clear of the rest");
 
 hipError_t launch_update(int rule, int gtype, int mkind, int vkind,
                          const Work &work, const StepScalars &sc,

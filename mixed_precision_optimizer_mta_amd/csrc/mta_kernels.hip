@@ -9,7 +9,7 @@
 //                 "Values that stay on the card"); with a loss-scale state it
 //                 also reports whether any unscaled gradient is not finite.
 //                 Launches over several lists chain through a float64
-//                 running total (one cap over the joint length of all).
+//                 running total (one threshold over the norm of all).
 //   k_adamw       AdamW over every (w, g, m, v) group (AdamWSteps, same
 //                 section), with the element arithmetic of "BendTorch
 //                 main.bend", section "Optimizers": adam_decay, adam_m, adam_v,
@@ -594,13 +594,43 @@ __device__ __forceinline__ void update_tile(
   if (amp.state) {
     // while the loads are in flight: the unscale factor, and for the Adam
     // family t and the two t-dependent constants, from the device state,
-    // formed in float64 as the host forms them
+    // formed in float64 as the host forms them.  Every workgroup of a
+    // launch needs the same two constants; the first ones to run form them
+    // (a few hundred float64 operations per lane) and leave them in the
+    // list's cache, tagged with
+    // the hyperparameters' generation and t; later workgroups find them
+    // there.  Each cache word carries its own tag, so a word is used only
+    // when it holds this step's value, and a word not yet visible here (a
+    // store from another XCD, or one still in flight) only means forming
+    // the constants again.  The accesses are therefore workgroup-scope
+    // atomics (plain loads and stores through this XCD's L2, never torn):
+    // agent-scope ones go past the L2 to memory and made every workgroup
+    // wait, 9% of the update on the 124M float16 list.
     if constexpr (kUsesV<R>) {
       const int64_t step = amp.state->step + 1;
-      const double q1 = 1.0 - pow_rn(amp.beta1, step);
-      const double q2 = 1.0 - pow_rn(amp.beta2, step);
-      sc.nstep = -static_cast<float>(amp.lr / q1);
-      sc.bc2 = static_cast<float>(sqrt(q2));
+      const uint64_t tag =
+          (uint64_t{amp.gen} << 24) | (static_cast<uint64_t>(step) & 0xFFFFFFu);
+      const uint64_t a = __hip_atomic_load(amp.cache, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint64_t b = __hip_atomic_load(amp.cache + 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+      if ((a >> 32) == tag && (b >> 32) == tag) {
+        sc.nstep = __uint_as_float(static_cast<uint32_t>(a));
+        sc.bc2 = __uint_as_float(static_cast<uint32_t>(b));
+      } else {
+        const double q1 = 1.0 - pow_rn(amp.beta1, step);
+        const double q2 = 1.0 - pow_rn(amp.beta2, step);
+        sc.nstep = -static_cast<float>(amp.lr / q1);
+        sc.bc2 = static_cast<float>(sqrt(q2));
+        if (threadIdx.x == 0) {
+          __hip_atomic_store(amp.cache,
+                             (tag << 32) | __float_as_uint(sc.nstep),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_store(amp.cache + 1,
+                             (tag << 32) | __float_as_uint(sc.bc2),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
     }
     sc.s = inv_scale(amp.state->scale);
   }

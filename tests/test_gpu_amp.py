@@ -243,3 +243,40 @@ def test_full_gpt2_124m_f16amp_every_element():
     del arena
     worst = lockstep(wl, wl.steps, inject=inject)
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
+def test_amp_constants_follow_the_hyperparameters_at_one_step_count():
+    # the update keeps the last step's t-dependent constants in a per-list
+    # cache keyed by t and by the generation of (lr, beta1, beta2): two
+    # loss-scaled steps at the same t (no mta_amp_update between them) with
+    # different lr, then with different betas, each match the oracle's
+    # amp_step_ with its own hyperparameters; a list of 600 tiles, so many
+    # workgroups read the cache within each launch
+    from mixed_precision_optimizer_mta_amd import AmpState
+    wl = WL.Workload("amp_cache", [4096 * 600 + 3, 77], WL.F16,
+                     WL.MOM_BF16X2, WL.MOM_F32, steps=1, g_mult=1024.0,
+                     amp=True, amp_scale=1024.0, ident=24)
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_weights()
+    arena.fill_grads(1)
+    ost = oracle_state(arena)
+    L = make_list(arena)
+    amp_d, amp_o = AmpState(1024.0), O.AmpState(1024.0)
+    cd = torch.zeros(1, device="cuda")
+    for hp in (dict(lr=3e-4, beta1=0.9, beta2=0.999),
+               dict(lr=1e-3, beta1=0.9, beta2=0.999),
+               dict(lr=1e-3, beta1=0.8, beta2=0.99),
+               dict(lr=1e-3, beta1=0.8, beta2=0.99)):
+        h = dict(hp, eps=1e-8, weight_decay=0.1)
+        L.amp_clip_norm(1.0, amp_d, None, cd)
+        L.amp_adamw_step(h, amp_d, cd)
+        torch.cuda.synchronize()
+        _, _, found = O.amp_step_(ost, wl.gtype, wl.mkind, wl.vkind, amp_o,
+                                  h["lr"], h["beta1"], h["beta2"], h["eps"],
+                                  h["weight_decay"], 1.0,
+                                  coef=np.float32(cd.item()))
+        assert not found
+        assert compare(arena, ost, what=str(hp)) == {"w": 0, "m": 0, "v": 0}
+    # the step counter was never advanced: every step above ran at t = 1
+    check_amp_state(amp_d.read(), amp_o, "no update")
+    L.close()
