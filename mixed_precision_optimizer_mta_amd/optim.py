@@ -55,9 +55,13 @@ Every step of the arithmetic runs in libmta.  Parameters are float32 CUDA
 tensors (with master_weights, also bfloat16 or float16 ones); gradients are
 float32, bfloat16 or float16, a 16-bit parameter's in its own dtype.  The
 device tables
-are rebuilt whenever a parameter, gradient or state buffer moved
-(``zero_grad(set_to_none=True)`` lets PyTorch reallocate gradients;
-``zero_grad=True`` here instead zeroes them inside the update launch).
+are rebuilt whenever a parameter, gradient or state buffer moved.  This
+class's ``zero_grad()`` therefore zeroes gradients in place by default
+(``set_to_none=False``), so a plain ``backward(); step(); zero_grad()`` loop
+keeps one plan; ``zero_grad(set_to_none=True)`` lets PyTorch reallocate
+the gradients and costs a rebuild at the next step, and ``zero_grad=True``
+in the constructor zeroes them inside the update launch instead.
+``tables_built`` counts the device tables built so far.
 ``load_state_dict`` keeps every state tensor in the dtype it was saved in
 (PyTorch's default would cast float32 masters and moments to a 16-bit
 parameter's dtype).
@@ -105,6 +109,7 @@ class MtaOptimizer(torch.optim.Optimizer):
         self._lists = {}       # (groups, grad dtype) -> (key, MtaList)
         self._norm_cache = {}  # grad dtype -> (pointer key, MtaList)
         self._plan = None      # see step()
+        self.tables_built = 0  # device tables built (list handles made)
         self.last_norm = None
         self.last_coef = None
         self.amp = None
@@ -120,6 +125,15 @@ class MtaOptimizer(torch.optim.Optimizer):
             self.loss_scale = self.amp.buf.view(torch.float32)[:1]
             self._amp_rule = (float(growth_factor), float(backoff_factor),
                               int(growth_interval))
+
+    def zero_grad(self, set_to_none: bool = False):
+        """PyTorch's zero_grad, with set_to_none False by default: every
+        gradient keeps its storage and is zeroed in place, so the next step
+        finds the gradients at the addresses its plan holds and reuses it.
+        With set_to_none=True the next backward allocates new gradients and
+        the next step builds new device tables (a device allocation, an
+        upload and a wait on the host), as any address change does."""
+        super().zero_grad(set_to_none=set_to_none)
 
     # -- state buffers ----------------------------------------------------
     def master(self, p):
@@ -190,6 +204,7 @@ class MtaOptimizer(torch.optim.Optimizer):
             if cached is not None:
                 cached[1].close()
             mk = B.MTA_MOM_BF16X2 if self.packed else B.MTA_MOM_F32
+            self.tables_built += 1
             L = MtaList([], entries=[(w.data_ptr(), g.data_ptr(),
                                       None if m is None else m.data_ptr(),
                                       None if v is None else v.data_ptr(),
@@ -245,6 +260,7 @@ class MtaOptimizer(torch.optim.Optimizer):
             if cached is None or cached[0] != key:
                 if cached is not None:
                     cached[1].close()
+                self.tables_built += 1
                 L = MtaList([], entries=[(w.data_ptr(), p.grad.data_ptr(),
                                           None, None, p.numel())
                                          for w, p in zip(ws, ps)],

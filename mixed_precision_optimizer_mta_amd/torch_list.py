@@ -218,10 +218,17 @@ def clip_norm_joint(lists, max_norm, norm_out, coef_out, amp=None):
 
 
 class GradClipper:
-    """PyTorch's clip_grad_norm_ on the device, for gradients an optimizer
-    of another kind will read: the joint L2 norm of every gradient, the
+    """Gradient clipping on the device, for gradients an optimizer of
+    another kind will read: the joint L2 norm of every gradient, the
     coefficient min(1, max_norm / (norm + 1e-6)) and every gradient scaled by
-    it in place (ClipGradNorms measured, decided and scaled on the card).
+    it in place (ClipGradNorms with the norm, the coefficient and the scaling
+    all on the device).  For float32 gradients this is PyTorch's
+    clip_grad_norm_ (same coefficient rule, in float32).  For bfloat16 and
+    float16 gradients the norm here is the float64-accumulated norm of the
+    exact values, rounded once to float32, while PyTorch's clip_grad_norm_
+    forms per-tensor norms and the total in the gradients' own dtype; the
+    two can then differ by about one ulp of that 16-bit dtype, and so can
+    the coefficients.
     One gradient-only list per gradient dtype (built once, on the first call
     and again whenever a gradient moves); a call launches one norm per list
     (chained to a joint norm) and one in-place scale per list, and reads

@@ -738,3 +738,31 @@ def test_works_under_torch_grad_scaler():
             if t == 3:
                 assert torch.equal(pa.detach(), p0), "overflow step taken"
             torch.testing.assert_close(pa, pb, rtol=1e-5, atol=1e-7)
+
+
+def test_default_zero_grad_loop_keeps_one_plan():
+    # the plain PyTorch loop: backward, step, zero_grad() with the default
+    # arguments.  The optimizer's zero_grad zeroes in place by default, so
+    # the gradients keep their addresses and every step after the first
+    # reuses the device tables; set_to_none=True reallocates them and costs
+    # a rebuild at the next step
+    from mixed_precision_optimizer_mta_amd import MtaOptimizer
+    model = _model()
+    opt = MtaOptimizer(model.parameters(), kind="adamw", lr=1e-3,
+                       weight_decay=0.01, max_norm=1.0)
+    x = torch.randn(64, 300, device="cuda")
+    y = torch.randint(0, 10, (64,), device="cuda")
+    for _ in range(6):
+        torch.nn.functional.cross_entropy(model(x), y).backward()
+        opt.step()
+        opt.zero_grad()
+    torch.cuda.synchronize()
+    built = opt.tables_built            # the update list and the norm list
+    assert built == 2, built
+    assert all(p.grad is not None and not p.grad.any()
+               for p in model.parameters())
+    opt.zero_grad(set_to_none=True)
+    torch.nn.functional.cross_entropy(model(x), y).backward()
+    opt.step()
+    torch.cuda.synchronize()
+    assert opt.tables_built == built + 2
