@@ -97,9 +97,9 @@
  * "Mica 7.7", section "The card a program uses", where an invalid card
  * number stops the program at its start).  A fault inside a kernel is
  * asynchronous: work is queued on the caller's stream, and a failure of a
- * queued kernel is reported by the caller's next act that waits on it
- * (section "Upgrading": a queued kernel's failure surfaces at the next
- * waiting act).  With the environment variable MTA_DEBUG_SYNC=1 every call
+ * queued kernel is reported when the caller next synchronizes with that
+ * stream (section "Upgrading": in an optimizing build such a failure
+ * surfaces when the program next waits on the device).  With the environment variable MTA_DEBUG_SYNC=1 every call
  * that launches work waits for it before returning, so a kernel failure is
  * reported, as MTA_EHIP, by the call that launched it (section "Kernels
  * ready at the start": the debug tier waits for each kernel so the failure

@@ -200,8 +200,9 @@ void mto_scale_tensor(int64_t n, void *g, int gtype, float s) {
 }
 
 /* ---------------------------------------------------------------------- */
-/* joint sum of squares (Mica: ClipGradNorms, "one cap over the joint     */
-/* length").  x = f32(g * s) is the unscaled gradient; x*x is exact in    */
+/* joint sum of squares (Mica: ClipGradNorms, a single clip threshold    */
+/* over the norm of all gradients).  x = f32(g * s) is the unscaled       */
+/* gradient; x*x is exact in                                               */
 /* float64, and the running sum carries a Neumaier compensation term, so  */
 /* the result is the exact sum up to a few float64 roundings.             */
 /* state[0] = running sum, state[1] = compensation; call once per tensor  */
@@ -242,7 +243,7 @@ float mto_clip_coef(float max_norm, float norm) {
 /* ---------------------------------------------------------------------- */
 /* AdamW over one tensor (BendTorch: adam_decay, adam_m, adam_v, adam_w;  */
 /* adamh_l for packed m and v, adamhv_l for packed m with float32 v;       */
-/* Mica: each group is updated exactly as AdamWStep updates it alone).     */
+/* Mica: the multi-tensor step leaves each group as AdamWStep would).    */
 /* sc = {step, bc2, c1, c2, b2, eps, dec} from mto_scalars.                */
 /* A packed moment is rounded to bfloat16 and the weight update reads the  */
 /* stored, rounded value.  The gradient is read, never written.            */

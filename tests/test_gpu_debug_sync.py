@@ -2,7 +2,7 @@
 work is done, so a kernel failure is reported by the call that launched it
 ("Mica 7.7", section "Kernels ready at the start": the debug tier waits for
 each kernel; section "Upgrading": without it a queued kernel's failure
-surfaces at the next act that waits).  The variable is read once per
+surfaces when the program next waits on the device).  The variable is read once per
 process, so each setting runs in a child process (tests/debug_sync_child.py)
 that checks, after each call, whether the caller's stream is already idle,
 and checks the results against the oracle.  Nothing here faults: the

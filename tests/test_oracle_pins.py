@@ -379,7 +379,7 @@ def test_adamw_against_torch_cpu():
 
 
 # ---------------------------------------------------------------------------
-# joint norm and clip (Mica: ClipGradNorms, "one cap over the joint length")
+# joint norm and clip (Mica: ClipGradNorms, one threshold over the joint norm)
 # ---------------------------------------------------------------------------
 
 def test_norm_is_exact_sum_of_squares():
