@@ -581,42 +581,55 @@ __device__ __forceinline__ void update_tile(
   const uint32_t e0 = threadIdx.x * kAdamVec;
   const StepTile rec = tiles[t];
   // loss-scaled step: skipped when an unscaled gradient was not finite
-  // (zeroing the gradients still happens when asked)
-  if (amp.state && amp.state->found_inf != 0.0f) {
-    if (sc.zero) zero_grad_tile<G>(rec, e0);
-    return;
+  // (zeroing the gradients still happens when asked).  The state is read
+  // before any of the tile's traffic.
+  float lscale = 1.0f;
+  int64_t step = 0;
+  if (amp.state) {
+    if (amp.state->found_inf != 0.0f) {
+      if (sc.zero) zero_grad_tile<G>(rec, e0);
+      return;
+    }
+    lscale = amp.state->scale;
+    step = amp.state->step + 1;
   }
+  // For the Adam family, t and the two t-dependent constants come from the
+  // device state, formed in float64 as the host forms them.  Every
+  // workgroup of a launch needs the same two constants; the first ones to
+  // run form them (a few hundred float64 operations per lane) and leave
+  // them in the list's cache, tagged with the hyperparameters' generation
+  // and t; later workgroups find them there.  Each cache word carries its
+  // own tag, so a word is used only when it holds this step's value, and a
+  // word not yet visible here (a store from another XCD, or one still in
+  // flight) only means forming the constants again.  The accesses are
+  // therefore workgroup-scope atomics (plain loads and stores through this
+  // XCD's L2, never torn): agent-scope ones go past the L2 to memory and
+  // made every workgroup wait, 9% of the update on the 124M float16 list.
+  // The two cache loads are issued before the tile's loads: loads return in
+  // order, so waiting for them later does not wait for the tile.
+  uint64_t cache_a = 0, cache_b = 0;
+  if constexpr (kUsesV<R>) {
+    if (amp.state) {
+      cache_a = __hip_atomic_load(amp.cache, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+      cache_b = __hip_atomic_load(amp.cache + 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const float coef = d_coef ? *d_coef : 1.0f;
   const Ref cur = tile_ref<G, MPacked, VPacked>(rec);
   TileRegs<R, G, MPacked, VPacked> X;
   if (cur.full) issue_tile(X, cur, e0);
   __builtin_amdgcn_sched_barrier(0);  // every load in flight first
   if (amp.state) {
-    // while the loads are in flight: the unscale factor, and for the Adam
-    // family t and the two t-dependent constants, from the device state,
-    // formed in float64 as the host forms them.  Every workgroup of a
-    // launch needs the same two constants; the first ones to run form them
-    // (a few hundred float64 operations per lane) and leave them in the
-    // list's cache, tagged with
-    // the hyperparameters' generation and t; later workgroups find them
-    // there.  Each cache word carries its own tag, so a word is used only
-    // when it holds this step's value, and a word not yet visible here (a
-    // store from another XCD, or one still in flight) only means forming
-    // the constants again.  The accesses are therefore workgroup-scope
-    // atomics (plain loads and stores through this XCD's L2, never torn):
-    // agent-scope ones go past the L2 to memory and made every workgroup
-    // wait, 9% of the update on the 124M float16 list.
+    // while the tile's loads are in flight
     if constexpr (kUsesV<R>) {
-      const int64_t step = amp.state->step + 1;
-      const uint64_t tag =
-          (uint64_t{amp.gen} << 24) | (static_cast<uint64_t>(step) & 0xFFFFFFu);
-      const uint64_t a = __hip_atomic_load(amp.cache, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-      const uint64_t b = __hip_atomic_load(amp.cache + 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-      if ((a >> 32) == tag && (b >> 32) == tag) {
-        sc.nstep = __uint_as_float(static_cast<uint32_t>(a));
-        sc.bc2 = __uint_as_float(static_cast<uint32_t>(b));
+      const uint64_t tag = (uint64_t{amp.gen} << 24) |
+                           (static_cast<uint64_t>(step) & 0xFFFFFFu);
+      if ((cache_a >> 32) == tag && (cache_b >> 32) == tag) {
+        sc.nstep = __uint_as_float(static_cast<uint32_t>(cache_a));
+        sc.bc2 = __uint_as_float(static_cast<uint32_t>(cache_b));
       } else {
         const double q1 = 1.0 - pow_rn(amp.beta1, step);
         const double q2 = 1.0 - pow_rn(amp.beta2, step);
@@ -632,7 +645,7 @@ __device__ __forceinline__ void update_tile(
         }
       }
     }
-    sc.s = inv_scale(amp.state->scale);
+    sc.s = inv_scale(lscale);
   }
   // a tensor flagged no-decay takes the step's constants for
   // weight_decay = 0: dec = f32(1 - lr*0) = 1 (AdamW), l2 = 0 (Adam)
