@@ -341,7 +341,8 @@ def torch_reference(arena, wl, steps=100, warmup=10):
 
 def cpu_baseline(arena, wl, steps, opt=None):
     """The oracle as it stands (single thread) on host copies of the same
-    list: `steps` whole steps (norm + update)."""
+    list: `steps` whole steps (norm + update), or, with steps None, as many
+    as cpu_steps_after() picks from the first step's time."""
     import numpy as np
     import torch
 
@@ -367,7 +368,9 @@ def cpu_baseline(arena, wl, steps, opt=None):
                                    opt["zero_grad"])
     zero = bool(opt and opt["zero_grad"])
     t0 = time.perf_counter()
-    for t in range(1, steps + 1):
+    t = 0
+    while steps is None or t < steps:
+        t += 1
         if general and amp is not None:
             O.amp_opt_step_(ts, opt, wl.gtype, wl.mkind, wl.vkind, amp,
                             wl.max_norm, zero=zero)
@@ -384,9 +387,11 @@ def cpu_baseline(arena, wl, steps, opt=None):
             O.step_(ts, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
                     wl.beta2, wl.eps, wl.weight_decay, t, s=wl.scale,
                     max_norm=wl.max_norm)
+        if steps is None:
+            steps = cpu_steps_after(time.perf_counter() - t0)
     dt = time.perf_counter() - t0
     return {"value": wl.n * steps / dt, "unit": "params/s", "cores": 1,
-            "kind": "oracle", "cpu": cpu_model(),
+            "kind": "oracle", "cpu": cpu_model(), "steps": steps,
             "sample": f"{steps} whole steps (joint norm + clip + "
                       f"{opt['kind'] if opt else 'adamw'} update"
                       f"{' + loss-scale update' if amp else ''}) of "
@@ -394,10 +399,13 @@ def cpu_baseline(arena, wl, steps, opt=None):
                       f"{dt:.2f} s"}
 
 
-def auto_cpu_steps(n):
-    """Whole oracle steps of the CPU baseline by default: about 20 s of one
-    host core at the oracle's ~3.4e8 params/s, at least 1, at most 60."""
-    return max(1, min(60, round(20 * 3.4e8 / n)))
+def cpu_steps_after(first_s, target_s=20.0):
+    """Whole oracle steps of the CPU baseline by default, given the first
+    step's time: about target_s of one host core in all, at least 1 (the
+    step already taken), at most 60.  The oracle's rate depends on the
+    list's kinds (packed 16-bit moments cost it about 3x per parameter), so
+    the count is taken from the list itself rather than from its size."""
+    return max(1, min(60, round(target_s / max(first_s, 1e-9))))
 
 
 def make_parser():
@@ -416,7 +424,8 @@ def make_parser():
     ap.add_argument("--cpu-steps", type=int, default=None,
                     help="oracle steps of the CPU baseline (0 = skip); by "
                          "default as many whole steps as take about 20 s "
-                         "of one host core (4 on the 1.56B list, 55 on "
+                         "of one host core, counted from the first step's "
+                         "time (1 on the 1.56B packed list, about 55 on "
                          "the 124M one), at least 1")
     ap.add_argument("--weight-copy", nargs="?", const="bf16", default=None,
                     choices=["bf16", "f16"],
@@ -770,10 +779,9 @@ def main():
         c["update_of_mix"] = achieved / c["update_mix_gbs"]
         c["update_of_serial_bound"] = achieved / c["serial_bound_gbs"]
         out["probe_ceiling"] = c
-    cpu_steps = auto_cpu_steps(wl.n) if args.cpu_steps is None \
-        else args.cpu_steps
-    if cpu_steps > 0:
-        out["cpu_baseline"] = cpu_baseline(arena, wl, cpu_steps, opt)
+    if args.cpu_steps is None or args.cpu_steps > 0:
+        out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)
+        cpu_steps = out["cpu_baseline"]["steps"]
         if not general and not wl.amp and not args.weight_copy:
             # the GPU machines give one GPU's job 16 cores: the pool takes at
             # most that many, and no more than this process may use

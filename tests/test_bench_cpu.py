@@ -87,8 +87,23 @@ def test_defaults_run_the_largest_single_gpu_workload():
     assert args.workload == "gpt2_xl"
     assert (args.gpus, args.torch_reference, args.probes) == (1, False,
                                                               False)
-    # about 20 s of one host core: 4 whole oracle steps of the 1.56B list,
-    # 55 of the 124M one
-    assert bench.auto_cpu_steps(WL.get("gpt2_xl").n) == 4
-    assert bench.auto_cpu_steps(WL.get("gpt2_124m").n) == 55
-    assert bench.auto_cpu_steps(WL.get("tiny").n) == 60
+    assert args.cpu_steps is None
+    # about 20 s of one host core, from the first step's time: a 14 s step
+    # (the 1.56B packed list) is the whole sample, a 0.36 s one (the 124M
+    # list) gives 56, a tiny list stops at 60
+    assert bench.cpu_steps_after(14.4) == 1
+    assert bench.cpu_steps_after(30.0) == 1
+    assert bench.cpu_steps_after(0.36) == 56
+    assert bench.cpu_steps_after(1e-4) == 60
+
+
+def test_cpu_baseline_default_sample_is_timed_from_the_first_step():
+    wl = WL.get("tiny")
+    arena = WL.Arena(wl, "cpu")
+    arena.fill_weights()
+    arena.fill_grads(1)
+    r = bench.cpu_baseline(arena, wl, None)
+    assert 1 <= r["steps"] <= 60 and r["cores"] == 1
+    assert r["sample"].startswith(f"{r['steps']} whole steps")
+    r = bench.cpu_baseline(arena, wl, 3)
+    assert r["steps"] == 3
