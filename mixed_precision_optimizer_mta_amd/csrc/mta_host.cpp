@@ -100,16 +100,19 @@ constexpr int kNormBlocksPerCu16 = 2;
 
 // Gradient bytes, at the end of the list, that the norm reads with
 // allocating loads so that the memory-side cache (256 MiB on MI355X) still
-// holds them when the update reads them again; the update's own accesses
-// stream past it.  Only while the update moves at most kNormKeepReachMiB
-// before it reaches those tiles (its w, g, m, v traffic over the tiles
-// before them): the kept lines survive about 2 GB of it (124M float32
-// list, 1.6 GB: they hit; one eighth of the 1.56B list, 2.6 GB: they no
-// longer do, and the allocating loads only slow the norm).
+// holds them when the update reads them again.  The update's full tiles
+// stream past that cache (their accesses carry the nontemporal hint), so the
+// kept lines survive however far it walks before reaching them: 1.6 GB on
+// the 124M float32 list, 31 GB on the 1.56B one.  What evicts them is the
+// update's element path (tail tiles and tensors off 16-byte alignment, read
+// and written with plain, allocating accesses): tiles are kept only while
+// that traffic before the kept tiles stays under kNormKeepElemMiB, a
+// quarter of the cache.  The 10,002-tensor list, with 240 MB of it, loses
+// 2.4% when keeping; the GPT-2 lists (under 10 MB) gain 0.4-5%.
 // MTA_NORM_KEEP_MIB sets the budget for any list at list creation (0:
 // every norm load streams).
 constexpr int kNormKeepMiB = 256;
-constexpr int64_t kNormKeepReachMiB = 2048;
+constexpr int64_t kNormKeepElemMiB = 64;
 
 int after_launch(hipError_t e, hipStream_t stream, const char *what) {
   if (e != hipSuccess)
@@ -659,22 +662,24 @@ int plan_list(const mta_tensor *tensors, int64_t count, int gtype, int mkind,
     uint64_t budget =
         static_cast<uint64_t>(keep_mib >= 0 ? keep_mib : kNormKeepMiB) << 20;
     keep_from = static_cast<uint32_t>(gtiles.size());
-    uint64_t kept_elems = 0;
     while (keep_from > 0) {
       const uint64_t bytes = uint64_t{gtiles[keep_from - 1].lim} * gsz;
       if (bytes > budget) break;
       budget -= bytes;
-      kept_elems += gtiles[keep_from - 1].lim;
       --keep_from;
     }
     // the update's bytes per element: w read and written, g, and m and v
     // read and written when the list has them
     const uint64_t upd = 8 + gsz + (state < 0 || (state & 1) ? 2 * msz : 0) +
                          (state < 0 || (state & 2) ? 2 * vsz : 0);
-    const uint64_t reach =
-        (static_cast<uint64_t>(elements) - kept_elems) * upd;
+    // elements the update takes on its element path before the kept tiles
+    uint64_t elem_path = 0;
+    for (uint32_t i = 0; i < keep_from; ++i)
+      if (!(stiles[i].flags & mta::kTileVec) ||
+          stiles[i].lim != static_cast<uint32_t>(mta::kTileElems))
+        elem_path += stiles[i].lim;
     if (keep_mib < 0 &&
-        reach > static_cast<uint64_t>(kNormKeepReachMiB) << 20)
+        elem_path * upd > static_cast<uint64_t>(kNormKeepElemMiB) << 20)
       keep_from = static_cast<uint32_t>(gtiles.size());
   } catch (const std::bad_alloc &) {
     return fail(MTA_ENOMEM, "host allocation failed");

@@ -79,21 +79,22 @@ def test_a_state_buffer_alone_can_block_the_vector_path():
 
 def _kept(sizes, gtype, mkind, vkind):
     """The norm's kept tiles of a padded list, from the tile lengths: the
-    last tiles whose gradients fit 256 MiB, provided the update moves at
-    most 2 GiB (w, g, m, v, read and written) before it reaches them."""
+    last tiles whose gradients fit 256 MiB, provided the update's element
+    path (here the tail tiles shorter than 4096) before them moves at most
+    64 MiB (w, g, m, v, read and written)."""
     lims = []
     for n in sizes:
         lims += [4096] * (n // 4096) + ([n % 4096] if n % 4096 else [])
     gsz = 4 if gtype == 0 else 2
-    budget, k, elems = 256 << 20, 0, 0
+    budget, k = 256 << 20, 0
     for lim in reversed(lims):
         if lim * gsz > budget:
             break
         budget -= lim * gsz
         k += 1
-        elems += lim
     upd = 8 + gsz + 2 * (2 if mkind else 4) + 2 * (2 if vkind else 4)
-    return 0 if (sum(sizes) - elems) * upd > 2 << 30 else k
+    tails = sum(lim for lim in lims[:len(lims) - k] if lim < 4096)
+    return 0 if tails * upd > 64 << 20 else k
 
 
 @pytest.mark.parametrize("name", ["gpt2_124m", "gpt2_124m_bf16g", "gpt2_xl",
@@ -110,15 +111,36 @@ def test_kept_tiles_follow_the_budget(name, monkeypatch):
     assert info["vector_tensors"] == sum(1 for n in wl.sizes if n)
     assert info["norm_kept_tiles"] == _kept(wl.sizes, wl.gtype, wl.mkind,
                                             wl.vkind)
-    if name in ("gpt2_xl", "ragged", "gpt2_xl_shard0of8"):
-        assert info["norm_kept_tiles"] == 0      # reached too late
-    if name == "gpt2_124m":
+    if name == "ragged":
+        # 10.9M elements in tail tiles: 240 MB of element-path traffic
+        assert info["norm_kept_tiles"] == 0
+    if name in ("gpt2_124m", "gpt2_xl", "gpt2_xl_shard0of8"):
         assert 0 < info["norm_kept_tiles"] < info["tiles"]
     if name in ("gpt2_124m_bf16g", "tiny"):
         assert info["norm_kept_tiles"] == info["tiles"]   # all of it fits
     monkeypatch.setenv("MTA_NORM_KEEP_MIB", "0")
     assert M.mta_list_plan(ents, wl.gtype, wl.mkind,
                            wl.vkind)["norm_kept_tiles"] == 0
+
+
+def test_an_unaligned_tensor_turns_the_kept_tiles_off(monkeypatch):
+    # one 100M-element float32 tensor: the norm would keep its last 256 MiB
+    # of gradients.  Aligned, the update takes every tile on the vector
+    # path and the tiles are kept; with m one element off, every tile is on
+    # the element path (28 B per element before the kept ones, far over
+    # 64 MiB) and none is kept.
+    monkeypatch.delenv("MTA_NORM_KEEP_MIB", raising=False)
+    n = 100 * 2**20
+    ok = M.mta_list_plan([tuple(BASE) + (n,)], 0, 0, 0)
+    assert ok["vector_tensors"] == 1
+    assert ok["norm_kept_tiles"] == (256 << 20) // (4096 * 4)
+    off = M.mta_list_plan([(BASE[0], BASE[1], BASE[2] + 4, BASE[3], n)],
+                          0, 0, 0)
+    assert off["vector_tensors"] == 0
+    assert off["norm_kept_tiles"] == 0
+    monkeypatch.setenv("MTA_NORM_KEEP_MIB", "256")      # the budget wins
+    assert M.mta_list_plan([(BASE[0], BASE[1], BASE[2] + 4, BASE[3], n)],
+                           0, 0, 0)["norm_kept_tiles"] == ok["norm_kept_tiles"]
 
 
 def test_plan_reports_the_errors_create_reports():
