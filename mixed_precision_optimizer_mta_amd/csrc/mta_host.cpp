@@ -1074,9 +1074,12 @@ int mta_clip_norm_noalloc(const mta_tensor *tensors, int64_t count,
     e = hipMemcpyAsync(b + off_gt, plan.gtiles.data(),
                        plan.gtiles.size() * sizeof(mta::GradTile),
                        hipMemcpyHostToDevice, s);
-  if (e != hipSuccess)
+  if (e != hipSuccess) {
+    // a copy queued before the failing call still reads the host vectors
+    (void)hipStreamSynchronize(s);
     return fail(MTA_EHIP, "mta_clip_norm_noalloc: staging: %s",
                 hipGetErrorString(e));
+  }
   mta::Work wk{};
   wk.gtiles = reinterpret_cast<const mta::GradTile *>(b + off_gt);
   wk.stiles = nullptr;
@@ -1089,9 +1092,11 @@ int mta_clip_norm_noalloc(const mta_tensor *tensors, int64_t count,
                              nullptr};
   e = mta::launch_sumsq(gtype, wk, scale, max_norm, scr, d_norm, d_coef,
                         nullptr);
-  if (e != hipSuccess)
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(s);  // the copies still read the host vectors
     return fail(MTA_EHIP, "mta_clip_norm_noalloc: launch failed: %s",
                 hipGetErrorString(e));
+  }
   // the staging vectors die with this call, and the next call reuses the
   // scratch: wait for this one's copies and kernel
   e = hipStreamSynchronize(s);
