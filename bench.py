@@ -724,7 +724,9 @@ def main():
             "bytes_per_param": bpp["norm"] + bpp["update"] +
             scale_bytes // wl.n,
             "tiles": info["tiles"], "grid_update": info["grid_update"],
-            "grid_norm": info["grid_norm"], "parallelism": "single GPU",
+            "grid_norm": info["grid_norm"],
+            "norm_kept_tiles": info["norm_kept_tiles"],
+            "parallelism": "single GPU",
             "weight_copy": args.weight_copy,
             "optimizer": args.opt, "zero_grad": bool(args.zero_grad),
             "graph": bool(args.graph),
