@@ -45,9 +45,10 @@
 // buffer, 8 bytes of a 16-bit one, so all buffers share one element mapping)
 // and 16 bytes' worth for the single-buffer kernels.  The tail tile of a
 // tensor, the head tile peeled off a tensor whose buffers reach alignment
-// only after a few elements, and the tiles of a tensor that never does use
-// the same mapping with one-element accesses: loads clamped into the tile
-// and issued before any use, stores masked to the tile.  A lane owns whole elements, so a packed
+// only after a few elements, and the tiles of a tensor that never does take
+// the element path: one-element accesses with consecutive lanes on
+// consecutive elements, loads clamped into the tile and issued before any
+// use, stores masked to the tile.  A lane owns whole elements, so a packed
 // bfloat16 moment is written with 8-byte or 16-bit stores and no 32-bit word
 // is ever shared between lanes (no read-modify-write of a neighbour's half).
 //
@@ -231,6 +232,19 @@ __device__ __forceinline__ float load1_clamped(MTA_GLOBAL const elem_t<D> *p,
                                                uint32_t e, uint32_t lim) {
   const float x = load1<D>(p, e < lim ? e : lim - 1);
   return e < lim ? x : 0.0f;
+}
+
+// This lane's element (j, k) of a tile on the element path, for a kernel
+// whose full tiles give each lane V consecutive elements per group j:
+// consecutive lanes take consecutive elements, so each single-element
+// access instruction of a wave covers one contiguous run and fetches each
+// line once.  (The full tiles' mapping would give such an instruction a
+// V-element stride across the lanes and touch every line V times: the
+// element path then moved its bytes at about half the vector path's rate.)
+// Every index is below kTileElems: j*(kBlock*V) + k*kBlock + lane.
+template <int V>
+__device__ __forceinline__ uint32_t elem_of(int j, int k) {
+  return static_cast<uint32_t>(j * (kBlock * V) + k * kBlock) + threadIdx.x;
 }
 
 // ---------------------------------------------------------------------------
@@ -516,7 +530,7 @@ __device__ __forceinline__ void finish_tile(
 
 template <int R, int G, bool MPacked, bool VPacked>
 __device__ __forceinline__ void partial_tile(
-    const TileRef<G, MPacked, VPacked> &T, uint32_t e0, const StepScalars &sc,
+    const TileRef<G, MPacked, VPacked> &T, const StepScalars &sc,
     float coef) {
   using Ref = TileRef<G, MPacked, VPacked>;
   float w[kAdamGroups][kAdamVec], g[kAdamGroups][kAdamVec],
@@ -525,7 +539,7 @@ __device__ __forceinline__ void partial_tile(
   for (int j = 0; j < kAdamGroups; ++j)
 #pragma unroll
     for (int k = 0; k < kAdamVec; ++k) {
-      const uint32_t e = e0 + j * kAdamStride + k;
+      const uint32_t e = elem_of<kAdamVec>(j, k);
       w[j][k] = load1_clamped<kF32>(T.pw, e, T.lim);
       g[j][k] = load1_clamped<G>(T.pg, e, T.lim);
       if constexpr (kUsesM<R>)
@@ -539,7 +553,7 @@ __device__ __forceinline__ void partial_tile(
     for (int k = 0; k < kAdamVec; ++k) {
       rule_elem<R, MPacked, VPacked>(w[j][k], g[j][k], m[j][k], v[j][k], sc,
                                      coef);
-      const uint32_t e = e0 + j * kAdamStride + k;
+      const uint32_t e = elem_of<kAdamVec>(j, k);
       if (e < T.lim) {
         T.pw[e] = w[j][k];
         if constexpr (kUsesM<R>) store1<Ref::M>(T.pm, e, m[j][k]);
@@ -564,7 +578,7 @@ __device__ __forceinline__ void zero_grad_tile(const StepTile &st,
     for (int j = 0; j < kAdamGroups; ++j)
 #pragma unroll
       for (int k = 0; k < kAdamVec; ++k) {
-        const uint32_t e = e0 + j * kAdamStride + k;
+        const uint32_t e = elem_of<kAdamVec>(j, k);
         if (e < st.lim) zero1<G>(pg, e);
       }
   }
@@ -656,7 +670,7 @@ __device__ __forceinline__ void update_tile(
   if (cur.full)
     finish_tile(X, cur, e0, sc, coef);
   else
-    partial_tile<R>(cur, e0, sc, coef);
+    partial_tile<R>(cur, sc, coef);
 }
 
 // AdamW (L2 = false) and Adam with coupled decay (L2 = true).
@@ -820,7 +834,7 @@ __device__ __forceinline__ void sumsq_walk(
           for (int j = 0; j < G; ++j)
 #pragma unroll
             for (int k = 0; k < V; ++k)
-              x[j][k] = load1_clamped<D>(pg, e0 + j * (kBlock * V) + k, lim);
+              x[j][k] = load1_clamped<D>(pg, elem_of<V>(j, k), lim);
         }
 #pragma unroll
         for (int j = 0; j < G; ++j)
@@ -1019,12 +1033,12 @@ __device__ __forceinline__ void scale_any_tile(const GradTile &tl, uint32_t e0,
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int k = 0; k < V; ++k)
-      x[j][k] = load1_clamped<D>(pg, e0 + j * (kBlock * V) + k, lim);
+      x[j][k] = load1_clamped<D>(pg, elem_of<V>(j, k), lim);
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      const uint32_t e = e0 + j * (kBlock * V) + k;
+      const uint32_t e = elem_of<V>(j, k);
       if (e < lim) {
         const float y = x[j][k] * s;
         if constexpr (D == kF32)
