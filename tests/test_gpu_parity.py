@@ -355,6 +355,23 @@ def test_full_gpt2_124m_bf16_grads_100_steps_every_element():
     assert worst == {"w": 0, "m": 0, "v": 0}, worst
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["gpt2_124m", "gpt2_124m_bf16g",
+                                  "gpt2_xl_shard0of8"])
+def test_full_list_on_the_element_path_every_element(name):
+    # the gradients one element off w, m and v: no tensor can reach the
+    # vector path, so every tile of the full list takes one-element
+    # accesses (the path of tail tiles and unaligned tensors)
+    wl = WL.get(name)
+    arena = WL.Arena(wl, "cuda", g_shift=1)
+    L = make_list(arena)
+    assert L.info()["vector_tensors"] == 0
+    L.close()
+    del arena
+    worst = lockstep(wl, 2, g_shift=1)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+
+
 @pytest.mark.timeout(600)
 def test_full_gpt2_xl_packed_every_element():
     wl = WL.get("gpt2_xl")
