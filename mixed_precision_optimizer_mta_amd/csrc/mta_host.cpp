@@ -31,7 +31,7 @@ struct mta_list {
   uint32_t keep_from = 0;  // first tile the norm reads with allocating loads
   int cus = 1;          // compute units of the device
   int grid_update = 1;  // workgroups of an update launch
-  int grid_norm = 1;    // workgroups of a norm or in-place scale launch
+  int grid_norm = 1;    // workgroups of a norm launch
   int state_buffers = 3;  // bit 0: tensors have m; bit 1: they have v
   bool has_w = true;      // false: a gradient-only list (no w, m, v)
   int vector_tensors = 0;
@@ -88,9 +88,9 @@ bool debug_sync() {
   return on;
 }
 
-// Launch shapes.  A workgroup is four wave64s.  The update kernels launch
-// one workgroup per tile (the hardware hands tiles out in order; see the
-// kernels).  The norm and the in-place scale are persistent grids that walk
+// Launch shapes.  A workgroup is four wave64s.  The update kernels and the
+// in-place scale launch one workgroup per tile (the hardware hands tiles
+// out in order; see the kernels).  The norm is a persistent grid that walks
 // the tile table with a grid stride, two tiles of loads in flight per
 // workgroup: one workgroup per CU for float32 gradients, two for 16-bit
 // ones (half the bytes per tile, so twice the workgroups for the same bytes
@@ -953,8 +953,8 @@ int mta_scale(mta_list *L, float factor, int flags, void *stream) {
   int rc = check_device(L);
   if (rc) return rc;
   if (L->ntiles == 0) return ok();
-  // the norm's grid: the same two-tile walk over the gradient alone
-  const mta::Work wk = work_of(L, L->grid_norm, stream);
+  // one workgroup per gradient tile
+  const mta::Work wk = work_of(L, static_cast<int>(L->ntiles), stream);
   return after_launch(mta::launch_scale(L->gtype, wk, factor, nullptr),
                       wk.stream, "mta_scale");
 }
@@ -967,7 +967,7 @@ int mta_scale_device(mta_list *L, const float *d_factor, void *stream) {
   int rc = check_device(L);
   if (rc) return rc;
   if (L->ntiles == 0) return ok();
-  const mta::Work wk = work_of(L, L->grid_norm, stream);
+  const mta::Work wk = work_of(L, static_cast<int>(L->ntiles), stream);
   return after_launch(mta::launch_scale(L->gtype, wk, 1.0f, d_factor),
                       wk.stream, "mta_scale_device");
 }

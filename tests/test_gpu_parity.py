@@ -231,8 +231,9 @@ def test_in_place_scale_matches_oracle(gtype):
 
 
 @pytest.mark.parametrize("gtype", [0, 1, 2])
-def test_in_place_scale_full_tile_pairs_and_flat_offsets(gtype):
-    # enough tiles that every workgroup walks pairs of full tiles, plus
+def test_in_place_scale_many_tiles_and_flat_offsets(gtype):
+    # over 2,200 tiles, one workgroup each: the runs of 32 tiles per XCD
+    # (the first 2,048 workgroups) and the remainder taken in order, plus
     # tensors at odd flat offsets (peeled heads) and ragged tails; nothing
     # outside the tensors is written
     sizes = [4096 * 2200 + 5, 3, 4096 * 3 + 1, 300]
@@ -247,7 +248,7 @@ def test_in_place_scale_full_tile_pairs_and_flat_offsets(gtype):
     before = arena.g.view(ity).clone()
     gs = oracle_grads(arena)
     L = make_list(arena)
-    assert L.info()["tiles"] > 4 * 512 >= 2 * L.info()["grid_norm"]
+    assert L.info()["tiles"] > 2048 + 100
     for s in (0.3, 2.0 ** 20):
         L.scale(s, defer=False)
         torch.cuda.synchronize()
