@@ -181,7 +181,8 @@ typedef struct {
   int64_t tiles;       /* work tiles (each covers up to tile_elems of one tensor) */
   int32_t tile_elems;  /* elements per tile */
   int32_t grid_update; /* workgroups of an update or in-place scale
-                          launch (one per tile) */
+                          launch: one per tile, at most 16,776,960 per
+                          launch (a longer list takes several launches) */
   int32_t grid_norm;   /* workgroups of a norm launch (= norm partials) */
   int32_t device;      /* HIP device the list lives on */
   int32_t vector_tensors; /* tensors that take the 16-byte vector path

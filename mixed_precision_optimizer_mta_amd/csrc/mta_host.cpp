@@ -31,6 +31,8 @@ struct mta_list {
   uint32_t keep_from = 0;  // first tile the norm reads with allocating loads
   int cus = 1;          // compute units of the device
   int grid_update = 1;  // workgroups of an update launch
+  uint32_t max_grid = mta::kMaxTileGrid;  // most tiles in one per-tile
+                                          // launch
   int grid_norm = 1;    // workgroups of a norm launch
   int state_buffers = 3;  // bit 0: tensors have m; bit 1: they have v
   bool has_w = true;      // false: a gradient-only list (no w, m, v)
@@ -362,7 +364,27 @@ mta::Work work_of(const mta_list *L, int grid, void *stream) {
   w.keep_from = L->keep_from;
   w.grid = grid;
   w.stream = static_cast<hipStream_t>(stream);
+  w.max_grid = L->max_grid;
   return w;
+}
+
+// The per-tile kernels (update, in-place scale) take one workgroup per
+// tile, and one launch holds at most max_grid of them: a longer list is
+// covered by consecutive launches over stretches of its tile table (every
+// tile is independent of the others).  A failing launch stops the rest.
+template <typename Launch>
+hipError_t per_tile_launches(const mta::Work &wk, Launch &&launch) {
+  const uint32_t cap = wk.max_grid ? wk.max_grid : mta::kMaxTileGrid;
+  for (uint32_t base = 0; base < wk.ntiles; base += cap) {  // < 2^31 + cap
+    mta::Work sub = wk;
+    sub.ntiles = std::min(cap, wk.ntiles - base);
+    sub.grid = static_cast<int>(sub.ntiles);
+    sub.stiles = wk.stiles + base;
+    sub.gtiles = wk.gtiles + base;
+    const hipError_t e = launch(sub);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Argument checks of a norm over `nlists` lists (one list: mta_clip_norm).
@@ -528,10 +550,13 @@ int step_common(mta_list *L, const mta_opt *o, int64_t t, const float *d_coef,
   }
   if (L->ntiles > 0) {
     const mta::Work wk = work_of(L, L->grid_update, stream);
-    const hipError_t e = mta::launch_update(o->kind, L->gtype, L->mkind,
-                                            L->vkind, wk, sc, d_coef, amp);
-    if (e != hipSuccess)  // nothing enqueued: a deferred factor stays
-      return after_launch(e, wk.stream, what);
+    const hipError_t e = per_tile_launches(wk, [&](const mta::Work &sub) {
+      return mta::launch_update(o->kind, L->gtype, L->mkind, L->vkind, sub,
+                                sc, d_coef, amp);
+    });
+    // a launch refused (with one launch per list, as below 2^24 tiles,
+    // nothing was enqueued): a deferred factor stays
+    if (e != hipSuccess) return after_launch(e, wk.stream, what);
     if (!d_amp) {
       L->deferred = false;
       L->deferred_s = 1.0f;
@@ -743,7 +768,13 @@ int mta_list_create(const mta_tensor *tensors, int64_t count, int gtype,
       "MTA_NORM_BLOCKS_PER_CU",
       gtype == MTA_F32 ? kNormBlocksPerCuF32 : kNormBlocksPerCu16, 1, 64);
   const int64_t tiles_or_one = std::max<int64_t>(1, L->ntiles);
-  L->grid_update = static_cast<int>(tiles_or_one);  // one per tile
+  // one workgroup per tile, in launches of at most max_grid tiles
+  // (MTA_MAX_TILE_GRID lowers the cap, to exercise several launches)
+  L->max_grid = static_cast<uint32_t>(env_int(
+      "MTA_MAX_TILE_GRID", static_cast<int>(mta::kMaxTileGrid), 1,
+      static_cast<int>(mta::kMaxTileGrid)));
+  L->grid_update = static_cast<int>(
+      std::min<int64_t>(tiles_or_one, static_cast<int64_t>(L->max_grid)));
   L->grid_norm = static_cast<int>(
       std::min<int64_t>(tiles_or_one, static_cast<int64_t>(cus) * bpc_n));
 
@@ -954,8 +985,11 @@ int mta_scale(mta_list *L, float factor, int flags, void *stream) {
   if (rc) return rc;
   if (L->ntiles == 0) return ok();
   // one workgroup per gradient tile
-  const mta::Work wk = work_of(L, static_cast<int>(L->ntiles), stream);
-  return after_launch(mta::launch_scale(L->gtype, wk, factor, nullptr),
+  const mta::Work wk = work_of(L, L->grid_update, stream);
+  return after_launch(per_tile_launches(wk, [&](const mta::Work &sub) {
+                        return mta::launch_scale(L->gtype, sub, factor,
+                                                 nullptr);
+                      }),
                       wk.stream, "mta_scale");
 }
 
@@ -967,8 +1001,11 @@ int mta_scale_device(mta_list *L, const float *d_factor, void *stream) {
   int rc = check_device(L);
   if (rc) return rc;
   if (L->ntiles == 0) return ok();
-  const mta::Work wk = work_of(L, static_cast<int>(L->ntiles), stream);
-  return after_launch(mta::launch_scale(L->gtype, wk, 1.0f, d_factor),
+  const mta::Work wk = work_of(L, L->grid_update, stream);
+  return after_launch(per_tile_launches(wk, [&](const mta::Work &sub) {
+                        return mta::launch_scale(L->gtype, sub, 1.0f,
+                                                 d_factor);
+                      }),
                       wk.stream, "mta_scale_device");
 }
 

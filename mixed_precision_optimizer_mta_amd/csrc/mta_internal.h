@@ -73,6 +73,14 @@ struct StepScalars {
   uint32_t copy_f16;  // weight copies are float16 (else bfloat16)
 };
 
+// Per-tile launches (the update kernels, the in-place scale) give every
+// tile its own workgroup.  The dispatch packet counts a grid's work-items
+// in 32 bits, so one launch of kBlock-thread workgroups holds fewer than
+// 2^24 of them; a list with more tiles is covered by consecutive launches
+// over stretches of its tile table, each at most kMaxTileGrid tiles (whole
+// runs of 256 workgroups).
+constexpr uint32_t kMaxTileGrid = (1u << 24) - 256;
+
 struct Work {
   const GradTile *gtiles;
   const StepTile *stiles;
@@ -80,6 +88,8 @@ struct Work {
   uint32_t keep_from;  // k_sumsq: first tile read with allocating loads
   int grid;
   hipStream_t stream;
+  uint32_t max_grid;   // per-tile launches: most tiles in one launch
+                       // (0: kMaxTileGrid)
 };
 
 // Norm scratch: one float64 partial slot per norm workgroup, then the

@@ -1,5 +1,6 @@
 """GPU invariants of the step beyond element-wise parity: every tile
-updated once at tile counts around the update's dispatch runs, the norm's
+updated once at tile counts around the update's dispatch runs, lists
+longer than one per-tile launch, the norm's
 launch shape changing only its summation order, deferred vs in-place
 unscale on bfloat16 gradients, the independent (non-lockstep) protocol, a
 tensor past 2^32 elements, and an informational cross-check against
@@ -12,7 +13,8 @@ import oracle as O
 from mixed_precision_optimizer_mta_amd import MtaList
 from mixed_precision_optimizer_mta_amd import workloads as WL
 
-from parity_util import compare, lockstep, oracle_grads, oracle_state
+from parity_util import (compare, lockstep, opt_for, oracle_grads,
+                         oracle_state, rule_lockstep)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +113,46 @@ def test_independent_protocol(name):
                 wl.eps, wl.weight_decay, t, s=wl.scale, max_norm=wl.max_norm)
         worst = compare(arena, ost, what=f"{name} independent t={t}")
         assert worst == {"w": 0, "m": 0, "v": 0}, worst
+    L.close()
+
+
+@pytest.mark.parametrize("cap", [1, 256, 300])
+def test_lists_longer_than_one_launch(monkeypatch, cap):
+    # a list with more tiles than one per-tile launch holds (2^24 - 256 of
+    # them) is updated and scaled in consecutive launches over stretches of
+    # its tile table; MTA_MAX_TILE_GRID lowers the cap so that a list of
+    # about 700 tiles takes several (every tile a launch of its own at 1).
+    # Every element against the oracle, for AdamW, Adam with zeroing, a
+    # loss-scaled step and the in-place scale.
+    monkeypatch.setenv("MTA_MAX_TILE_GRID", str(cap))
+    sizes = [4096 * 690 + 5, 3, 4096 * 3 + 1, 300]
+    wl = WL.Workload("chunks", sizes, WL.BF16, WL.MOM_BF16X2, WL.MOM_F32,
+                     steps=2, ident=41)
+    arena = WL.Arena(wl, "cuda")
+    L = _list(arena)
+    info = L.info()
+    assert info["tiles"] == 691 + 1 + 4 + 1
+    assert info["grid_update"] == min(info["tiles"], cap)
+    L.close()
+    del arena
+    worst = lockstep(wl, 2)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+    rule_lockstep(wl, opt_for("adam", True), 2)
+    amp = WL.scaled_down(WL.get("gpt2_124m_f16amp"), sizes, name="chunks_amp")
+    worst = lockstep(amp, 3)
+    assert worst == {"w": 0, "m": 0, "v": 0}, worst
+    # the in-place scale
+    arena = WL.Arena(wl, "cuda")
+    arena.fill_grads(1)
+    gs = oracle_grads(arena)
+    L = _list(arena)
+    for s in (0.3, 2.0 ** 12):
+        L.scale(s, defer=False)
+        torch.cuda.synchronize()
+        for g in gs:
+            O.scale_(g, wl.gtype, s)
+        for a, b in zip(oracle_grads(arena), gs):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
     L.close()
 
 
