@@ -198,6 +198,18 @@ def test_no_decay_loss_scaled(kind):
     L.close()
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind", ["adamw", "adam"])
+def test_no_decay_on_the_full_124m_list(kind):
+    # the GPT-2 biases and layer-norm gains (the 60 tensors under 2^14
+    # elements) flagged, as the 124M benchmark runs them with --no-decay:
+    # every element of the full list against per-tensor oracle steps
+    wl = WL.get("gpt2_124m")
+    flags = [n < (1 << 14) for n in wl.sizes]
+    assert sum(flags) == 60
+    nodecay_lockstep(wl, opt_for(kind), flags, 2)
+
+
 def test_no_decay_argument_checks():
     from mixed_precision_optimizer_mta_amd import MtaError
     wl = WL.Workload("nodecay_args", [9, 4096], 0, 0, 0, steps=1, ident=48)
