@@ -12,8 +12,8 @@ from mixed_precision_optimizer_mta_amd import (AmpState, MtaError,
                                                clip_norm_joint)
 from mixed_precision_optimizer_mta_amd import workloads as WL
 
-from parity_util import (check_norm, compare, make_list, oracle_grads,
-                         oracle_state)
+from parity_util import (check_norm, compare, in_groups, make_list,
+                         oracle_grads, oracle_state)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,47 @@ def test_joint_clip_over_mixed_gradient_types(order):
             O.step_(o, a.wl.gtype, a.wl.mkind, a.wl.vkind, a.wl.lr,
                     a.wl.beta1, a.wl.beta2, a.wl.eps, a.wl.weight_decay, t,
                     s=a.wl.scale, coef=coef)
+            assert compare(a, o) == {"w": 0, "m": 0, "v": 0}
+    for L in lists:
+        L.close()
+
+
+@pytest.mark.timeout(300)
+def test_joint_clip_over_two_full_lists():
+    # the full 124M float32 list and the full 124M bfloat16-gradient list
+    # (its gradients under a deferred 2^-16) clipped as one model: the joint
+    # norm within 1e-6 of the oracle's, and every element of both lists'
+    # updates with the joint coefficient, two steps
+    arenas = []
+    for name in ("gpt2_124m", "gpt2_124m_bf16g"):
+        a = WL.Arena(WL.get(name), "cuda")
+        a.fill_weights()
+        arenas.append(a)
+    lists = [make_list(a) for a in arenas]
+    ost = [oracle_state(a) for a in arenas]
+    nd = torch.zeros(1, device="cuda")
+    cd = torch.zeros(1, device="cuda")
+    for t in (1, 2):
+        parts = []
+        for a, L, o in zip(arenas, lists, ost):
+            a.fill_grads(t)
+            for x, g in zip(o, oracle_grads(a)):
+                x.g = g
+            if a.wl.scale != 1.0:
+                L.scale(a.wl.scale, defer=True)
+            parts.append(([x.g for x in o], a.wl.gtype, a.wl.scale))
+        clip_norm_joint(lists, 1.0, nd, cd)
+        for a, L in zip(arenas, lists):
+            L.adamw_step(a.wl.hparams, t, cd)
+        torch.cuda.synchronize()
+        coef = np.float32(cd.item())
+        check_norm(np.float32(nd.item()), coef, O.joint_norm(parts), 1.0,
+                   f"joint full t={t}")
+        for a, o in zip(arenas, ost):
+            wl = a.wl
+            in_groups(o, lambda grp, wl=wl: O.step_(
+                grp, wl.gtype, wl.mkind, wl.vkind, wl.lr, wl.beta1,
+                wl.beta2, wl.eps, wl.weight_decay, t, s=wl.scale, coef=coef))
             assert compare(a, o) == {"w": 0, "m": 0, "v": 0}
     for L in lists:
         L.close()
