@@ -785,8 +785,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(arena, wl, args.cpu_steps, opt)
         cpu_steps = out["cpu_baseline"]["steps"]
         if not general and not wl.amp and not args.weight_copy:
-            # the GPU machines give one GPU's job 16 cores: the pool takes at
-            # most that many, and no more than this process may use
+            # a one-GPU job is given 16 cores on an MI355X node: the pool
+            # takes at most that many, and no more than this process may use
             try:
                 usable = len(os.sched_getaffinity(0))
             except (AttributeError, OSError):
