@@ -22,8 +22,8 @@ NORM_RTOL = 1e-6
 F32_ULP = 2
 BF16_ULP = 1
 
-# host threads for the oracle's per-tensor work on large lists (the GPU
-# boxes give one GPU's job 16 cores); the oracle is called through ctypes,
+# host threads for the oracle's per-tensor work on large lists (a one-GPU
+# job is given 16 cores on an MI355X node); the oracle is called through ctypes,
 # which releases the GIL, so its calls on disjoint tensors run in parallel
 THREADS = max(1, min(16, os.cpu_count() or 1))
 
